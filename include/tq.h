@@ -1,0 +1,181 @@
+/*
+ * tq.h -- C ABI of libtq: TurboQuant KV-cache compression and compressed-key
+ * attention scoring on AMD Instinct MI355X (gfx950).
+ *
+ * The method (page "turboquant-plus-rs 0.1.0 README", section "Architecture"):
+ *   keys   : rotate each head vector by a random sign diagonal D followed by a
+ *            Walsh-Hadamard transform H, store the norm, quantize every rotated
+ *            coordinate with the (bits-1)-bit Lloyd-Max quantizer of N(0,1),
+ *            then store the 1-bit signs of a Gaussian projection S of the
+ *            residual together with the residual norm (QJL);
+ *   values : the same rotation and a bits-bit Lloyd-Max quantizer only (MSE).
+ * A quantizer is fully determined by (head_dim, bits, projections, seed)
+ * (page "bitpolar 0.3.3 src/kv_cache.rs", KvCacheConfig).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Ownership: the caller owns all memory.  The library allocates nothing
+ *    and keeps no state between calls; calls are thread-safe.
+ *  - Device calls take device pointers and a `stream` (a hipStream_t; NULL is
+ *    the null stream).  They enqueue work and return; argument validation is
+ *    done on the host before anything is enqueued.  A non-zero return means
+ *    nothing was enqueued.
+ *  - Data errors found by kernels are OR-ed into an optional device int32
+ *    status word (`status`, may be NULL): TQ_STATUS_NON_FINITE when an input
+ *    vector holds NaN/Inf or its squared norm exceeds the float32 range (the
+ *    pages' NonFiniteInput), TQ_STATUS_BAD_BLOB when a codebook header does
+ *    not match the call's parameters.  The caller clears it and reads it after
+ *    synchronising.
+ *  - Layouts are dense and row-major unless a stride is given:
+ *      inputs   x   [G][N][head_dim]   (element (g,t,j) at x + g*sx_g + t*sx_n + j)
+ *      records      [G][N][record_bytes/4] uint32 words
+ *      queries  q   [B][H_q][head_dim]
+ *      scores       [B][H_q][T] float32
+ *    Group g uses codebook (g mod n_cb); codebooks are stored back to back with
+ *    stride tq_codebook_bytes().  For a cache [B][H_kv][T] with one codebook
+ *    per kv head, n_cb = H_kv; for [L][H_kv][T] with one per (layer, head),
+ *    n_cb = L*H_kv.
+ *  - Query head hq attends kv head floor(hq * H_kv / H_q) (grouped queries).
+ *
+ * Record layout (canonical, what parity is checked on), little-endian uint32:
+ *   k planes of W = ceil(head_dim/32) words: bit (j mod 32) of word p*W + j/32
+ *     is bit p of the quantizer index of coordinate j   (k = bits-1 for keys,
+ *     k = bits for values);
+ *   keys: ceil(projections/32) sign words, bit i = [(S rho)_i >= 0], unused
+ *     high bits zero;
+ *   float32 norm |x|; keys: float32 residual norm |rho|.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+
+/* Return codes (host side).  Names follow the pages' error enum where one exists
+ * (bitpolar: ZeroDimension, OddDimension, InvalidBitWidth, ZeroProjections,
+ * DimensionMismatch, NonFiniteInput, EmptyInput). */
+enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_ZERO_DIMENSION = -1,      /* head_dim == 0                                   */
+  TQ_ERR_BAD_DIMENSION = -2,       /* head_dim not a power of two in [2, 512]         */
+  TQ_ERR_INVALID_BIT_WIDTH = -3,   /* keys: bits not in [2, 9]; values: not in [1, 8] */
+  TQ_ERR_ZERO_PROJECTIONS = -4,    /* keys with projections == 0                      */
+  TQ_ERR_DIMENSION_MISMATCH = -5,  /* sizes/strides inconsistent (e.g. H_q % H_kv)   */
+  TQ_ERR_NON_FINITE_INPUT = -6,    /* reserved: non-finite data is reported on device */
+  TQ_ERR_EMPTY_INPUT = -7,         /* n_cb == 0 or a size < 0                         */
+  TQ_ERR_NULL = -8,                /* a required pointer is NULL                      */
+  TQ_ERR_BAD_BLOB = -9,            /* blob buffer too small                            */
+  TQ_ERR_HIP = -10,                /* a HIP launch failed                              */
+  TQ_ERR_INVALID_ROLE = -11,       /* role not TQ_ROLE_KEY / TQ_ROLE_VALUE             */
+  TQ_ERR_INVALID_PROJECTIONS = -12,/* projections > 1024                               */
+  TQ_ERR_UNSUPPORTED = -13,        /* dtype or alignment not supported                 */
+};
+
+/* Device status bits (OR-ed into *status). */
+#define TQ_STATUS_NON_FINITE 1
+#define TQ_STATUS_BAD_BLOB 2
+
+enum tq_role {
+  TQ_ROLE_KEY = 0,    /* TurboQuant: (bits-1)-bit Lloyd-Max + 1-bit QJL of the residual */
+  TQ_ROLE_VALUE = 1,  /* MSE only: bits-bit Lloyd-Max                                  */
+};
+
+enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 };
+
+/* Byte size of one codebook blob (multiple of 256; also the stride between
+ * blobs).  0 when the parameters are invalid.  Host only. */
+size_t tq_codebook_bytes(int head_dim, int bits, int projections, int role);
+
+/* Byte size of one record (multiple of 4).  0 when the parameters are invalid. */
+size_t tq_record_bytes(int head_dim, int bits, int projections, int role);
+
+/* Build the quantizer state for (head_dim, bits, projections, seed, role) into
+ * the caller's HOST buffer `blob` of `blob_bytes` >= tq_codebook_bytes():
+ *   64-byte header (magic "TQCB", version, parameters, section offsets),
+ *   float32 Lloyd-Max centroids c[2^k] and thresholds t[2^k - 1] of N(0,1)
+ *     ("Modules" codebook: Lloyd's algorithm, closed form at 1 bit),
+ *   sign-diagonal bits D (bit j set: D_j = -1),
+ *   keys only: S, projections x head_dim binary16, row-major.
+ * D and S come from SplitMix64 counters seeded by `seed` (Box-Muller for S).
+ * For several heads use seed + h, as MultiHeadKvCache::new does.  The caller
+ * uploads the blob.  Host only; deterministic. */
+int tq_make_codebook(int head_dim, int bits, int projections, uint64_t seed, int role,
+                     void* blob, size_t blob_bytes);
+
+/* Encode keys: x [G][N][head_dim] (dtype TQ_F32/TQ_BF16/TQ_F16, strides in
+ * elements; head_dim contiguous) -> records [G][N][tq_record_bytes/4] at `rec`.
+ * (page "bitpolar 0.3.3 src/kv_cache.rs", KvCacheCompressor::push; README
+ * "Architecture" steps 1-2.)  cbs: n_cb key blobs back to back. */
+int tq_encode_keys(int head_dim, int bits, int projections,
+                   const void* cbs, int64_t n_cb,
+                   const void* x, int x_dtype, int64_t G, int64_t N,
+                   int64_t sx_g, int64_t sx_n,
+                   void* rec, int32_t* status, void* stream);
+
+/* Encode values (MSE-only path, README "Architecture", last paragraph). */
+int tq_encode_values(int head_dim, int bits,
+                     const void* cbs, int64_t n_cb,
+                     const void* x, int x_dtype, int64_t G, int64_t N,
+                     int64_t sx_g, int64_t sx_n,
+                     void* rec, int32_t* status, void* stream);
+
+/* Decode value records [G][N] -> out [G][N][head_dim] float32:
+ * x^ = (n/head_dim) * D (H c[idx])  (bitpolar decode_values). */
+int tq_decode_values(int head_dim, int bits,
+                     const void* cbs, int64_t n_cb,
+                     const void* rec, int64_t G, int64_t N,
+                     float* out, int32_t* status, void* stream);
+
+/* Pre-softmax attention scores from compressed keys, without decoding
+ * (bitpolar KvCacheCompressor::attention_scores: estimate(q, k) * scale):
+ *   scores[b][hq][t] = scale * ( (n_t/d) sum_j qt_j c[idx_tj]
+ *                     + sqrt(pi/2)/m * gamma_t * sum_i p_i (2 s_ti - 1) ),
+ * qt = H(D q), p = S qt / sqrt(d), for the kv head of hq.  krec [B][H_kv][T]
+ * records; q [B][H_q][head_dim] (TQ_F32/TQ_BF16/TQ_F16); scale <= 0 means
+ * 1/sqrt(head_dim).  Group (b, h) uses codebook (b*H_kv + h) mod n_cb. */
+int tq_scores(int head_dim, int bits, int projections,
+              const void* cbs, int64_t n_cb,
+              const void* krec, int64_t B, int64_t H_kv, int64_t T,
+              const void* q, int q_dtype, int64_t H_q, float scale,
+              float* scores, int32_t* status, void* stream);
+
+/* Attention output over compressed K and V for one decode step:
+ * o[b][hq] = sum_t softmax_t(scores[b][hq][t]) * x^_t, the values decoded on
+ * the fly (never materialised).  `work` is caller scratch of
+ * tq_attend_workspace_bytes(...) bytes.  Key and value codebooks are separate
+ * arrays (kcbs, vcbs) with their own n_cb. */
+size_t tq_attend_workspace_bytes(int head_dim, int64_t B, int64_t H_q, int64_t T);
+int tq_attend(int head_dim, int k_bits, int v_bits, int projections,
+              const void* kcbs, int64_t n_kcb, const void* vcbs, int64_t n_vcb,
+              const void* krec, const void* vrec, int64_t B, int64_t H_kv, int64_t T,
+              const void* q, int q_dtype, int64_t H_q, float scale,
+              float* out, void* work, size_t work_bytes, int32_t* status, void* stream);
+
+/* Test hook: u = H(D x) (unnormalised rotation) and n = |x| for every vector,
+ * with the D of the group's codebook.  u [G][N][head_dim] f32, norms [G][N] f32. */
+int tq_rotate(int head_dim, int bits, int projections, int role,
+              const void* cbs, int64_t n_cb,
+              const void* x, int x_dtype, int64_t G, int64_t N,
+              int64_t sx_g, int64_t sx_n,
+              float* u, float* norms, void* stream);
+
+/* Memory footprint of a K+V cache of seq_len x layers x kv_heads vectors
+ * (README "Modules" utils; "Compression formats").  out[0] = fp16 bytes,
+ * out[1] = f32 bytes, out[2] = compressed bytes, out[3] = ratio vs fp16
+ * (1.0 when empty).  Host only. */
+int tq_memory_stats(int head_dim, int k_bits, int v_bits, int projections,
+                    int64_t seq_len, int64_t layers, int64_t kv_heads, double out[4]);
+
+/* Human-readable name of a return code. */
+const char* tq_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H */

@@ -1,0 +1,216 @@
+"""ctypes binding of libtq (include/tq.h): argument marshalling only.
+
+Torch tensors supply device memory; the current torch stream of the tensor's
+device is passed as the hipStream_t.  Functions keep the C names.  Errors come
+back as ``TQError`` carrying the C status code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import c_double, c_float, c_int, c_int64, c_size_t, c_uint64, c_void_p
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+ROLE_KEY = 0
+ROLE_VALUE = 1
+F32, BF16, F16 = 0, 1, 2
+STATUS_NON_FINITE = 1
+STATUS_BAD_BLOB = 2
+
+EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encode_keys",
+           "tq_encode_values", "tq_decode_values", "tq_scores", "tq_attend_workspace_bytes",
+           "tq_attend", "tq_rotate", "tq_memory_stats", "tq_status_string"]
+
+_lib = None
+
+
+class TQError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = load().tq_status_string(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{where}: {msg} (code {code})")
+        self.code = code
+
+
+def load() -> ctypes.CDLL:
+    """Load libtq.so (built in-tree by build_lib.build()).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libtq.so not found at {LIB_PATH}; run kv_cache_vector_diag_amd.build_lib.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "tq_codebook_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "tq_record_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+        "tq_make_codebook": (c_int, [c_int, c_int, c_int, c_uint64, c_int, c_void_p, c_size_t]),
+        "tq_encode_keys": (c_int, [c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int, c_int64, c_int64,
+                                   c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_encode_values": (c_int, [c_int, c_int, c_void_p, c_int64, c_void_p, c_int, c_int64, c_int64,
+                                     c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_decode_values": (c_int, [c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p,
+                                     c_void_p, c_void_p]),
+        "tq_scores": (c_int, [c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int64,
+                              c_void_p, c_int, c_int64, c_float, c_void_p, c_void_p, c_void_p]),
+        "tq_attend_workspace_bytes": (c_size_t, [c_int, c_int64, c_int64, c_int64]),
+        "tq_attend": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                              c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float, c_void_p,
+                              c_void_p, c_size_t, c_void_p, c_void_p]),
+        "tq_rotate": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int, c_int64, c_int64,
+                              c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_memory_stats": (c_int, [c_int, c_int, c_int, c_int, c_int64, c_int64, c_int64,
+                                    ctypes.POINTER(c_double)]),
+        "tq_status_string": (ctypes.c_char_p, [c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise TQError(rc, where)
+
+
+# ---------------------------------------------------------------------------
+# host-only calls
+# ---------------------------------------------------------------------------
+def tq_codebook_bytes(head_dim: int, bits: int, projections: int, role: int) -> int:
+    return int(load().tq_codebook_bytes(head_dim, bits, projections, role))
+
+
+def tq_record_bytes(head_dim: int, bits: int, projections: int, role: int) -> int:
+    return int(load().tq_record_bytes(head_dim, bits, projections, role))
+
+
+def tq_make_codebook(head_dim: int, bits: int, projections: int, seed: int, role: int) -> np.ndarray:
+    """One host blob (uint8 array of tq_codebook_bytes)."""
+    lib = load()
+    nbytes = lib.tq_codebook_bytes(head_dim, bits, projections, role)
+    buf = np.zeros(max(int(nbytes), 1), dtype=np.uint8)
+    _check(lib.tq_make_codebook(head_dim, bits, projections, seed & ((1 << 64) - 1), role,
+                                buf.ctypes.data, buf.nbytes), "tq_make_codebook")
+    return buf
+
+
+def make_codebooks(n_cb: int, head_dim: int, bits: int, projections: int, seed: int, role: int,
+                   device=None):
+    """n_cb blobs back to back, blob i seeded with seed + i (wrapping), as a uint8
+    torch tensor on `device` (host numpy array when device is None)."""
+    blobs = np.concatenate([tq_make_codebook(head_dim, bits, projections, seed + i, role)
+                            for i in range(n_cb)])
+    if device is None:
+        return blobs
+    import torch
+    return torch.from_numpy(blobs).to(device)
+
+
+def tq_memory_stats(head_dim: int, k_bits: int, v_bits: int, projections: int, seq_len: int, layers: int,
+                    kv_heads: int) -> dict:
+    out = (c_double * 4)()
+    _check(load().tq_memory_stats(head_dim, k_bits, v_bits, projections, seq_len, layers, kv_heads, out),
+           "tq_memory_stats")
+    return {"orig_fp16_bytes": out[0], "orig_f32_bytes": out[1], "compressed_bytes": out[2],
+            "ratio_vs_fp16": out[3]}
+
+
+# ---------------------------------------------------------------------------
+# device calls (torch tensors)
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}[t.dtype]
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _groups(x, head_dim):
+    """(G, N, sx_g, sx_n) of x viewed as [G][N][head_dim] with a contiguous last dim."""
+    if x.dim() != 3 or x.shape[2] != head_dim or x.stride(2) != 1:
+        raise ValueError(f"expected [G][N][{head_dim}] with contiguous last dim, got {tuple(x.shape)}")
+    return x.shape[0], x.shape[1], x.stride(0), x.stride(1)
+
+
+def tq_encode_keys(cbs, n_cb, x, head_dim, bits, projections, rec=None, status=None):
+    import torch
+    G, N, sg, sn = _groups(x, head_dim)
+    words = tq_record_bytes(head_dim, bits, projections, ROLE_KEY) // 4
+    if rec is None:
+        rec = torch.empty((G, N, words), dtype=torch.int32, device=x.device)
+    _check(load().tq_encode_keys(head_dim, bits, projections, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N,
+                                 sg, sn, _ptr(rec), _ptr(status), _stream(x)), "tq_encode_keys")
+    return rec
+
+
+def tq_encode_values(cbs, n_cb, x, head_dim, bits, rec=None, status=None):
+    import torch
+    G, N, sg, sn = _groups(x, head_dim)
+    words = tq_record_bytes(head_dim, bits, 0, ROLE_VALUE) // 4
+    if rec is None:
+        rec = torch.empty((G, N, words), dtype=torch.int32, device=x.device)
+    _check(load().tq_encode_values(head_dim, bits, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N, sg, sn,
+                                   _ptr(rec), _ptr(status), _stream(x)), "tq_encode_values")
+    return rec
+
+
+def tq_decode_values(cbs, n_cb, rec, head_dim, bits, out=None, status=None):
+    import torch
+    G, N = rec.shape[0], rec.shape[1]
+    if out is None:
+        out = torch.empty((G, N, head_dim), dtype=torch.float32, device=rec.device)
+    _check(load().tq_decode_values(head_dim, bits, _ptr(cbs), n_cb, _ptr(rec), G, N, _ptr(out), _ptr(status),
+                                   _stream(rec)), "tq_decode_values")
+    return out
+
+
+def tq_scores(cbs, n_cb, krec, q, head_dim, bits, projections, scale=0.0, out=None, status=None):
+    """krec [B][H_kv][T][words] (int32 view of uint32), q [B][H_q][head_dim] -> [B][H_q][T] float32."""
+    import torch
+    B, Hkv, T = krec.shape[0], krec.shape[1], krec.shape[2]
+    Hq = q.shape[1]
+    if not q.is_contiguous() or q.shape[0] != B or q.shape[2] != head_dim:
+        raise ValueError("q must be contiguous [B][H_q][head_dim]")
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(load().tq_scores(head_dim, bits, projections, _ptr(cbs), n_cb, _ptr(krec), B, Hkv, T, _ptr(q),
+                            _dtype_code(q), Hq, scale, _ptr(out), _ptr(status), _stream(q)), "tq_scores")
+    return out
+
+
+def tq_attend(kcbs, n_kcb, vcbs, n_vcb, krec, vrec, q, head_dim, k_bits, v_bits, projections, scale=0.0,
+              out=None, work=None, status=None):
+    import torch
+    B, Hkv, T = krec.shape[0], krec.shape[1], krec.shape[2]
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, head_dim), dtype=torch.float32, device=q.device)
+    need = int(load().tq_attend_workspace_bytes(head_dim, B, Hq, T))
+    if work is None:
+        work = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(load().tq_attend(head_dim, k_bits, v_bits, projections, _ptr(kcbs), n_kcb, _ptr(vcbs), n_vcb,
+                            _ptr(krec), _ptr(vrec), B, Hkv, T, _ptr(q), _dtype_code(q), Hq, scale, _ptr(out),
+                            _ptr(work), work.numel(), _ptr(status), _stream(q)), "tq_attend")
+    return out
+
+
+def tq_rotate(cbs, n_cb, x, head_dim, bits, projections, role):
+    import torch
+    G, N, sg, sn = _groups(x, head_dim)
+    u = torch.empty((G, N, head_dim), dtype=torch.float32, device=x.device)
+    norms = torch.empty((G, N), dtype=torch.float32, device=x.device)
+    _check(load().tq_rotate(head_dim, bits, projections, role, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N,
+                            sg, sn, _ptr(u), _ptr(norms), _stream(x)), "tq_rotate")
+    return u, norms

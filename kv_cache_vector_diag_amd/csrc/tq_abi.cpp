@@ -1,0 +1,136 @@
+// extern "C" entry points of libtq that touch the device: host-side argument
+// validation (synchronous, nothing enqueued on error), then dispatch to the
+// kernel launchers.  Contract: include/tq.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/tq.h"
+#include "tq_kernels.h"
+#include "tq_layout.h"
+
+using namespace tq;
+
+namespace {
+
+bool dtype_ok(int dt) { return dt == TQ_F32 || dt == TQ_BF16 || dt == TQ_F16; }
+
+// Checks shared by the encode/rotate entry points.
+int check_input(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
+                int64_t N, int64_t sx_g, int64_t sx_n) {
+  if (n_cb <= 0 || G < 0 || N < 0) return TQ_ERR_EMPTY_INPUT;
+  if (G == 0 || N == 0) return TQ_OK;
+  if (!cbs || !x) return TQ_ERR_NULL;
+  if (!dtype_ok(dtype)) return TQ_ERR_UNSUPPORTED;
+  if ((N > 1 && sx_n < L.d) || (G > 1 && sx_g < L.d) || sx_n < 0 || sx_g < 0) return TQ_ERR_DIMENSION_MISMATCH;
+  return TQ_OK;
+}
+
+int encode_common(int role, int head_dim, int bits, int projections, const void* cbs, int64_t n_cb,
+                  const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec,
+                  int32_t* status, void* stream) {
+  Layout L;
+  int rc = make_layout(head_dim, bits, projections, role, &L);
+  if (rc) return rc;
+  rc = check_input(L, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n);
+  if (rc || G * N == 0) return rc;
+  if (!rec) return TQ_ERR_NULL;
+  CodebookArgs cb = make_cb_args(cbs, n_cb, L);
+  return launch_encode_generic(cb, x, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
+                               static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_encode_keys(int head_dim, int bits, int projections, const void* cbs, int64_t n_cb, const void* x,
+                   int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec, int32_t* status,
+                   void* stream) {
+  return encode_common(TQ_ROLE_KEY, head_dim, bits, projections, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, rec,
+                       status, stream);
+}
+
+int tq_encode_values(int head_dim, int bits, const void* cbs, int64_t n_cb, const void* x, int x_dtype,
+                     int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec, int32_t* status,
+                     void* stream) {
+  return encode_common(TQ_ROLE_VALUE, head_dim, bits, 0, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, rec, status,
+                       stream);
+}
+
+int tq_decode_values(int head_dim, int bits, const void* cbs, int64_t n_cb, const void* rec, int64_t G,
+                     int64_t N, float* out, int32_t* status, void* stream) {
+  Layout L;
+  int rc = make_layout(head_dim, bits, 0, TQ_ROLE_VALUE, &L);
+  if (rc) return rc;
+  if (n_cb <= 0 || G < 0 || N < 0) return TQ_ERR_EMPTY_INPUT;
+  if (G * N == 0) return TQ_OK;
+  if (!cbs || !rec || !out) return TQ_ERR_NULL;
+  CodebookArgs cb = make_cb_args(cbs, n_cb, L);
+  return launch_decode_generic(cb, static_cast<const uint32_t*>(rec), G, N, out, status,
+                               static_cast<hipStream_t>(stream));
+}
+
+int tq_scores(int head_dim, int bits, int projections, const void* cbs, int64_t n_cb, const void* krec,
+              int64_t B, int64_t H_kv, int64_t T, const void* q, int q_dtype, int64_t H_q, float scale,
+              float* scores, int32_t* status, void* stream) {
+  Layout L;
+  int rc = make_layout(head_dim, bits, projections, TQ_ROLE_KEY, &L);
+  if (rc) return rc;
+  if (n_cb <= 0 || B < 0 || H_kv <= 0 || T < 0 || H_q <= 0) return TQ_ERR_EMPTY_INPUT;
+  if (H_q % H_kv) return TQ_ERR_DIMENSION_MISMATCH;
+  if (B * T == 0) return TQ_OK;
+  if (!cbs || !krec || !q || !scores) return TQ_ERR_NULL;
+  if (!dtype_ok(q_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)head_dim);
+  CodebookArgs cb = make_cb_args(cbs, n_cb, L);
+  return launch_scores_generic(cb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q, scale,
+                               scores, status, static_cast<hipStream_t>(stream));
+}
+
+size_t tq_attend_workspace_bytes(int head_dim, int64_t B, int64_t H_q, int64_t T) {
+  (void)head_dim;
+  if (B < 0 || H_q < 0 || T < 0) return 0;
+  return (size_t)(B * H_q * T) * sizeof(float) + 256;
+}
+
+int tq_attend(int head_dim, int k_bits, int v_bits, int projections, const void* kcbs, int64_t n_kcb,
+              const void* vcbs, int64_t n_vcb, const void* krec, const void* vrec, int64_t B, int64_t H_kv,
+              int64_t T, const void* q, int q_dtype, int64_t H_q, float scale, float* out, void* work,
+              size_t work_bytes, int32_t* status, void* stream) {
+  Layout K, V;
+  int rc = make_layout(head_dim, k_bits, projections, TQ_ROLE_KEY, &K);
+  if (rc) return rc;
+  rc = make_layout(head_dim, v_bits, 0, TQ_ROLE_VALUE, &V);
+  if (rc) return rc;
+  if (n_kcb <= 0 || n_vcb <= 0 || B < 0 || H_kv <= 0 || T < 0 || H_q <= 0) return TQ_ERR_EMPTY_INPUT;
+  if (H_q % H_kv) return TQ_ERR_DIMENSION_MISMATCH;
+  if (B == 0) return TQ_OK;
+  if (!kcbs || !vcbs || !q || !out || (T > 0 && (!krec || !vrec || !work))) return TQ_ERR_NULL;
+  if (!dtype_ok(q_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (work_bytes < tq_attend_workspace_bytes(head_dim, B, H_q, T)) return TQ_ERR_DIMENSION_MISMATCH;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* sc = static_cast<float*>(work);
+  CodebookArgs kcb = make_cb_args(kcbs, n_kcb, K);
+  CodebookArgs vcb = make_cb_args(vcbs, n_vcb, V);
+  if (T > 0) {
+    rc = launch_scores_generic(kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q, scale, sc,
+                               status, s);
+    if (rc) return rc;
+  }
+  return launch_attend_generic(vcb, static_cast<const uint32_t*>(vrec), sc, B, H_kv, T, H_q, out, s);
+}
+
+int tq_rotate(int head_dim, int bits, int projections, int role, const void* cbs, int64_t n_cb, const void* x,
+              int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, float* u, float* norms,
+              void* stream) {
+  Layout L;
+  int rc = make_layout(head_dim, bits, projections, role, &L);
+  if (rc) return rc;
+  rc = check_input(L, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n);
+  if (rc || G * N == 0) return rc;
+  if (!u || !norms) return TQ_ERR_NULL;
+  CodebookArgs cb = make_cb_args(cbs, n_cb, L);
+  return launch_rotate_generic(cb, x, x_dtype, G, N, sx_g, sx_n, u, norms, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,90 @@
+// Device-side helpers shared by the libtq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+#include "tq_layout.h"
+
+namespace tq {
+
+// Arguments common to every kernel that reads a codebook array.
+struct CodebookArgs {
+  const uint8_t* cbs;
+  int64_t stride;      // bytes between blobs
+  int64_t n_cb;
+  int d, bits, m, role, k, levels;
+  uint32_t off_c, off_t, off_d, off_s;
+  int plane_words, sign_words, rec_words;
+};
+
+inline CodebookArgs make_cb_args(const void* cbs, int64_t n_cb, const Layout& L) {
+  CodebookArgs a;
+  a.cbs = static_cast<const uint8_t*>(cbs);
+  a.stride = L.total;
+  a.n_cb = n_cb;
+  a.d = L.d; a.bits = L.bits; a.m = L.m; a.role = L.role; a.k = L.k; a.levels = L.levels;
+  a.off_c = L.off_c; a.off_t = L.off_t; a.off_d = L.off_d; a.off_s = L.off_s;
+  a.plane_words = L.plane_words; a.sign_words = L.sign_words; a.rec_words = L.rec_words;
+  return a;
+}
+
+__device__ inline const uint8_t* blob_of(const CodebookArgs& a, int64_t g) {
+  return a.cbs + (g % a.n_cb) * a.stride;
+}
+
+// True when the blob header disagrees with the call's parameters.
+__device__ inline bool blob_mismatch(const CodebookArgs& a, const uint8_t* blob) {
+  const BlobHeader* h = reinterpret_cast<const BlobHeader*>(blob);
+  return h->magic != kBlobMagic || h->version != kBlobVersion || h->head_dim != a.d ||
+         h->bits != a.bits || h->role != a.role || h->projections != a.m;
+}
+
+__device__ inline float bf16_bits_to_float(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ inline float load_elem(const void* x, int dtype, int64_t off) {
+  if (dtype == 1) {
+    return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(x)[off]);
+  } else if (dtype == 2) {
+    return (float)reinterpret_cast<const _Float16*>(x)[off];
+  }
+  return reinterpret_cast<const float*>(x)[off];
+}
+
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ inline float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ inline float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Number of thresholds strictly below z (lower_bound over t[0 .. L-2]).
+__device__ inline int quantize_index(const float* t, int levels, float z) {
+  int lo = 0, n = levels - 1;
+  while (n > 0) {
+    int half = n >> 1;
+    if (t[lo + half] < z) {
+      lo += half + 1;
+      n -= half + 1;
+    } else {
+      n = half;
+    }
+  }
+  return lo;
+}
+
+constexpr float kQjlConst = 1.2533141373155002512f;  // sqrt(pi/2)
+
+}  // namespace tq

@@ -1,0 +1,24 @@
+// Kernel launchers of libtq (host functions defined next to their kernels).
+// Each returns 0 or TQ_ERR_HIP after enqueueing on stream `s`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_device.h"
+
+namespace tq {
+
+int launch_encode_generic(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N,
+                          int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
+int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
+                          int32_t* status, hipStream_t s);
+int launch_rotate_generic(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N,
+                          int64_t sx_g, int64_t sx_n, float* u, float* norms, hipStream_t s);
+int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t B, int64_t Hkv, int64_t T,
+                          const void* q, int q_dtype, int64_t Hq, float scale, float* scores,
+                          int32_t* status, hipStream_t s);
+int launch_attend_generic(const CodebookArgs& vcb, const uint32_t* vrec, const float* scores, int64_t B,
+                          int64_t Hkv, int64_t T, int64_t Hq, float* out, hipStream_t s);
+
+}  // namespace tq

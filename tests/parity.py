@@ -1,0 +1,80 @@
+"""Comparison helpers for GPU-vs-oracle parity (used by the gpu tests).
+
+Tolerances (the benchmark spec): codes and signs bit-exact except coordinates within
+1e-6 of a decision boundary (z within 1e-6 of a threshold; |(S rho)_i| within
+1e-6 gamma of 0); the number of such mismatches must stay below 1e-5 of all
+coordinates; a vector with an excepted index mismatch is left out of the sign,
+norm and score checks.  Rotated vectors and norms: 1e-5 relative.  Scores and
+decoded values: |gpu - oracle| <= 1e-4 + 1e-3 |oracle|.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from oracle import turboquant as tq
+
+BAND = 1e-6
+MISMATCH_FRACTION = 1e-5
+ATOL, RTOL = 1e-4, 1e-3
+
+
+@dataclass
+class RecordReport:
+    vectors: int
+    coords: int
+    idx_mismatch_in_band: int
+    sign_mismatch_in_band: int
+    excluded_vectors: int
+    max_rel_n: float
+    max_rel_gamma: float
+
+
+def compare_records(qz: tq.Quantizer, gpu_rec: np.ndarray, enc: tq.Encoded) -> RecordReport:
+    gpu_rec = np.ascontiguousarray(gpu_rec).view(np.uint32).reshape(-1, qz.words)
+    ok = ~enc.flags
+    g = tq.unpack_record(qz, gpu_rec)
+    o = tq.unpack_record(qz, enc.records)
+    mism = (g.idx != o.idx) & ok[:, None]
+    z = enc.z
+    dist = np.min(np.abs(z[..., None] - qz.t32[None, None, :]), axis=-1) if qz.k > 0 else np.full(z.shape, np.inf)
+    bad = mism & ~(dist < BAND)
+    assert not bad.any(), f"{int(bad.sum())} index mismatches outside the 1e-6 band, first at {np.argwhere(bad)[:5]}"
+    n_idx = int(mism.sum())
+    assert n_idx <= MISMATCH_FRACTION * mism.size, f"{n_idx} in-band index mismatches of {mism.size}"
+    keep = ok & ~mism.any(axis=1)
+    rel_n = np.abs(g.n32 - o.n32)[keep] / np.maximum(np.abs(o.n32[keep]), 1e-30)
+    assert np.all(rel_n <= 1e-5), f"norm rel err {rel_n.max()}"
+    n_sign = 0
+    rel_g = np.zeros(0)
+    if qz.role == tq.ROLE_KEY:
+        smis = (g.signs != o.signs) & keep[:, None]
+        ratio = np.abs(enc.proj) / (math.sqrt(qz.d) * np.maximum(enc.gamma, 1e-300))[:, None]
+        bad = smis & ~(ratio < BAND)
+        assert not bad.any(), f"{int(bad.sum())} sign mismatches outside the band, first at {np.argwhere(bad)[:5]}"
+        n_sign = int(smis.sum())
+        assert n_sign <= MISMATCH_FRACTION * smis.size
+        # unused sign bits are zero on both sides (bit-exact on the sign words of kept vectors)
+        rel_g = np.abs(g.gamma32 - o.gamma32)[keep] / np.maximum(np.abs(o.gamma32[keep]), 1e-30)
+        small = o.gamma32[keep] < 1e-30
+        assert np.all((rel_g <= 1e-5) | small), f"gamma rel err {rel_g.max()}"
+    return RecordReport(gpu_rec.shape[0], int(mism.size), n_idx, n_sign, int((~keep).sum()),
+                        float(rel_n.max(initial=0.0)), float(rel_g.max(initial=0.0)))
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str, atol=ATOL, rtol=RTOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    err = np.abs(gpu - ref)
+    lim = atol + rtol * np.abs(ref)
+    bad = ~(err <= lim)
+    assert not bad.any(), (f"{what}: {int(bad.sum())}/{bad.size} outside tolerance, worst err "
+                           f"{err.max():.3e} at {np.unravel_index(np.argmax(err - lim), err.shape)}")
+
+
+def rec_np(t) -> np.ndarray:
+    """int32 torch records -> uint32 numpy."""
+    return t.detach().cpu().numpy().view(np.uint32)
