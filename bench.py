@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Throughput of the TurboQuant KV-cache hot path on one MI355X.
+
+Default workload (32K-context decode config): 16 sequences x 8 kv heads x
+32768 cached tokens, head_dim 128, bf16 keys encoded as turbo3 (2-bit
+Lloyd-Max + 128 QJL signs, 56-byte records), 32 bf16 query heads (grouped
+4:1) scored from the compressed keys.  One step = encode the whole key cache
++ score every query head against a whole (previously encoded) cache.
+
+Inputs are resident in HBM before timing.  Buffers rotate (2 input caches,
+3 record caches) so that neither kernel reads data the 256 MB memory-side
+cache still holds from the previous launch.  Kernel durations come from HIP
+events on the stream the kernels are launched on.
+
+Prints ONE JSON line.  `--config c2|c4` measures the prefill-encode and the
+long-context attend rows instead (also one line each).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-K score tokens/s + encode GB/s at 32K ctx; % of HBM roofline"
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_vector_diag_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key: str, launches_bytes: float):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel sources changed since the counters were taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data[kernel_key]
+    except (KeyError, ValueError):
+        return None
+    if ent.get("source_sha") != _kernel_sources_sha():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def cpu_baseline_c3(budget_s: float = 15.0) -> dict:
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    whole (sequence, kv-head) groups of 32768 keys, encode + score of the 4
+    query heads of each group, single thread (BLAS limited to 1)."""
+    from threadpoolctl import threadpool_limits
+
+    from kv_cache_vector_diag_amd import inputs
+    from oracle import turboquant as tq
+    T, d, Hkv, Hq_per = 32768, 128, 8, 4
+    with threadpool_limits(1):
+        qzs = tq.quantizers(Hkv, d, 3, 128, 3, tq.ROLE_KEY)
+        q = inputs.exact_values(inputs.to_torch(inputs.queries(3, 16, 32, d), "bf16"))
+        done = 0
+        spent = 0.0
+        while done < 16 and spent < budget_s:
+            g = done
+            K = inputs.exact_values(inputs.to_torch(inputs.kv_normal(3, 128, T, d, groups=[g]), "bf16"))[0]
+            t0 = time.perf_counter()
+            enc = tq.encode(qzs[g % Hkv], K)
+            b, h = divmod(g, Hkv)
+            tq.scores([qzs[g % Hkv]], enc.records[None, None], q[b:b + 1, h * Hq_per:(h + 1) * Hq_per])
+            spent += time.perf_counter() - t0
+            done += 1
+    tokens = done / Hkv * T   # sequence positions fully processed (all kv heads of a position)
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of 128 (sequence, kv-head) groups x {T} keys: encode + score of 4 query "
+                      f"heads each, float64 NumPy, 1 thread, {spent:.1f} s"}
+
+
+def bench_c3(args, torch, b):
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    B, Hkv, Hq, T, d, bits, m, seed = 16, 8, 32, 32768, 128, 3, 128, 3
+    G = B * Hkv
+    words = b.tq_record_bytes(d, bits, m, b.ROLE_KEY) // 4
+    kcb = b.make_codebooks(Hkv, d, bits, m, seed, b.ROLE_KEY, device=dev)
+    K0 = inputs.to_torch(inputs.kv_normal(seed, G, T, d), "bf16", dev)
+    K1 = inputs.to_torch(inputs.kv_normal(seed + 1000, G, T, d), "bf16", dev)
+    Ks = [K0, K1]
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", dev)
+    recs = [torch.empty((G, T, words), dtype=torch.int32, device=dev) for _ in range(3)]
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for i in range(3):
+        b.tq_encode_keys(kcb, Hkv, Ks[i % 2], d, bits, m, rec=recs[i], status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_encode_keys(kcb, Hkv, Ks[i % 2], d, bits, m, rec=recs[i % 3], status=status)
+        if ev:
+            ev[1].record()
+        b.tq_scores(kcb, Hkv, recs[(i + 1) % 3].view(B, Hkv, T, words), q, d, bits, m, out=scores)
+        if ev:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [_events(torch, 3) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0
+    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+
+    enc_bytes = G * T * d * 2 + G * T * words * 4 + kcb.numel()           # 312 B per key + codebooks
+    sc_bytes = G * T * words * 4 + B * Hq * T * 4 + q.numel() * 2 + kcb.numel()  # 56 B + 4 scores per key
+    enc_gbps = enc_bytes / (enc_ms * 1e-3) / 1e9
+    sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
+    tokens = B * T
+    dominant = "encode" if enc_ms >= sc_ms else "score"
+    dom_gbps, dom_bytes = (enc_gbps, enc_bytes) if dominant == "encode" else (sc_gbps, sc_bytes)
+    tr = _traffic(f"{dominant}_c3", dom_bytes)
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "32K-context decode step: encode turbo3 keys + score from compressed keys",
+                   "batch": B, "kv_heads": Hkv, "q_heads": Hq, "ctx": T, "head_dim": d, "key_bits": bits,
+                   "projections": m, "input": "bf16 N(0,1), seed 3", "record_bytes": words * 4},
+        "encode_ms": enc_ms, "encode_GBps": enc_gbps, "encode_frac_hbm": enc_gbps / HBM_PEAK_GBPS,
+        "encode_keys_per_s": G * T / (enc_ms * 1e-3),
+        "score_ms": sc_ms, "score_GBps": sc_gbps, "score_frac_hbm": sc_gbps / HBM_PEAK_GBPS,
+        "score_tokens_per_s": tokens / (sc_ms * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": tr, "kernel": dominant,
+                     "algorithmic_bytes_per_launch": dom_bytes},
+        "roofline_score": {"bound": "hbm", "achieved": sc_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": sc_gbps / HBM_PEAK_GBPS, "traffic": _traffic("score_c3", sc_bytes),
+                           "algorithmic_bytes_per_launch": sc_bytes},
+    }
+    return line
+
+
+def bench_c2(args, torch, b):
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    L, Hkv, T, d, seed = 32, 8, 4096, 128, 1
+    G = L * Hkv
+    kw = b.tq_record_bytes(d, 4, 128, b.ROLE_KEY) // 4
+    vw = b.tq_record_bytes(d, 4, 0, b.ROLE_VALUE) // 4
+    kcb = b.make_codebooks(G, d, 4, 128, seed, b.ROLE_KEY, device=dev)
+    vcb = b.make_codebooks(G, d, 4, 0, seed, b.ROLE_VALUE, device=dev)
+    Kf, Vf, _ = inputs.kv_outliers(seed, G, T, d)
+    K = inputs.to_torch(Kf, "bf16", dev)
+    V = inputs.to_torch(Vf, "bf16", dev)
+    krec = [torch.empty((G, T, kw), dtype=torch.int32, device=dev) for _ in range(2)]
+    vrec = [torch.empty((G, T, vw), dtype=torch.int32, device=dev) for _ in range(2)]
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_encode_keys(kcb, G, K, d, 4, 128, rec=krec[i % 2])
+        if ev:
+            ev[1].record()
+        b.tq_encode_values(vcb, G, V, d, 4, rec=vrec[i % 2])
+        if ev:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [_events(torch, 3) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    v_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    kb = G * T * (d * 2 + kw * 4) + kcb.numel()
+    vb = G * T * (d * 2 + vw * 4) + vcb.numel()
+    return {"metric": "prefill encode GB/s (K turbo4 + V 4-bit)", "value": (kb + vb) / (ms_step * 1e-3) / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic",
+            "config": {"workload": "prefill encode: 32 layers x 8 kv heads x 4096 tokens, d=128, bf16 with "
+                                   "4 outlier channels x8, K b=4 + V 4-bit"},
+            "encode_keys_ms": k_ms, "encode_keys_GBps": kb / (k_ms * 1e-3) / 1e9,
+            "encode_values_ms": v_ms, "encode_values_GBps": vb / (v_ms * 1e-3) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": kb / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": kb / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "traffic": _traffic("encode_c2", kb), "kernel": "encode_keys"}}
+
+
+def bench_c4(args, torch, b):
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    B, Hkv, Hq, T, d, seed = 4, 8, 8, 131072, 128, 4
+    G = B * Hkv
+    kw = b.tq_record_bytes(d, 2, 128, b.ROLE_KEY) // 4
+    vw = b.tq_record_bytes(d, 2, 0, b.ROLE_VALUE) // 4
+    kcb = b.make_codebooks(Hkv, d, 2, 128, seed, b.ROLE_KEY, device=dev)
+    vcb = b.make_codebooks(Hkv, d, 2, 0, seed, b.ROLE_VALUE, device=dev)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_K), "bf16", dev)
+    V = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_V), "bf16", dev)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", dev)
+    krecs = [b.tq_encode_keys(kcb, Hkv, K, d, 2, 128).view(B, Hkv, T, kw) for _ in range(2)]
+    vrecs = [b.tq_encode_values(vcb, Hkv, V, d, 2).view(B, Hkv, T, vw) for _ in range(2)]
+    del K, V
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    work = torch.empty(b.load().tq_attend_workspace_bytes(d, B, Hq, T), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        b.tq_attend(kcb, Hkv, vcb, Hkv, krecs[i % 2], vrecs[i % 2], q, d, 2, 2, 128, out=out, work=work)
+
+    for i in range(args.warmup):
+        step(i)
+    ev = _events(torch, 2)
+    torch.cuda.synchronize()
+    ev[0].record()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    fused_bytes = G * T * (kw + vw) * 4 + q.numel() * 2 + out.numel() * 4
+    return {"metric": "long-context decode step tokens/s (scores -> softmax -> V from compressed K, V)",
+            "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "long-context step: B=4, 8 kv heads, 8 q heads, 131072 tokens, d=128, "
+                                   "turbo2 K + 2-bit V"},
+            "roofline": {"bound": "hbm", "achieved": fused_bytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": fused_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "traffic": _traffic("attend_c4", fused_bytes), "kernel": "attend"}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path runs on a single MI355X); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from kv_cache_vector_diag_amd import binding as b
+    b.load()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4}[args.config]
+    line = fn(args, torch, b)
+    if args.config == "c3":
+        line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_c3()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,430 @@
+// head_dim-128 encode kernels for gfx950 (CDNA4, wave64).
+//
+// Method (page "turboquant-plus-rs 0.1.0 README", "Architecture"): rotate
+// each head vector by D then the Walsh-Hadamard matrix H, quantize every
+// rotated coordinate with the Lloyd-Max quantizer of N(0,1) (keys: bits-1,
+// values: bits), keys additionally keep the signs of a Gaussian projection S
+// of the residual and the residual norm (QJL).  Same device semantics as
+// encode_generic_kernel, restated for throughput:
+//
+//  * One wave encodes a tile of 32 vectors.  Lane l owns vector l%32 and, in
+//    every 32x32 MFMA result, the 16 rows 8i + 4(l/32) + j of each 32-row
+//    tile.
+//  * The rotation u = H (D x) is a dense +-1 contraction: MFMA
+//    v_mfma_f32_32x32x16_bf16 with A = (H D) fragments (exact +-1 in bf16)
+//    and B = the bf16 input itself, so products are exact and only the fp32
+//    accumulation rounds.  (Float32 inputs are split exactly into three bf16
+//    pieces; float16 inputs use the f16 MFMA.)
+//  * |x|^2 is accumulated in float64 from exact pair sums so that the stored
+//    float32 norm is the correctly rounded one (the residual depends on it).
+//  * Quantizer: symmetric codebook, so idx is the sign of u plus the count of
+//    positive thresholds below |u|/|x|; bits are packed in registers.
+//  * Keys: residual w = u - n c[idx] (one fma, then the half's sign), scaled by a
+//    power of two and split into binary16 hi + lo; the QJL projection S w is
+//    two f16 MFMA passes.  The rotation's result layout is used directly as
+//    the projection's B operand: the contraction index is permuted and S's
+//    columns are permuted to match when its fragments are built in LDS.
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+#include "tq_fast.h"
+
+namespace tq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;
+constexpr int kM = 128;
+constexpr int kWaves = 4;
+constexpr int kTile = 32;
+
+struct Enc128Args {
+  const uint8_t* cbs;
+  int64_t stride;
+  int64_t n_cb;
+  const void* x;
+  int64_t G, N, sx_g, sx_n;
+  uint32_t* rec;
+  int32_t* status;
+  int bits, role, rec_words;
+  uint32_t off_c, off_t, off_d, off_s;
+  int64_t tiles_per_group;   // ceil(N / 32)
+  int64_t tiles_per_block;
+  int64_t blocks_per_group;
+};
+
+__device__ inline uint32_t h_sign(int i, int j) { return __popc(i & j) & 1; }
+
+template <typename V>
+__device__ inline V as(u32x4 v) {
+  return __builtin_bit_cast(V, v);
+}
+
+// Build the (H D) A-operand fragments of MFMA#1 in LDS: fragment (M, c) for
+// lane l holds A[32M + l%32][16c + 8(l/32) + e], e = 0..7.
+template <bool F16>
+__device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
+  for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
+    const int lane = f & 63, c = (f >> 6) & 7, M = f >> 9;
+    const int row = 32 * M + (lane & 31);
+    u32x4 v;
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;
+        const uint32_t neg = h_sign(row, col) ^ ((dbits[col >> 5] >> (col & 31)) & 1u);
+        const uint32_t one = F16 ? 0x3C00u : 0x3F80u;
+        word |= (one | (neg << 15)) << (16 * hh);
+      }
+      v[q] = word;
+    }
+    hfrag[f] = v;
+  }
+}
+
+// Coordinate fed by B-operand element e (0..7) of lane half h in projection
+// K-chunk c = 2M + p: the rotation's result row 8i + 4h + j of tile M with
+// i = 2p + e/4, j = e%4.
+__device__ inline int qjl_coord(int c, int h, int e) {
+  const int M = c >> 1, p = c & 1;
+  return 32 * M + 16 * p + 8 * (e >> 2) + 4 * h + (e & 3);
+}
+
+// S fragments (A operand of MFMA#2): fragment (Mp, c), lane l: row 32Mp + l%32,
+// element e: S[row][qjl_coord(c, l/32, e)] as binary16.
+__device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
+  for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
+    const int lane = f & 63, c = (f >> 6) & 7, Mp = f >> 9;
+    const int row = 32 * Mp + (lane & 31);
+    u32x4 v;
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t lo = S[row * kD + qjl_coord(c, lane >> 5, 2 * q)];
+      const uint32_t hi = S[row * kD + qjl_coord(c, lane >> 5, 2 * q + 1)];
+      v[q] = lo | (hi << 16);
+    }
+    sfrag[f] = v;
+  }
+}
+
+__device__ inline double pair_sumsq_bf16(uint32_t w) {
+  s16x2 v = __builtin_bit_cast(s16x2, w);
+  return (double)__builtin_amdgcn_fdot2_f32_bf16(v, v, 0.0f, false);
+}
+
+__device__ inline double pair_sumsq_f16(uint32_t w) {
+  f16x2 v = __builtin_bit_cast(f16x2, w);
+  return (double)__builtin_amdgcn_fdot2(v, v, 0.0f, false);
+}
+
+// bf16 round-to-nearest-even of a float (bit pattern in the low 16 bits).
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <int K, bool KEY, int DT>
+__global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  u32x4* hfrag = reinterpret_cast<u32x4*>(smem);                // 32 KB
+  u32x4* sfrag = reinterpret_cast<u32x4*>(smem + 32768);        // 32 KB (keys)
+  float* consts = reinterpret_cast<float*>(smem + (KEY ? 65536 : 32768));
+
+  constexpr int L = 1 << K;
+  constexpr int NT = L / 2 - 1;  // positive thresholds
+  const int64_t g = blockIdx.x / a.blocks_per_group;
+  const int64_t chunk = blockIdx.x % a.blocks_per_group;
+  const uint8_t* blob = a.cbs + (g % a.n_cb) * a.stride;
+  if (threadIdx.x == 0 && a.status) {
+    const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(blob);
+    if (hd->magic != kBlobMagic || hd->version != kBlobVersion || hd->head_dim != kD || hd->bits != a.bits ||
+        hd->role != a.role || hd->projections != (KEY ? kM : 0))
+      atomicOr(a.status, TQ_STATUS_BAD_BLOB);
+  }
+  build_hfrag<DT == 2>(hfrag, reinterpret_cast<const uint32_t*>(blob + a.off_d));
+  if (KEY) build_sfrag(sfrag, reinterpret_cast<const uint16_t*>(blob + a.off_s));
+  if (threadIdx.x < L / 2) consts[threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_c)[L / 2 + threadIdx.x];
+  if (threadIdx.x < NT) consts[16 + threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_t)[L / 2 + threadIdx.x];
+  __syncthreads();
+
+  float cpos[L / 2];
+#pragma unroll
+  for (int i = 0; i < L / 2; ++i) cpos[i] = consts[i];
+  float tpos[NT > 0 ? NT : 1];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) tpos[i] = consts[16 + i];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, col = lane & 31;
+  const int64_t tile0 = chunk * a.tiles_per_block;
+  const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles_per_group);
+  const uint32_t* xb16 = reinterpret_cast<const uint32_t*>(a.x);
+
+  for (int64_t tile = tile0 + wave; tile < tile_end; tile += kWaves) {
+    const int64_t tok = tile * kTile + col;
+    const bool valid = tok < a.N;
+    const int64_t xoff = g * a.sx_g + (valid ? tok : 0) * a.sx_n;
+
+    // ---- load x (B operand of the rotation), K-chunk c: coords 16c + 8h .. +7
+    u32x4 xb[8];
+    u32x4 xb2[DT == 0 ? 8 : 1], xb3[DT == 0 ? 8 : 1];
+    double ss = 0.0;
+    if (DT == 0) {
+      const float4* xp = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + xoff);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float4 v0 = valid ? xp[4 * c + 2 * h] : make_float4(0, 0, 0, 0);
+        float4 v1 = valid ? xp[4 * c + 2 * h + 1] : make_float4(0, 0, 0, 0);
+        float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        u32x4 p1, p2, p3;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w1 = 0, w2 = 0, w3 = 0;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            float xv = f[2 * q + hh];
+            ss = fma((double)xv, (double)xv, ss);
+            uint32_t b1 = f32_to_bf16_rne(xv);
+            float r1 = xv - __uint_as_float(b1 << 16);
+            uint32_t b2 = f32_to_bf16_rne(r1);
+            float r2 = r1 - __uint_as_float(b2 << 16);
+            uint32_t b3 = f32_to_bf16_rne(r2);
+            w1 |= b1 << (16 * hh);
+            w2 |= b2 << (16 * hh);
+            w3 |= b3 << (16 * hh);
+          }
+          p1[q] = w1; p2[q] = w2; p3[q] = w3;
+        }
+        xb[c] = p1; xb2[c] = p2; xb3[c] = p3;
+      }
+    } else {
+      const u32x4* xp = reinterpret_cast<const u32x4*>(xb16 + xoff / 2);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) xb[c] = valid ? xp[2 * c + h] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ss += DT == 1 ? pair_sumsq_bf16(xb[c][q]) : pair_sumsq_f16(xb[c][q]);
+    }
+
+    // ---- rotation on MFMA
+    f32x16 u[4];
+#pragma unroll
+    for (int M = 0; M < 4; ++M) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const u32x4 hf = hfrag[(M * 8 + c) * 64 + lane];
+        if (DT == 2) {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(hf), as<f16x8>(xb[c]), acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb[c]), acc, 0, 0, 0);
+          if (DT == 0) {
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb2[c]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb3[c]), acc, 0, 0, 0);
+          }
+        }
+      }
+      u[M] = acc;
+      __builtin_amdgcn_sched_barrier(0);   // keep one tile row of fragments live at a time
+    }
+
+    // ---- norm (float64, both halves of the vector)
+    {
+      uint32_t lo = __double2loint(ss), hi = __double2hiint(ss);
+      auto plo = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+      auto phi = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+      const uint32_t olo = h ? plo[0] : plo[1], ohi = h ? phi[0] : phi[1];
+      ss += __hiloint2double((int)ohi, (int)olo);
+    }
+    const bool finite = ss <= 3.4028234663852886e38;
+    if (a.status && __ballot(valid && !finite && h == 0) != 0 && lane == 0) atomicOr(a.status, TQ_STATUS_NON_FINITE);
+    const float n32 = (float)sqrt(ss);
+    const float inv = n32 > 0.0f ? 1.0f / n32 : 0.0f;
+    // power-of-two scale that brings the residual to O(1) for the f16 split
+    const uint32_t nexp = (__float_as_uint(n32) >> 23) & 0xFFu;
+    const float sc = (n32 > 0.0f && nexp < 253u) ? __uint_as_float((254u - nexp) << 23) : 1.0f;
+
+    // ---- quantize, pack planes, residual
+    uint32_t planes[K][4];
+#pragma unroll
+    for (int p = 0; p < K; ++p)
+#pragma unroll
+      for (int M = 0; M < 4; ++M) planes[p][M] = 0;
+    u32x4 whi[KEY ? 8 : 1], wlo[KEY ? 8 : 1];
+#pragma unroll
+    for (int c = 0; c < (KEY ? 8 : 1); ++c) whi[c] = wlo[c] = u32x4{0, 0, 0, 0};
+    float wsq = 0.0f;
+#pragma unroll
+    for (int M = 0; M < 4; ++M) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = r >> 2, j = r & 3;
+        const int b = 8 * i + 4 * h + j;   // bit position inside word M
+        const float uu = u[M][r];
+        const float z = uu * inv;
+        const float az = fabsf(z);
+        int cnt = 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) cnt += az > tpos[t] ? 1 : 0;
+        const bool pos = z > 0.0f;
+        const int idx = pos ? (L / 2 + cnt) : (L / 2 - 1 - cnt);
+#pragma unroll
+        for (int p = 0; p < K; ++p) planes[p][M] |= (uint32_t)((idx >> p) & 1) << b;
+        if (KEY) {
+          float mag = cpos[0];
+#pragma unroll
+          for (int t = 1; t < L / 2; ++t) mag = cnt >= t ? cpos[t] : mag;
+          // w = u - n c[idx] = (+-)(|u| - n mag), the sign being the quantizer's
+          // half (z > 0 or not), which also covers u = -0 / +0
+          const float rr = fmaf(-n32, mag, fabsf(uu));
+          const float w = pos ? rr : -rr;
+          wsq = fmaf(w, w, wsq);
+          const float ws = w * sc;
+          const _Float16 hv = (_Float16)ws;
+          const _Float16 lv = (_Float16)(ws - (float)hv);
+          // B operand of projection chunk c = 2M + p, element e = 4(i - 2p) + j
+          const int c = 2 * M + (i >> 1);
+          const int e = 4 * (i & 1) + j;
+          const uint32_t hb = __builtin_bit_cast(uint16_t, hv), lb = __builtin_bit_cast(uint16_t, lv);
+          if (e & 1) {
+            whi[c][e >> 1] |= hb << 16;
+            wlo[c][e >> 1] |= lb << 16;
+          } else {
+            whi[c][e >> 1] = hb;
+            wlo[c][e >> 1] = lb;
+          }
+        }
+      }
+    }
+
+    // ---- QJL projection on MFMA (keys)
+    uint32_t signs[4] = {0, 0, 0, 0};
+    float gam = 0.0f;
+    if (KEY) {
+#pragma unroll
+      for (int Mp = 0; Mp < 4; ++Mp) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4 sf = sfrag[(Mp * 8 + c) * 64 + lane];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(whi[c]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(wlo[c]), acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int b = 8 * (r >> 2) + 4 * h + (r & 3);
+          signs[Mp] |= (acc[r] >= 0.0f ? 1u : 0u) << b;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq), __float_as_uint(wsq), false, false);
+      const float tot = __uint_as_float(pg[0]) + __uint_as_float(pg[1]);
+      gam = sqrtf(tot) * 0.08838834764831845f;   // |w| / sqrt(128)
+    }
+
+    // ---- combine the two halves of every word and store the record
+    constexpr int R = KEY ? (K * 4 + 4 + 2) : (K * 4 + 1);
+    uint32_t words[R];
+#pragma unroll
+    for (int p = 0; p < K; ++p)
+#pragma unroll
+      for (int M = 0; M < 4; ++M) {
+        auto pw = __builtin_amdgcn_permlane32_swap(planes[p][M], planes[p][M], false, false);
+        words[p * 4 + M] = pw[0] | pw[1];
+      }
+    if (KEY) {
+#pragma unroll
+      for (int Mp = 0; Mp < 4; ++Mp) {
+        auto pw = __builtin_amdgcn_permlane32_swap(signs[Mp], signs[Mp], false, false);
+        words[K * 4 + Mp] = pw[0] | pw[1];
+      }
+      words[K * 4 + 4] = __float_as_uint(n32);
+      words[K * 4 + 5] = __float_as_uint(gam);
+    } else {
+      words[K * 4] = __float_as_uint(n32);
+    }
+    if (valid) {
+      uint32_t* out = a.rec + (g * a.N + tok) * R;
+#pragma unroll
+      for (int q = 0; q < (R + 1) / 2; ++q) {
+        const int wi = 2 * q + h;
+        if (wi < R) out[wi] = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
+      }
+    }
+  }
+}
+
+template <int K, bool KEY, int DT>
+int launch_one(const Enc128Args& a, hipStream_t s) {
+  const size_t lds = (KEY ? 65536 : 32768) + 128;
+  static bool attr_set = false;   // idempotent; a race only repeats the call
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_kernel<K, KEY, DT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return -10;
+    attr_set = true;
+  }
+  const int64_t blocks = a.G * a.blocks_per_group;
+  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT>), dim3((unsigned)blocks), dim3(256), lds, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+template <int K, bool KEY>
+int launch_dt(const Enc128Args& a, int dt, hipStream_t s) {
+  if (dt == TQ_BF16) return launch_one<K, KEY, 1>(a, s);
+  if (dt == TQ_F16) return launch_one<K, KEY, 2>(a, s);
+  return launch_one<K, KEY, 0>(a, s);
+}
+
+}  // namespace
+
+bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n) {
+  if (L.d != kD) return false;
+  if (L.role == TQ_ROLE_KEY && (L.m != kM || L.k < 1 || L.k > 3)) return false;
+  if (L.role == TQ_ROLE_VALUE && (L.k < 1 || L.k > 4)) return false;
+  const int esz = dtype == TQ_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || ((sx_g * esz) & 15) || ((sx_n * esz) & 15)) return false;
+  return true;
+}
+
+int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
+                          int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s) {
+  Enc128Args a;
+  a.cbs = static_cast<const uint8_t*>(cbs);
+  a.stride = L.total;
+  a.n_cb = n_cb;
+  a.x = x;
+  a.G = G; a.N = N; a.sx_g = sx_g; a.sx_n = sx_n;
+  a.rec = rec;
+  a.status = status;
+  a.bits = L.bits; a.role = L.role; a.rec_words = L.rec_words;
+  a.off_c = L.off_c; a.off_t = L.off_t; a.off_d = L.off_d; a.off_s = L.off_s;
+  a.tiles_per_group = (N + kTile - 1) / kTile;
+  // ~2048 blocks in total, at least 8 tiles per wave, never more than the group holds
+  int64_t per_block = (a.tiles_per_group * G + 2047) / 2048;
+  per_block = per_block < 4 * 8 ? 4 * 8 : per_block;
+  per_block = (per_block + 3) / 4 * 4;
+  if (per_block > a.tiles_per_group) per_block = (a.tiles_per_group + 3) / 4 * 4;
+  a.tiles_per_block = per_block;
+  a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
+  const bool key = L.role == TQ_ROLE_KEY;
+  switch (L.k * 2 + (key ? 1 : 0)) {
+    case 1 * 2 + 1: return launch_dt<1, true>(a, dtype, s);
+    case 2 * 2 + 1: return launch_dt<2, true>(a, dtype, s);
+    case 3 * 2 + 1: return launch_dt<3, true>(a, dtype, s);
+    case 1 * 2: return launch_dt<1, false>(a, dtype, s);
+    case 2 * 2: return launch_dt<2, false>(a, dtype, s);
+    case 3 * 2: return launch_dt<3, false>(a, dtype, s);
+    case 4 * 2: return launch_dt<4, false>(a, dtype, s);
+    default: return -13;
+  }
+}
+
+}  // namespace tq
