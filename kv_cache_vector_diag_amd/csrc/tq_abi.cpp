@@ -85,6 +85,9 @@ int tq_scores(int head_dim, int bits, int projections, const void* cbs, int64_t 
   if (!cbs || !krec || !q || !scores) return TQ_ERR_NULL;
   if (!dtype_ok(q_dtype)) return TQ_ERR_UNSUPPORTED;
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)head_dim);
+  if (fast128_scores_supported(L, H_kv, H_q))
+    return launch_scores_fast128(L, cbs, n_cb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q,
+                                 scale, scores, status, static_cast<hipStream_t>(stream));
   CodebookArgs cb = make_cb_args(cbs, n_cb, L);
   return launch_scores_generic(cb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q, scale,
                                scores, status, static_cast<hipStream_t>(stream));
@@ -117,8 +120,11 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections, const void*
   CodebookArgs kcb = make_cb_args(kcbs, n_kcb, K);
   CodebookArgs vcb = make_cb_args(vcbs, n_vcb, V);
   if (T > 0) {
-    rc = launch_scores_generic(kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q, scale, sc,
-                               status, s);
+    rc = fast128_scores_supported(K, H_kv, H_q)
+             ? launch_scores_fast128(K, kcbs, n_kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype,
+                                     H_q, scale, sc, status, s)
+             : launch_scores_generic(kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q, scale,
+                                     sc, status, s);
     if (rc) return rc;
   }
   return launch_attend_generic(vcb, static_cast<const uint32_t*>(vrec), sc, B, H_kv, T, H_q, out, s);

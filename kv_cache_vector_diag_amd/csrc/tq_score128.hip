@@ -1,0 +1,330 @@
+// head_dim-128 scoring from compressed keys for gfx950 (CDNA4, wave64).
+//
+// Score of query head hq against key t (page "bitpolar 0.3.3
+// src/kv_cache.rs", attention_scores: inner-product estimate times
+// 1/sqrt(head_dim); page "turboquant-plus-rs 0.1.0 README", "Architecture":
+// MSE stage + QJL residual correction):
+//   s = scale * ( (n_t/d) sum_j qt_j c[idx_tj] + sqrt(pi/2)/m gamma_t sum_i p_i (2 s_ti - 1) ),
+//   qt = H(D q), p = S qt / sqrt(d).
+// No key is decoded.  The Lloyd-Max codebook is symmetric, so with
+// sigma_p = 2 b_p - 1 (b_p = bit-plane p of idx)
+//   c[idx] = sum over odd subsets P of planes of a_P * prod_{p in P} sigma_p,
+// and prod_{p in P} sigma_p = 2 (XOR of the planes in P) - 1.  Both sums
+// are then subset sums over bit masks of the record:
+//   sum_j qt_j c[idx_j] = sum_P sum_{j in mask_P} 2 a_P qt_j - c_max sum_j qt_j
+//   sum_i p_i (2 s_i - 1) = sum_{i in signs} 2 p_i - sum_i p_i.
+// They run as int8 MFMA (v_mfma_i32_32x32x32_i8): B = mask bits expanded by
+// one AND per dword (bytes in {0, 2^e}, e = bit offset in the byte), A = the
+// query-side values 2 a_P qt_j and 2 p_i in 32-bit fixed point, split into 4
+// signed int8 limbs and pre-divided by 2^e.  A rows: 4 query heads x
+// {mse part, qjl part} x 4 limbs.  Integer accumulation is exact; only the
+// fixed-point rounding of the query side (2^-23 of its largest entry, or
+// less) enters the score.
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+#include "tq_fast.h"
+
+namespace tq {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 128;
+constexpr int kM = 128;
+constexpr int kBlock = 256;
+
+struct Score128Args {
+  const uint8_t* cbs;
+  int64_t stride, n_cb;
+  const uint32_t* krec;
+  int64_t B, Hkv, T, Hq;
+  const void* q;
+  int q_dtype;
+  float scale;
+  float* scores;
+  int32_t* status;
+  int bits, rec_words, gq;   // gq = query heads per kv head (1, 2 or 4)
+  uint32_t off_c, off_d, off_s;
+  int64_t tiles, tiles_per_block, blocks_per_group;
+};
+
+// Number of odd subsets of k planes = 2^(k-1) mask words sets; plus signs.
+template <int K>
+struct Masks {
+  static constexpr int kPlaneMasks = 1 << (K - 1);
+  static constexpr int kMasks = kPlaneMasks + 1;
+  static constexpr int kWords = 4 * kMasks;      // 32-bit words per key fed to MFMA
+  static constexpr int kMfma = 2 * kWords / 2;   // each word feeds 2 MFMAs, 2 words per MFMA
+};
+
+// Odd subsets of {0..K-1} in a fixed order: for K=1 {0}; K=2 {0},{1};
+// K=3 {0},{1},{2},{0,1,2}.
+template <int K>
+__device__ __host__ constexpr int subset_bits(int s) {
+  return K == 1 ? 1 : K == 2 ? (1 << s) : (s < 3 ? (1 << s) : 7);
+}
+
+template <int K>
+__global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
+  using Mk = Masks<K>;
+  constexpr int L = 1 << K;
+  constexpr int NMF = Mk::kMfma;                 // MFMAs per tile
+  __shared__ float qt[4][kD];
+  __shared__ float pp[4][kM];
+  __shared__ float vmax[4][2];
+  __shared__ float consts[4][4];                 // per head: delta_mse, delta_qjl, C_mse, C_qjl
+  __shared__ float coef[8];                      // a_P
+  __shared__ __align__(16) i32x4 afrag[NMF * 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t grp = blockIdx.x / a.blocks_per_group;      // (b, kv head)
+  const int64_t chunk = blockIdx.x % a.blocks_per_group;
+  const int64_t b = grp / a.Hkv, hkv = grp % a.Hkv;
+  const uint8_t* blob = a.cbs + (grp % a.n_cb) * a.stride;
+  if (tid == 0 && a.status) {
+    const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(blob);
+    if (hd->magic != kBlobMagic || hd->version != kBlobVersion || hd->head_dim != kD || hd->bits != a.bits ||
+        hd->role != TQ_ROLE_KEY || hd->projections != kM)
+      atomicOr(a.status, TQ_STATUS_BAD_BLOB);
+  }
+  const float* cent = reinterpret_cast<const float*>(blob + a.off_c);
+  const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob + a.off_d);
+  const _Float16* S = reinterpret_cast<const _Float16*>(blob + a.off_s);
+
+  // ---- prologue: rotated queries, projected queries, fixed-point fragments
+  if (tid < Mk::kPlaneMasks) {
+    // a_P = (1/L) sum_v c_v prod_{p in P} sigma_p(v)
+    const int sb = subset_bits<K>(tid);
+    double acc = 0.0;
+    for (int v = 0; v < L; ++v) {
+      const int par = __popc(~v & sb) & 1;       // number of -1 factors
+      acc += par ? -(double)cent[v] : (double)cent[v];
+    }
+    coef[tid] = (float)(acc / L);
+  }
+  for (int e = tid; e < 4 * kD; e += kBlock) {
+    const int hh = e >> 7, j = e & 127;
+    float v = 0.0f;
+    if (hh < a.gq) {
+      const int64_t off = ((b * a.Hq) + hkv * a.gq + hh) * kD + j;
+      v = load_elem(a.q, a.q_dtype, off);
+      if ((dbits[j >> 5] >> (j & 31)) & 1u) v = -v;
+    }
+    qt[hh][j] = v;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < kD; hs <<= 1) {
+    for (int p = tid; p < 4 * kD / 2; p += kBlock) {
+      const int hh = p >> 6, pr = p & 63;
+      const int i = (pr / hs) * 2 * hs + (pr % hs);
+      const float x0 = qt[hh][i], x1 = qt[hh][i + hs];
+      qt[hh][i] = x0 + x1;
+      qt[hh][i + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < 4 * kM; e += kBlock) {
+    const int hh = e >> 7, i = e & 127;
+    float acc = 0.0f;
+    const _Float16* row = S + i * kD;
+    for (int j = 0; j < kD; ++j) acc = fmaf((float)row[j], qt[hh][j], acc);
+    pp[hh][i] = acc * 0.08838834764831845f;     // 1/sqrt(128)
+  }
+  __syncthreads();
+  if (wave < 4) {
+    // per head: largest |2 a_P qt_j| and |2 p_i|, and the constant terms
+    const int hh = wave;
+    float amax = 0.0f;
+    for (int s = 0; s < Mk::kPlaneMasks; ++s) amax = fmaxf(amax, fabsf(coef[s]));
+    float m1 = 0.0f, m2 = 0.0f, s1 = 0.0f, s2 = 0.0f;
+    for (int j = lane; j < kD; j += 64) {
+      m1 = fmaxf(m1, fabsf(qt[hh][j]));
+      m2 = fmaxf(m2, fabsf(pp[hh][j]));
+      s1 += qt[hh][j];
+      s2 += pp[hh][j];
+    }
+    m1 = wave_max_f32(m1);
+    m2 = wave_max_f32(m2);
+    s1 = wave_sum_f32(s1);
+    s2 = wave_sum_f32(s2);
+    if (lane == 0) {
+      vmax[hh][0] = 2.0f * amax * m1;
+      vmax[hh][1] = 2.0f * m2;
+      consts[hh][2] = cent[L - 1] * s1;          // c_max * sum qt
+      consts[hh][3] = s2;                        // sum p
+    }
+  }
+  __syncthreads();
+  if (tid < 8) {
+    const int hh = tid >> 1, part = tid & 1;
+    const float vm = vmax[hh][part];
+    consts[hh][part] = vm > 0.0f ? vm * (1.0f / 1073741824.0f) : 1.0f;   // value of one unit, 2^30 units max
+  }
+  __syncthreads();
+  // A fragment of MFMA f = 2*w2 + g, lane l: row m = l%32, K = 16(l/32) + 4q + byte.
+  // Lane half hl of MFMA (w2, g) carries list word 2*w2 + hl; bit (8*byte + 4g + q)
+  // of that word, pre-divided by 2^(4g+q) (-128 for the top bit).
+  for (int idx = tid; idx < NMF * 64 * 16; idx += kBlock) {
+    const int ent = idx & 15, ln = (idx >> 4) & 63, f = idx >> 10;
+    const int w2 = f >> 1, g = f & 1;
+    const int m = ln & 31, hl = ln >> 5;
+    const int q = ent >> 2, byt = ent & 3;
+    const int li = 2 * w2 + hl;                 // list word: mask li/4, word li%4
+    const int mask = li >> 2, ww = li & 3;
+    const int hh = m >> 3, part = (m >> 2) & 1, limb = m & 3;
+    const int bitpos = 8 * byt + 4 * g + q;
+    const int jj = 32 * ww + bitpos;             // coordinate or projection index
+    int v8 = 0;
+    const bool is_sign_mask = mask == Mk::kPlaneMasks;
+    if (hh < a.gq && part == (is_sign_mask ? 1 : 0)) {
+      const float val = is_sign_mask ? 2.0f * pp[hh][jj] : 2.0f * coef[mask] * qt[hh][jj];
+      const int sh = 4 * g + q;
+      const float div = sh == 7 ? -128.0f : (float)(1 << sh);
+      const double units = (double)val / ((double)consts[hh][part] * (double)div);
+      int V = (int)rint(units);
+      int l0 = (int)(signed char)(V & 0xFF);
+      int r = (V - l0) >> 8;
+      int l1 = (int)(signed char)(r & 0xFF);
+      r = (r - l1) >> 8;
+      int l2 = (int)(signed char)(r & 0xFF);
+      int l3 = (r - l2) >> 8;
+      v8 = limb == 0 ? l0 : limb == 1 ? l1 : limb == 2 ? l2 : l3;
+    }
+    reinterpret_cast<signed char*>(afrag)[((f * 64 + ln) * 16) + ent] = (signed char)v8;
+  }
+  __syncthreads();
+
+  i32x4 A[NMF];
+#pragma unroll
+  for (int f = 0; f < NMF; ++f) A[f] = afrag[f * 64 + lane];
+  float dmse[4], dqjl[4], cmse[4], cqjl[4];
+#pragma unroll
+  for (int hh = 0; hh < 4; ++hh) {
+    dmse[hh] = consts[hh][0];
+    dqjl[hh] = consts[hh][1];
+    cmse[hh] = consts[hh][2];
+    cqjl[hh] = consts[hh][3];
+  }
+
+  const int h = lane >> 5, col = lane & 31;
+  const int R = a.rec_words;
+  const float kqjl = kQjlConst / (float)kM;
+  const float inv_d = 1.0f / (float)kD;
+  const int64_t tile0 = chunk * a.tiles_per_block;
+  const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles);
+  for (int64_t tile = tile0 + wave; tile < tile_end; tile += 4) {
+    const int64_t tok = tile * 32 + col;
+    const bool valid = tok < a.T;
+    const uint32_t* r = a.krec + (grp * a.T + (valid ? tok : 0)) * R;
+    uint32_t wv[Mk::kWords / 2];
+#pragma unroll
+    for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
+      const int li = 2 * w2 + h, mask = li >> 2, ww = li & 3;
+      uint32_t word;
+      if (mask == Mk::kPlaneMasks) {
+        word = r[K * 4 + ww];
+      } else {
+        const int sb = subset_bits<K>(mask);
+        word = 0;
+#pragma unroll
+        for (int p = 0; p < K; ++p)
+          if ((sb >> p) & 1) word ^= r[p * 4 + ww];
+      }
+      wv[w2] = valid ? word : 0u;
+    }
+    const float nrm = valid ? __uint_as_float(r[K * 4 + 4]) : 0.0f;
+    const float gam = valid ? __uint_as_float(r[K * 4 + 5]) : 0.0f;
+
+    i32x16 acc = {};
+#pragma unroll
+    for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        i32x4 bv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bv[q] = (int)(wv[w2] & (0x01010101u << (4 * g + q)));
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[2 * w2 + g], bv, acc, 0, 0, 0);
+      }
+    }
+    // rows 8*hh + 4*h + limb: this lane holds part h (0: mse, 1: qjl) of heads 0..3
+    float part[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh)
+      part[hh] = (float)acc[4 * hh] + 256.0f * (float)acc[4 * hh + 1] + 65536.0f * (float)acc[4 * hh + 2] +
+                 16777216.0f * (float)acc[4 * hh + 3];
+    // lane half 0 finishes heads 0,1; half 1 heads 2,3 (swap the parts they lack)
+    // permlane32_swap(x, y): lanes 0-31 get x of lanes 32-63 in [1]; lanes 32-63 get y of lanes 0-31 in [0]
+    auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+    auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+    // after the swap: half 0 holds (mse0, mse1) own + (qjl0, qjl1) received;
+    //                 half 1 holds (qjl2, qjl3) own + (mse2, mse3) received
+    float mse_a, mse_b, qjl_a, qjl_b;
+    if (h == 0) {
+      mse_a = part[0]; mse_b = part[1];
+      qjl_a = __uint_as_float(s0[1]); qjl_b = __uint_as_float(s1[1]);
+    } else {
+      qjl_a = part[2]; qjl_b = part[3];
+      mse_a = __uint_as_float(s0[0]); mse_b = __uint_as_float(s1[0]);
+    }
+    const int ha = 2 * h, hb = 2 * h + 1;
+    const float sa = a.scale * ((nrm * inv_d) * (dmse[ha] * mse_a - cmse[ha]) +
+                                kqjl * gam * (dqjl[ha] * qjl_a - cqjl[ha]));
+    const float sb2 = a.scale * ((nrm * inv_d) * (dmse[hb] * mse_b - cmse[hb]) +
+                                 kqjl * gam * (dqjl[hb] * qjl_b - cqjl[hb]));
+    if (valid) {
+      const int64_t base = (b * a.Hq + hkv * a.gq) * a.T + tok;
+      if (ha < a.gq) a.scores[base + ha * a.T] = sa;
+      if (hb < a.gq) a.scores[base + hb * a.T] = sb2;
+    }
+  }
+}
+
+template <int K>
+int launch_k(const Score128Args& a, hipStream_t s) {
+  const int64_t blocks = a.B * a.Hkv * a.blocks_per_group;
+  hipLaunchKernelGGL(score128_kernel<K>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+}  // namespace
+
+bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq) {
+  if (L.d != kD || L.m != kM || L.k < 1 || L.k > 3) return false;
+  const int64_t gq = Hq / Hkv;
+  return gq == 1 || gq == 2 || gq == 4;
+}
+
+int launch_scores_fast128(const Layout& L, const void* cbs, int64_t n_cb, const uint32_t* krec, int64_t B,
+                          int64_t Hkv, int64_t T, const void* q, int q_dtype, int64_t Hq, float scale,
+                          float* scores, int32_t* status, hipStream_t s) {
+  Score128Args a;
+  a.cbs = static_cast<const uint8_t*>(cbs);
+  a.stride = L.total;
+  a.n_cb = n_cb;
+  a.krec = krec;
+  a.B = B; a.Hkv = Hkv; a.T = T; a.Hq = Hq;
+  a.q = q; a.q_dtype = q_dtype;
+  a.scale = scale;
+  a.scores = scores;
+  a.status = status;
+  a.bits = L.bits; a.rec_words = L.rec_words; a.gq = (int)(Hq / Hkv);
+  a.off_c = L.off_c; a.off_d = L.off_d; a.off_s = L.off_s;
+  a.tiles = (T + 31) / 32;
+  const int64_t groups = B * Hkv;
+  // about 1024 blocks, at least 16 tiles per wave
+  int64_t per_block = (a.tiles * groups + 1023) / 1024;
+  if (per_block < 64) per_block = 64;
+  if (per_block > a.tiles) per_block = a.tiles;
+  a.tiles_per_block = per_block;
+  a.blocks_per_group = (a.tiles + per_block - 1) / per_block;
+  switch (L.k) {
+    case 1: return launch_k<1>(a, s);
+    case 2: return launch_k<2>(a, s);
+    case 3: return launch_k<3>(a, s);
+    default: return -13;
+  }
+}
+
+}  // namespace tq
