@@ -66,13 +66,18 @@ __device__ inline V as(u32x4 v) {
   return __builtin_bit_cast(V, v);
 }
 
+// Row rho of a 32-row result tile lands in lane half (rho>>2)&1, register
+// 4(rho>>3) + (rho&3).  Tile rows are permuted so that lane half h holds the
+// 16 consecutive indices 16h .. 16h+15 of its tile in registers 0..15.
+__device__ inline int tile_row_index(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
+
 // Build the (H D) A-operand fragments of MFMA#1 in LDS: fragment (M, c) for
-// lane l holds A[32M + l%32][16c + 8(l/32) + e], e = 0..7.
+// lane l holds A[rho = l%32][16c + 8(l/32) + e] = (H D)[32M + tile_row_index(rho)][...].
 template <bool F16>
 __device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
   for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
     const int lane = f & 63, c = (f >> 6) & 7, M = f >> 9;
-    const int row = 32 * M + (lane & 31);
+    const int row = 32 * M + tile_row_index(lane & 31);
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
       uint32_t word = 0;
@@ -89,19 +94,17 @@ __device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
 }
 
 // Coordinate fed by B-operand element e (0..7) of lane half h in projection
-// K-chunk c = 2M + p: the rotation's result row 8i + 4h + j of tile M with
-// i = 2p + e/4, j = e%4.
+// K-chunk c = 2M + p: register 8p + e of tile M, i.e. coordinate 32M + 16h + 8p + e.
 __device__ inline int qjl_coord(int c, int h, int e) {
-  const int M = c >> 1, p = c & 1;
-  return 32 * M + 16 * p + 8 * (e >> 2) + 4 * h + (e & 3);
+  return 32 * (c >> 1) + 16 * h + 8 * (c & 1) + e;
 }
 
-// S fragments (A operand of MFMA#2): fragment (Mp, c), lane l: row 32Mp + l%32,
-// element e: S[row][qjl_coord(c, l/32, e)] as binary16.
+// S fragments (A operand of MFMA#2): fragment (Mp, c), lane l: row rho = l%32 is
+// projection 32Mp + tile_row_index(rho); element e: S[proj][qjl_coord(c, l/32, e)].
 __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
   for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
     const int lane = f & 63, c = (f >> 6) & 7, Mp = f >> 9;
-    const int row = 32 * Mp + (lane & 31);
+    const int row = 32 * Mp + tile_row_index(lane & 31);
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
       const uint32_t lo = S[row * kD + qjl_coord(c, lane >> 5, 2 * q)];
@@ -120,6 +123,45 @@ __device__ inline double pair_sumsq_bf16(uint32_t w) {
 __device__ inline double pair_sumsq_f16(uint32_t w) {
   f16x2 v = __builtin_bit_cast(f16x2, w);
   return (double)__builtin_amdgcn_fdot2(v, v, 0.0f, false);
+}
+
+
+// ---- per-element ALU sequences pinned in inline assembly (register-only,
+// no memory access).  Each helper documents the exact operation.
+
+// First threshold step of the quantizer: above = |u| > tn; acc = 2*acc + above;
+// mag = above ? c1 : c0.
+__device__ inline float thr_first(uint32_t& acc, float u, float tn, float c0, float c1) {
+  uint64_t m, c;
+  float mag;
+  asm("v_cmp_gt_f32_e64 %[m], |%[u]|, %[t]\n\t"
+      "v_addc_co_u32_e64 %[acc], %[c], %[acc], %[acc], %[m]\n\t"
+      "v_cndmask_b32_e64 %[mag], %[c0], %[c1], %[m]"
+      : [acc] "+v"(acc), [mag] "=v"(mag), [m] "=&s"(m), [c] "=&s"(c)
+      : [u] "v"(u), [t] "v"(tn), [c0] "v"(c0), [c1] "v"(c1));
+  return mag;
+}
+
+// Further threshold steps: above = |u| > tn; acc = 2*acc + above; mag = above ? cnext : mag.
+__device__ inline void thr_step(uint32_t& acc, float& mag, float u, float tn, float cnext) {
+  uint64_t m, c;
+  asm("v_cmp_gt_f32_e64 %[m], |%[u]|, %[t]\n\t"
+      "v_addc_co_u32_e64 %[acc], %[c], %[acc], %[acc], %[m]\n\t"
+      "v_cndmask_b32_e64 %[mag], %[mag], %[cn], %[m]"
+      : [acc] "+v"(acc), [mag] "+v"(mag), [m] "=&s"(m), [c] "=&s"(c)
+      : [u] "v"(u), [t] "v"(tn), [cn] "v"(cnext));
+}
+
+// Sign half: pos = u > 0 as the top bit of (0 - bits(u)) (exact for every u
+// except -0, which the MFMA never produces from a +0 accumulator); acc = 2*acc + pos;
+// nsg = pos ? -n : n.
+__device__ inline void pos_step(uint32_t& acc, float& nsg, float u, uint32_t nbits, uint32_t signmask) {
+  uint32_t t;
+  asm("v_sub_u32 %[t], 0, %[u]\n\t"
+      "v_alignbit_b32 %[acc], %[acc], %[t], 31\n\t"
+      "v_and_or_b32 %[nsg], %[t], %[sm], %[nb]"
+      : [acc] "+v"(acc), [nsg] "=&v"(nsg), [t] "=&v"(t)
+      : [u] "v"(u), [sm] "s"(signmask), [nb] "v"(nbits));
 }
 
 // bf16 round-to-nearest-even of a float (bit pattern in the low 16 bits).
@@ -166,12 +208,23 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
   const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles_per_group);
   const uint32_t* xb16 = reinterpret_cast<const uint32_t*>(a.x);
 
+  // bf16/f16 inputs: the next tile's rows are loaded while this tile is encoded
+  const auto row_ptr = [&](int64_t t) {
+    const int64_t tk = t * kTile + col;
+    return reinterpret_cast<const u32x4*>(xb16 + (g * a.sx_g + (tk < a.N ? tk : 0) * a.sx_n) / 2);
+  };
+  u32x4 xr[8];
+  if (DT != 0 && tile0 + wave < tile_end) {
+    const u32x4* xp = row_ptr(tile0 + wave);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) xr[c] = xp[2 * c + h];   // tail lanes read row 0, never stored
+  }
   for (int64_t tile = tile0 + wave; tile < tile_end; tile += kWaves) {
     const int64_t tok = tile * kTile + col;
     const bool valid = tok < a.N;
     const int64_t xoff = g * a.sx_g + (valid ? tok : 0) * a.sx_n;
 
-    // ---- load x (B operand of the rotation), K-chunk c: coords 16c + 8h .. +7
+    // ---- x as the B operand of the rotation, K-chunk c: coords 16c + 8h .. +7
     u32x4 xb[8];
     u32x4 xb2[DT == 0 ? 8 : 1], xb3[DT == 0 ? 8 : 1];
     double ss = 0.0;
@@ -179,8 +232,8 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
       const float4* xp = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.x) + xoff);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        float4 v0 = valid ? xp[4 * c + 2 * h] : make_float4(0, 0, 0, 0);
-        float4 v1 = valid ? xp[4 * c + 2 * h + 1] : make_float4(0, 0, 0, 0);
+        const float4 v0 = xp[4 * c + 2 * h];   // tail lanes read row 0; their results are never stored
+        const float4 v1 = xp[4 * c + 2 * h + 1];
         float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
         u32x4 p1, p2, p3;
 #pragma unroll
@@ -204,35 +257,40 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
         xb[c] = p1; xb2[c] = p2; xb3[c] = p3;
       }
     } else {
-      const u32x4* xp = reinterpret_cast<const u32x4*>(xb16 + xoff / 2);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) xb[c] = valid ? xp[2 * c + h] : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < 8; ++c) xb[c] = xr[c];
 #pragma unroll
       for (int c = 0; c < 8; ++c)
 #pragma unroll
         for (int q = 0; q < 4; ++q) ss += DT == 1 ? pair_sumsq_bf16(xb[c][q]) : pair_sumsq_f16(xb[c][q]);
     }
 
-    // ---- rotation on MFMA
+    // ---- rotation on MFMA: the four row tiles are independent accumulation
+    // chains, interleaved so that consecutive MFMAs do not wait on each other
     f32x16 u[4];
 #pragma unroll
-    for (int M = 0; M < 4; ++M) {
-      f32x16 acc = {};
+    for (int M = 0; M < 4; ++M) u[M] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 8; ++c) {
+#pragma unroll
+      for (int M = 0; M < 4; ++M) {
         const u32x4 hf = hfrag[(M * 8 + c) * 64 + lane];
         if (DT == 2) {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(hf), as<f16x8>(xb[c]), acc, 0, 0, 0);
+          u[M] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(hf), as<f16x8>(xb[c]), u[M], 0, 0, 0);
         } else {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb[c]), acc, 0, 0, 0);
+          u[M] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb[c]), u[M], 0, 0, 0);
           if (DT == 0) {
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb2[c]), acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb3[c]), acc, 0, 0, 0);
+            u[M] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb2[c]), u[M], 0, 0, 0);
+            u[M] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb3[c]), u[M], 0, 0, 0);
           }
         }
       }
-      u[M] = acc;
-      __builtin_amdgcn_sched_barrier(0);   // keep one tile row of fragments live at a time
+      __builtin_amdgcn_sched_barrier(0);   // keep one K-chunk of fragments live at a time
+    }
+    if (DT != 0 && tile + kWaves < tile_end) {
+      const u32x4* xp = row_ptr(tile + kWaves);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) xr[c] = xp[2 * c + h];
     }
 
     // ---- norm (float64, both halves of the vector)
@@ -251,100 +309,126 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
     const uint32_t nexp = (__float_as_uint(n32) >> 23) & 0xFFu;
     const float sc = (n32 > 0.0f && nexp < 253u) ? __uint_as_float((254u - nexp) << 23) : 1.0f;
 
-    // ---- quantize, pack planes, residual
-    uint32_t planes[K][4];
+    // ---- quantize, pack planes, residual.  Lane half h holds coordinates
+    // 32M + 16h + r in register r of tile M; bits are shifted in from r = 15 down
+    // to 0 so that bit r of the 16-bit partial word is coordinate 32M + 16h + r.
+    float tn[NT > 0 ? NT : 1];
 #pragma unroll
-    for (int p = 0; p < K; ++p)
-#pragma unroll
-      for (int M = 0; M < 4; ++M) planes[p][M] = 0;
+    for (int t = 0; t < NT; ++t) tn[t] = tpos[t] * n32;   // thresholds in units of u
+    const uint32_t nbits = __float_as_uint(n32);
+    uint32_t pw[4], tw[NT > 0 ? NT : 1][4];                // sign-half words, thermometer words
     u32x4 whi[KEY ? 8 : 1], wlo[KEY ? 8 : 1];
-#pragma unroll
-    for (int c = 0; c < (KEY ? 8 : 1); ++c) whi[c] = wlo[c] = u32x4{0, 0, 0, 0};
     float wsq = 0.0f;
 #pragma unroll
     for (int M = 0; M < 4; ++M) {
+      uint32_t pacc = 0;
+      uint32_t tacc[NT > 0 ? NT : 1];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = r >> 2, j = r & 3;
-        const int b = 8 * i + 4 * h + j;   // bit position inside word M
+      for (int t = 0; t < NT; ++t) tacc[t] = 0;
+      float wv[16];
+#pragma unroll
+      for (int r = 15; r >= 0; --r) {
         const float uu = u[M][r];
-        const float z = uu * inv;
-        const float az = fabsf(z);
-        int cnt = 0;
+        float nsg;
+        pos_step(pacc, nsg, uu, nbits, 0x80000000u);
+        float mag = cpos[0];
+        if (NT > 0) mag = thr_first(tacc[0], uu, tn[0], cpos[0], cpos[NT > 0 ? 1 : 0]);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) cnt += az > tpos[t] ? 1 : 0;
-        const bool pos = z > 0.0f;
-        const int idx = pos ? (L / 2 + cnt) : (L / 2 - 1 - cnt);
-#pragma unroll
-        for (int p = 0; p < K; ++p) planes[p][M] |= (uint32_t)((idx >> p) & 1) << b;
+        for (int t = 1; t < NT; ++t) thr_step(tacc[t], mag, uu, tn[t], cpos[t + 1]);
         if (KEY) {
-          float mag = cpos[0];
-#pragma unroll
-          for (int t = 1; t < L / 2; ++t) mag = cnt >= t ? cpos[t] : mag;
-          // w = u - n c[idx] = (+-)(|u| - n mag), the sign being the quantizer's
-          // half (z > 0 or not), which also covers u = -0 / +0
-          const float rr = fmaf(-n32, mag, fabsf(uu));
-          const float w = pos ? rr : -rr;
+          // w = u - n c[idx] with c[idx] = +-mag: fma(+-n, mag, u), -n on the positive half
+          const float w = fmaf(nsg, mag, uu);
           wsq = fmaf(w, w, wsq);
-          const float ws = w * sc;
-          const _Float16 hv = (_Float16)ws;
-          const _Float16 lv = (_Float16)(ws - (float)hv);
-          // B operand of projection chunk c = 2M + p, element e = 4(i - 2p) + j
-          const int c = 2 * M + (i >> 1);
-          const int e = 4 * (i & 1) + j;
-          const uint32_t hb = __builtin_bit_cast(uint16_t, hv), lb = __builtin_bit_cast(uint16_t, lv);
-          if (e & 1) {
-            whi[c][e >> 1] |= hb << 16;
-            wlo[c][e >> 1] |= lb << 16;
-          } else {
-            whi[c][e >> 1] = hb;
-            wlo[c][e >> 1] = lb;
-          }
+          wv[r] = w;
         }
+      }
+      pw[M] = pacc;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) tw[t][M] = tacc[t];
+      if (KEY) {
+        // B operand of projection chunk c = 2M + p: element e = register 8p + e
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float w0 = wv[8 * p + 2 * q] * sc, w1 = wv[8 * p + 2 * q + 1] * sc;
+            f16x2 hv, lv;
+            hv[0] = (_Float16)w0;
+            hv[1] = (_Float16)w1;
+            lv[0] = (_Float16)(w0 - (float)hv[0]);
+            lv[1] = (_Float16)(w1 - (float)hv[1]);
+            whi[2 * M + p][q] = __builtin_bit_cast(uint32_t, hv);
+            wlo[2 * M + p][q] = __builtin_bit_cast(uint32_t, lv);
+          }
       }
     }
 
-    // ---- QJL projection on MFMA (keys)
-    uint32_t signs[4] = {0, 0, 0, 0};
+    // ---- QJL projection on MFMA (keys); sign bits packed with one alignbit each
+    uint32_t sw[4] = {0, 0, 0, 0};   // inverted sign bits (1 = negative)
     float gam = 0.0f;
     if (KEY) {
+      f32x16 acc[4];
+#pragma unroll
+      for (int Mp = 0; Mp < 4; ++Mp) acc[Mp] = f32x16{};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x4 sf[4];
+#pragma unroll
+        for (int Mp = 0; Mp < 4; ++Mp) sf[Mp] = sfrag[(Mp * 8 + c) * 64 + lane];
+#pragma unroll
+        for (int Mp = 0; Mp < 4; ++Mp)
+          acc[Mp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[Mp]), as<f16x8>(whi[c]), acc[Mp], 0, 0, 0);
+#pragma unroll
+        for (int Mp = 0; Mp < 4; ++Mp)
+          acc[Mp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[Mp]), as<f16x8>(wlo[c]), acc[Mp], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int Mp = 0; Mp < 4; ++Mp) {
-        f32x16 acc = {};
+        uint32_t a2 = 0;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const u32x4 sf = sfrag[(Mp * 8 + c) * 64 + lane];
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(whi[c]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(wlo[c]), acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int b = 8 * (r >> 2) + 4 * h + (r & 3);
-          signs[Mp] |= (acc[r] >= 0.0f ? 1u : 0u) << b;
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int r = 15; r >= 0; --r) a2 = __builtin_amdgcn_alignbit(a2, __float_as_uint(acc[Mp][r]), 31);
+        sw[Mp] = a2;
       }
       auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq), __float_as_uint(wsq), false, false);
       const float tot = __uint_as_float(pg[0]) + __uint_as_float(pg[1]);
       gam = sqrtf(tot) * 0.08838834764831845f;   // |w| / sqrt(128)
     }
 
-    // ---- combine the two halves of every word and store the record
+    // ---- plane words: MSB plane = [z > 0]; the lower planes hold cnt on the
+    // positive half and its complement (L/2 - 1 - cnt) on the other half, cnt
+    // being the number of positive thresholds below |z| (thermometer -> binary)
     constexpr int R = KEY ? (K * 4 + 4 + 2) : (K * 4 + 1);
     uint32_t words[R];
+    uint32_t part[KEY ? K * 4 + 4 : K * 4];
 #pragma unroll
-    for (int p = 0; p < K; ++p)
+    for (int M = 0; M < 4; ++M) {
+      uint32_t pl[K];
+      pl[K - 1] = pw[M];
 #pragma unroll
-      for (int M = 0; M < 4; ++M) {
-        auto pw = __builtin_amdgcn_permlane32_swap(planes[p][M], planes[p][M], false, false);
-        words[p * 4 + M] = pw[0] | pw[1];
+      for (int p = 0; p < K - 1; ++p) {
+        // bit p of cnt = XOR of the thermometer bits [cnt >= j] for j a multiple of 2^p
+        uint32_t cb = 0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (((t + 1) & ((1 << p) - 1)) == 0) cb ^= tw[t][M];
+        pl[p] = ~(cb ^ pw[M]) & 0xFFFFu;   // pos ? cnt_p : ~cnt_p
       }
+      for (int p = 0; p < K; ++p) part[p * 4 + M] = h ? (pl[p] << 16) : (pl[p] & 0xFFFFu);
+    }
     if (KEY) {
 #pragma unroll
-      for (int Mp = 0; Mp < 4; ++Mp) {
-        auto pw = __builtin_amdgcn_permlane32_swap(signs[Mp], signs[Mp], false, false);
-        words[K * 4 + Mp] = pw[0] | pw[1];
-      }
+      for (int Mp = 0; Mp < 4; ++Mp) part[K * 4 + Mp] = h ? ((~sw[Mp]) << 16) : ((~sw[Mp]) & 0xFFFFu);
+    }
+    // complete two words per swap: half 0 finishes word 2i (and stores it), half 1 word 2i+1
+    constexpr int NP = KEY ? K * 4 + 4 : K * 4;
+#pragma unroll
+    for (int i = 0; i < NP / 2; ++i) {
+      auto sp = __builtin_amdgcn_permlane32_swap(part[2 * i], part[2 * i + 1], false, false);
+      words[2 * i] = part[2 * i] | sp[1];          // valid in half 0
+      words[2 * i + 1] = part[2 * i + 1] | sp[0];  // valid in half 1
+    }
+    if (KEY) {
       words[K * 4 + 4] = __float_as_uint(n32);
       words[K * 4 + 5] = __float_as_uint(gam);
     } else {

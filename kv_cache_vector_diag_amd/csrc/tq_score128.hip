@@ -214,30 +214,49 @@ __global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
   const float inv_d = 1.0f / (float)kD;
   const int64_t tile0 = chunk * a.tiles_per_block;
   const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles);
+  // Lane half h feeds words ww in {h, h+2} of every bit plane and of the sign
+  // mask.  The next tile's words are loaded while this tile is scored.
+  constexpr int NRAW = 2 * K + 2;
+  uint32_t cur[NRAW], nxt[NRAW];
+  float cur_n = 0.0f, cur_g = 0.0f, nxt_n = 0.0f, nxt_g = 0.0f;
+  const auto load_raw = [&](int64_t t, uint32_t* rw, float& nn, float& gg) {
+    const int64_t tk = t * 32 + col;
+    const uint32_t* r = a.krec + (grp * a.T + (tk < a.T ? tk : 0)) * R;   // tail lanes read key 0
+#pragma unroll
+    for (int p = 0; p < K; ++p)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) rw[2 * p + s2] = r[p * 4 + h + 2 * s2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) rw[2 * K + s2] = r[K * 4 + h + 2 * s2];
+    nn = __uint_as_float(r[K * 4 + 4]);
+    gg = __uint_as_float(r[K * 4 + 5]);
+  };
+  if (tile0 + wave < tile_end) load_raw(tile0 + wave, cur, cur_n, cur_g);
   for (int64_t tile = tile0 + wave; tile < tile_end; tile += 4) {
     const int64_t tok = tile * 32 + col;
     const bool valid = tok < a.T;
-    const uint32_t* r = a.krec + (grp * a.T + (valid ? tok : 0)) * R;
+    if (tile + 4 < tile_end) load_raw(tile + 4, nxt, nxt_n, nxt_g);
     uint32_t wv[Mk::kWords / 2];
 #pragma unroll
     for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
-      const int li = 2 * w2 + h, mask = li >> 2, ww = li & 3;
+      const int li = 2 * w2 + h, mask = li >> 2, s2 = (li & 3) >> 1;
       uint32_t word;
       if (mask == Mk::kPlaneMasks) {
-        word = r[K * 4 + ww];
+        word = cur[2 * K + s2];
       } else {
         const int sb = subset_bits<K>(mask);
         word = 0;
 #pragma unroll
         for (int p = 0; p < K; ++p)
-          if ((sb >> p) & 1) word ^= r[p * 4 + ww];
+          if ((sb >> p) & 1) word ^= cur[2 * p + s2];
       }
       wv[w2] = valid ? word : 0u;
     }
-    const float nrm = valid ? __uint_as_float(r[K * 4 + 4]) : 0.0f;
-    const float gam = valid ? __uint_as_float(r[K * 4 + 5]) : 0.0f;
+    const float nrm = valid ? cur_n : 0.0f;
+    const float gam = valid ? cur_g : 0.0f;
 
-    i32x16 acc = {};
+    // two independent accumulation chains (even / odd MFMAs)
+    i32x16 acc0 = {}, acc1 = {};
 #pragma unroll
     for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
 #pragma unroll
@@ -245,9 +264,17 @@ __global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
         i32x4 bv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) bv[q] = (int)(wv[w2] & (0x01010101u << (4 * g + q)));
-        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[2 * w2 + g], bv, acc, 0, 0, 0);
+        if (g == 0)
+          acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[2 * w2 + g], bv, acc0, 0, 0, 0);
+        else
+          acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[2 * w2 + g], bv, acc1, 0, 0, 0);
       }
     }
+    const i32x16 acc = acc0 + acc1;
+#pragma unroll
+    for (int i = 0; i < NRAW; ++i) cur[i] = nxt[i];
+    cur_n = nxt_n;
+    cur_g = nxt_g;
     // rows 8*hh + 4*h + limb: this lane holds part h (0: mse, 1: qjl) of heads 0..3
     float part[4];
 #pragma unroll
