@@ -115,6 +115,7 @@ __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
   }
 }
 
+// x0^2 + x1^2 of a packed pair, widened to fp64.
 __device__ inline double pair_sumsq_bf16(uint32_t w) {
   s16x2 v = __builtin_bit_cast(s16x2, w);
   return (double)__builtin_amdgcn_fdot2_f32_bf16(v, v, 0.0f, false);
@@ -128,6 +129,19 @@ __device__ inline double pair_sumsq_f16(uint32_t w) {
 
 // ---- per-element ALU sequences pinned in inline assembly (register-only,
 // no memory access).  Each helper documents the exact operation.
+
+// Scaled two-term half-precision split of a pair: hi = f16(w*sc) (round to
+// nearest even), lo = f16(w*sc - hi), packed two per word (element 0 in the low
+// half).  w*sc is exact for the power-of-two sc used here, and w*sc - hi is
+// exact in fp32, so hi + lo carries 22 significant bits of w*sc.
+__device__ inline void split_f16x2(float w0, float w1, float sc, uint32_t& hi, uint32_t& lo) {
+  asm("v_fma_mixlo_f16 %[h], %[w0], %[sc], 0\n\t"
+      "v_fma_mixhi_f16 %[h], %[w1], %[sc], 0\n\t"
+      "v_fma_mixlo_f16 %[l], %[w0], %[sc], -%[h] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %[l], %[w1], %[sc], -%[h] op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : [h] "=&v"(hi), [l] "=&v"(lo)
+      : [w0] "v"(w0), [w1] "v"(w1), [sc] "v"(sc));
+}
 
 // First threshold step of the quantizer: above = |u| > tn; acc = 2*acc + above;
 // mag = above ? c1 : c0.
@@ -287,8 +301,10 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
       }
       __builtin_amdgcn_sched_barrier(0);   // keep one K-chunk of fragments live at a time
     }
-    if (DT != 0 && tile + kWaves < tile_end) {
-      const u32x4* xp = row_ptr(tile + kWaves);
+    if (DT != 0) {
+      // the last tile re-reads itself (a cache hit) so that the prefetch
+      // registers are written on every iteration
+      const u32x4* xp = row_ptr(tile + kWaves < tile_end ? tile + kWaves : tile);
 #pragma unroll
       for (int c = 0; c < 8; ++c) xr[c] = xp[2 * c + h];
     }
@@ -304,7 +320,6 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
     const bool finite = ss <= 3.4028234663852886e38;
     if (a.status && __ballot(valid && !finite && h == 0) != 0 && lane == 0) atomicOr(a.status, TQ_STATUS_NON_FINITE);
     const float n32 = (float)sqrt(ss);
-    const float inv = n32 > 0.0f ? 1.0f / n32 : 0.0f;
     // power-of-two scale that brings the residual to O(1) for the f16 split
     const uint32_t nexp = (__float_as_uint(n32) >> 23) & 0xFFu;
     const float sc = (n32 > 0.0f && nexp < 253u) ? __uint_as_float((254u - nexp) << 23) : 1.0f;
@@ -351,14 +366,10 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
         for (int p = 0; p < 2; ++p)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float w0 = wv[8 * p + 2 * q] * sc, w1 = wv[8 * p + 2 * q + 1] * sc;
-            f16x2 hv, lv;
-            hv[0] = (_Float16)w0;
-            hv[1] = (_Float16)w1;
-            lv[0] = (_Float16)(w0 - (float)hv[0]);
-            lv[1] = (_Float16)(w1 - (float)hv[1]);
-            whi[2 * M + p][q] = __builtin_bit_cast(uint32_t, hv);
-            wlo[2 * M + p][q] = __builtin_bit_cast(uint32_t, lv);
+            uint32_t h, l;
+            split_f16x2(wv[8 * p + 2 * q], wv[8 * p + 2 * q + 1], sc, h, l);
+            whi[2 * M + p][q] = h;
+            wlo[2 * M + p][q] = l;
           }
       }
     }
