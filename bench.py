@@ -18,7 +18,6 @@ long-context attend rows instead (also one line each).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -34,12 +33,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def _kernel_sources_sha() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "kv_cache_vector_diag_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
-    return h.hexdigest()[:16]
+    from kv_cache_vector_diag_amd.rocprof_summary import kernel_sources_sha
+    return kernel_sources_sha(ROOT)
 
 
 def _traffic(kernel_key: str, launches_bytes: float):
@@ -76,7 +71,7 @@ def cpu_baseline_c3(budget_s: float = 15.0) -> dict:
         q = inputs.exact_values(inputs.to_torch(inputs.queries(3, 16, 32, d), "bf16"))
         done = 0
         spent = 0.0
-        while done < 16 and spent < budget_s:
+        while done < 128 and spent < budget_s:
             g = done
             K = inputs.exact_values(inputs.to_torch(inputs.kv_normal(3, 128, T, d, groups=[g]), "bf16"))[0]
             t0 = time.perf_counter()
@@ -290,10 +285,18 @@ def main():
         n = 1 << 30
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
-        for _ in range(max(args.steps, 1)):
-            dst.copy_(src)
+        dst.copy_(src)
+        reps = max(args.steps, 1)
+        ev = _events(torch, 2)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": max(args.steps, 1)}}))
+        ev[0].record()
+        for _ in range(reps):
+            dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / reps
+        print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": reps + 1,
+                                               "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}}))
         return
     fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4}[args.config]
     line = fn(args, torch, b)

@@ -1,0 +1,120 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept with the project.
+
+    python -m kv_cache_vector_diag_amd.rocprof_summary stats <kernel_stats.csv>
+    python -m kv_cache_vector_diag_amd.rocprof_summary counters <counter_collection.csv> [...]
+    python -m kv_cache_vector_diag_amd.rocprof_summary traffic --fetch F.csv --write W.csv \\
+        --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --out traffic.json
+
+``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE readings (KiB) of
+each kernel by the factor that makes the same counter read the known byte
+count of a plain device copy, and records the hash of the kernel sources the
+counters were taken with (a later source change makes the entry stale).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+KERNELS = {
+    "encode128_kernel": "encode",
+    "score128_kernel": "score",
+    "encode_generic": "encode_generic",
+    "scores_generic": "score_generic",
+    "decode_generic": "decode_generic",
+    "attend": "attend",
+}
+
+
+def short_name(kernel_name: str) -> str:
+    for key, short in KERNELS.items():
+        if key in kernel_name:
+            return short
+    if "copyBuffer" in kernel_name:
+        return "copy"
+    if "FillFunctor" in kernel_name:
+        return "fill"
+    return kernel_name[:48]
+
+
+def kernel_sources_sha(root: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(root, "kv_cache_vector_diag_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cmd_stats(path: str) -> None:
+    rows = list(csv.DictReader(open(path)))
+    print(f"{'kernel':<16} {'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'pct':>6}")
+    for r in rows:
+        print(f"{short_name(r['Name']):<16} {int(r['Calls']):>6} {float(r['AverageNs']) / 1e3:>10.2f} "
+              f"{float(r['MinNs']) / 1e3:>10.2f} {float(r['MaxNs']) / 1e3:>10.2f} {float(r['Percentage']):>6.2f}")
+
+
+def per_kernel_counters(paths):
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for p in paths:
+        for r in csv.DictReader(open(p)):
+            agg[short_name(r["Kernel_Name"])][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return agg
+
+
+def cmd_counters(paths) -> None:
+    for k, d in sorted(per_kernel_counters(paths).items()):
+        print(k)
+        for c, v in sorted(d.items()):
+            print(f"   {c:<28} {sum(v) / len(v):>16.1f}   (mean of {len(v)} dispatches)")
+
+
+def cmd_traffic(a) -> None:
+    fetch = per_kernel_counters([a.fetch])
+    write = per_kernel_counters([a.write])
+    cf = per_kernel_counters([a.copy_fetch])["copy"]["FETCH_SIZE"]
+    cw = per_kernel_counters([a.copy_write])["copy"]["WRITE_SIZE"]
+    # the largest dispatches of the copy kernel are the 1 GiB copies
+    f_factor = a.copy_bytes / (max(cf) * 1024.0)
+    w_factor = a.copy_bytes / (max(cw) * 1024.0)
+    out = json.load(open(a.out)) if os.path.exists(a.out) else {}
+    sha = kernel_sources_sha(a.root)
+    for kern, key in (k.split("=") for k in a.map):
+        fv = fetch[kern]["FETCH_SIZE"]
+        wv = write[kern]["WRITE_SIZE"]
+        rd = sum(fv) / len(fv) * 1024.0 * f_factor
+        wr = sum(wv) / len(wv) * 1024.0 * w_factor
+        out[key] = {"hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                    "fetch_factor": f_factor, "write_factor": w_factor, "source_sha": sha}
+        print(f"{key}: read {rd / 1e6:.1f} MB  write {wr / 1e6:.1f} MB  (factors {f_factor:.3f}, {w_factor:.3f})")
+    json.dump(out, open(a.out, "w"), indent=1, sort_keys=True)
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats"); s.add_argument("csv")
+    c = sub.add_parser("counters"); c.add_argument("csv", nargs="+")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True); t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True); t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    t.add_argument("--map", nargs="+", default=["encode=encode_c3", "score=score_c3"],
+                   help="kernel=key pairs")
+    t.add_argument("--root", default=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        cmd_stats(a.csv)
+    elif a.cmd == "counters":
+        cmd_counters(a.csv)
+    else:
+        cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
