@@ -114,6 +114,12 @@ def gaussians(seed: int, count: int, base: int) -> np.ndarray:
     return out
 
 
+def haar_gaussian(seed: int, d: int) -> np.ndarray:
+    """d x d standard normals (float64, row-major entry e = i*d + j) from the
+    Haar stream: the matrix whose orthogonal QR factor is the dense rotation."""
+    return gaussians(seed, d * d, STREAM_HAAR).reshape(d, d)
+
+
 def qjl_matrix(seed: int, m: int, d: int) -> np.ndarray:
     """S (m x d, row-major entry e = i*d + j) as float64 values of binary16 numbers."""
     g = gaussians(seed, m * d, STREAM_S)

@@ -40,6 +40,12 @@ Readings where the pages are silent (each also listed in the design doc):
   R6  zero vector: z := 0; hence x^ = 0, rho = 0, gamma = 0, all s = 1.
   R7  a vector with a non-finite element, or whose squared norm exceeds the
       binary32 range, is flagged; its record is unspecified.
+  R8  Haar alternative ("Architecture" step 1, "Modules" rotation): Pi = Q,
+      the orthogonal QR factor of a seeded d x d Gaussian matrix with the
+      columns signed so that the triangular factor has a positive diagonal.
+      The stored matrix R = float32(sqrt(d) Q) takes the place of H D in
+      every formula (u = R x, x^ = (n32/d) R^T c[idx], qt = R q), so head_dim
+      need not be a power of two.
 
 Pins: tests/test_oracle_codec.py (lattice round trip, nearest-centroid brute
 force, distortion law, QJL unbiasedness over seeds, compressed-score
@@ -53,10 +59,12 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from .lloyd import stored_codebook
-from .prng import qjl_matrix, qjl_matrix_fast, sign_diagonal, sign_diagonal_fast
+from .prng import haar_gaussian, qjl_matrix, qjl_matrix_fast, sign_diagonal, sign_diagonal_fast
 
 ROLE_KEY = 0
 ROLE_VALUE = 1
+ROT_HADAMARD = 0     # Pi = H D / sqrt(d)
+ROT_HAAR = 1         # Pi = Q, Q Haar-distributed (QR of a Gaussian matrix)
 FLT_MAX = float(np.finfo(np.float32).max)
 QJL_CONST = math.sqrt(math.pi / 2.0)
 
@@ -80,13 +88,33 @@ def hadamard(d: int) -> np.ndarray:
     return np.where(pc % 2 == 0, 1.0, -1.0)
 
 
-def check_args(d: int, bits: int, m: int, role: int) -> int:
+def haar_rotation(seed: int, d: int) -> np.ndarray:
+    """R = float32(sqrt(d) Q) as float64, with Q the orthogonal factor of the QR
+    decomposition of the seeded Gaussian matrix, columns signed so that the
+    triangular factor has a positive diagonal (this makes Q Haar-distributed).
+
+    Page "turboquant-plus-rs 0.1.0 README", "Architecture" step 1 and "Modules"
+    ``rotation`` (Haar-distributed rotation via QR, the alternative to the
+    Walsh-Hadamard transform).  sqrt(d) Q plays the part of H D: u = R x has
+    |u| = sqrt(d) |x| (up to the float32 rounding of R), so z = u/|x| ~ N(0,1)."""
+    G = haar_gaussian(seed, d)
+    Q, Rt = np.linalg.qr(G)
+    Q = Q * np.sign(np.diag(Rt))[None, :]
+    return (math.sqrt(d) * Q).astype(np.float32).astype(np.float64)
+
+
+def check_args(d: int, bits: int, m: int, role: int, rotation: int = ROT_HADAMARD) -> int:
     """Validate (head_dim, bits, projections, role) and return k = Lloyd bits."""
     if role not in (ROLE_KEY, ROLE_VALUE):
         raise OracleError("INVALID_ROLE", str(role))
+    if rotation not in (ROT_HADAMARD, ROT_HAAR):
+        raise OracleError("INVALID_ROTATION", str(rotation))
     if d == 0:
         raise OracleError("ZERO_DIMENSION")
-    if d < 2 or d > 512 or (d & (d - 1)) != 0:
+    if rotation == ROT_HAAR:
+        if d < 2 or d > 512:
+            raise OracleError("BAD_DIMENSION", f"head_dim {d} not in [2, 512]")
+    elif d < 2 or d > 512 or (d & (d - 1)) != 0:
         raise OracleError("BAD_DIMENSION", f"head_dim {d} must be a power of two in [2, 512]")
     if role == ROLE_KEY:
         if not 2 <= bits <= 9:
@@ -101,8 +129,8 @@ def check_args(d: int, bits: int, m: int, role: int) -> int:
     return bits
 
 
-def record_words(d: int, bits: int, m: int, role: int) -> int:
-    k = check_args(d, bits, m, role)
+def record_words(d: int, bits: int, m: int, role: int, rotation: int = ROT_HADAMARD) -> int:
+    k = check_args(d, bits, m, role, rotation)
     w = (d + 31) // 32
     if role == ROLE_KEY:
         return k * w + (m + 31) // 32 + 2
@@ -118,17 +146,24 @@ class Quantizer:
     seed: int
     role: int
     fast_prng: bool = False      # vectorised generator: only for many-seed statistics
+    rotation: int = ROT_HADAMARD
     k: int = field(init=False)
     c32: np.ndarray = field(init=False, repr=False)
     t32: np.ndarray = field(init=False, repr=False)
-    D: np.ndarray = field(init=False, repr=False)
+    D: np.ndarray | None = field(init=False, repr=False)
+    R: np.ndarray | None = field(init=False, repr=False)   # Haar: float32(sqrt(d) Q)
     S: np.ndarray | None = field(init=False, repr=False)
 
     def __post_init__(self):
-        self.k = check_args(self.d, self.bits, self.m, self.role)
+        self.k = check_args(self.d, self.bits, self.m, self.role, self.rotation)
         self.seed &= (1 << 64) - 1
         self.c32, self.t32 = stored_codebook(self.k)
-        if self.fast_prng:
+        self.R = None
+        if self.rotation == ROT_HAAR:
+            self.D = None
+            self.R = haar_rotation(self.seed, self.d)
+            self.S = qjl_matrix(self.seed, self.m, self.d) if self.role == ROLE_KEY else None
+        elif self.fast_prng:
             self.D = sign_diagonal_fast(self.seed, self.d)
             self.S = qjl_matrix_fast(self.seed, self.m, self.d) if self.role == ROLE_KEY else None
         else:
@@ -137,7 +172,7 @@ class Quantizer:
 
     @property
     def words(self) -> int:
-        return record_words(self.d, self.bits, self.m, self.role)
+        return record_words(self.d, self.bits, self.m, self.role, self.rotation)
 
 
 def quantizers(n_cb: int, d: int, bits: int, m: int, seed: int, role: int) -> list[Quantizer]:
@@ -189,7 +224,9 @@ class Encoded:
 
 
 def _rotate(qz: Quantizer, X: np.ndarray) -> np.ndarray:
-    """u = H (D x) for each row (dense matrix product)."""
+    """u = H (D x) for each row (dense matrix product); Haar: u = R x."""
+    if qz.rotation == ROT_HAAR:
+        return X @ qz.R.T
     H = hadamard(qz.d)
     return (X * qz.D[None, :]) @ H.T
 
@@ -259,6 +296,8 @@ def unpack_record(qz: Quantizer, records) -> Fields:
 def decode_values(qz: Quantizer, records) -> np.ndarray:
     """x^ = Pi^T (n32/sqrt d) c[idx] = (n32/d) D (H c[idx])  (MSE reconstruction)."""
     f = unpack_record(qz, records)
+    if qz.rotation == ROT_HAAR:                       # x^ = (n32/d) R^T c[idx]
+        return (f.n32[:, None] / qz.d) * (qz.c32[f.idx] @ qz.R)
     H = hadamard(qz.d)
     return (f.n32[:, None] / qz.d) * ((qz.c32[f.idx] @ H.T) * qz.D[None, :])
 
@@ -266,9 +305,11 @@ def decode_values(qz: Quantizer, records) -> np.ndarray:
 def dequantize_keys(qz: Quantizer, records) -> np.ndarray:
     """x~ = Pi^T y~, y~ = (n32/sqrt d) c[idx] + sqrt(pi/2)/m * gamma32 * S^T (2s - 1)."""
     f = unpack_record(qz, records)
-    H = hadamard(qz.d)
     y = (f.n32[:, None] / math.sqrt(qz.d)) * qz.c32[f.idx]
     y = y + (QJL_CONST / qz.m) * f.gamma32[:, None] * ((2.0 * f.signs - 1.0) @ qz.S)
+    if qz.rotation == ROT_HAAR:                       # Pi^T y = R^T y / sqrt(d)
+        return (y @ qz.R) / math.sqrt(qz.d)
+    H = hadamard(qz.d)
     return ((y @ H.T) * qz.D[None, :]) / math.sqrt(qz.d)
 
 
@@ -326,8 +367,10 @@ def compressed_score_terms(qz: Quantizer, records, q) -> np.ndarray:
     (n32/d) sum_j qt_j c[idx_j] + sqrt(pi/2)/m gamma32 sum_i p_i (2 s_i - 1),
     with qt = H(D q) and p = S qt / sqrt(d).  Unscaled (no 1/sqrt d)."""
     f = unpack_record(qz, records)
-    H = hadamard(qz.d)
-    qt = H @ (qz.D * np.asarray(q, dtype=np.float64))
+    if qz.rotation == ROT_HAAR:
+        qt = qz.R @ np.asarray(q, dtype=np.float64)
+    else:
+        qt = hadamard(qz.d) @ (qz.D * np.asarray(q, dtype=np.float64))
     mse = (f.n32 / qz.d) * (qz.c32[f.idx] @ qt)
     if qz.role != ROLE_KEY:
         return mse
