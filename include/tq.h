@@ -75,11 +75,13 @@ enum tq_status {
   TQ_ERR_INVALID_ROLE = -11,       /* role not TQ_ROLE_KEY / TQ_ROLE_VALUE             */
   TQ_ERR_INVALID_PROJECTIONS = -12,/* projections > 1024                               */
   TQ_ERR_UNSUPPORTED = -13,        /* dtype or alignment not supported                 */
+  TQ_ERR_INVALID_ROTATION = -14,   /* rotation not TQ_ROT_HADAMARD / TQ_ROT_HAAR       */
 };
 
 /* Device status bits (OR-ed into *status). */
 #define TQ_STATUS_NON_FINITE 1
 #define TQ_STATUS_BAD_BLOB 2
+#define TQ_STATUS_BAD_CHANNEL 4   /* a channel map entry outside [0, head_dim) */
 
 enum tq_role {
   TQ_ROLE_KEY = 0,    /* TurboQuant: (bits-1)-bit Lloyd-Max + 1-bit QJL of the residual */
@@ -107,6 +109,25 @@ size_t tq_record_bytes(int head_dim, int bits, int projections, int role);
  * uploads the blob.  Host only; deterministic. */
 int tq_make_codebook(int head_dim, int bits, int projections, uint64_t seed, int role,
                      void* blob, size_t blob_bytes);
+
+/* Rotation of a codebook (README "Architecture" step 1 and "Modules" rotation:
+ * the random rotation is Haar-distributed via QR, or the fast Walsh-Hadamard
+ * transform).  TQ_ROT_HADAMARD: Pi = H D / sqrt(head_dim), head_dim a power of
+ * two; the blob section at off_d holds the bits of D.  TQ_ROT_HAAR: Pi = Q, the
+ * orthogonal QR factor (Householder, float64) of the head_dim x head_dim Gaussian
+ * matrix drawn from SplitMix64 counters 2^33 + e (Box-Muller, row-major entry e),
+ * columns signed so the triangular factor has a positive diagonal; the blob
+ * section at off_d holds float32 R = sqrt(head_dim) Q, row-major, which takes the
+ * place of H D everywhere (u = R x, x^ = (n/head_dim) R^T c[idx], qt = R q).  Any
+ * head_dim in [2, 512]. */
+enum tq_rotation { TQ_ROT_HADAMARD = 0, TQ_ROT_HAAR = 1 };
+
+/* As tq_codebook_bytes / tq_record_bytes / tq_make_codebook, with the rotation
+ * named.  Host only. */
+size_t tq_codebook_bytes_ex(int head_dim, int bits, int projections, int role, int rotation);
+size_t tq_record_bytes_ex(int head_dim, int bits, int projections, int role, int rotation);
+int tq_make_codebook_ex(int head_dim, int bits, int projections, uint64_t seed, int role, int rotation,
+                        void* blob, size_t blob_bytes);
 
 /* Encode keys: x [G][N][head_dim] (dtype TQ_F32/TQ_BF16/TQ_F16, strides in
  * elements; head_dim contiguous) -> records [G][N][tq_record_bytes/4] at `rec`.
@@ -164,6 +185,59 @@ int tq_rotate(int head_dim, int bits, int projections, int role,
               const void* x, int x_dtype, int64_t G, int64_t N,
               int64_t sx_g, int64_t sx_n,
               float* u, float* norms, void* stream);
+
+/* ---- Outlier/normal channel split (mixed-precision layers) ----------------
+ * README "Modules" outlier (non-integer bit rates by splitting the channels of a
+ * head vector into outlier and normal parts); "Key ideas" 3 (boundary layers at
+ * higher precision are plain calls at a higher `bits`).
+ * A channel map chan [G][head_dim] int32 lists, for group g, the n_outlier
+ * outlier channels ascending, then the other head_dim - n_outlier channels
+ * ascending.  Coordinate j of a part is channel chan[g][offset + j] of x.
+ *   normal part : head_dim - n_outlier coordinates, TQ_ROT_HAAR codebooks at
+ *                 `bits` (keys: projections = head_dim - n_outlier);
+ *   outlier part: n_outlier coordinates (a power of two), TQ_ROT_HADAMARD
+ *                 codebooks at bits + 1 (keys: projections = n_outlier).
+ * Each part has its own records ([G][N][tq_record_bytes_ex(part)/4]) and its own
+ * codebook array (n_cb blobs each, group g uses blob g mod n_cb).  Keys: bits in
+ * [2, 8]; values: bits in [1, 7].  A map entry outside [0, head_dim) sets
+ * TQ_STATUS_BAD_CHANNEL and reads channel 0. */
+
+/* Scratch for tq_outlier_channels: G * chunks * head_dim * 16 bytes, chunks =
+ * clamp(ceil(N/512), 1, 64).  0 on invalid sizes. */
+size_t tq_outlier_workspace_bytes(int head_dim, int64_t G, int64_t N);
+
+/* chan[g] for every group of x [G][N][head_dim] (strides in elements): the
+ * n_outlier channels with the largest population variance over the N vectors
+ * (float64 sums; ties to the lower channel index), ascending, then the rest
+ * ascending.  N == 0 gives channels 0 .. n_outlier-1 as outliers.  `work` is
+ * caller scratch of tq_outlier_workspace_bytes.  head_dim in [2, 512],
+ * 0 < n_outlier < head_dim. */
+int tq_outlier_channels(int head_dim, int n_outlier, const void* x, int x_dtype, int64_t G, int64_t N,
+                        int64_t sx_g, int64_t sx_n, int32_t* chan, void* work, size_t work_bytes,
+                        void* stream);
+
+/* Encode both parts of every vector (role TQ_ROLE_KEY or TQ_ROLE_VALUE). */
+int tq_encode_split(int role, int head_dim, int n_outlier, int bits,
+                    const void* cbs_normal, const void* cbs_outlier, int64_t n_cb,
+                    const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n,
+                    const int32_t* chan, void* rec_normal, void* rec_outlier, int32_t* status, void* stream);
+
+/* Scores from split key records: scores[b][hq][t] = scale * (estimate of the
+ * normal part + estimate of the outlier part), each part scored from its records
+ * against the query channels the map selects; scale <= 0 means 1/sqrt(head_dim).
+ * chan has one row per (b, kv head) group, b*H_kv + h. */
+int tq_scores_split(int head_dim, int n_outlier, int bits,
+                    const void* cbs_normal, const void* cbs_outlier, int64_t n_cb, const int32_t* chan,
+                    const void* krec_normal, const void* krec_outlier, int64_t B, int64_t H_kv, int64_t T,
+                    const void* q, int q_dtype, int64_t H_q, float scale, float* scores, int32_t* status,
+                    void* stream);
+
+/* Decode split value records to out [G][N][head_dim] float32 (both parts
+ * decoded and scattered back to their channels). */
+int tq_decode_values_split(int head_dim, int n_outlier, int bits,
+                           const void* cbs_normal, const void* cbs_outlier, int64_t n_cb, const int32_t* chan,
+                           const void* rec_normal, const void* rec_outlier, int64_t G, int64_t N,
+                           float* out, int32_t* status, void* stream);
 
 /* Memory footprint of a K+V cache of seq_len x layers x kv_heads vectors
  * (README "Modules" utils; "Compression formats").  out[0] = fp16 bytes,

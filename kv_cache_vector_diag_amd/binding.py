@@ -17,13 +17,19 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 ROLE_KEY = 0
 ROLE_VALUE = 1
+ROT_HADAMARD = 0
+ROT_HAAR = 1
 F32, BF16, F16 = 0, 1, 2
 STATUS_NON_FINITE = 1
 STATUS_BAD_BLOB = 2
+STATUS_BAD_CHANNEL = 4
+OUTLIER_SEED_XOR = 0x9E3779B97F4A7C15   # seed of an outlier part = head seed XOR this
 
 EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encode_keys",
            "tq_encode_values", "tq_decode_values", "tq_scores", "tq_attend_workspace_bytes",
-           "tq_attend", "tq_rotate", "tq_memory_stats", "tq_status_string"]
+           "tq_attend", "tq_rotate", "tq_memory_stats", "tq_status_string", "tq_codebook_bytes_ex",
+           "tq_record_bytes_ex", "tq_make_codebook_ex", "tq_outlier_workspace_bytes", "tq_outlier_channels",
+           "tq_encode_split", "tq_scores_split", "tq_decode_values_split"]
 
 _lib = None
 
@@ -64,6 +70,20 @@ def load() -> ctypes.CDLL:
         "tq_memory_stats": (c_int, [c_int, c_int, c_int, c_int, c_int64, c_int64, c_int64,
                                     ctypes.POINTER(c_double)]),
         "tq_status_string": (ctypes.c_char_p, [c_int]),
+        "tq_codebook_bytes_ex": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+        "tq_record_bytes_ex": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+        "tq_make_codebook_ex": (c_int, [c_int, c_int, c_int, c_uint64, c_int, c_int, c_void_p, c_size_t]),
+        "tq_outlier_workspace_bytes": (c_size_t, [c_int, c_int64, c_int64]),
+        "tq_outlier_channels": (c_int, [c_int, c_int, c_void_p, c_int, c_int64, c_int64, c_int64, c_int64,
+                                        c_void_p, c_void_p, c_size_t, c_void_p]),
+        "tq_encode_split": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int64, c_void_p, c_int,
+                                    c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
+                                    c_void_p]),
+        "tq_scores_split": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                    c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float,
+                                    c_void_p, c_void_p, c_void_p]),
+        "tq_decode_values_split": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                           c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -99,12 +119,30 @@ def tq_make_codebook(head_dim: int, bits: int, projections: int, seed: int, role
     return buf
 
 
+def tq_codebook_bytes_ex(head_dim: int, bits: int, projections: int, role: int, rotation: int) -> int:
+    return int(load().tq_codebook_bytes_ex(head_dim, bits, projections, role, rotation))
+
+
+def tq_record_bytes_ex(head_dim: int, bits: int, projections: int, role: int, rotation: int) -> int:
+    return int(load().tq_record_bytes_ex(head_dim, bits, projections, role, rotation))
+
+
+def tq_make_codebook_ex(head_dim: int, bits: int, projections: int, seed: int, role: int,
+                        rotation: int) -> np.ndarray:
+    lib = load()
+    nbytes = lib.tq_codebook_bytes_ex(head_dim, bits, projections, role, rotation)
+    buf = np.zeros(max(int(nbytes), 1), dtype=np.uint8)
+    _check(lib.tq_make_codebook_ex(head_dim, bits, projections, seed & ((1 << 64) - 1), role, rotation,
+                                   buf.ctypes.data, buf.nbytes), "tq_make_codebook_ex")
+    return buf
+
+
 def make_codebooks(n_cb: int, head_dim: int, bits: int, projections: int, seed: int, role: int,
-                   device=None):
-    """n_cb blobs back to back, blob i seeded with seed + i (wrapping), as a uint8
-    torch tensor on `device` (host numpy array when device is None)."""
-    blobs = np.concatenate([tq_make_codebook(head_dim, bits, projections, seed + i, role)
-                            for i in range(n_cb)])
+                   device=None, rotation: int = ROT_HADAMARD, seeds=None):
+    """n_cb blobs back to back, blob i seeded with seed + i (wrapping) or seeds[i],
+    as a uint8 torch tensor on `device` (host numpy array when device is None)."""
+    sl = [seed + i for i in range(n_cb)] if seeds is None else list(seeds)
+    blobs = np.concatenate([tq_make_codebook_ex(head_dim, bits, projections, s, role, rotation) for s in sl])
     if device is None:
         return blobs
     import torch
@@ -203,6 +241,81 @@ def tq_attend(kcbs, n_kcb, vcbs, n_vcb, krec, vrec, q, head_dim, k_bits, v_bits,
     _check(load().tq_attend(head_dim, k_bits, v_bits, projections, _ptr(kcbs), n_kcb, _ptr(vcbs), n_vcb,
                             _ptr(krec), _ptr(vrec), B, Hkv, T, _ptr(q), _dtype_code(q), Hq, scale, _ptr(out),
                             _ptr(work), work.numel(), _ptr(status), _stream(q)), "tq_attend")
+    return out
+
+
+def split_codebooks(n_cb: int, head_dim: int, n_outlier: int, bits: int, seed: int, role: int, device=None):
+    """(normal-part blobs, outlier-part blobs) for groups seeded seed + i: Haar at
+    `bits` over head_dim - n_outlier channels, Walsh-Hadamard at bits + 1 over
+    n_outlier channels with seed (seed + i) XOR OUTLIER_SEED_XOR."""
+    dn = head_dim - n_outlier
+    key = role == ROLE_KEY
+    seeds = [(seed + i) & ((1 << 64) - 1) for i in range(n_cb)]
+    normal = make_codebooks(n_cb, dn, bits, dn if key else 0, seed, role, device, ROT_HAAR, seeds)
+    outlier = make_codebooks(n_cb, n_outlier, bits + 1, n_outlier if key else 0, seed, role, device,
+                             ROT_HADAMARD, [s ^ OUTLIER_SEED_XOR for s in seeds])
+    return normal, outlier
+
+
+def split_record_words(head_dim: int, n_outlier: int, bits: int, role: int) -> tuple[int, int]:
+    dn = head_dim - n_outlier
+    key = role == ROLE_KEY
+    return (tq_record_bytes_ex(dn, bits, dn if key else 0, role, ROT_HAAR) // 4,
+            tq_record_bytes_ex(n_outlier, bits + 1, n_outlier if key else 0, role, ROT_HADAMARD) // 4)
+
+
+def tq_outlier_channels(x, head_dim, n_outlier, chan=None, work=None):
+    import torch
+    G, N, sg, sn = _groups(x, head_dim)
+    if chan is None:
+        chan = torch.empty((G, head_dim), dtype=torch.int32, device=x.device)
+    need = int(load().tq_outlier_workspace_bytes(head_dim, G, N))
+    if work is None:
+        work = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(load().tq_outlier_channels(head_dim, n_outlier, _ptr(x), _dtype_code(x), G, N, sg, sn, _ptr(chan),
+                                      _ptr(work), work.numel(), _stream(x)), "tq_outlier_channels")
+    return chan
+
+
+def tq_encode_split(role, cbs_normal, cbs_outlier, n_cb, x, head_dim, n_outlier, bits, chan,
+                    rec_normal=None, rec_outlier=None, status=None):
+    import torch
+    G, N, sg, sn = _groups(x, head_dim)
+    wn, wo = split_record_words(head_dim, n_outlier, bits, role)
+    if rec_normal is None:
+        rec_normal = torch.empty((G, N, wn), dtype=torch.int32, device=x.device)
+    if rec_outlier is None:
+        rec_outlier = torch.empty((G, N, wo), dtype=torch.int32, device=x.device)
+    _check(load().tq_encode_split(role, head_dim, n_outlier, bits, _ptr(cbs_normal), _ptr(cbs_outlier), n_cb,
+                                  _ptr(x), _dtype_code(x), G, N, sg, sn, _ptr(chan), _ptr(rec_normal),
+                                  _ptr(rec_outlier), _ptr(status), _stream(x)), "tq_encode_split")
+    return rec_normal, rec_outlier
+
+
+def tq_scores_split(cbs_normal, cbs_outlier, n_cb, chan, krec_normal, krec_outlier, q, head_dim, n_outlier, bits,
+                    scale=0.0, out=None, status=None):
+    import torch
+    B, Hkv, T = krec_normal.shape[0], krec_normal.shape[1], krec_normal.shape[2]
+    Hq = q.shape[1]
+    if not q.is_contiguous() or q.shape[0] != B or q.shape[2] != head_dim:
+        raise ValueError("q must be contiguous [B][H_q][head_dim]")
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(load().tq_scores_split(head_dim, n_outlier, bits, _ptr(cbs_normal), _ptr(cbs_outlier), n_cb, _ptr(chan),
+                                  _ptr(krec_normal), _ptr(krec_outlier), B, Hkv, T, _ptr(q), _dtype_code(q), Hq,
+                                  scale, _ptr(out), _ptr(status), _stream(q)), "tq_scores_split")
+    return out
+
+
+def tq_decode_values_split(cbs_normal, cbs_outlier, n_cb, chan, rec_normal, rec_outlier, head_dim, n_outlier, bits,
+                           out=None, status=None):
+    import torch
+    G, N = rec_normal.shape[0], rec_normal.shape[1]
+    if out is None:
+        out = torch.empty((G, N, head_dim), dtype=torch.float32, device=rec_normal.device)
+    _check(load().tq_decode_values_split(head_dim, n_outlier, bits, _ptr(cbs_normal), _ptr(cbs_outlier), n_cb,
+                                         _ptr(chan), _ptr(rec_normal), _ptr(rec_outlier), G, N, _ptr(out),
+                                         _ptr(status), _stream(rec_normal)), "tq_decode_values_split")
     return out
 
 

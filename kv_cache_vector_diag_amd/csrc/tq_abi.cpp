@@ -25,6 +25,21 @@ int check_input(const Layout& L, const void* cbs, int64_t n_cb, const void* x, i
   return TQ_OK;
 }
 
+// Layouts of the two parts of a split head vector: normal part (Haar, bits),
+// outlier part (Walsh-Hadamard, bits + 1); keys project each part onto as many
+// signs as it has coordinates.
+int split_layouts(int role, int head_dim, int n_outlier, int bits, Layout* Ln, Layout* Lo) {
+  if (role != TQ_ROLE_KEY && role != TQ_ROLE_VALUE) return TQ_ERR_INVALID_ROLE;
+  if (head_dim == 0) return TQ_ERR_ZERO_DIMENSION;
+  if (head_dim < 2 || head_dim > kMaxHeadDim) return TQ_ERR_BAD_DIMENSION;
+  if (n_outlier <= 0 || n_outlier >= head_dim) return TQ_ERR_DIMENSION_MISMATCH;
+  const int dn = head_dim - n_outlier;
+  const bool key = role == TQ_ROLE_KEY;
+  int rc = make_layout(dn, bits, key ? dn : 0, role, Ln, kRotHaar);
+  if (rc) return rc;
+  return make_layout(n_outlier, bits + 1, key ? n_outlier : 0, role, Lo, kRotHadamard);
+}
+
 int encode_common(int role, int head_dim, int bits, int projections, const void* cbs, int64_t n_cb,
                   const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec,
                   int32_t* status, void* stream) {
@@ -141,6 +156,91 @@ int tq_rotate(int head_dim, int bits, int projections, int role, const void* cbs
   if (!u || !norms) return TQ_ERR_NULL;
   CodebookArgs cb = make_cb_args(cbs, n_cb, L);
   return launch_rotate_generic(cb, x, x_dtype, G, N, sx_g, sx_n, u, norms, static_cast<hipStream_t>(stream));
+}
+
+size_t tq_outlier_workspace_bytes(int head_dim, int64_t G, int64_t N) {
+  if (head_dim < 2 || head_dim > kMaxHeadDim || G < 0 || N < 0) return 0;
+  return (size_t)(G * outlier_chunks(N) * head_dim) * 16 + 256;
+}
+
+int tq_outlier_channels(int head_dim, int n_outlier, const void* x, int x_dtype, int64_t G, int64_t N,
+                        int64_t sx_g, int64_t sx_n, int32_t* chan, void* work, size_t work_bytes,
+                        void* stream) {
+  if (head_dim == 0) return TQ_ERR_ZERO_DIMENSION;
+  if (head_dim < 2 || head_dim > kMaxHeadDim) return TQ_ERR_BAD_DIMENSION;
+  if (n_outlier <= 0 || n_outlier >= head_dim) return TQ_ERR_DIMENSION_MISMATCH;
+  if (G < 0 || N < 0) return TQ_ERR_EMPTY_INPUT;
+  if (G == 0) return TQ_OK;
+  if (!chan || !work || (N > 0 && !x)) return TQ_ERR_NULL;
+  if (!dtype_ok(x_dtype)) return TQ_ERR_UNSUPPORTED;
+  if ((N > 1 && sx_n < head_dim) || (G > 1 && sx_g < head_dim) || sx_n < 0 || sx_g < 0)
+    return TQ_ERR_DIMENSION_MISMATCH;
+  if (work_bytes < tq_outlier_workspace_bytes(head_dim, G, N)) return TQ_ERR_DIMENSION_MISMATCH;
+  return launch_outlier_channels(x, x_dtype, G, N, sx_g, sx_n, head_dim, n_outlier, chan,
+                                 static_cast<double*>(work), static_cast<hipStream_t>(stream));
+}
+
+int tq_encode_split(int role, int head_dim, int n_outlier, int bits, const void* cbs_normal,
+                    const void* cbs_outlier, int64_t n_cb, const void* x, int x_dtype, int64_t G, int64_t N,
+                    int64_t sx_g, int64_t sx_n, const int32_t* chan, void* rec_normal, void* rec_outlier,
+                    int32_t* status, void* stream) {
+  Layout Ln, Lo;
+  int rc = split_layouts(role, head_dim, n_outlier, bits, &Ln, &Lo);
+  if (rc) return rc;
+  if (n_cb <= 0 || G < 0 || N < 0) return TQ_ERR_EMPTY_INPUT;
+  if (G == 0 || N == 0) return TQ_OK;
+  if (!cbs_normal || !cbs_outlier || !x || !chan || !rec_normal || !rec_outlier) return TQ_ERR_NULL;
+  if (!dtype_ok(x_dtype)) return TQ_ERR_UNSUPPORTED;
+  if ((N > 1 && sx_n < head_dim) || (G > 1 && sx_g < head_dim) || sx_n < 0 || sx_g < 0)
+    return TQ_ERR_DIMENSION_MISMATCH;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_encode_generic(make_cb_args(cbs_normal, n_cb, Ln), x, x_dtype, G, N, sx_g, sx_n,
+                             static_cast<uint32_t*>(rec_normal), status, s,
+                             ChannelMap{chan, head_dim, n_outlier, head_dim});
+  if (rc) return rc;
+  return launch_encode_generic(make_cb_args(cbs_outlier, n_cb, Lo), x, x_dtype, G, N, sx_g, sx_n,
+                               static_cast<uint32_t*>(rec_outlier), status, s,
+                               ChannelMap{chan, head_dim, 0, head_dim});
+}
+
+int tq_scores_split(int head_dim, int n_outlier, int bits, const void* cbs_normal, const void* cbs_outlier,
+                    int64_t n_cb, const int32_t* chan, const void* krec_normal, const void* krec_outlier,
+                    int64_t B, int64_t H_kv, int64_t T, const void* q, int q_dtype, int64_t H_q, float scale,
+                    float* scores, int32_t* status, void* stream) {
+  Layout Ln, Lo;
+  int rc = split_layouts(TQ_ROLE_KEY, head_dim, n_outlier, bits, &Ln, &Lo);
+  if (rc) return rc;
+  if (n_cb <= 0 || B < 0 || H_kv <= 0 || T < 0 || H_q <= 0) return TQ_ERR_EMPTY_INPUT;
+  if (H_q % H_kv) return TQ_ERR_DIMENSION_MISMATCH;
+  if (B * T == 0) return TQ_OK;
+  if (!cbs_normal || !cbs_outlier || !chan || !krec_normal || !krec_outlier || !q || !scores) return TQ_ERR_NULL;
+  if (!dtype_ok(q_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_scores_generic(make_cb_args(cbs_normal, n_cb, Ln), static_cast<const uint32_t*>(krec_normal), B,
+                             H_kv, T, q, q_dtype, H_q, scale, scores, status, s, head_dim,
+                             ChannelMap{chan, head_dim, n_outlier, head_dim}, false);
+  if (rc) return rc;
+  return launch_scores_generic(make_cb_args(cbs_outlier, n_cb, Lo), static_cast<const uint32_t*>(krec_outlier), B,
+                               H_kv, T, q, q_dtype, H_q, scale, scores, status, s, head_dim,
+                               ChannelMap{chan, head_dim, 0, head_dim}, true);
+}
+
+int tq_decode_values_split(int head_dim, int n_outlier, int bits, const void* cbs_normal, const void* cbs_outlier,
+                           int64_t n_cb, const int32_t* chan, const void* rec_normal, const void* rec_outlier,
+                           int64_t G, int64_t N, float* out, int32_t* status, void* stream) {
+  Layout Ln, Lo;
+  int rc = split_layouts(TQ_ROLE_VALUE, head_dim, n_outlier, bits, &Ln, &Lo);
+  if (rc) return rc;
+  if (n_cb <= 0 || G < 0 || N < 0) return TQ_ERR_EMPTY_INPUT;
+  if (G * N == 0) return TQ_OK;
+  if (!cbs_normal || !cbs_outlier || !chan || !rec_normal || !rec_outlier || !out) return TQ_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_decode_generic(make_cb_args(cbs_normal, n_cb, Ln), static_cast<const uint32_t*>(rec_normal), G, N,
+                             out, status, s, head_dim, ChannelMap{chan, head_dim, n_outlier, head_dim});
+  if (rc) return rc;
+  return launch_decode_generic(make_cb_args(cbs_outlier, n_cb, Lo), static_cast<const uint32_t*>(rec_outlier), G,
+                               N, out, status, s, head_dim, ChannelMap{chan, head_dim, 0, head_dim});
 }
 
 }  // extern "C"

@@ -14,7 +14,7 @@ struct CodebookArgs {
   const uint8_t* cbs;
   int64_t stride;      // bytes between blobs
   int64_t n_cb;
-  int d, bits, m, role, k, levels;
+  int d, bits, m, role, k, levels, rotation;
   uint32_t off_c, off_t, off_d, off_s;
   int plane_words, sign_words, rec_words;
 };
@@ -25,6 +25,7 @@ inline CodebookArgs make_cb_args(const void* cbs, int64_t n_cb, const Layout& L)
   a.stride = L.total;
   a.n_cb = n_cb;
   a.d = L.d; a.bits = L.bits; a.m = L.m; a.role = L.role; a.k = L.k; a.levels = L.levels;
+  a.rotation = L.rotation;
   a.off_c = L.off_c; a.off_t = L.off_t; a.off_d = L.off_d; a.off_s = L.off_s;
   a.plane_words = L.plane_words; a.sign_words = L.sign_words; a.rec_words = L.rec_words;
   return a;
@@ -38,8 +39,28 @@ __device__ inline const uint8_t* blob_of(const CodebookArgs& a, int64_t g) {
 __device__ inline bool blob_mismatch(const CodebookArgs& a, const uint8_t* blob) {
   const BlobHeader* h = reinterpret_cast<const BlobHeader*>(blob);
   return h->magic != kBlobMagic || h->version != kBlobVersion || h->head_dim != a.d ||
-         h->bits != a.bits || h->role != a.role || h->projections != a.m;
+         h->bits != a.bits || h->role != a.role || h->projections != a.m || (int)h->rotation != a.rotation;
 }
+
+// Optional channel map of a split head vector: coordinate j of group g's part
+// is channel map[g*stride + off + j] of the full row (of `full` channels).
+// Without a map coordinate j is channel j.  An entry outside [0, full) is
+// reported in the status word and replaced by channel 0.
+struct ChannelMap {
+  const int32_t* map;
+  int64_t stride;
+  int off;
+  int full;
+  __device__ inline int channel(int64_t g, int j, int32_t* status) const {
+    if (!map) return j;
+    int c = map[g * stride + off + j];
+    if ((unsigned)c >= (unsigned)full) {
+      if (status) atomicOr(status, TQ_STATUS_BAD_CHANNEL);
+      c = 0;
+    }
+    return c;
+  }
+};
 
 __device__ inline float bf16_bits_to_float(uint32_t b16) { return __uint_as_float(b16 << 16); }
 

@@ -26,10 +26,12 @@ struct EncodeArgs {
   int64_t G, N, sx_g, sx_n;
   uint32_t* rec;
   int32_t* status;
+  ChannelMap cm;
 };
 
 // Encode one vector per workgroup (64 lanes).  Steps, in the README's order:
-// norm; u = H(D x) (rotation without the 1/sqrt(d), so z = u/|x| ~ N(0,1));
+// norm; u = H(D x) (rotation without the 1/sqrt(d), so z = u/|x| ~ N(0,1)),
+// or u = R x with the stored dense Haar matrix R = sqrt(d) Q;
 // idx_j = #{t_i < z_j}; keys only: residual w = u - n32 c[idx] (sqrt(d) times
 // the rotated residual), gamma = |w|/sqrt(d), signs of S w.
 // This kernel works in float64 (full rate on CDNA4): the rotation of
@@ -53,24 +55,38 @@ __global__ __launch_bounds__(64) void encode_generic_kernel(EncodeArgs a) {
     const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob + a.cb.off_d);
     const int64_t base = g * a.sx_g + t * a.sx_n;
 
+    const bool haar = a.cb.rotation == kRotHaar;
     double ss = 0.0;
     for (int j = lane; j < d; j += kWave) {
-      double xv = (double)load_elem(a.x, a.dtype, base + j);
+      double xv = (double)load_elem(a.x, a.dtype, base + a.cm.channel(g, j, a.status));
       ss += xv * xv;
-      u[j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -xv : xv;
+      if (haar) w[j] = xv;
+      else u[j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -xv : xv;
     }
     ss = wave_sum_f64(ss);
     const bool finite = ss <= 3.4028234663852886e38;
     if (lane == 0 && a.status && !finite) atomicOr(a.status, TQ_STATUS_NON_FINITE);
     __syncthreads();
-    for (int h = 1; h < d; h <<= 1) {
-      for (int p = lane; p < d / 2; p += kWave) {
-        int i = (p / h) * 2 * h + (p % h);
-        double x0 = u[i], x1 = u[i + h];
-        u[i] = x0 + x1;
-        u[i + h] = x0 - x1;
+    if (haar) {
+      // u_j = sum_i R[j][i] x_i: float32 R times float32/bf16/f16 x is exact in float64
+      const float* R = reinterpret_cast<const float*>(blob + a.cb.off_d);
+      for (int j = lane; j < d; j += kWave) {
+        const float* row = R + (int64_t)j * d;
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc = fma((double)row[i], w[i], acc);
+        u[j] = acc;
       }
       __syncthreads();
+    } else {
+      for (int h = 1; h < d; h <<= 1) {
+        for (int p = lane; p < d / 2; p += kWave) {
+          int i = (p / h) * 2 * h + (p % h);
+          double x0 = u[i], x1 = u[i + h];
+          u[i] = x0 + x1;
+          u[i + h] = x0 - x1;
+        }
+        __syncthreads();
+      }
     }
     const double nrm = sqrt(ss);
     const float n32 = (float)nrm;
@@ -138,9 +154,11 @@ struct DecodeArgs {
   int64_t G, N;
   float* out;
   int32_t* status;
+  int64_t out_stride;   // floats between output rows
+  ChannelMap cm;        // output channel of coordinate j (scatter)
 };
 
-// x^ = (n32/d) D (H c[idx]) per vector.
+// x^ = (n32/d) D (H c[idx]) per vector; Haar: x^ = (n32/d) R^T c[idx].
 __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
   __shared__ float u[kMaxHeadDim];
   const int lane = threadIdx.x;
@@ -159,20 +177,29 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeArgs a) {
       u[j] = cent[q];
     }
     __syncthreads();
-    for (int h = 1; h < d; h <<= 1) {
-      for (int p = lane; p < d / 2; p += kWave) {
-        int i = (p / h) * 2 * h + (p % h);
-        float x0 = u[i], x1 = u[i + h];
-        u[i] = x0 + x1;
-        u[i + h] = x0 - x1;
-      }
-      __syncthreads();
-    }
     const float scale = __uint_as_float(r[a.cb.k * W]) / (float)d;
-    float* o = a.out + v * d;
-    for (int j = lane; j < d; j += kWave) {
-      float val = u[j] * scale;
-      o[j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -val : val;
+    float* o = a.out + v * a.out_stride;
+    if (a.cb.rotation == kRotHaar) {
+      const float* R = reinterpret_cast<const float*>(blob + a.cb.off_d);
+      for (int i = lane; i < d; i += kWave) {
+        float acc = 0.0f;
+        for (int j = 0; j < d; ++j) acc = fmaf(R[(int64_t)j * d + i], u[j], acc);
+        o[a.cm.channel(g, i, a.status)] = acc * scale;
+      }
+    } else {
+      for (int h = 1; h < d; h <<= 1) {
+        for (int p = lane; p < d / 2; p += kWave) {
+          int i = (p / h) * 2 * h + (p % h);
+          float x0 = u[i], x1 = u[i + h];
+          u[i] = x0 + x1;
+          u[i + h] = x0 - x1;
+        }
+        __syncthreads();
+      }
+      for (int j = lane; j < d; j += kWave) {
+        float val = u[j] * scale;
+        o[a.cm.channel(g, j, a.status)] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -val : val;
+      }
     }
     __syncthreads();
   }
@@ -230,15 +257,19 @@ struct ScoreArgs {
   float scale;
   float* scores;
   int32_t* status;
+  int64_t q_row;        // elements between query rows
+  ChannelMap cm;        // query channel of coordinate j (gather)
+  int accumulate;       // add into scores instead of overwriting
 };
 
 constexpr int kScoreBlock = 256;
 
-// One workgroup per (b, hq, chunk of 256 tokens).  Prologue: qt = H(D q) in
-// LDS, p = S qt / sqrt(d); then one token per thread:
+// One workgroup per (b, hq, chunk of 256 tokens).  Prologue: qt = H(D q) (Haar:
+// qt = R q) in LDS, p = S qt / sqrt(d); then one token per thread:
 //   s = scale * ((n/d) sum_j qt_j c[idx_j] + sqrt(pi/2)/m gamma sum_i p_i (2 s_i - 1)).
 __global__ __launch_bounds__(kScoreBlock) void scores_generic_kernel(ScoreArgs a) {
   __shared__ float qt[kMaxHeadDim];
+  __shared__ float qraw[kMaxHeadDim];
   __shared__ float p[kMaxProjections];
   __shared__ float cent_s[256];
   const int tid = threadIdx.x;
@@ -255,19 +286,31 @@ __global__ __launch_bounds__(kScoreBlock) void scores_generic_kernel(ScoreArgs a
   const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob + a.cb.off_d);
   const _Float16* S = reinterpret_cast<const _Float16*>(blob + a.cb.off_s);
   for (int i = tid; i < a.cb.levels; i += kScoreBlock) cent_s[i] = cent[i];
+  const bool haar = a.cb.rotation == kRotHaar;
   for (int j = tid; j < d; j += kScoreBlock) {
-    float qv = load_elem(a.q, a.q_dtype, (b * a.Hq + hq) * d + j);
-    qt[j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -qv : qv;
+    float qv = load_elem(a.q, a.q_dtype, (b * a.Hq + hq) * a.q_row + a.cm.channel(g, j, a.status));
+    if (haar) qraw[j] = qv;
+    else qt[j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -qv : qv;
   }
   __syncthreads();
-  for (int hh = 1; hh < d; hh <<= 1) {
-    for (int pp = tid; pp < d / 2; pp += kScoreBlock) {
-      int i = (pp / hh) * 2 * hh + (pp % hh);
-      float x0 = qt[i], x1 = qt[i + hh];
-      qt[i] = x0 + x1;
-      qt[i + hh] = x0 - x1;
+  if (haar) {
+    const float* R = reinterpret_cast<const float*>(blob + a.cb.off_d);
+    for (int j = tid; j < d; j += kScoreBlock) {
+      float acc = 0.0f;
+      for (int i = 0; i < d; ++i) acc = fmaf(R[(int64_t)j * d + i], qraw[i], acc);
+      qt[j] = acc;
     }
     __syncthreads();
+  } else {
+    for (int hh = 1; hh < d; hh <<= 1) {
+      for (int pp = tid; pp < d / 2; pp += kScoreBlock) {
+        int i = (pp / hh) * 2 * hh + (pp % hh);
+        float x0 = qt[i], x1 = qt[i + hh];
+        qt[i] = x0 + x1;
+        qt[i + hh] = x0 - x1;
+      }
+      __syncthreads();
+    }
   }
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
   for (int i = tid; i < m; i += kScoreBlock) {
@@ -295,7 +338,8 @@ __global__ __launch_bounds__(kScoreBlock) void scores_generic_kernel(ScoreArgs a
   const float n = __uint_as_float(r[off + a.cb.sign_words]);
   const float gam = __uint_as_float(r[off + a.cb.sign_words + 1]);
   const float s = (n / (float)d) * mse + (kQjlConst / (float)m) * gam * qjl;
-  a.scores[(b * a.Hq + hq) * a.T + t] = a.scale * s;
+  float* o = a.scores + (b * a.Hq + hq) * a.T + t;
+  *o = a.accumulate ? *o + a.scale * s : a.scale * s;
 }
 
 struct AttendArgs {
@@ -373,17 +417,18 @@ inline int grid_for(int64_t items, int64_t cap) { return (int)(items < cap ? (it
 }  // namespace
 
 int launch_encode_generic(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N,
-                          int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s) {
+                          int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
+                          const ChannelMap& cm) {
   if (G * N == 0) return 0;
-  EncodeArgs a{cb, x, dtype, G, N, sx_g, sx_n, rec, status};
+  EncodeArgs a{cb, x, dtype, G, N, sx_g, sx_n, rec, status, cm};
   hipLaunchKernelGGL(encode_generic_kernel, dim3(grid_for(G * N, 1 << 16)), dim3(64), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
-                          int32_t* status, hipStream_t s) {
+                          int32_t* status, hipStream_t s, int64_t out_stride, const ChannelMap& cm) {
   if (G * N == 0) return 0;
-  DecodeArgs a{cb, rec, G, N, out, status};
+  DecodeArgs a{cb, rec, G, N, out, status, out_stride > 0 ? out_stride : cb.d, cm};
   hipLaunchKernelGGL(decode_generic_kernel, dim3(grid_for(G * N, 1 << 16)), dim3(64), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
@@ -398,9 +443,10 @@ int launch_rotate_generic(const CodebookArgs& cb, const void* x, int dtype, int6
 
 int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t B, int64_t Hkv, int64_t T,
                           const void* q, int q_dtype, int64_t Hq, float scale, float* scores,
-                          int32_t* status, hipStream_t s) {
+                          int32_t* status, hipStream_t s, int64_t q_row, const ChannelMap& cm, bool accumulate) {
   if (B * Hq * T == 0) return 0;
-  ScoreArgs a{cb, krec, B, Hkv, T, q, q_dtype, Hq, scale, scores, status};
+  ScoreArgs a{cb, krec, B, Hkv, T, q, q_dtype, Hq, scale, scores, status, q_row > 0 ? q_row : cb.d, cm,
+              accumulate ? 1 : 0};
   const int64_t chunks = (T + kScoreBlock - 1) / kScoreBlock;
   hipLaunchKernelGGL(scores_generic_kernel, dim3((unsigned)(B * Hq * chunks)), dim3(kScoreBlock), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;

@@ -23,6 +23,7 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 constexpr uint64_t kStreamS = 1ull << 32;
+constexpr uint64_t kStreamHaar = 2ull << 32;
 
 inline uint64_t splitmix64(uint64_t seed, uint64_t i) {
   uint64_t z = seed + (i + 1) * kGamma;
@@ -176,6 +177,74 @@ void lloyd_max(int k, std::vector<double>* cent, std::vector<double>* thr) {
   for (int i = 0; i < L - 1; ++i) (*thr)[i] = 0.5 * (best[i] + best[i + 1]);
 }
 
+// Standard normals from stream `base`: entry e is the cos (even e) or sin (odd
+// e) member of the Box-Muller pair on outputs base + 2*(e/2) and base + 2*(e/2) + 1,
+// u1 = ((x1 >> 11) + 1) 2^-53 in (0, 1], u2 = (x2 >> 11) 2^-53, in float64.
+void gaussians(uint64_t seed, uint64_t base, uint64_t count, double* out) {
+  const double two_pi = 6.283185307179586476925286766559;
+  const double two_m53 = 1.0 / 9007199254740992.0;
+  for (uint64_t e = 0; e < count; e += 2) {
+    uint64_t x1 = splitmix64(seed, base + e);
+    uint64_t x2 = splitmix64(seed, base + e + 1);
+    double u1 = (double)((x1 >> 11) + 1) * two_m53;
+    double u2 = (double)(x2 >> 11) * two_m53;
+    double r = std::sqrt(-2.0 * std::log(u1));
+    double ang = two_pi * u2;
+    out[e] = r * std::cos(ang);
+    if (e + 1 < count) out[e + 1] = r * std::sin(ang);
+  }
+}
+
+// Haar-distributed rotation (README "Modules" rotation: Haar via QR).  G is
+// the d x d Gaussian matrix of the Haar stream (row-major); its QR
+// factorisation by Householder reflections gives Q, whose columns are then
+// signed so that the triangular factor has a positive diagonal (the unique
+// factor with that property, Haar-distributed for Gaussian G).  Output
+// R = float32(sqrt(d) Q), row-major.
+void haar_rotation(uint64_t seed, int d, float* R) {
+  const size_t n = (size_t)d;
+  std::vector<double> A(n * n), Q(n * n, 0.0), V(n * n, 0.0), diag(n);
+  gaussians(seed, kStreamHaar, (uint64_t)n * n, A.data());
+  for (size_t k = 0; k < n; ++k) {
+    // reflector v (unit) with (I - 2 v v^T) A[k:, k] = alpha e_k
+    double nrm = 0.0;
+    for (size_t i = k; i < n; ++i) nrm += A[i * n + k] * A[i * n + k];
+    nrm = std::sqrt(nrm);
+    const double x0 = A[k * n + k];
+    const double alpha = x0 >= 0.0 ? -nrm : nrm;
+    double* v = &V[k * n];
+    for (size_t i = k; i < n; ++i) v[i] = A[i * n + k];
+    v[k] -= alpha;
+    double vn = 0.0;
+    for (size_t i = k; i < n; ++i) vn += v[i] * v[i];
+    vn = std::sqrt(vn);
+    if (vn > 0.0)
+      for (size_t i = k; i < n; ++i) v[i] /= vn;
+    for (size_t j = k; j < n; ++j) {
+      double dot = 0.0;
+      for (size_t i = k; i < n; ++i) dot += v[i] * A[i * n + j];
+      for (size_t i = k; i < n; ++i) A[i * n + j] -= 2.0 * v[i] * dot;
+    }
+    diag[k] = A[k * n + k];
+  }
+  // Q = H_0 H_1 ... H_{n-1}: apply the reflectors to I from the last one
+  for (size_t i = 0; i < n; ++i) Q[i * n + i] = 1.0;
+  for (size_t kk = n; kk-- > 0;) {
+    const double* v = &V[kk * n];
+    for (size_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (size_t i = kk; i < n; ++i) dot += v[i] * Q[i * n + j];
+      for (size_t i = kk; i < n; ++i) Q[i * n + j] -= 2.0 * v[i] * dot;
+    }
+  }
+  const double sd = std::sqrt((double)d);
+  for (size_t i = 0; i < n; ++i)
+    for (size_t j = 0; j < n; ++j) R[i * n + j] = (float)(sd * (diag[j] < 0.0 ? -Q[i * n + j] : Q[i * n + j]));
+}
+
+int make_codebook(int head_dim, int bits, int projections, uint64_t seed, int role, int rotation, void* blob,
+                  size_t blob_bytes);
+
 }  // namespace
 }  // namespace tq
 
@@ -184,21 +253,44 @@ using namespace tq;
 extern "C" {
 
 size_t tq_codebook_bytes(int head_dim, int bits, int projections, int role) {
+  return tq_codebook_bytes_ex(head_dim, bits, projections, role, TQ_ROT_HADAMARD);
+}
+
+size_t tq_codebook_bytes_ex(int head_dim, int bits, int projections, int role, int rotation) {
   Layout L;
-  if (make_layout(head_dim, bits, projections, role, &L)) return 0;
+  if (make_layout(head_dim, bits, projections, role, &L, rotation)) return 0;
   return L.total;
 }
 
 size_t tq_record_bytes(int head_dim, int bits, int projections, int role) {
+  return tq_record_bytes_ex(head_dim, bits, projections, role, TQ_ROT_HADAMARD);
+}
+
+size_t tq_record_bytes_ex(int head_dim, int bits, int projections, int role, int rotation) {
   Layout L;
-  if (make_layout(head_dim, bits, projections, role, &L)) return 0;
+  if (make_layout(head_dim, bits, projections, role, &L, rotation)) return 0;
   return 4u * (size_t)L.rec_words;
 }
 
 int tq_make_codebook(int head_dim, int bits, int projections, uint64_t seed, int role,
                      void* blob, size_t blob_bytes) {
+  return make_codebook(head_dim, bits, projections, seed, role, TQ_ROT_HADAMARD, blob, blob_bytes);
+}
+
+int tq_make_codebook_ex(int head_dim, int bits, int projections, uint64_t seed, int role, int rotation,
+                        void* blob, size_t blob_bytes) {
+  return make_codebook(head_dim, bits, projections, seed, role, rotation, blob, blob_bytes);
+}
+
+}  // extern "C"
+
+namespace tq {
+namespace {
+
+int make_codebook(int head_dim, int bits, int projections, uint64_t seed, int role, int rotation, void* blob,
+                  size_t blob_bytes) {
   Layout L;
-  int rc = make_layout(head_dim, bits, projections, role, &L);
+  int rc = make_layout(head_dim, bits, projections, role, &L, rotation);
   if (rc) return rc;
   if (!blob) return TQ_ERR_NULL;
   if (blob_bytes < L.total) return TQ_ERR_BAD_BLOB;
@@ -220,6 +312,7 @@ int tq_make_codebook(int head_dim, int bits, int projections, uint64_t seed, int
   h.off_d = L.off_d;
   h.off_s = L.off_s;
   h.total_bytes = L.total;
+  h.rotation = (uint32_t)rotation;
   std::memcpy(p, &h, sizeof h);
 
   std::vector<double> c, t;
@@ -230,30 +323,30 @@ int tq_make_codebook(int head_dim, int bits, int projections, uint64_t seed, int
   for (int i = 0; i < L.levels - 1; ++i) tf[i] = (float)t[i];
   tf[L.levels - 1] = INFINITY;
 
-  uint32_t* dw = reinterpret_cast<uint32_t*>(p + L.off_d);
-  for (int j = 0; j < head_dim; ++j) {
-    uint64_t word = splitmix64(seed, (uint64_t)(j / 64));
-    if ((word >> (j % 64)) & 1) dw[j / 32] |= 1u << (j % 32);
+  if (rotation == TQ_ROT_HAAR) {
+    haar_rotation(seed, head_dim, reinterpret_cast<float*>(p + L.off_d));
+  } else {
+    uint32_t* dw = reinterpret_cast<uint32_t*>(p + L.off_d);
+    for (int j = 0; j < head_dim; ++j) {
+      uint64_t word = splitmix64(seed, (uint64_t)(j / 64));
+      if ((word >> (j % 64)) & 1) dw[j / 32] |= 1u << (j % 32);
+    }
   }
 
   if (role == TQ_ROLE_KEY) {
     uint16_t* s = reinterpret_cast<uint16_t*>(p + L.off_s);
     const uint64_t count = (uint64_t)L.m * (uint64_t)head_dim;
-    const double two_pi = 6.283185307179586476925286766559;
-    const double two_m53 = 1.0 / 9007199254740992.0;
-    for (uint64_t e = 0; e < count; e += 2) {
-      uint64_t x1 = splitmix64(seed, kStreamS + e);
-      uint64_t x2 = splitmix64(seed, kStreamS + e + 1);
-      double u1 = (double)((x1 >> 11) + 1) * two_m53;
-      double u2 = (double)(x2 >> 11) * two_m53;
-      double r = std::sqrt(-2.0 * std::log(u1));
-      double ang = two_pi * u2;
-      s[e] = double_to_half(r * std::cos(ang));
-      if (e + 1 < count) s[e + 1] = double_to_half(r * std::sin(ang));
-    }
+    std::vector<double> g(count);
+    gaussians(seed, kStreamS, count, g.data());
+    for (uint64_t e = 0; e < count; ++e) s[e] = double_to_half(g[e]);
   }
   return TQ_OK;
 }
+
+}  // namespace
+}  // namespace tq
+
+extern "C" {
 
 int tq_memory_stats(int head_dim, int k_bits, int v_bits, int projections, int64_t seq_len,
                     int64_t layers, int64_t kv_heads, double out[4]) {
@@ -276,7 +369,7 @@ const char* tq_status_string(int code) {
   switch (code) {
     case TQ_OK: return "ok";
     case TQ_ERR_ZERO_DIMENSION: return "ZeroDimension: head_dim is 0";
-    case TQ_ERR_BAD_DIMENSION: return "BadDimension: head_dim must be a power of two in [2, 512]";
+    case TQ_ERR_BAD_DIMENSION: return "BadDimension: head_dim must be in [2, 512] (a power of two for Walsh-Hadamard)";
     case TQ_ERR_INVALID_BIT_WIDTH: return "InvalidBitWidth: keys need bits in [2, 9], values in [1, 8]";
     case TQ_ERR_ZERO_PROJECTIONS: return "ZeroProjections: keys need projections >= 1";
     case TQ_ERR_DIMENSION_MISMATCH: return "DimensionMismatch: sizes or strides are inconsistent";
@@ -288,6 +381,7 @@ const char* tq_status_string(int code) {
     case TQ_ERR_INVALID_ROLE: return "InvalidRole";
     case TQ_ERR_INVALID_PROJECTIONS: return "InvalidProjections: projections must be <= 1024";
     case TQ_ERR_UNSUPPORTED: return "Unsupported dtype or alignment";
+    case TQ_ERR_INVALID_ROTATION: return "InvalidRotation: rotation must be TQ_ROT_HADAMARD or TQ_ROT_HAAR";
     default: return "unknown status";
   }
 }

@@ -10,14 +10,22 @@
 namespace tq {
 
 int launch_encode_generic(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N,
-                          int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
+                          int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
+                          const ChannelMap& cm = ChannelMap{});
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
-                          int32_t* status, hipStream_t s);
+                          int32_t* status, hipStream_t s, int64_t out_stride = 0,
+                          const ChannelMap& cm = ChannelMap{});
 int launch_rotate_generic(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N,
                           int64_t sx_g, int64_t sx_n, float* u, float* norms, hipStream_t s);
 int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t B, int64_t Hkv, int64_t T,
                           const void* q, int q_dtype, int64_t Hq, float scale, float* scores,
-                          int32_t* status, hipStream_t s);
+                          int32_t* status, hipStream_t s, int64_t q_row = 0,
+                          const ChannelMap& cm = ChannelMap{}, bool accumulate = false);
+// Outlier channel selection: float64 channel sums over token chunks, then a
+// per-group ranking into the channel map.
+int64_t outlier_chunks(int64_t N);
+int launch_outlier_channels(const void* x, int dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, int d,
+                            int n_out, int32_t* chan, double* work, hipStream_t s);
 int launch_attend_generic(const CodebookArgs& vcb, const uint32_t* vrec, const float* scores, int64_t B,
                           int64_t Hkv, int64_t T, int64_t Hq, float* out, hipStream_t s);
 

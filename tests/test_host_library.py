@@ -31,10 +31,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def _parse_blob(blob):
-    (magic, ver, d, bits, m, role, k, levels, seed, oc, ot, od, os_, total, _) = struct.unpack_from(
+    (magic, ver, d, bits, m, role, k, levels, seed, oc, ot, od, os_, total, rot) = struct.unpack_from(
         "<IIiiiiiiQIIIIII", blob.tobytes(), 0)
     return dict(magic=magic, ver=ver, d=d, bits=bits, m=m, role=role, k=k, levels=levels, seed=seed,
-                off_c=oc, off_t=ot, off_d=od, off_s=os_, total=total)
+                off_c=oc, off_t=ot, off_d=od, off_s=os_, total=total, rotation=rot)
 
 
 @pytest.mark.parametrize("d,bits,m,role,seed", [
@@ -47,7 +47,7 @@ def test_blob_matches_oracle(d, bits, m, role, seed):
     assert blob.nbytes == b.tq_codebook_bytes(d, bits, m, role) and blob.nbytes % 256 == 0
     h = _parse_blob(blob)
     qz = tq.Quantizer(d, bits, m, seed, role)
-    assert h["magic"] == 0x42435154 and h["ver"] == 1
+    assert h["magic"] == 0x42435154 and h["ver"] == 1 and h["rotation"] == 0
     assert (h["d"], h["bits"], h["role"], h["k"], h["levels"], h["seed"]) == (d, bits, role, qz.k, 1 << qz.k, seed)
     assert h["m"] == (m if role == 0 else 0)
     L = 1 << qz.k
@@ -65,6 +65,60 @@ def test_blob_matches_oracle(d, bits, m, role, seed):
         assert np.array_equal(S.reshape(m, d), qjl_matrix(seed, m, d))
     else:
         assert h["off_s"] == 0
+
+
+@pytest.mark.parametrize("d,bits,m,role,seed", [
+    (224, 3, 224, 0, 5), (224, 3, 0, 1, 5), (224, 8, 0, 1, 77), (12, 4, 12, 0, 99), (3, 2, 1, 0, 1), (2, 1, 0, 1, 8),
+])
+def test_haar_blob_matches_oracle(d, bits, m, role, seed):
+    blob = b.tq_make_codebook_ex(d, bits, m, seed, role, b.ROT_HAAR)
+    assert blob.nbytes == b.tq_codebook_bytes_ex(d, bits, m, role, b.ROT_HAAR) and blob.nbytes % 256 == 0
+    h = _parse_blob(blob)
+    qz = tq.Quantizer(d, bits, m, seed, role, rotation=tq.ROT_HAAR)
+    assert h["rotation"] == 1 and (h["d"], h["bits"], h["k"], h["seed"]) == (d, bits, qz.k, seed)
+    L = 1 << qz.k
+    c = np.frombuffer(blob[h["off_c"]:h["off_c"] + 4 * L].tobytes(), dtype="<f4").astype(np.float64)
+    assert np.array_equal(c, qz.c32)
+    R = np.frombuffer(blob[h["off_d"]:h["off_d"] + 4 * d * d].tobytes(), dtype="<f4").astype(np.float64)
+    R = R.reshape(d, d)
+    # two independent float64 QR factorisations (Householder here, LAPACK in the
+    # oracle) agree to ~1e-14; after rounding to float32 an entry may sit on the
+    # other side of a rounding boundary: allow a handful of one-ulp differences
+    diff = R != qz.R
+    ulp = np.spacing(np.abs(qz.R).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(R - qz.R)[diff] <= ulp[diff])
+    assert diff.sum() <= max(2, d * d // 5000)
+    if role == 0:
+        S = np.frombuffer(blob[h["off_s"]:h["off_s"] + 2 * m * d].tobytes(), dtype="<f2").astype(np.float64)
+        assert np.array_equal(S.reshape(m, d), qz.S)
+    assert b.tq_record_bytes_ex(d, bits, m, role, b.ROT_HAAR) == 4 * qz.words
+
+
+def test_split_host_validation():
+    lib = b.load()
+    # normal part Haar 224 at bits, outlier part Hadamard 32 at bits + 1
+    assert b.split_record_words(256, 32, 3, b.ROLE_KEY) == (23, 6)
+    assert b.split_record_words(256, 32, 3, b.ROLE_VALUE) == (22, 5)
+    assert lib.tq_encode_split(0, 256, 24, 3, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None,
+                               None) == -2                                  # outlier width not a power of two
+    assert lib.tq_encode_split(0, 256, 32, 9, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None,
+                               None) == -3                                  # outlier part would need 10 bits
+    assert lib.tq_encode_split(0, 256, 0, 3, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None,
+                               None) == -5
+    assert lib.tq_encode_split(0, 256, 32, 3, None, None, 1, None, 1, 0, 1, 256, 256, None, None, None, None,
+                               None) == 0
+    assert lib.tq_encode_split(0, 256, 32, 3, None, None, 1, None, 1, 2, 1, 256, 256, None, None, None, None,
+                               None) == -8
+    assert lib.tq_outlier_channels(256, 256, None, 1, 1, 1, 256, 256, None, None, 0, None) == -5
+    assert lib.tq_outlier_channels(600, 8, None, 1, 1, 1, 600, 600, None, None, 0, None) == -2
+    assert lib.tq_outlier_workspace_bytes(256, 256, 16384) == 256 * 32 * 256 * 16 + 256
+    assert b.tq_codebook_bytes_ex(224, 3, 224, 0, 2) == 0
+    with pytest.raises(b.TQError) as e:
+        b.tq_make_codebook_ex(224, 3, 224, 1, 0, 2)
+    assert e.value.code == -14
+    with pytest.raises(b.TQError) as e:
+        b.tq_make_codebook_ex(224, 3, 224, 1, 0, b.ROT_HADAMARD)
+    assert e.value.code == -2
 
 
 def test_record_and_codebook_sizes_match_oracle():
