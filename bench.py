@@ -260,12 +260,102 @@ def bench_c4(args, torch, b):
                          "traffic": _traffic("attend_c4", fused_bytes), "kernel": "attend"}}
 
 
+def bench_c5(args, torch, b):
+    """Mixed-precision layers: 32 layers x 8 kv heads x 16384 tokens, d=256, bf16 K and V
+    with per-channel std log-uniform in [0.5, 8] (seed 5).  Layers 0, 1, 30, 31: K b=8
+    (7-bit Lloyd-Max + 256 QJL signs) and V 8-bit; other layers: 32 outlier channels by
+    variance at b+1 = 4 bits (Walsh-Hadamard), 224 normal channels at b = 3 bits (Haar)."""
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    L, Hkv, T, d, n_out, seed = 32, 8, 16384, 256, 32, 5
+    G = L * Hkv
+    Kd = torch.empty((G, T, d), dtype=torch.bfloat16, device=dev)
+    Vd = torch.empty((G, T, d), dtype=torch.bfloat16, device=dev)
+    for l in range(L):
+        gl = list(range(l * Hkv, (l + 1) * Hkv))
+        Kd[gl[0]:gl[-1] + 1] = inputs.to_torch(inputs.kv_channel_std(seed, G, T, d, stream=inputs.STREAM_K,
+                                                                     groups=gl)[0], "bf16", dev)
+        Vd[gl[0]:gl[-1] + 1] = inputs.to_torch(inputs.kv_channel_std(seed, G, T, d, stream=inputs.STREAM_V,
+                                                                     groups=gl)[0], "bf16", dev)
+    edges = [(0, 2 * Hkv), ((L - 2) * Hkv, L * Hkv)]          # boundary layers 0,1 and 30,31
+    s0, s1 = 2 * Hkv, (L - 2) * Hkv                            # split layers 2..29
+    GS = s1 - s0
+    kcb8 = [b.make_codebooks(e1 - e0, d, 8, d, seed, b.ROLE_KEY, dev, seeds=[seed + g for g in range(e0, e1)])
+            for e0, e1 in edges]
+    vcb8 = [b.make_codebooks(e1 - e0, d, 8, 0, seed, b.ROLE_VALUE, dev, seeds=[seed + g for g in range(e0, e1)])
+            for e0, e1 in edges]
+    kcbn, kcbo = b.split_codebooks(GS, d, n_out, 3, seed + s0, b.ROLE_KEY, device=dev)
+    vcbn, vcbo = b.split_codebooks(GS, d, n_out, 3, seed + s0, b.ROLE_VALUE, device=dev)
+    kw8 = b.tq_record_bytes(d, 8, d, b.ROLE_KEY) // 4
+    vw8 = b.tq_record_bytes(d, 8, 0, b.ROLE_VALUE) // 4
+    kwn, kwo = b.split_record_words(d, n_out, 3, b.ROLE_KEY)
+    vwn, vwo = b.split_record_words(d, n_out, 3, b.ROLE_VALUE)
+    krec8 = [torch.empty((e1 - e0, T, kw8), dtype=torch.int32, device=dev) for e0, e1 in edges]
+    vrec8 = [torch.empty((e1 - e0, T, vw8), dtype=torch.int32, device=dev) for e0, e1 in edges]
+    krn = torch.empty((GS, T, kwn), dtype=torch.int32, device=dev)
+    kro = torch.empty((GS, T, kwo), dtype=torch.int32, device=dev)
+    vrn = torch.empty((GS, T, vwn), dtype=torch.int32, device=dev)
+    vro = torch.empty((GS, T, vwo), dtype=torch.int32, device=dev)
+    kchan = torch.empty((GS, d), dtype=torch.int32, device=dev)
+    vchan = torch.empty((GS, d), dtype=torch.int32, device=dev)
+    work = torch.empty(b.load().tq_outlier_workspace_bytes(d, GS, T), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_outlier_channels(Kd[s0:s1], d, n_out, chan=kchan, work=work)
+        b.tq_encode_split(b.ROLE_KEY, kcbn, kcbo, GS, Kd[s0:s1], d, n_out, 3, kchan, krn, kro, status)
+        for (e0, e1), cb, rec in zip(edges, kcb8, krec8):
+            b.tq_encode_keys(cb, e1 - e0, Kd[e0:e1], d, 8, d, rec=rec, status=status)
+        if ev:
+            ev[1].record()
+        b.tq_outlier_channels(Vd[s0:s1], d, n_out, chan=vchan, work=work)
+        b.tq_encode_split(b.ROLE_VALUE, vcbn, vcbo, GS, Vd[s0:s1], d, n_out, 3, vchan, vrn, vro, status)
+        for (e0, e1), cb, rec in zip(edges, vcb8, vrec8):
+            b.tq_encode_values(cb, e1 - e0, Vd[e0:e1], d, 8, rec=rec, status=status)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    evs = [_events(torch, 3) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0
+    k_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    v_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    GB = G - GS
+    row = T * d * 2
+    cbk = sum(c.numel() for c in kcb8) + kcbn.numel() + kcbo.numel()
+    cbv = sum(c.numel() for c in vcb8) + vcbn.numel() + vcbo.numel()
+    # algorithmic bytes: boundary layers read once; split layers read twice (variance pass + encode)
+    kb = GB * row + 2 * GS * row + GB * T * kw8 * 4 + GS * T * (kwn + kwo) * 4 + cbk
+    vb = GB * row + 2 * GS * row + GB * T * vw8 * 4 + GS * T * (vwn + vwo) * 4 + cbv
+    return {"metric": "mixed-precision encode GB/s (K and V, 32 layers)", "value": (kb + vb) / (ms_step * 1e-3) / 1e9,
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+            "config": {"workload": "mixed-precision layers: 32 layers x 8 kv heads x 16384 tokens, d=256, bf16 "
+                                   "with per-channel std log-U[0.5,8]; layers 0,1,30,31 b=8; others b=3 with 32 "
+                                   "outlier channels at 4 bits (Walsh-Hadamard) + 224 at 3 bits (Haar)"},
+            "encode_keys_ms": k_ms, "encode_keys_GBps": kb / (k_ms * 1e-3) / 1e9,
+            "encode_values_ms": v_ms, "encode_values_GBps": vb / (v_ms * 1e-3) / 1e9,
+            "roofline": {"bound": "hbm", "achieved": kb / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": kb / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "traffic": _traffic("encode_c5", kb), "kernel": "encode_keys (all layers)"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4"])
+    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -298,7 +388,7 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": reps + 1,
                                                "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}}))
         return
-    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4}[args.config]
+    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5}[args.config]
     line = fn(args, torch, b)
     if args.config == "c3":
         line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_c3()
