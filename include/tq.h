@@ -168,9 +168,12 @@ int tq_scores(int head_dim, int bits, int projections,
 
 /* Attention output over compressed K and V for one decode step:
  * o[b][hq] = sum_t softmax_t(scores[b][hq][t]) * x^_t, the values decoded on
- * the fly (never materialised).  `work` is caller scratch of
- * tq_attend_workspace_bytes(...) bytes.  Key and value codebooks are separate
- * arrays (kcbs, vcbs) with their own n_cb. */
+ * the fly (never materialised) and summed in the rotated domain, one inverse
+ * transform per (b, hq); the softmax is split over chunks of 1024 tokens and
+ * merged by log-sum-exp.  `work` is caller scratch of
+ * tq_attend_workspace_bytes(...) bytes (scores, then per-chunk partials).  Key
+ * and value codebooks are separate arrays (kcbs, vcbs) with their own n_cb.
+ * T == 0 gives o = 0. */
 size_t tq_attend_workspace_bytes(int head_dim, int64_t B, int64_t H_q, int64_t T);
 int tq_attend(int head_dim, int k_bits, int v_bits, int projections,
               const void* kcbs, int64_t n_kcb, const void* vcbs, int64_t n_vcb,

@@ -108,10 +108,16 @@ int tq_scores(int head_dim, int bits, int projections, const void* cbs, int64_t 
                                scores, status, static_cast<hipStream_t>(stream));
 }
 
+// Scratch of tq_attend: the scores [B][H_q][T], then (256-byte aligned) the
+// per-chunk partials [B*H_q][ceil(T/1024)][head_dim + 2] of the split softmax.
+static size_t attend_scores_bytes(int64_t B, int64_t H_q, int64_t T) {
+  return ((size_t)(B * H_q * T) * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t tq_attend_workspace_bytes(int head_dim, int64_t B, int64_t H_q, int64_t T) {
-  (void)head_dim;
-  if (B < 0 || H_q < 0 || T < 0) return 0;
-  return (size_t)(B * H_q * T) * sizeof(float) + 256;
+  if (head_dim < 2 || head_dim > kMaxHeadDim || B < 0 || H_q < 0 || T < 0) return 0;
+  return attend_scores_bytes(B, H_q, T) + (size_t)(B * H_q * attend_chunks(T) * (head_dim + 2)) * sizeof(float) +
+         256;
 }
 
 int tq_attend(int head_dim, int k_bits, int v_bits, int projections, const void* kcbs, int64_t n_kcb,
@@ -141,6 +147,10 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections, const void*
              : launch_scores_generic(kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q, scale,
                                      sc, status, s);
     if (rc) return rc;
+  }
+  if (attend_split_supported(vcb)) {
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(work) + attend_scores_bytes(B, H_q, T));
+    return launch_attend_split(vcb, static_cast<const uint32_t*>(vrec), sc, B, H_kv, T, H_q, part, out, s);
   }
   return launch_attend_generic(vcb, static_cast<const uint32_t*>(vrec), sc, B, H_kv, T, H_q, out, s);
 }

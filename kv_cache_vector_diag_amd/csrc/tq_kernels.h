@@ -21,6 +21,12 @@ int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t 
                           const void* q, int q_dtype, int64_t Hq, float scale, float* scores,
                           int32_t* status, hipStream_t s, int64_t q_row = 0,
                           const ChannelMap& cm = ChannelMap{}, bool accumulate = false);
+// Split-token attention output (any power-of-two d in [8, 512], value k <= 8):
+// per-chunk partials in `part` ([B*Hq][attend_chunks(T)][d + 2] floats), then a merge.
+int64_t attend_chunks(int64_t T);
+bool attend_split_supported(const CodebookArgs& vcb);
+int launch_attend_split(const CodebookArgs& vcb, const uint32_t* vrec, const float* scores, int64_t B,
+                        int64_t Hkv, int64_t T, int64_t Hq, float* part, float* out, hipStream_t s);
 // Outlier channel selection: float64 channel sums over token chunks, then a
 // per-group ranking into the channel map.
 int64_t outlier_chunks(int64_t N);

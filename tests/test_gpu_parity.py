@@ -133,6 +133,44 @@ def test_long_context_attend(gpu_lib):
     assert_close(o.cpu().numpy(), ref, "attend")
 
 
+@pytest.mark.parametrize("d,kb,vb,m,B,Hkv,Hq,T", [
+    (128, 3, 4, 128, 2, 2, 8, 2500),      # GQA 4:1, 3 chunks with a ragged last one
+    (64, 2, 8, 64, 1, 2, 2, 1030),        # 8-bit values, generic scores
+    (256, 4, 1, 256, 1, 1, 2, 1),         # one token
+    (8, 2, 3, 16, 1, 1, 1, 2049),         # one lane per token
+    (512, 3, 2, 512, 1, 1, 1, 700),
+])
+def test_attend_shapes(gpu_lib, d, kb, vb, m, B, Hkv, Hq, T):
+    import torch
+    b = gpu_lib
+    seed = 9
+    K = inputs.to_torch(inputs.kv_normal(seed, B * Hkv, T, d, inputs.STREAM_K), "bf16", DEV)
+    V = inputs.to_torch(inputs.kv_normal(seed, B * Hkv, T, d, inputs.STREAM_V), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    kcb, kq = _codebooks(b, Hkv, d, kb, m, seed, tq.ROLE_KEY)
+    vcb, vq = _codebooks(b, Hkv, d, vb, 0, seed + 100, tq.ROLE_VALUE)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, kb, m).view(B, Hkv, T, -1)
+    vrec = b.tq_encode_values(vcb, Hkv, V, d, vb).view(B, Hkv, T, -1)
+    o = b.tq_attend(kcb, Hkv, vcb, Hkv, krec, vrec, q, d, kb, vb, m)
+    torch.cuda.synchronize()
+    ref = tq.attend(kq, rec_np(krec), vq, rec_np(vrec), inputs.exact_values(q))
+    assert_close(o.cpu().numpy(), ref, "attend")
+
+
+def test_attend_empty_context_gives_zero(gpu_lib):
+    import torch
+    b = gpu_lib
+    d = 128
+    kcb, _ = _codebooks(b, 2, d, 2, 128, 1, tq.ROLE_KEY)
+    vcb, _ = _codebooks(b, 2, d, 2, 0, 1, tq.ROLE_VALUE)
+    krec = torch.empty((1, 2, 0, 10), dtype=torch.int32, device=DEV)
+    vrec = torch.empty((1, 2, 0, 9), dtype=torch.int32, device=DEV)
+    q = inputs.to_torch(inputs.queries(1, 1, 4, d), "bf16", DEV)
+    o = b.tq_attend(kcb, 2, vcb, 2, krec, vrec, q, d, 2, 2, 128, out=torch.full((1, 4, d), 7.0, device=DEV))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(o).item() == 0
+
+
 @pytest.mark.parametrize("d,bits,m,dtype", [(8, 4, 16, "f32"), (2, 2, 1, "bf16"), (32, 5, 33, "f16"),
                                             (256, 8, 256, "bf16"), (512, 9, 1024, "bf16"), (64, 3, 64, "f32")])
 def test_generic_shapes(gpu_lib, d, bits, m, dtype):
