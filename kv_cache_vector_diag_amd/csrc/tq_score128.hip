@@ -30,10 +30,14 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kM = 128;
-constexpr int kBlock = 256;
+// Workgroup size: 16 waves (one workgroup per CU) while the A fragments fit in
+// 128 VGPRs; 8 waves for the 3-plane codebook, whose fragments need more.
+template <int K>
+constexpr int block_threads() { return K <= 2 ? 1024 : 512; }
 
 struct Score128Args {
   const uint8_t* cbs;
@@ -67,8 +71,10 @@ __device__ __host__ constexpr int subset_bits(int s) {
 }
 
 template <int K>
-__global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
+__global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Args a) {
   using Mk = Masks<K>;
+  constexpr int kBlock = block_threads<K>();
+  constexpr int kWaves = kBlock / 64;
   constexpr int L = 1 << K;
   constexpr int NMF = Mk::kMfma;                 // MFMAs per tile
   __shared__ float qt[4][kD];
@@ -77,6 +83,7 @@ __global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
   __shared__ float consts[4][4];                 // per head: delta_mse, delta_qjl, C_mse, C_qjl
   __shared__ float coef[8];                      // a_P
   __shared__ __align__(16) i32x4 afrag[NMF * 64];
+  __shared__ int fx[4 * Mk::kMasks * kD];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t grp = blockIdx.x / a.blocks_per_group;      // (b, kv head)
@@ -125,12 +132,35 @@ __global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
     }
     __syncthreads();
   }
-  for (int e = tid; e < 4 * kM; e += kBlock) {
-    const int hh = e >> 7, i = e & 127;
-    float acc = 0.0f;
-    const _Float16* row = S + i * kD;
-    for (int j = 0; j < kD; ++j) acc = fmaf((float)row[j], qt[hh][j], acc);
-    pp[hh][i] = acc * 0.08838834764831845f;     // 1/sqrt(128)
+  if (tid < 4 * kM) {
+    // p = S qt / sqrt(d): threads 4i .. 4i+3 own row i, a quarter of it each (four
+    // 16-byte loads issued together), all four heads; then a 4-lane reduction
+    const int i = tid >> 2, qtr = tid & 3;
+    const uint4* row = reinterpret_cast<const uint4*>(S + i * kD + 32 * qtr);
+    uint4 w[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) w[v] = row[v];
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t ww[4] = {w[v].x, w[v].y, w[v].z, w[v].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 pr = __builtin_bit_cast(f16x2, ww[e]);
+        const int j = 32 * qtr + 8 * v + 2 * e;
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          acc[hh] = fmaf((float)pr[0], qt[hh][j], acc[hh]);
+          acc[hh] = fmaf((float)pr[1], qt[hh][j + 1], acc[hh]);
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      acc[hh] += __shfl_xor(acc[hh], 1, 64);
+      acc[hh] += __shfl_xor(acc[hh], 2, 64);
+    }
+    pp[qtr][i] = acc[qtr] * 0.08838834764831845f;       // 1/sqrt(128)
   }
   __syncthreads();
   if (wave < 4) {
@@ -163,36 +193,50 @@ __global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
     consts[hh][part] = vm > 0.0f ? vm * (1.0f / 1073741824.0f) : 1.0f;   // value of one unit, 2^30 units max
   }
   __syncthreads();
+  // Fixed-point query values, once each: fx[hh][s][j] for mask s (s == kPlaneMasks:
+  // the sign mask, value 2 p_j; else 2 a_s qt_j), in units of consts[hh][part],
+  // pre-divided by 2^(j mod 8) (-128 for j mod 8 == 7: the top bit of a byte).
+  for (int e = tid; e < 4 * Mk::kMasks * kD; e += kBlock) {
+    const int j = e & (kD - 1), sm = (e >> 7) % Mk::kMasks, hh = (e >> 7) / Mk::kMasks;
+    int V = 0;
+    if (hh < a.gq) {
+      const bool sign_mask = sm == Mk::kPlaneMasks;
+      const float val = sign_mask ? 2.0f * pp[hh][j] : 2.0f * coef[sm] * qt[hh][j];
+      const int sh = j & 7;
+      const float div = sh == 7 ? -128.0f : (float)(1 << sh);
+      V = (int)rint((double)val / ((double)consts[hh][sign_mask ? 1 : 0] * (double)div));
+    }
+    fx[(hh * Mk::kMasks + sm) * kD + j] = V;
+  }
+  __syncthreads();
   // A fragment of MFMA f = 2*w2 + g, lane l: row m = l%32, K = 16(l/32) + 4q + byte.
   // Lane half hl of MFMA (w2, g) carries list word 2*w2 + hl; bit (8*byte + 4g + q)
-  // of that word, pre-divided by 2^(4g+q) (-128 for the top bit).
-  for (int idx = tid; idx < NMF * 64 * 16; idx += kBlock) {
-    const int ent = idx & 15, ln = (idx >> 4) & 63, f = idx >> 10;
+  // of that word.  Row m = 8 hh + 4 part + limb holds signed int8 limb `limb` of
+  // the value (zero where the mask belongs to the other part).
+  for (int idx = tid; idx < NMF * 64 * 4; idx += kBlock) {
+    const int q = idx & 3, ln = (idx >> 2) & 63, f = idx >> 8;
     const int w2 = f >> 1, g = f & 1;
     const int m = ln & 31, hl = ln >> 5;
-    const int q = ent >> 2, byt = ent & 3;
     const int li = 2 * w2 + hl;                 // list word: mask li/4, word li%4
     const int mask = li >> 2, ww = li & 3;
     const int hh = m >> 3, part = (m >> 2) & 1, limb = m & 3;
-    const int bitpos = 8 * byt + 4 * g + q;
-    const int jj = 32 * ww + bitpos;             // coordinate or projection index
-    int v8 = 0;
     const bool is_sign_mask = mask == Mk::kPlaneMasks;
+    uint32_t packed = 0;
     if (hh < a.gq && part == (is_sign_mask ? 1 : 0)) {
-      const float val = is_sign_mask ? 2.0f * pp[hh][jj] : 2.0f * coef[mask] * qt[hh][jj];
-      const int sh = 4 * g + q;
-      const float div = sh == 7 ? -128.0f : (float)(1 << sh);
-      const double units = (double)val / ((double)consts[hh][part] * (double)div);
-      int V = (int)rint(units);
-      int l0 = (int)(signed char)(V & 0xFF);
-      int r = (V - l0) >> 8;
-      int l1 = (int)(signed char)(r & 0xFF);
-      r = (r - l1) >> 8;
-      int l2 = (int)(signed char)(r & 0xFF);
-      int l3 = (r - l2) >> 8;
-      v8 = limb == 0 ? l0 : limb == 1 ? l1 : limb == 2 ? l2 : l3;
+#pragma unroll
+      for (int byt = 0; byt < 4; ++byt) {
+        const int jj = 32 * ww + 8 * byt + 4 * g + q;
+        const int V = fx[(hh * Mk::kMasks + mask) * kD + jj];
+        // signed base-256 digits: V = l0 + 256 l1 + 65536 l2 + 2^24 l3
+        int r = V, l = 0;
+        for (int t = 0; t <= limb; ++t) {
+          l = (int)(signed char)(r & 0xFF);
+          r = (r - l) >> 8;
+        }
+        packed |= (uint32_t)(l & 0xFF) << (8 * byt);
+      }
     }
-    reinterpret_cast<signed char*>(afrag)[((f * 64 + ln) * 16) + ent] = (signed char)v8;
+    reinterpret_cast<uint32_t*>(afrag)[(f * 64 + ln) * 4 + q] = packed;
   }
   __syncthreads();
 
@@ -232,10 +276,10 @@ __global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
     gg = __uint_as_float(r[K * 4 + 5]);
   };
   if (tile0 + wave < tile_end) load_raw(tile0 + wave, cur, cur_n, cur_g);
-  for (int64_t tile = tile0 + wave; tile < tile_end; tile += 4) {
+  for (int64_t tile = tile0 + wave; tile < tile_end; tile += kWaves) {
     const int64_t tok = tile * 32 + col;
     const bool valid = tok < a.T;
-    if (tile + 4 < tile_end) load_raw(tile + 4, nxt, nxt_n, nxt_g);
+    if (tile + kWaves < tile_end) load_raw(tile + kWaves, nxt, nxt_n, nxt_g);
     uint32_t wv[Mk::kWords / 2];
 #pragma unroll
     for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
@@ -309,9 +353,17 @@ __global__ __launch_bounds__(kBlock) void score128_kernel(Score128Args a) {
 }
 
 template <int K>
-int launch_k(const Score128Args& a, hipStream_t s) {
-  const int64_t blocks = a.B * a.Hkv * a.blocks_per_group;
-  hipLaunchKernelGGL(score128_kernel<K>, dim3((unsigned)blocks), dim3(kBlock), 0, s, a);
+int launch_k(Score128Args a, hipStream_t s) {
+  constexpr int kWaves = block_threads<K>() / 64;
+  // about one workgroup of 16 waves per CU, at least 16 tiles per wave
+  const int64_t groups = a.B * a.Hkv;
+  int64_t per_block = (a.tiles * groups + 256 * (16 / kWaves) - 1) / (256 * (16 / kWaves));
+  if (per_block < 16 * kWaves) per_block = 16 * kWaves;
+  if (per_block > a.tiles) per_block = a.tiles;
+  a.tiles_per_block = per_block;
+  a.blocks_per_group = (a.tiles + per_block - 1) / per_block;
+  const int64_t blocks = groups * a.blocks_per_group;
+  hipLaunchKernelGGL(score128_kernel<K>, dim3((unsigned)blocks), dim3(block_threads<K>()), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
@@ -339,13 +391,6 @@ int launch_scores_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
   a.bits = L.bits; a.rec_words = L.rec_words; a.gq = (int)(Hq / Hkv);
   a.off_c = L.off_c; a.off_d = L.off_d; a.off_s = L.off_s;
   a.tiles = (T + 31) / 32;
-  const int64_t groups = B * Hkv;
-  // about 1024 blocks, at least 16 tiles per wave
-  int64_t per_block = (a.tiles * groups + 1023) / 1024;
-  if (per_block < 64) per_block = 64;
-  if (per_block > a.tiles) per_block = a.tiles;
-  a.tiles_per_block = per_block;
-  a.blocks_per_group = (a.tiles + per_block - 1) / per_block;
   switch (L.k) {
     case 1: return launch_k<1>(a, s);
     case 2: return launch_k<2>(a, s);
