@@ -243,14 +243,6 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   i32x4 A[NMF];
 #pragma unroll
   for (int f = 0; f < NMF; ++f) A[f] = afrag[f * 64 + lane];
-  float dmse[4], dqjl[4], cmse[4], cqjl[4];
-#pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {
-    dmse[hh] = consts[hh][0];
-    dqjl[hh] = consts[hh][1];
-    cmse[hh] = consts[hh][2];
-    cqjl[hh] = consts[hh][3];
-  }
 
   const int h = lane >> 5, col = lane & 31;
   const int R = a.rec_words;
@@ -259,10 +251,12 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   const int64_t tile0 = chunk * a.tiles_per_block;
   const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles);
   // Lane half h feeds words ww in {h, h+2} of every bit plane and of the sign
-  // mask.  The next tile's words are loaded while this tile is scored.
+  // mask.  The raw words of the wave's next kPrefetch tiles are in flight (a ring of
+  // register slots) while it scores the current one.
   constexpr int NRAW = 2 * K + 2;
-  uint32_t cur[NRAW], nxt[NRAW];
-  float cur_n = 0.0f, cur_g = 0.0f, nxt_n = 0.0f, nxt_g = 0.0f;
+  constexpr int kPrefetch = K <= 2 ? 2 : 1;
+  uint32_t raw[kPrefetch][NRAW];
+  float raw_n[kPrefetch], raw_g[kPrefetch];
   const auto load_raw = [&](int64_t t, uint32_t* rw, float& nn, float& gg) {
     const int64_t tk = t * 32 + col;
     const uint32_t* r = a.krec + (grp * a.T + (tk < a.T ? tk : 0)) * R;   // tail lanes read key 0
@@ -275,32 +269,39 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
     nn = __uint_as_float(r[K * 4 + 4]);
     gg = __uint_as_float(r[K * 4 + 5]);
   };
-  if (tile0 + wave < tile_end) load_raw(tile0 + wave, cur, cur_n, cur_g);
-  for (int64_t tile = tile0 + wave; tile < tile_end; tile += kWaves) {
+#pragma unroll
+  for (int sl = 0; sl < kPrefetch; ++sl)
+    if (tile0 + wave + sl * kWaves < tile_end) load_raw(tile0 + wave + sl * kWaves, raw[sl], raw_n[sl], raw_g[sl]);
+  for (int64_t tile_base = tile0 + wave; tile_base < tile_end; tile_base += kPrefetch * kWaves) {
+#pragma unroll
+   for (int sl = 0; sl < kPrefetch; ++sl) {
+    const int64_t tile = tile_base + sl * kWaves;
+    if (tile >= tile_end) break;
     const int64_t tok = tile * 32 + col;
     const bool valid = tok < a.T;
-    if (tile + kWaves < tile_end) load_raw(tile + kWaves, nxt, nxt_n, nxt_g);
     uint32_t wv[Mk::kWords / 2];
 #pragma unroll
     for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
       const int li = 2 * w2 + h, mask = li >> 2, s2 = (li & 3) >> 1;
       uint32_t word;
       if (mask == Mk::kPlaneMasks) {
-        word = cur[2 * K + s2];
+        word = raw[sl][2 * K + s2];
       } else {
         const int sb = subset_bits<K>(mask);
         word = 0;
 #pragma unroll
         for (int p = 0; p < K; ++p)
-          if ((sb >> p) & 1) word ^= cur[2 * p + s2];
+          if ((sb >> p) & 1) word ^= raw[sl][2 * p + s2];
       }
       wv[w2] = valid ? word : 0u;
     }
-    const float nrm = valid ? cur_n : 0.0f;
-    const float gam = valid ? cur_g : 0.0f;
+    const float nrm = valid ? raw_n[sl] : 0.0f;
+    const float gam = valid ? raw_g[sl] : 0.0f;
+    if (tile + kPrefetch * kWaves < tile_end) load_raw(tile + kPrefetch * kWaves, raw[sl], raw_n[sl], raw_g[sl]);
 
-    // two independent accumulation chains (even / odd MFMAs)
-    i32x16 acc0 = {}, acc1 = {};
+    // one accumulation chain (registers are the occupancy limit; the other waves of
+    // the SIMD fill the MFMA latency)
+    i32x16 acc = {};
 #pragma unroll
     for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
 #pragma unroll
@@ -308,17 +309,9 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
         i32x4 bv;
 #pragma unroll
         for (int q = 0; q < 4; ++q) bv[q] = (int)(wv[w2] & (0x01010101u << (4 * g + q)));
-        if (g == 0)
-          acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[2 * w2 + g], bv, acc0, 0, 0, 0);
-        else
-          acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[2 * w2 + g], bv, acc1, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(A[2 * w2 + g], bv, acc, 0, 0, 0);
       }
     }
-    const i32x16 acc = acc0 + acc1;
-#pragma unroll
-    for (int i = 0; i < NRAW; ++i) cur[i] = nxt[i];
-    cur_n = nxt_n;
-    cur_g = nxt_g;
     // rows 8*hh + 4*h + limb: this lane holds part h (0: mse, 1: qjl) of heads 0..3
     float part[4];
 #pragma unroll
@@ -340,15 +333,17 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
       mse_a = __uint_as_float(s0[0]); mse_b = __uint_as_float(s1[0]);
     }
     const int ha = 2 * h, hb = 2 * h + 1;
-    const float sa = a.scale * ((nrm * inv_d) * (dmse[ha] * mse_a - cmse[ha]) +
-                                kqjl * gam * (dqjl[ha] * qjl_a - cqjl[ha]));
-    const float sb2 = a.scale * ((nrm * inv_d) * (dmse[hb] * mse_b - cmse[hb]) +
-                                 kqjl * gam * (dqjl[hb] * qjl_b - cqjl[hb]));
+    // per-head constants stay in LDS (registers are the occupancy limit here)
+    const float sa = a.scale * ((nrm * inv_d) * (consts[ha][0] * mse_a - consts[ha][2]) +
+                                kqjl * gam * (consts[ha][1] * qjl_a - consts[ha][3]));
+    const float sb2 = a.scale * ((nrm * inv_d) * (consts[hb][0] * mse_b - consts[hb][2]) +
+                                 kqjl * gam * (consts[hb][1] * qjl_b - consts[hb][3]));
     if (valid) {
       const int64_t base = (b * a.Hq + hkv * a.gq) * a.T + tok;
       if (ha < a.gq) a.scores[base + ha * a.T] = sa;
       if (hb < a.gq) a.scores[base + hb * a.T] = sb2;
     }
+   }
   }
 }
 
