@@ -41,7 +41,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kM = 128;
-constexpr int kWaves = 4;
+// Waves per workgroup (one workgroup per CU): 12 (three per SIMD) where the
+// kernel fits in 168 VGPRs, else 8 (two per SIMD, up to 256 VGPRs).
+template <int K, bool KEY, int DT>
+constexpr int waves_for() {
+  return (DT == 0 || (KEY && (K == 3 || (K == 2 && DT == 2)))) ? 8 : 12;
+}
 constexpr int kTile = 32;
 
 struct Enc128Args {
@@ -71,19 +76,24 @@ __device__ inline V as(u32x4 v) {
 // 16 consecutive indices 16h .. 16h+15 of its tile in registers 0..15.
 __device__ inline int tile_row_index(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
 
-// Build the (H D) A-operand fragments of MFMA#1 in LDS: fragment (M, c) for
-// lane l holds A[rho = l%32][16c + 8(l/32) + e] = (H D)[32M + tile_row_index(rho)][...].
+// H_128 = H_4 (x) H_32 (Sylvester order): with row r = 32M + r', column
+// c = 32p + c', H[r][c] = (-1)^popc(M & p) H_32[r'][c'].  So
+//   u = H (D x):  u[32M + r'] = sum_p (-1)^popc(M & p) t_p[r'],
+//   t_p = H_32 (D_p x_p)  (the 32-point transform of block p of D x),
+// i.e. four 32-row MFMA products (two K-chunks each) and a 4-point butterfly.
+// Fragment (p, c2) of the A operand (K-chunk c = 2p + c2 of x), lane l:
+// A[rho = l%32][k = 8(l/32) + e] = H_32[tile_row_index(rho)][16 c2 + k] * D[32p + 16 c2 + k].
 template <bool F16>
 __device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
-  for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
-    const int lane = f & 63, c = (f >> 6) & 7, M = f >> 9;
-    const int row = 32 * M + tile_row_index(lane & 31);
+  for (int f = threadIdx.x; f < 8 * 64; f += blockDim.x) {
+    const int lane = f & 63, c = f >> 6;      // c = 2p + c2
+    const int row = tile_row_index(lane & 31);
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
       uint32_t word = 0;
       for (int hh = 0; hh < 2; ++hh) {
-        const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;
-        const uint32_t neg = h_sign(row, col) ^ ((dbits[col >> 5] >> (col & 31)) & 1u);
+        const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;     // coordinate of x
+        const uint32_t neg = h_sign(row, col & 31) ^ ((dbits[col >> 5] >> (col & 31)) & 1u);
         const uint32_t one = F16 ? 0x3C00u : 0x3F80u;
         word |= (one | (neg << 15)) << (16 * hh);
       }
@@ -186,7 +196,8 @@ __device__ inline uint32_t f32_to_bf16_rne(float f) {
 }
 
 template <int K, bool KEY, int DT>
-__global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
+__global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kernel(Enc128Args a) {
+  constexpr int kWaves = waves_for<K, KEY, DT>();
   extern __shared__ __align__(16) uint8_t smem[];
   u32x4* hfrag = reinterpret_cast<u32x4*>(smem);                // 32 KB
   u32x4* sfrag = reinterpret_cast<u32x4*>(smem + 32768);        // 32 KB (keys)
@@ -279,27 +290,36 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
         for (int q = 0; q < 4; ++q) ss += DT == 1 ? pair_sumsq_bf16(xb[c][q]) : pair_sumsq_f16(xb[c][q]);
     }
 
-    // ---- rotation on MFMA: the four row tiles are independent accumulation
-    // chains, interleaved so that consecutive MFMAs do not wait on each other
+    // ---- rotation: t_p = H_32 (D_p x_p) on MFMA (four independent accumulation
+    // chains), then the H_4 butterfly across blocks gives u = H (D x)
     f32x16 u[4];
 #pragma unroll
-    for (int M = 0; M < 4; ++M) u[M] = f32x16{};
+    for (int p = 0; p < 4; ++p) u[p] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c2 = 0; c2 < 2; ++c2) {
 #pragma unroll
-      for (int M = 0; M < 4; ++M) {
-        const u32x4 hf = hfrag[(M * 8 + c) * 64 + lane];
+      for (int p = 0; p < 4; ++p) {
+        const int c = 2 * p + c2;
+        const u32x4 hf = hfrag[c * 64 + lane];
         if (DT == 2) {
-          u[M] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(hf), as<f16x8>(xb[c]), u[M], 0, 0, 0);
+          u[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(hf), as<f16x8>(xb[c]), u[p], 0, 0, 0);
         } else {
-          u[M] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb[c]), u[M], 0, 0, 0);
+          u[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb[c]), u[p], 0, 0, 0);
           if (DT == 0) {
-            u[M] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb2[c]), u[M], 0, 0, 0);
-            u[M] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb3[c]), u[M], 0, 0, 0);
+            u[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb2[c]), u[p], 0, 0, 0);
+            u[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb3[c]), u[p], 0, 0, 0);
           }
         }
       }
-      __builtin_amdgcn_sched_barrier(0);   // keep one K-chunk of fragments live at a time
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float a0 = u[0][r] + u[1][r], b0 = u[0][r] - u[1][r];
+      const float a1 = u[2][r] + u[3][r], b1 = u[2][r] - u[3][r];
+      u[0][r] = a0 + a1;    // M = 0: + + + +
+      u[1][r] = b0 + b1;    // M = 1: + - + -
+      u[2][r] = a0 - a1;    // M = 2: + + - -
+      u[3][r] = b0 - b1;    // M = 3: + - - +
     }
     if (DT != 0) {
       // the last tile re-reads itself (a cache hit) so that the prefetch
@@ -378,28 +398,33 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
     uint32_t sw[4] = {0, 0, 0, 0};   // inverted sign bits (1 = negative)
     float gam = 0.0f;
     if (KEY) {
-      f32x16 acc[4];
+      // two passes of two projection row tiles each (two accumulators live, not
+      // four: the register budget of three waves per SIMD)
 #pragma unroll
-      for (int Mp = 0; Mp < 4; ++Mp) acc[Mp] = f32x16{};
+      for (int hp = 0; hp < 2; ++hp) {
+        f32x16 acc[2];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        u32x4 sf[4];
+        for (int j = 0; j < 2; ++j) acc[j] = f32x16{};
 #pragma unroll
-        for (int Mp = 0; Mp < 4; ++Mp) sf[Mp] = sfrag[(Mp * 8 + c) * 64 + lane];
+        for (int c = 0; c < 8; ++c) {
+          u32x4 sf[2];
 #pragma unroll
-        for (int Mp = 0; Mp < 4; ++Mp)
-          acc[Mp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[Mp]), as<f16x8>(whi[c]), acc[Mp], 0, 0, 0);
+          for (int j = 0; j < 2; ++j) sf[j] = sfrag[((2 * hp + j) * 8 + c) * 64 + lane];
 #pragma unroll
-        for (int Mp = 0; Mp < 4; ++Mp)
-          acc[Mp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[Mp]), as<f16x8>(wlo[c]), acc[Mp], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+          for (int j = 0; j < 2; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[j]), as<f16x8>(whi[c]), acc[j], 0, 0, 0);
 #pragma unroll
-      for (int Mp = 0; Mp < 4; ++Mp) {
-        uint32_t a2 = 0;
+          for (int j = 0; j < 2; ++j)
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[j]), as<f16x8>(wlo[c]), acc[j], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-        for (int r = 15; r >= 0; --r) a2 = __builtin_amdgcn_alignbit(a2, __float_as_uint(acc[Mp][r]), 31);
-        sw[Mp] = a2;
+        for (int j = 0; j < 2; ++j) {
+          uint32_t a2 = 0;
+#pragma unroll
+          for (int r = 15; r >= 0; --r) a2 = __builtin_amdgcn_alignbit(a2, __float_as_uint(acc[j][r]), 31);
+          sw[2 * hp + j] = a2;
+        }
       }
       auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq), __float_as_uint(wsq), false, false);
       const float tot = __uint_as_float(pg[0]) + __uint_as_float(pg[1]);
@@ -457,7 +482,16 @@ __global__ __launch_bounds__(256, 2) void encode128_kernel(Enc128Args a) {
 }
 
 template <int K, bool KEY, int DT>
-int launch_one(const Enc128Args& a, hipStream_t s) {
+int launch_one(Enc128Args a, hipStream_t s) {
+  constexpr int kWaves = waves_for<K, KEY, DT>();
+  // ~256 workgroups (one per CU) in total, at least 8 tiles per wave, never more
+  // than the group holds; a multiple of the wave count
+  int64_t per_block = (a.tiles_per_group * a.G + 255) / 256;
+  per_block = per_block < kWaves * 8 ? kWaves * 8 : per_block;
+  per_block = (per_block + kWaves - 1) / kWaves * kWaves;
+  if (per_block > a.tiles_per_group) per_block = (a.tiles_per_group + kWaves - 1) / kWaves * kWaves;
+  a.tiles_per_block = per_block;
+  a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
   const size_t lds = (KEY ? 65536 : 32768) + 128;
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
@@ -467,7 +501,8 @@ int launch_one(const Enc128Args& a, hipStream_t s) {
     attr_set = true;
   }
   const int64_t blocks = a.G * a.blocks_per_group;
-  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT>), dim3((unsigned)blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT>), dim3((unsigned)blocks), dim3(64 * waves_for<K, KEY, DT>()), lds,
+                     s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
@@ -502,13 +537,6 @@ int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
   a.bits = L.bits; a.role = L.role; a.rec_words = L.rec_words;
   a.off_c = L.off_c; a.off_t = L.off_t; a.off_d = L.off_d; a.off_s = L.off_s;
   a.tiles_per_group = (N + kTile - 1) / kTile;
-  // ~2048 blocks in total, at least 8 tiles per wave, never more than the group holds
-  int64_t per_block = (a.tiles_per_group * G + 2047) / 2048;
-  per_block = per_block < 4 * 8 ? 4 * 8 : per_block;
-  per_block = (per_block + 3) / 4 * 4;
-  if (per_block > a.tiles_per_group) per_block = (a.tiles_per_group + 3) / 4 * 4;
-  a.tiles_per_block = per_block;
-  a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
   const bool key = L.role == TQ_ROLE_KEY;
   switch (L.k * 2 + (key ? 1 : 0)) {
     case 1 * 2 + 1: return launch_dt<1, true>(a, dtype, s);
