@@ -43,15 +43,25 @@ __global__ __launch_bounds__(64) void encode_generic_kernel(EncodeArgs a) {
   __shared__ double w[kMaxHeadDim];
   __shared__ int idx[kMaxHeadDim];
   __shared__ uint32_t words[kMaxWords];
+  __shared__ float cent[256];
+  __shared__ float thr[256];
   const int lane = threadIdx.x;
   const int d = a.cb.d;
   const int64_t total = a.G * a.N;
+  int64_t g_loaded = -1;
   for (int64_t v = blockIdx.x; v < total; v += gridDim.x) {
     const int64_t g = v / a.N, t = v % a.N;
     const uint8_t* blob = blob_of(a.cb, g);
     if (lane == 0 && a.status && blob_mismatch(a.cb, blob)) atomicOr(a.status, TQ_STATUS_BAD_BLOB);
-    const float* cent = reinterpret_cast<const float*>(blob + a.cb.off_c);
-    const float* thr = reinterpret_cast<const float*>(blob + a.cb.off_t);
+    if (g % a.cb.n_cb != g_loaded) {
+      // centroids and thresholds in LDS: the quantizer's binary search then
+      // costs LDS latency, not a chain of dependent global loads
+      for (int i = lane; i < a.cb.levels; i += kWave) {
+        cent[i] = reinterpret_cast<const float*>(blob + a.cb.off_c)[i];
+        thr[i] = reinterpret_cast<const float*>(blob + a.cb.off_t)[i];
+      }
+      g_loaded = g % a.cb.n_cb;
+    }
     const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob + a.cb.off_d);
     const int64_t base = g * a.sx_g + t * a.sx_n;
 
@@ -73,7 +83,17 @@ __global__ __launch_bounds__(64) void encode_generic_kernel(EncodeArgs a) {
       for (int j = lane; j < d; j += kWave) {
         const float* row = R + (int64_t)j * d;
         double acc = 0.0;
-        for (int i = 0; i < d; ++i) acc = fma((double)row[i], w[i], acc);
+        if ((d & 3) == 0) {
+          for (int i = 0; i < d; i += 4) {        // 16-byte row reads
+            const float4 r4 = *reinterpret_cast<const float4*>(row + i);
+            acc = fma((double)r4.x, w[i], acc);
+            acc = fma((double)r4.y, w[i + 1], acc);
+            acc = fma((double)r4.z, w[i + 2], acc);
+            acc = fma((double)r4.w, w[i + 3], acc);
+          }
+        } else {
+          for (int i = 0; i < d; ++i) acc = fma((double)row[i], w[i], acc);
+        }
         u[j] = acc;
       }
       __syncthreads();
@@ -124,7 +144,21 @@ __global__ __launch_bounds__(64) void encode_generic_kernel(EncodeArgs a) {
         double acc = 0.0;
         if (i < m) {
           const _Float16* row = S + (int64_t)i * d;
-          for (int j = 0; j < d; ++j) acc = fma((double)row[j], w[j], acc);
+          if ((d & 7) == 0) {
+            for (int j = 0; j < d; j += 8) {      // 16-byte row reads
+              const uint4 q4 = *reinterpret_cast<const uint4*>(row + j);
+              const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(qw[e] & 0xFFFFu));
+                const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(qw[e] >> 16));
+                acc = fma((double)lo, w[j + 2 * e], acc);
+                acc = fma((double)hi, w[j + 2 * e + 1], acc);
+              }
+            }
+          } else {
+            for (int j = 0; j < d; ++j) acc = fma((double)row[j], w[j], acc);
+          }
         }
         uint64_t b = __ballot(i < m && acc >= 0.0);
         if (lane == 0) {
