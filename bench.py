@@ -299,19 +299,23 @@ def bench_c5(args, torch, b):
     kchan = torch.empty((GS, d), dtype=torch.int32, device=dev)
     vchan = torch.empty((GS, d), dtype=torch.int32, device=dev)
     work = torch.empty(b.load().tq_outlier_workspace_bytes(d, GS, T), dtype=torch.uint8, device=dev)
+    kwork = torch.empty(b.tq_encode_split_workspace_bytes(b.ROLE_KEY, d, n_out, 3, GS), dtype=torch.uint8, device=dev)
+    vwork = torch.empty(b.tq_encode_split_workspace_bytes(b.ROLE_VALUE, d, n_out, 3, GS), dtype=torch.uint8,
+                        device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def step(ev=None):
         if ev:
             ev[0].record()
         b.tq_outlier_channels(Kd[s0:s1], d, n_out, chan=kchan, work=work)
-        b.tq_encode_split(b.ROLE_KEY, kcbn, kcbo, GS, Kd[s0:s1], d, n_out, 3, kchan, krn, kro, status)
+        b.tq_encode_split(b.ROLE_KEY, kcbn, kcbo, GS, Kd[s0:s1], d, n_out, 3, kchan, krn, kro, status, work=kwork)
         for (e0, e1), cb, rec in zip(edges, kcb8, krec8):
             b.tq_encode_keys(cb, e1 - e0, Kd[e0:e1], d, 8, d, rec=rec, status=status)
         if ev:
             ev[1].record()
         b.tq_outlier_channels(Vd[s0:s1], d, n_out, chan=vchan, work=work)
-        b.tq_encode_split(b.ROLE_VALUE, vcbn, vcbo, GS, Vd[s0:s1], d, n_out, 3, vchan, vrn, vro, status)
+        b.tq_encode_split(b.ROLE_VALUE, vcbn, vcbo, GS, Vd[s0:s1], d, n_out, 3, vchan, vrn, vro, status,
+                          work=vwork)
         for (e0, e1), cb, rec in zip(edges, vcb8, vrec8):
             b.tq_encode_values(cb, e1 - e0, Vd[e0:e1], d, 8, rec=rec, status=status)
         if ev:

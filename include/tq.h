@@ -219,11 +219,22 @@ int tq_outlier_channels(int head_dim, int n_outlier, const void* x, int x_dtype,
                         int64_t sx_g, int64_t sx_n, int32_t* chan, void* work, size_t work_bytes,
                         void* stream);
 
-/* Encode both parts of every vector (role TQ_ROLE_KEY or TQ_ROLE_VALUE). */
+/* Scratch for the MFMA path of tq_encode_split (per-group rotation and
+ * projection fragments built from the channel map): G * 356 KiB for keys,
+ * G * 256 KiB for values.  Non-zero only for the shapes that path serves
+ * (head_dim 256, 32 outliers, bits 2 or 3); 0 otherwise. */
+size_t tq_encode_split_workspace_bytes(int role, int head_dim, int n_outlier, int bits, int64_t G);
+
+/* Encode both parts of every vector (role TQ_ROLE_KEY or TQ_ROLE_VALUE).
+ * `work` (caller scratch of tq_encode_split_workspace_bytes, may be NULL)
+ * enables the MFMA path for bf16 input with 16-byte aligned rows; without it,
+ * or for other shapes, the generic kernels run.  Both give the same records up
+ * to the parity tolerances. */
 int tq_encode_split(int role, int head_dim, int n_outlier, int bits,
                     const void* cbs_normal, const void* cbs_outlier, int64_t n_cb,
                     const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n,
-                    const int32_t* chan, void* rec_normal, void* rec_outlier, int32_t* status, void* stream);
+                    const int32_t* chan, void* rec_normal, void* rec_outlier, void* work, size_t work_bytes,
+                    int32_t* status, void* stream);
 
 /* Scores from split key records: scores[b][hq][t] = scale * (estimate of the
  * normal part + estimate of the outlier part), each part scored from its records

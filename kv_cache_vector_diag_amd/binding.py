@@ -29,7 +29,7 @@ EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encod
            "tq_encode_values", "tq_decode_values", "tq_scores", "tq_attend_workspace_bytes",
            "tq_attend", "tq_rotate", "tq_memory_stats", "tq_status_string", "tq_codebook_bytes_ex",
            "tq_record_bytes_ex", "tq_make_codebook_ex", "tq_outlier_workspace_bytes", "tq_outlier_channels",
-           "tq_encode_split", "tq_scores_split", "tq_decode_values_split"]
+           "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes"]
 
 _lib = None
 
@@ -78,7 +78,8 @@ def load() -> ctypes.CDLL:
                                         c_void_p, c_void_p, c_size_t, c_void_p]),
         "tq_encode_split": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int64, c_void_p, c_int,
                                     c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p, c_void_p,
-                                    c_void_p]),
+                                    c_size_t, c_void_p, c_void_p]),
+        "tq_encode_split_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int64]),
         "tq_scores_split": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                     c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float,
                                     c_void_p, c_void_p, c_void_p]),
@@ -277,8 +278,14 @@ def tq_outlier_channels(x, head_dim, n_outlier, chan=None, work=None):
     return chan
 
 
+def tq_encode_split_workspace_bytes(role, head_dim, n_outlier, bits, G) -> int:
+    return int(load().tq_encode_split_workspace_bytes(role, head_dim, n_outlier, bits, G))
+
+
 def tq_encode_split(role, cbs_normal, cbs_outlier, n_cb, x, head_dim, n_outlier, bits, chan,
-                    rec_normal=None, rec_outlier=None, status=None):
+                    rec_normal=None, rec_outlier=None, status=None, work=None, use_workspace=True):
+    """Split encode; `work` is scratch for the MFMA path (allocated here when None
+    and use_workspace; use_workspace=False runs the generic kernels)."""
     import torch
     G, N, sg, sn = _groups(x, head_dim)
     wn, wo = split_record_words(head_dim, n_outlier, bits, role)
@@ -286,9 +293,14 @@ def tq_encode_split(role, cbs_normal, cbs_outlier, n_cb, x, head_dim, n_outlier,
         rec_normal = torch.empty((G, N, wn), dtype=torch.int32, device=x.device)
     if rec_outlier is None:
         rec_outlier = torch.empty((G, N, wo), dtype=torch.int32, device=x.device)
+    if work is None and use_workspace:
+        need = tq_encode_split_workspace_bytes(role, head_dim, n_outlier, bits, G)
+        work = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    wbytes = 0 if work is None else work.numel() * work.element_size()
     _check(load().tq_encode_split(role, head_dim, n_outlier, bits, _ptr(cbs_normal), _ptr(cbs_outlier), n_cb,
                                   _ptr(x), _dtype_code(x), G, N, sg, sn, _ptr(chan), _ptr(rec_normal),
-                                  _ptr(rec_outlier), _ptr(status), _stream(x)), "tq_encode_split")
+                                  _ptr(rec_outlier), _ptr(work), wbytes, _ptr(status), _stream(x)),
+           "tq_encode_split")
     return rec_normal, rec_outlier
 
 

@@ -190,10 +190,17 @@ int tq_outlier_channels(int head_dim, int n_outlier, const void* x, int x_dtype,
                                  static_cast<double*>(work), static_cast<hipStream_t>(stream));
 }
 
+size_t tq_encode_split_workspace_bytes(int role, int head_dim, int n_outlier, int bits, int64_t G) {
+  Layout Ln, Lo;
+  if (split_layouts(role, head_dim, n_outlier, bits, &Ln, &Lo) || G < 0) return 0;
+  if (!split256_supported(role, head_dim, n_outlier, bits, TQ_BF16, nullptr, 0, 0)) return 0;
+  return split256_workspace_bytes(role, G);
+}
+
 int tq_encode_split(int role, int head_dim, int n_outlier, int bits, const void* cbs_normal,
                     const void* cbs_outlier, int64_t n_cb, const void* x, int x_dtype, int64_t G, int64_t N,
                     int64_t sx_g, int64_t sx_n, const int32_t* chan, void* rec_normal, void* rec_outlier,
-                    int32_t* status, void* stream) {
+                    void* work, size_t work_bytes, int32_t* status, void* stream) {
   Layout Ln, Lo;
   int rc = split_layouts(role, head_dim, n_outlier, bits, &Ln, &Lo);
   if (rc) return rc;
@@ -204,6 +211,10 @@ int tq_encode_split(int role, int head_dim, int n_outlier, int bits, const void*
   if ((N > 1 && sx_n < head_dim) || (G > 1 && sx_g < head_dim) || sx_n < 0 || sx_g < 0)
     return TQ_ERR_DIMENSION_MISMATCH;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (work && work_bytes >= split256_workspace_bytes(role, G) &&
+      split256_supported(role, head_dim, n_outlier, bits, x_dtype, x, sx_g, sx_n))
+    return launch_split256(role, bits, Ln, Lo, cbs_normal, cbs_outlier, n_cb, x, G, N, sx_g, sx_n, chan,
+                           static_cast<uint32_t*>(rec_normal), static_cast<uint32_t*>(rec_outlier), work, status, s);
   rc = launch_encode_generic(make_cb_args(cbs_normal, n_cb, Ln), x, x_dtype, G, N, sx_g, sx_n,
                              static_cast<uint32_t*>(rec_normal), status, s,
                              ChannelMap{chan, head_dim, n_outlier, head_dim});

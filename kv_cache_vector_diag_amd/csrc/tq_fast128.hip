@@ -28,16 +28,12 @@
 
 #include "tq_device.h"
 #include "tq_fast.h"
+#include "tq_mfma.h"
 
 namespace tq {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+using namespace mf;
 
 constexpr int kD = 128;
 constexpr int kM = 128;
@@ -63,18 +59,6 @@ struct Enc128Args {
   int64_t tiles_per_block;
   int64_t blocks_per_group;
 };
-
-__device__ inline uint32_t h_sign(int i, int j) { return __popc(i & j) & 1; }
-
-template <typename V>
-__device__ inline V as(u32x4 v) {
-  return __builtin_bit_cast(V, v);
-}
-
-// Row rho of a 32-row result tile lands in lane half (rho>>2)&1, register
-// 4(rho>>3) + (rho&3).  Tile rows are permuted so that lane half h holds the
-// 16 consecutive indices 16h .. 16h+15 of its tile in registers 0..15.
-__device__ inline int tile_row_index(int rho) { return 16 * ((rho >> 2) & 1) + 4 * (rho >> 3) + (rho & 3); }
 
 // H_128 = H_4 (x) H_32 (Sylvester order): with row r = 32M + r', column
 // c = 32p + c', H[r][c] = (-1)^popc(M & p) H_32[r'][c'].  So
@@ -103,12 +87,6 @@ __device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
   }
 }
 
-// Coordinate fed by B-operand element e (0..7) of lane half h in projection
-// K-chunk c = 2M + p: register 8p + e of tile M, i.e. coordinate 32M + 16h + 8p + e.
-__device__ inline int qjl_coord(int c, int h, int e) {
-  return 32 * (c >> 1) + 16 * h + 8 * (c & 1) + e;
-}
-
 // S fragments (A operand of MFMA#2): fragment (Mp, c), lane l: row rho = l%32 is
 // projection 32Mp + tile_row_index(rho); element e: S[proj][qjl_coord(c, l/32, e)].
 __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
@@ -123,69 +101,6 @@ __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
     }
     sfrag[f] = v;
   }
-}
-
-// x0^2 + x1^2 of a packed pair, widened to fp64.
-__device__ inline double pair_sumsq_bf16(uint32_t w) {
-  s16x2 v = __builtin_bit_cast(s16x2, w);
-  return (double)__builtin_amdgcn_fdot2_f32_bf16(v, v, 0.0f, false);
-}
-
-__device__ inline double pair_sumsq_f16(uint32_t w) {
-  f16x2 v = __builtin_bit_cast(f16x2, w);
-  return (double)__builtin_amdgcn_fdot2(v, v, 0.0f, false);
-}
-
-
-// ---- per-element ALU sequences pinned in inline assembly (register-only,
-// no memory access).  Each helper documents the exact operation.
-
-// Scaled two-term half-precision split of a pair: hi = f16(w*sc) (round to
-// nearest even), lo = f16(w*sc - hi), packed two per word (element 0 in the low
-// half).  w*sc is exact for the power-of-two sc used here, and w*sc - hi is
-// exact in fp32, so hi + lo carries 22 significant bits of w*sc.
-__device__ inline void split_f16x2(float w0, float w1, float sc, uint32_t& hi, uint32_t& lo) {
-  asm("v_fma_mixlo_f16 %[h], %[w0], %[sc], 0\n\t"
-      "v_fma_mixhi_f16 %[h], %[w1], %[sc], 0\n\t"
-      "v_fma_mixlo_f16 %[l], %[w0], %[sc], -%[h] op_sel_hi:[0,0,1]\n\t"
-      "v_fma_mixhi_f16 %[l], %[w1], %[sc], -%[h] op_sel:[0,0,1] op_sel_hi:[0,0,1]"
-      : [h] "=&v"(hi), [l] "=&v"(lo)
-      : [w0] "v"(w0), [w1] "v"(w1), [sc] "v"(sc));
-}
-
-// First threshold step of the quantizer: above = |u| > tn; acc = 2*acc + above;
-// mag = above ? c1 : c0.
-__device__ inline float thr_first(uint32_t& acc, float u, float tn, float c0, float c1) {
-  uint64_t m, c;
-  float mag;
-  asm("v_cmp_gt_f32_e64 %[m], |%[u]|, %[t]\n\t"
-      "v_addc_co_u32_e64 %[acc], %[c], %[acc], %[acc], %[m]\n\t"
-      "v_cndmask_b32_e64 %[mag], %[c0], %[c1], %[m]"
-      : [acc] "+v"(acc), [mag] "=v"(mag), [m] "=&s"(m), [c] "=&s"(c)
-      : [u] "v"(u), [t] "v"(tn), [c0] "v"(c0), [c1] "v"(c1));
-  return mag;
-}
-
-// Further threshold steps: above = |u| > tn; acc = 2*acc + above; mag = above ? cnext : mag.
-__device__ inline void thr_step(uint32_t& acc, float& mag, float u, float tn, float cnext) {
-  uint64_t m, c;
-  asm("v_cmp_gt_f32_e64 %[m], |%[u]|, %[t]\n\t"
-      "v_addc_co_u32_e64 %[acc], %[c], %[acc], %[acc], %[m]\n\t"
-      "v_cndmask_b32_e64 %[mag], %[mag], %[cn], %[m]"
-      : [acc] "+v"(acc), [mag] "+v"(mag), [m] "=&s"(m), [c] "=&s"(c)
-      : [u] "v"(u), [t] "v"(tn), [cn] "v"(cnext));
-}
-
-// Sign half: pos = u > 0 as the top bit of (0 - bits(u)) (exact for every u
-// except -0, which the MFMA never produces from a +0 accumulator); acc = 2*acc + pos;
-// nsg = pos ? -n : n.
-__device__ inline void pos_step(uint32_t& acc, float& nsg, float u, uint32_t nbits, uint32_t signmask) {
-  uint32_t t;
-  asm("v_sub_u32 %[t], 0, %[u]\n\t"
-      "v_alignbit_b32 %[acc], %[acc], %[t], 31\n\t"
-      "v_and_or_b32 %[nsg], %[t], %[sm], %[nb]"
-      : [acc] "+v"(acc), [nsg] "=&v"(nsg), [t] "=&v"(t)
-      : [u] "v"(u), [sm] "s"(signmask), [nb] "v"(nbits));
 }
 
 // bf16 round-to-nearest-even of a float (bit pattern in the low 16 bits).

@@ -84,13 +84,17 @@ __global__ __launch_bounds__(64) void encode_generic_kernel(EncodeArgs a) {
         const float* row = R + (int64_t)j * d;
         double acc = 0.0;
         if ((d & 3) == 0) {
-          for (int i = 0; i < d; i += 4) {        // 16-byte row reads
+          // 16-byte row reads; four independent partial sums (not one chain of
+          // dependent FMAs)
+          double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+          for (int i = 0; i < d; i += 4) {
             const float4 r4 = *reinterpret_cast<const float4*>(row + i);
-            acc = fma((double)r4.x, w[i], acc);
-            acc = fma((double)r4.y, w[i + 1], acc);
-            acc = fma((double)r4.z, w[i + 2], acc);
-            acc = fma((double)r4.w, w[i + 3], acc);
+            a0 = fma((double)r4.x, w[i], a0);
+            a1 = fma((double)r4.y, w[i + 1], a1);
+            a2 = fma((double)r4.z, w[i + 2], a2);
+            a3 = fma((double)r4.w, w[i + 3], a3);
           }
+          acc = (a0 + a1) + (a2 + a3);
         } else {
           for (int i = 0; i < d; ++i) acc = fma((double)row[i], w[i], acc);
         }
@@ -145,17 +149,20 @@ __global__ __launch_bounds__(64) void encode_generic_kernel(EncodeArgs a) {
         if (i < m) {
           const _Float16* row = S + (int64_t)i * d;
           if ((d & 7) == 0) {
-            for (int j = 0; j < d; j += 8) {      // 16-byte row reads
+            // 16-byte row reads; four independent partial sums
+            double pa[4] = {0.0, 0.0, 0.0, 0.0};
+            for (int j = 0; j < d; j += 8) {
               const uint4 q4 = *reinterpret_cast<const uint4*>(row + j);
               const uint32_t qw[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const _Float16 lo = __builtin_bit_cast(_Float16, (uint16_t)(qw[e] & 0xFFFFu));
                 const _Float16 hi = __builtin_bit_cast(_Float16, (uint16_t)(qw[e] >> 16));
-                acc = fma((double)lo, w[j + 2 * e], acc);
-                acc = fma((double)hi, w[j + 2 * e + 1], acc);
+                pa[e] = fma((double)lo, w[j + 2 * e], pa[e]);
+                pa[e] = fma((double)hi, w[j + 2 * e + 1], pa[e]);
               }
             }
+            acc = (pa[0] + pa[1]) + (pa[2] + pa[3]);
           } else {
             for (int j = 0; j < d; ++j) acc = fma((double)row[j], w[j], acc);
           }

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "tq_device.h"
+#include "tq_layout.h"
 
 namespace tq {
 
@@ -27,6 +28,15 @@ int64_t attend_chunks(int64_t T);
 bool attend_split_supported(const CodebookArgs& vcb);
 int launch_attend_split(const CodebookArgs& vcb, const uint32_t* vrec, const float* scores, int64_t B,
                         int64_t Hkv, int64_t T, int64_t Hq, float* part, float* out, hipStream_t s);
+// Split encode on MFMA (head_dim 256, 32 outlier channels, bf16 input): a prep
+// kernel writes the per-group fragments into `work`, then the encode kernel.
+bool split256_supported(int role, int head_dim, int n_outlier, int bits, int dtype, const void* x, int64_t sx_g,
+                        int64_t sx_n);
+size_t split256_workspace_bytes(int role, int64_t G);
+int launch_split256(int role, int bits, const Layout& Ln, const Layout& Lo, const void* cbn, const void* cbo,
+                    int64_t n_cb, const void* x, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n,
+                    const int32_t* chan, uint32_t* rec_n, uint32_t* rec_o, void* work, int32_t* status,
+                    hipStream_t s);
 // Outlier channel selection: float64 channel sums over token chunks, then a
 // per-group ranking into the channel map.
 int64_t outlier_chunks(int64_t N);

@@ -56,7 +56,7 @@ def test_outlier_channels_empty_sequence(gpu_lib):
     assert all(chan.cpu().numpy()[g].tolist() == ref.tolist() for g in range(2))
 
 
-def _split_setup(b, role, G, N, d, n_out, bits, seed, n_cb=None):
+def _split_setup(b, role, G, N, d, n_out, bits, seed, n_cb=None, use_workspace=True):
     import torch
     n_cb = n_cb or G
     Xf, _ = inputs.kv_channel_std(seed, G, N, d, stream=inputs.STREAM_K if role == tq.ROLE_KEY else inputs.STREAM_V)
@@ -65,17 +65,21 @@ def _split_setup(b, role, G, N, d, n_out, bits, seed, n_cb=None):
     cbn, cbo = b.split_codebooks(n_cb, d, n_out, bits, seed, role, device=DEV)
     sqs = split.split_quantizers(n_cb, d, n_out, bits, seed, role)
     st = _status()
-    rn, ro = b.tq_encode_split(role, cbn, cbo, n_cb, X, d, n_out, bits, chan, status=st)
+    rn, ro = b.tq_encode_split(role, cbn, cbo, n_cb, X, d, n_out, bits, chan, status=st, use_workspace=use_workspace)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     return X, chan, sqs, (cbn, cbo), rn, ro
 
 
+# head_dim 256 / 32 outliers / bits 2-3 with scratch runs the MFMA split kernel;
+# without scratch (or other shapes) the generic kernels
 @pytest.mark.parametrize("role", [tq.ROLE_KEY, tq.ROLE_VALUE])
-@pytest.mark.parametrize("G,N,d,n_out,bits", [(3, 333, 256, 32, 3), (2, 65, 64, 16, 2)])
-def test_split_encode_parity(gpu_lib, role, G, N, d, n_out, bits):
+@pytest.mark.parametrize("G,N,d,n_out,bits,ws", [(3, 333, 256, 32, 3, True), (3, 333, 256, 32, 3, False),
+                                                 (2, 300, 256, 32, 2, True), (1, 1, 256, 32, 3, True),
+                                                 (2, 65, 64, 16, 2, True)])
+def test_split_encode_parity(gpu_lib, role, G, N, d, n_out, bits, ws):
     b = gpu_lib
-    X, chan, sqs, _, rn, ro = _split_setup(b, role, G, N, d, n_out, bits, 5)
+    X, chan, sqs, _, rn, ro = _split_setup(b, role, G, N, d, n_out, bits, 5, use_workspace=ws)
     xv = inputs.exact_values(X)
     c = chan.cpu().numpy()
     for g in range(G):
@@ -122,6 +126,21 @@ def test_split_bad_channel_flagged(gpu_lib):
     X = inputs.to_torch(Xf, "bf16", DEV)
     chan = torch.arange(d, dtype=torch.int32, device=DEV).reshape(1, d).clone()
     chan[0, 3] = d + 5                                   # out of range: flagged, read as channel 0
+    cbn, cbo = b.split_codebooks(1, d, n_out, bits, 7, tq.ROLE_KEY, device=DEV)
+    st = _status()
+    b.tq_encode_split(tq.ROLE_KEY, cbn, cbo, 1, X, d, n_out, bits, chan, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & b.STATUS_BAD_CHANNEL
+
+
+def test_split_mfma_path_bad_channel_flagged(gpu_lib):
+    import torch
+    b = gpu_lib
+    G, N, d, n_out, bits = 1, 40, 256, 32, 3
+    Xf, _ = inputs.kv_channel_std(7, G, N, d)
+    X = inputs.to_torch(Xf, "bf16", DEV)
+    chan = torch.arange(d, dtype=torch.int32, device=DEV).reshape(1, d).clone()
+    chan[0, 100] = -3                                    # out of range: flagged by the fragment builder
     cbn, cbo = b.split_codebooks(1, d, n_out, bits, 7, tq.ROLE_KEY, device=DEV)
     st = _status()
     b.tq_encode_split(tq.ROLE_KEY, cbn, cbo, 1, X, d, n_out, bits, chan, status=st)

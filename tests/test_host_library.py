@@ -99,19 +99,24 @@ def test_split_host_validation():
     # normal part Haar 224 at bits, outlier part Hadamard 32 at bits + 1
     assert b.split_record_words(256, 32, 3, b.ROLE_KEY) == (23, 6)
     assert b.split_record_words(256, 32, 3, b.ROLE_VALUE) == (22, 5)
-    assert lib.tq_encode_split(0, 256, 24, 3, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None,
-                               None) == -2                                  # outlier width not a power of two
-    assert lib.tq_encode_split(0, 256, 32, 9, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None,
-                               None) == -3                                  # outlier part would need 10 bits
-    assert lib.tq_encode_split(0, 256, 0, 3, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None,
-                               None) == -5
-    assert lib.tq_encode_split(0, 256, 32, 3, None, None, 1, None, 1, 0, 1, 256, 256, None, None, None, None,
-                               None) == 0
-    assert lib.tq_encode_split(0, 256, 32, 3, None, None, 1, None, 1, 2, 1, 256, 256, None, None, None, None,
-                               None) == -8
+    assert lib.tq_encode_split(0, 256, 24, 3, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None, 0,
+                               None, None) == -2                                  # outlier width not a power of two
+    assert lib.tq_encode_split(0, 256, 32, 9, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None, 0,
+                               None, None) == -3                                  # outlier part would need 10 bits
+    assert lib.tq_encode_split(0, 256, 0, 3, None, None, 1, None, 1, 1, 1, 256, 256, None, None, None, None, 0,
+                               None, None) == -5
+    assert lib.tq_encode_split(0, 256, 32, 3, None, None, 1, None, 1, 0, 1, 256, 256, None, None, None, None, 0,
+                               None, None) == 0
+    assert lib.tq_encode_split(0, 256, 32, 3, None, None, 1, None, 1, 2, 1, 256, 256, None, None, None, None, 0,
+                               None, None) == -8
     assert lib.tq_outlier_channels(256, 256, None, 1, 1, 1, 256, 256, None, None, 0, None) == -5
     assert lib.tq_outlier_channels(600, 8, None, 1, 1, 1, 600, 600, None, None, 0, None) == -2
     assert lib.tq_outlier_workspace_bytes(256, 256, 16384) == 256 * 32 * 256 * 16 + 256
+    # MFMA split path scratch: per-group fragments (keys 468, values 368 of 1 KiB)
+    assert b.tq_encode_split_workspace_bytes(0, 256, 32, 3, 224) == 224 * 468 * 1024
+    assert b.tq_encode_split_workspace_bytes(1, 256, 32, 3, 224) == 224 * 368 * 1024
+    assert b.tq_encode_split_workspace_bytes(0, 256, 32, 5, 224) == 0      # shape without the MFMA path
+    assert b.tq_encode_split_workspace_bytes(0, 128, 32, 3, 224) == 0
     assert b.tq_codebook_bytes_ex(224, 3, 224, 0, 2) == 0
     with pytest.raises(b.TQError) as e:
         b.tq_make_codebook_ex(224, 3, 224, 1, 0, 2)
