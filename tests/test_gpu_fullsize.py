@@ -1,0 +1,152 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times:
+the GPU encodes / scores / attends the whole workload; the oracle checks
+sampled groups and tokens, regenerating exactly those inputs on the CPU.
+
+  * 32K-context decode step: 16 x 8 kv heads x 32768 tokens, d=128, bf16 keys
+    (seed 3) -> turbo3 records; 32 bf16 query heads (GQA 4:1) scored.
+  * prefill encode: 32 layers x 8 kv heads x 4096 tokens, d=128, bf16 with 4
+    outlier channels x8 (seed 1); K b=4, V 4-bit.
+  * long-context step: 4 x 8 kv heads x 131072 tokens, d=128, turbo2 K + 2-bit V
+    (seed 4); attention output of sampled (sequence, head) pairs.
+  * mixed-precision layers: 32 layers x 8 kv heads x 16384 tokens, d=256, per-
+    channel std log-uniform in [0.5, 8] (seed 5); boundary layers b=8, others
+    split (32 outliers at 4 bits, 224 channels at 3 bits, Haar)."""
+import numpy as np
+import pytest
+
+from kv_cache_vector_diag_amd import inputs
+from oracle import split
+from oracle import turboquant as tq
+
+from .parity import assert_close, compare_records, rec_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _sample_tokens(rng, N, n):
+    t = np.unique(np.concatenate([[0, N - 1], rng.choice(N, n, replace=False)]))
+    return t
+
+
+def _bf16_exact(a):
+    return inputs.exact_values(inputs.to_torch(a, "bf16"))
+
+
+def test_decode_step_32k_encode_and_scores(gpu_lib):
+    import torch
+    b = gpu_lib
+    B, Hkv, Hq, T, d, bits, m, seed = 16, 8, 32, 32768, 128, 3, 128, 3
+    G = B * Hkv
+    kcb = b.make_codebooks(Hkv, d, bits, m, seed, b.ROLE_KEY, device=DEV)
+    qzs = tq.quantizers(Hkv, d, bits, m, seed, tq.ROLE_KEY)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rec = b.tq_encode_keys(kcb, Hkv, K, d, bits, m, status=st)
+    scores = b.tq_scores(kcb, Hkv, rec.view(B, Hkv, T, -1), q, d, bits, m)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    del K
+    rng = np.random.default_rng(0)
+    qv = inputs.exact_values(q)
+    for g in (0, 77, G - 1):
+        toks = _sample_tokens(rng, T, 1500)
+        X = _bf16_exact(inputs.kv_normal(seed, G, T, d, groups=[g]))[0][toks]
+        grec = rec_np(rec[g])[toks]
+        compare_records(qzs[g % Hkv], grec, tq.encode(qzs[g % Hkv], X))
+        bb, h = divmod(g, Hkv)
+        ref = tq.scores([qzs[h]], grec[None, None], qv[bb:bb + 1, 4 * h:4 * h + 4])
+        got = scores[bb, 4 * h:4 * h + 4][:, torch.from_numpy(toks).to(DEV)].cpu().numpy()[None]
+        assert_close(got, ref, f"scores g={g}")
+
+
+def test_prefill_encode_full(gpu_lib):
+    import torch
+    b = gpu_lib
+    L, Hkv, T, d, seed = 32, 8, 4096, 128, 1
+    G = L * Hkv
+    Kf, Vf, _ = inputs.kv_outliers(seed, G, T, d)
+    K, V = inputs.to_torch(Kf, "bf16", DEV), inputs.to_torch(Vf, "bf16", DEV)
+    kcb = b.make_codebooks(G, d, 4, 128, seed, b.ROLE_KEY, device=DEV)
+    vcb = b.make_codebooks(G, d, 4, 0, seed, b.ROLE_VALUE, device=DEV)
+    krec = b.tq_encode_keys(kcb, G, K, d, 4, 128)
+    vrec = b.tq_encode_values(vcb, G, V, d, 4)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    for g in (0, 131, G - 1):
+        toks = _sample_tokens(rng, T, 800)
+        kq = tq.Quantizer(d, 4, 128, seed + g, tq.ROLE_KEY)
+        vq = tq.Quantizer(d, 4, 0, seed + g, tq.ROLE_VALUE)
+        kx = inputs.exact_values(K[g])[toks]
+        vx = inputs.exact_values(V[g])[toks]
+        compare_records(kq, rec_np(krec[g])[toks], tq.encode(kq, kx))
+        compare_records(vq, rec_np(vrec[g])[toks], tq.encode(vq, vx))
+    # the inputs the GPU encoded are the generator's, regenerated alone on the CPU
+    assert np.array_equal(inputs.exact_values(K[5]), _bf16_exact(inputs.kv_outliers(seed, G, T, d, groups=[5])[0])[0])
+
+
+def test_long_context_attend_full(gpu_lib):
+    import torch
+    b = gpu_lib
+    B, Hkv, Hq, T, d, seed = 4, 8, 8, 131072, 128, 4
+    G = B * Hkv
+    kcb = b.make_codebooks(Hkv, d, 2, 128, seed, b.ROLE_KEY, device=DEV)
+    vcb = b.make_codebooks(Hkv, d, 2, 0, seed, b.ROLE_VALUE, device=DEV)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_K), "bf16", DEV)
+    V = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_V), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, 2, 128).view(B, Hkv, T, -1)
+    vrec = b.tq_encode_values(vcb, Hkv, V, d, 2).view(B, Hkv, T, -1)
+    del K, V
+    out = b.tq_attend(kcb, Hkv, vcb, Hkv, krec, vrec, q, d, 2, 2, 128)
+    torch.cuda.synchronize()
+    kq = tq.quantizers(Hkv, d, 2, 128, seed, tq.ROLE_KEY)
+    vq = tq.quantizers(Hkv, d, 2, 0, seed, tq.ROLE_VALUE)
+    qv = inputs.exact_values(q)
+    for bb, h in ((0, 0), (3, 5)):
+        ref = tq.attend([kq[h]], rec_np(krec[bb, h])[None, None], [vq[h]], rec_np(vrec[bb, h])[None, None],
+                        qv[bb:bb + 1, h:h + 1])
+        assert_close(out[bb, h].cpu().numpy()[None, None], ref, f"attend b={bb} h={h}")
+
+
+def test_mixed_precision_layers_full(gpu_lib):
+    import torch
+    b = gpu_lib
+    L, Hkv, T, d, n_out, seed = 32, 8, 16384, 256, 32, 5
+    G = L * Hkv
+    s0, s1 = 2 * Hkv, (L - 2) * Hkv
+    GS = s1 - s0
+    rng = np.random.default_rng(2)
+    for role, stream in ((b.ROLE_KEY, inputs.STREAM_K), (b.ROLE_VALUE, inputs.STREAM_V)):
+        X = torch.empty((G, T, d), dtype=torch.bfloat16, device=DEV)
+        for l in range(L):
+            gl = list(range(l * Hkv, (l + 1) * Hkv))
+            X[gl[0]:gl[-1] + 1] = inputs.to_torch(inputs.kv_channel_std(seed, G, T, d, stream=stream, groups=gl)[0],
+                                                  "bf16", DEV)
+        # split layers: channel maps, split encode (MFMA path), sampled parity
+        chan = b.tq_outlier_channels(X[s0:s1], d, n_out)
+        cbn, cbo = b.split_codebooks(GS, d, n_out, 3, seed + s0, role, device=DEV)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        rn, ro = b.tq_encode_split(role, cbn, cbo, GS, X[s0:s1], d, n_out, 3, chan, status=st)
+        # boundary layers 0, 1: b=8, no split
+        key = role == b.ROLE_KEY
+        cb8 = b.make_codebooks(s0, d, 8, d if key else 0, seed, role, device=DEV)
+        r8 = (b.tq_encode_keys(cb8, s0, X[:s0], d, 8, d, status=st) if key
+              else b.tq_encode_values(cb8, s0, X[:s0], d, 8, status=st))
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        for gs in (0, GS - 1):
+            g = s0 + gs
+            Xg = inputs.exact_values(X[g])
+            ch = chan[gs].cpu().numpy()
+            assert ch.tolist() == split.outlier_channels(Xg, n_out).tolist()
+            sq = split.split_quantizer(d, n_out, 3, seed + g, role)
+            toks = _sample_tokens(rng, T, 600)
+            en, eo = split.encode_split(sq, Xg[toks], ch)
+            compare_records(sq.normal, rec_np(rn[gs])[toks], en)
+            compare_records(sq.outlier, rec_np(ro[gs])[toks], eo)
+        toks = _sample_tokens(rng, T, 300)
+        q8 = tq.Quantizer(d, 8, d if key else 0, seed + 3, role)
+        compare_records(q8, rec_np(r8[3])[toks], tq.encode(q8, inputs.exact_values(X[3])[toks]))
+        del X
