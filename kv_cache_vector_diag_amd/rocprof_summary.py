@@ -26,7 +26,13 @@ KERNELS = {
     "encode_generic": "encode_generic",
     "scores_generic": "score_generic",
     "decode_generic": "decode_generic",
+    "attend_part": "attend_part",
+    "attend_merge": "attend_merge",
     "attend": "attend",
+    "split256_prep": "split256_prep",
+    "split256_kernel": "split256",
+    "channel_stats": "channel_stats",
+    "select_outliers": "select_outliers",
 }
 
 
