@@ -62,14 +62,27 @@ __global__ __launch_bounds__(kBlock) void attend_part_kernel(PartArgs a) {
   const int word = sub >> 2, shift = (sub & 3) * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   float esum = 0.0f;
+  // the next token's plane words, norm and score are loaded while this one is
+  // accumulated (one token in flight per lane group is latency-bound)
+  const uint32_t* rv = a.vrec + g * a.T * a.vcb.rec_words;
+  uint32_t nw[K];
+  float nn = 0.0f, ns = 0.0f;
+  const auto load_tok = [&](int64_t t) {
+    const uint32_t* r = rv + t * a.vcb.rec_words;
+#pragma unroll
+    for (int p = 0; p < K; ++p) nw[p] = r[p * W + word];
+    nn = __uint_as_float(r[K * W]);
+    ns = s[t];
+  };
+  if (t0 + slot < t1) load_tok(t0 + slot);
   for (int64_t t = t0 + slot; t < t1; t += slots) {
-    const uint32_t* r = a.vrec + (g * a.T + t) * a.vcb.rec_words;
-    const float e = expf(s[t] - mx);
-    const float w = e * __uint_as_float(r[K * W]);
-    esum += e;
     uint32_t by[K];
 #pragma unroll
-    for (int p = 0; p < K; ++p) by[p] = r[p * W + word] >> shift;
+    for (int p = 0; p < K; ++p) by[p] = nw[p] >> shift;
+    const float e = expf(ns - mx);
+    const float w = e * nn;
+    if (t + slots < t1) load_tok(t + slots);
+    esum += e;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       uint32_t idx = 0;
@@ -110,7 +123,9 @@ struct MergeArgs {
 };
 
 __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
+  constexpr int kWTile = 2048;             // chunk weights held in LDS at a time
   __shared__ float v[kMaxHeadDim];
+  __shared__ float wsh[kWTile];
   __shared__ float red[kBlock / 64];
   const int tid = threadIdx.x;
   const int d = a.vcb.d;
@@ -127,17 +142,40 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   float l = 0.0f;
-  for (int64_t c = tid; c < a.chunks; c += kBlock) l += p[c * (d + 2) + d + 1] * expf(p[c * (d + 2) + d] - mx);
+  float aj[kMaxHeadDim / kBlock > 0 ? kMaxHeadDim / kBlock : 1] = {};
+  for (int64_t c0 = 0; c0 < a.chunks; c0 += kWTile) {
+    const int nc = (int)(a.chunks - c0 < kWTile ? a.chunks - c0 : kWTile);
+    // rescale factor of each chunk, once
+    for (int c = tid; c < nc; c += kBlock) {
+      const float wc = expf(p[(c0 + c) * (d + 2) + d] - mx);
+      wsh[c] = wc;
+      l = fmaf(p[(c0 + c) * (d + 2) + d + 1], wc, l);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxHeadDim / kBlock; ++k) {
+      const int j = tid + k * kBlock;
+      if (j < d) {
+        const float* pj = p + c0 * (d + 2) + j;
+        float s0 = 0.0f, s1 = 0.0f;
+        int c = 0;
+        for (; c + 1 < nc; c += 2) {
+          s0 = fmaf(pj[c * (d + 2)], wsh[c], s0);
+          s1 = fmaf(pj[(c + 1) * (d + 2)], wsh[c + 1], s1);
+        }
+        if (c < nc) s0 = fmaf(pj[c * (d + 2)], wsh[c], s0);
+        aj[k] += s0 + s1;
+      }
+    }
+    __syncthreads();
+  }
   l = wave_sum_f32(l);
   if ((tid & 63) == 0) red[tid >> 6] = l;
+#pragma unroll
+  for (int k = 0; k < kMaxHeadDim / kBlock; ++k)
+    if (tid + k * kBlock < d) v[tid + k * kBlock] = aj[k];
   __syncthreads();
   l = red[0] + red[1] + red[2] + red[3];
-  for (int j = tid; j < d; j += kBlock) {
-    float aj = 0.0f;
-    for (int64_t c = 0; c < a.chunks; ++c) aj = fmaf(p[c * (d + 2) + j], expf(p[c * (d + 2) + d] - mx), aj);
-    v[j] = aj;
-  }
-  __syncthreads();
   for (int h = 1; h < d; h <<= 1) {
     for (int q = tid; q < d / 2; q += kBlock) {
       int i = (q / h) * 2 * h + (q % h);
