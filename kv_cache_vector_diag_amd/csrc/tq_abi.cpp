@@ -53,6 +53,9 @@ int encode_common(int role, int head_dim, int bits, int projections, const void*
     return launch_encode_fast128(L, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
                                  static_cast<hipStream_t>(stream));
   CodebookArgs cb = make_cb_args(cbs, n_cb, L);
+  if (tiled_encode_supported(cb))
+    return launch_encode_tiled(cb, x, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
+                               static_cast<hipStream_t>(stream));
   return launch_encode_generic(cb, x, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
                                static_cast<hipStream_t>(stream));
 }

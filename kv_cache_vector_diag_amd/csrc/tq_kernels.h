@@ -13,6 +13,11 @@ namespace tq {
 int launch_encode_generic(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N,
                           int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
                           const ChannelMap& cm = ChannelMap{});
+// Hadamard encode, 32 vectors per workgroup step (power-of-two d in [32, 512]):
+// the projection matrix is staged through LDS once per step.
+bool tiled_encode_supported(const CodebookArgs& cb);
+int launch_encode_tiled(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N, int64_t sx_g,
+                        int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
                           int32_t* status, hipStream_t s, int64_t out_stride = 0,
                           const ChannelMap& cm = ChannelMap{});

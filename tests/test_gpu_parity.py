@@ -193,6 +193,38 @@ def test_generic_shapes(gpu_lib, d, bits, m, dtype):
         assert_close(dec[g].cpu().numpy(), tq.decode_values(vq[g], rec_np(vrec)[g]), "decode")
 
 
+@pytest.mark.parametrize("d,bits,m,dtype,G,N,n_cb,stride", [
+    (32, 8, 100, "f16", 3, 95, 2, 1),      # projections not a multiple of the 64-row S chunk
+    (64, 2, 64, "f32", 2, 33, 2, 2),       # strided tokens, one vector past a 32-vector step
+    (128, 8, 128, "bf16", 2, 130, 2, 1),   # head_dim 128 with a codebook the MFMA kernel does not take
+    (256, 7, 256, "bf16", 3, 70, 1, 1),    # one codebook shared by three groups
+    (512, 8, 1024, "bf16", 1, 40, 1, 1),   # largest record: 8 x 16 plane words + 32 sign words
+    (256, 8, 256, "bf16", 1, 1, 1, 1),     # a single vector
+])
+def test_tiled_encode_shapes(gpu_lib, d, bits, m, dtype, G, N, n_cb, stride):
+    """The 32-vector encode (Hadamard, head_dim >= 32) against the oracle, keys and values,
+    with ragged steps, shared codebooks and strided inputs; scores and decode on top."""
+    import torch
+    b = gpu_lib
+    Xf = inputs.to_torch(inputs.kv_normal(13, G, N * stride, d), dtype, DEV)
+    X = Xf[:, ::stride, :]
+    kcb, kq = _codebooks(b, n_cb, d, bits, m, 13, tq.ROLE_KEY)
+    krec, _, _ = _encode_and_check(b, tq.ROLE_KEY, X, kcb, kq, d, bits, m, G, N)
+    vb = min(bits, 8)
+    vcb, vq = _codebooks(b, n_cb, d, vb, 0, 13, tq.ROLE_VALUE)
+    vrec, _, _ = _encode_and_check(b, tq.ROLE_VALUE, X, vcb, vq, d, vb, 0, G, N)
+    if G % n_cb == 0:
+        q = inputs.to_torch(inputs.queries(13, G // n_cb, n_cb, d), dtype, DEV)
+        s = b.tq_scores(kcb, n_cb, krec.view(G // n_cb, n_cb, N, -1), q, d, bits, m)
+        torch.cuda.synchronize()
+        ref = tq.scores(kq, rec_np(krec).reshape(G // n_cb, n_cb, N, -1), inputs.exact_values(q))
+        assert_close(s.cpu().numpy(), ref, "scores")
+    dec = b.tq_decode_values(vcb, n_cb, vrec, d, vb)
+    torch.cuda.synchronize()
+    for g in range(G):
+        assert_close(dec[g].cpu().numpy(), tq.decode_values(vq[g % n_cb], rec_np(vrec)[g]), "decode")
+
+
 def test_bitpolar_contract_on_gpu(gpu_lib):
     """head_dim 8, bits 4, projections 16, seed 42; constant keys 0.1 and values 0.2
     (exact zeros after the rotation land on the middle threshold); 5 pushes -> 5 scores."""
