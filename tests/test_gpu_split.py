@@ -32,12 +32,23 @@ def _chan_ok(X, chan_gpu, n_out):
     assert chan_gpu.tolist() == ref.tolist()
 
 
-@pytest.mark.parametrize("G,N,d,n_out", [(4, 3000, 256, 32), (3, 1, 64, 16), (2, 700, 48, 16)])
-def test_outlier_channels(gpu_lib, G, N, d, n_out):
+# 4-channel loads (head_dim % 4 == 0, aligned rows) and the one-channel kernel
+# (head_dim 50, odd token stride)
+@pytest.mark.parametrize("G,N,d,n_out,dtype,stride", [(4, 3000, 256, 32, "bf16", 1), (3, 1, 64, 16, "bf16", 1),
+                                                      (2, 700, 48, 16, "bf16", 1), (2, 900, 128, 16, "f32", 1),
+                                                      (2, 600, 64, 8, "f16", 1), (2, 500, 50, 8, "bf16", 1),
+                                                      (2, 400, 64, 8, "bf16", 3)])
+def test_outlier_channels(gpu_lib, G, N, d, n_out, dtype, stride):
     import torch
     b = gpu_lib
     Xf, _ = inputs.kv_channel_std(5, G, N, d)
-    X = inputs.to_torch(Xf, "bf16", DEV)
+    if stride > 1:
+        # rows of d + 1 elements: every row start is misaligned for the wide loads
+        Xp = np.zeros((G, N, d + 1), dtype=Xf.dtype)
+        Xp[..., :d] = Xf
+        X = inputs.to_torch(Xp, dtype, DEV)[..., :d]
+    else:
+        X = inputs.to_torch(Xf, dtype, DEV)
     chan = b.tq_outlier_channels(X, d, n_out)
     torch.cuda.synchronize()
     xv = inputs.exact_values(X)
