@@ -32,14 +32,14 @@ HBM_PEAK_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def _kernel_sources_sha() -> str:
+def _kernel_sources_sha(kernel: str) -> str:
     from kv_cache_vector_diag_amd.rocprof_summary import kernel_sources_sha
-    return kernel_sources_sha(ROOT)
+    return kernel_sources_sha(ROOT, kernel)
 
 
 def _traffic(kernel_key: str, launches_bytes: float):
     """HBM bytes per launch from the committed counter summary, or None when the
-    kernel sources changed since the counters were taken."""
+    kernel's sources changed since the counters were taken."""
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
@@ -48,7 +48,7 @@ def _traffic(kernel_key: str, launches_bytes: float):
         ent = data[kernel_key]
     except (KeyError, ValueError):
         return None
-    if ent.get("source_sha") != _kernel_sources_sha():
+    if "kernel" not in ent or ent.get("source_sha") != _kernel_sources_sha(ent["kernel"]):
         return None
     return ent.get("hbm_bytes_per_launch")
 

@@ -36,7 +36,26 @@ KERNELS = {
 }
 
 
+# kernels instantiated for keys and values: (short name, index of the KEY template argument)
+ROLE_KERNELS = {"encode128_kernel": ("encode", 1), "encode_tiled_kernel": ("tiled", -1),
+                "split256_kernel": ("split256", -1)}
+
+# sources each measured kernel is built from (a change to any makes its counters stale)
+_COMMON = ["tq_device.h", "tq_layout.h", "tq_mfma.h", "tq_fast.h", "../../include/tq.h"]
+KERNEL_SOURCES = {
+    "encode_keys": ["tq_fast128.hip"] + _COMMON,
+    "score": ["tq_score128.hip"] + _COMMON,
+}
+
+
 def short_name(kernel_name: str) -> str:
+    for key, (short, pos) in ROLE_KERNELS.items():
+        if key in kernel_name:
+            args = kernel_name.split(key, 1)[1]
+            if args.startswith("<"):
+                arg = args[1:args.index(">")].split(",")[pos].strip()
+                return short + ("_keys" if arg == "true" else "_values" if arg == "false" else "")
+            return short
     for key, short in KERNELS.items():
         if key in kernel_name:
             return short
@@ -47,12 +66,12 @@ def short_name(kernel_name: str) -> str:
     return kernel_name[:48]
 
 
-def kernel_sources_sha(root: str) -> str:
+def kernel_sources_sha(root: str, kernel: str) -> str:
+    """Hash of the sources of one measured kernel (short name, e.g. encode_keys)."""
     h = hashlib.sha256()
     csrc = os.path.join(root, "kv_cache_vector_diag_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            h.update(open(os.path.join(csrc, name), "rb").read())
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(open(os.path.normpath(os.path.join(csrc, name)), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -88,13 +107,13 @@ def cmd_traffic(a) -> None:
     f_factor = a.copy_bytes / (max(cf) * 1024.0)
     w_factor = a.copy_bytes / (max(cw) * 1024.0)
     out = json.load(open(a.out)) if os.path.exists(a.out) else {}
-    sha = kernel_sources_sha(a.root)
     for kern, key in (k.split("=") for k in a.map):
+        sha = kernel_sources_sha(a.root, kern)
         fv = fetch[kern]["FETCH_SIZE"]
         wv = write[kern]["WRITE_SIZE"]
         rd = sum(fv) / len(fv) * 1024.0 * f_factor
         wr = sum(wv) / len(wv) * 1024.0 * w_factor
-        out[key] = {"hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+        out[key] = {"kernel": kern, "hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
                     "fetch_factor": f_factor, "write_factor": w_factor, "source_sha": sha}
         print(f"{key}: read {rd / 1e6:.1f} MB  write {wr / 1e6:.1f} MB  (factors {f_factor:.3f}, {w_factor:.3f})")
     json.dump(out, open(a.out, "w"), indent=1, sort_keys=True)
@@ -109,7 +128,7 @@ def main(argv=None) -> None:
     t.add_argument("--fetch", required=True); t.add_argument("--write", required=True)
     t.add_argument("--copy-fetch", required=True); t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
-    t.add_argument("--map", nargs="+", default=["encode=encode_c3", "score=score_c3"],
+    t.add_argument("--map", nargs="+", default=["encode_keys=encode_c3", "score=score_c3"],
                    help="kernel=key pairs")
     t.add_argument("--root", default=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     t.add_argument("--out", required=True)
