@@ -15,9 +15,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["tq_host.cpp", "tq_abi.cpp", "tq_generic.hip", "tq_fast128.hip", "tq_score128.hip", "tq_split.hip", "tq_attend.hip", "tq_split256.hip", "tq_tiled.hip"]
 
 # Packed-FP32 VALU forms are disabled for every device pass; the host pass
-# warns that it does not know the feature, which is harmless.
+# warns that it does not know the feature, which is harmless.  MFMA results
+# are kept in ordinary VGPRs (gfx950 reads and writes them there directly):
+# otherwise accumulators that also feed VALU code get copied through AGPRs
+# around every matrix instruction.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-function"]
 
 

@@ -115,6 +115,294 @@ __global__ __launch_bounds__(kBlock) void attend_part_kernel(PartArgs a) {
   }
 }
 
+// ---- the same chunk partials on int8 MFMA (value codebooks of k <= 3 bits)
+//
+// With the symmetric codebook written in the sign basis (as in the score
+// kernel), c[idx_tj] = sum over odd plane subsets P of a_P (2 mask_P,tj - 1),
+// mask_P = XOR of the planes in P.  With weights w_t = exp(s_t - m_c) n_t:
+//   a_c[j] = sum_P a_P (2 M_P[j] - W),  M_P[j] = sum_t w_t mask_P,tj,  W = sum_t w_t.
+// M_P is a product over the token axis, [heads x tokens] x [tokens x coordinates],
+// run as v_mfma_i32_32x32x32_i8 per 32 tokens and 32 coordinates:
+//  * A: w_t in 27-bit fixed point (unit = chunk max / 2^27), four 7-bit digits;
+//    rows 8q + 4hc + l = digit l of query head 2q + hc of the GQA group.
+//  * B: lane (column n = coordinate 32w + n, token half) takes byte n/8 of the
+//    mask word of 16 tokens, from a byte-transposed copy of the records in LDS,
+//    AND bit n%8: values {0, 2^(n%8)} (-128 for bit 7), undone after the sum.
+// Integer sums are exact; only the fixed-point rounding of w_t (2^-28 of the
+// chunk's largest weight) enters the result.
+constexpr int kSub = 256;                  // tokens per staged sub-chunk
+constexpr double kFix = 134217728.0;       // 2^27
+
+struct MfmaPartArgs {
+  CodebookArgs vcb;
+  const uint32_t* vrec;
+  const float* scores;   // [B][Hq][T]
+  int64_t Hkv, T, Hq, chunks;
+  int gq;                // query heads per kv head (<= 8)
+  float* part;
+};
+
+// LDS carve-up (bytes) of attend_mfma_kernel, shared with its launcher.
+constexpr int kRecStride = kSub + 4;       // words per record-word row (16-byte aligned, bank offset 4)
+constexpr int kTbStride = kSub + 32;       // bytes per transposed mask-byte row: the 4 rows read by one
+                                           // MFMA operand fall in different banks
+constexpr int kAfGroup = 66;               // fragment entries per 32-token group: 2 halves of 33
+
+struct AttendLds {
+  size_t wq, rec, tb, af, total;
+};
+
+__host__ __device__ inline size_t a16(size_t x) { return (x + 15) / 16 * 16; }
+
+__host__ __device__ inline AttendLds attend_lds(int gq, int rec_words, int masks, int W) {
+  AttendLds o;
+  o.wq = 0;                                                   // float weights, then digit bytes [gq][kChunk]
+  o.rec = a16((size_t)gq * kChunk * 4);                       // uint32 [rec_words][kRecStride]
+  o.tb = o.rec + a16((size_t)rec_words * kRecStride * 4);     // bytes [masks][W][4][kTbStride]
+  o.af = o.tb + (size_t)masks * W * 4 * kTbStride;            // i32x4 [kSub/32][2][33]
+  o.total = o.af + (size_t)(kSub / 32) * kAfGroup * 16;
+  return o;
+}
+
+typedef int i32x4v __attribute__((ext_vector_type(4)));
+typedef int i32x16v __attribute__((ext_vector_type(16)));
+
+template <int K>
+__device__ __host__ constexpr int odd_subset(int s) {
+  return K == 1 ? 1 : K == 2 ? (1 << s) : (s < 3 ? (1 << s) : 7);
+}
+
+// Block-wide reductions over 256 threads (4 waves) through `red` (4 slots).
+__device__ inline float block_max(float v, float* red) {
+  v = wave_max_f32(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ inline float block_sum(float v, float* red) {
+  v = wave_sum_f32(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__device__ inline double block_sum_f64(double v, double* red) {
+  v = wave_sum_f64(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// 4 x 4 byte transpose: y[b] = byte b of x[0], x[1], x[2], x[3] (in that order).
+__device__ inline void transpose4x4(const uint32_t* x, uint32_t* y) {
+  const uint32_t p01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);
+  const uint32_t p23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t q01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);
+  const uint32_t q23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  y[0] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+  y[1] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
+  y[2] = __builtin_amdgcn_perm(q23, q01, 0x05040100u);
+  y[3] = __builtin_amdgcn_perm(q23, q01, 0x07060302u);
+}
+
+// One workgroup per (b, kv head, chunk of kChunk tokens), all gq query heads.
+// Wave v owns record words w = v, v + 4, ... (WPW of them) and every mask of each.
+template <int K, int WPW>
+__global__ __launch_bounds__(kBlock) void attend_mfma_kernel(MfmaPartArgs a) {
+  constexpr int NM = 1 << (K - 1);          // odd plane subsets
+  constexpr int RWMAX = K * 4 * WPW + 1;    // record words (planes + norm)
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float red[4];
+  __shared__ double redd[4];
+  __shared__ double coef[NM];
+  __shared__ float hm[8], hl[8], hunit[8];
+  __shared__ double homega[8];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches on it stay scalar
+  const int d = a.vcb.d, W = a.vcb.plane_words, RW = a.vcb.rec_words, gq = a.gq;
+  const AttendLds lay = attend_lds(gq, RW, NM, W);
+  float* wf = reinterpret_cast<float*>(smem + lay.wq);
+  uint32_t* wd = reinterpret_cast<uint32_t*>(smem + lay.wq);   // digit bytes of the codes
+  uint32_t* rec = reinterpret_cast<uint32_t*>(smem + lay.rec);
+  uint8_t* tb = smem + lay.tb;
+  i32x4v* af = reinterpret_cast<i32x4v*>(smem + lay.af);
+
+  const int64_t g = blockIdx.x / a.chunks, c = blockIdx.x % a.chunks;
+  const int64_t b = g / a.Hkv, hkv = g % a.Hkv;
+  const uint8_t* blob = blob_of(a.vcb, g);
+  const int64_t t0 = c * kChunk;
+  const int nt = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+  const uint32_t* rv = a.vrec + (g * a.T + t0) * RW;
+
+  // records of sub-chunk 0 in flight (thread = token) while the weights are formed
+  uint32_t pre[RWMAX];
+  const auto load_sub = [&](int s0) {
+    const bool ok = s0 + tid < nt;
+    const uint32_t* r = rv + (int64_t)(ok ? s0 + tid : 0) * RW;
+#pragma unroll
+    for (int i = 0; i < RWMAX; ++i)
+      if (i < RW) pre[i] = ok ? r[i] : 0u;
+  };
+  load_sub(0);
+
+  if (tid < NM) {
+    // a_P = (1/L) sum_v c_v prod_{p in P} sigma_p(v)
+    const float* cent = reinterpret_cast<const float*>(blob + a.vcb.off_c);
+    const int sb = odd_subset<K>(tid);
+    double acc = 0.0;
+    for (int v = 0; v < (1 << K); ++v) acc += (__popc(~v & sb) & 1) ? -(double)cent[v] : (double)cent[v];
+    coef[tid] = acc / (1 << K);
+  }
+  for (int e = tid; e < (kSub / 32) * kAfGroup; e += kBlock) af[e] = i32x4v{0, 0, 0, 0};   // rows of absent heads
+
+  // ---- weights: per head, chunk max, exp, sum, and the fixed-point codes
+  constexpr int kPer = kChunk / kBlock;
+  float nrm[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int t = tid + i * kBlock;
+    nrm[i] = t < nt ? __uint_as_float(rv[(int64_t)t * RW + K * W]) : 0.0f;
+  }
+  for (int h = 0; h < gq; ++h) {
+    const float* sc = a.scores + ((b * a.Hq + hkv * gq + h) * a.T + t0);
+    float sv[kPer], mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int t = tid + i * kBlock;
+      sv[i] = t < nt ? sc[t] : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
+    }
+    mx = block_max(mx, red);
+    float es = 0.0f, om = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int t = tid + i * kBlock;
+      const float e = t < nt ? expf(sv[i] - mx) : 0.0f;
+      es += e;
+      const float w = e * nrm[i];
+      om = fmaxf(om, w);
+      wf[h * kChunk + t] = w;
+    }
+    es = block_sum(es, red);
+    om = block_max(om, red);
+    const double fs = kFix / (double)(om > 0.0f ? om : 1.0f);
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int t = tid + i * kBlock;
+      const uint32_t v = (uint32_t)rint((double)wf[h * kChunk + t] * fs);   // <= 2^27
+      tot += (double)v;                           // integers: exact in any order
+      // 7-bit digits of v in the four bytes
+      wd[h * kChunk + t] = (v & 0x7Fu) | ((v << 1) & 0x7F00u) | ((v << 2) & 0x7F0000u) | ((v << 3) & 0x7F000000u);
+    }
+    tot = block_sum_f64(tot, redd);
+    if (tid == 0) {
+      hm[h] = mx;
+      hl[h] = es;
+      hunit[h] = om > 0.0f ? om : 1.0f;
+      homega[h] = tot;
+    }
+  }
+
+  i32x16v acc[WPW][NM];
+#pragma unroll
+  for (int x = 0; x < WPW; ++x)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[x][m] = i32x16v{};
+  const int col = lane & 31, kh = lane >> 5;
+
+  for (int s0 = 0; s0 < nt; s0 += kSub) {
+    const int ns = nt - s0 < kSub ? nt - s0 : kSub;
+    // record words of this sub-chunk, word-major; then the next sub-chunk's loads
+#pragma unroll
+    for (int i = 0; i < RWMAX; ++i)
+      if (i < RW) rec[i * kRecStride + tid] = pre[i];
+    if (s0 + kSub < nt) load_sub(s0 + kSub);
+    __syncthreads();                              // records, codes in; last sub-chunk's fragments consumed
+    // A fragments: head hh, tokens 4 qd .. 4 qd + 3 -> dword q of lanes (row 8(hh/2) + 4(hh%2) + l, half)
+    for (int e = tid; e < gq * (kSub / 4); e += kBlock) {
+      const int hh = e / (kSub / 4), qd = e % (kSub / 4);
+      const int gi = qd >> 3, half = (qd >> 2) & 1, q = qd & 3;
+      const uint4 x4 = *reinterpret_cast<const uint4*>(wd + hh * kChunk + s0 + 4 * qd);
+      const uint32_t x[4] = {x4.x, x4.y, x4.z, x4.w};
+      uint32_t y[4];
+      transpose4x4(x, y);
+      const int row0 = 8 * (hh >> 1) + 4 * (hh & 1);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) reinterpret_cast<uint32_t*>(af + gi * kAfGroup + 33 * half + row0 + l)[q] = y[l];
+    }
+    // byte transpose of the mask words: tb[m][w][byte][token]
+    for (int e = tid; e < NM * W * (kSub / 4); e += kBlock) {
+      const int tq = e % (kSub / 4), mw = e / (kSub / 4), w = mw % W, m = mw / W;
+      const int sb = odd_subset<K>(m);
+      uint32_t x[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int p = 0; p < K; ++p)
+        if ((sb >> p) & 1) {
+          const uint4 r4 = *reinterpret_cast<const uint4*>(rec + (p * W + w) * kRecStride + 4 * tq);
+          x[0] ^= r4.x; x[1] ^= r4.y; x[2] ^= r4.z; x[3] ^= r4.w;
+        }
+      uint32_t y[4];
+      transpose4x4(x, y);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(tb + (size_t)(m * W + w) * 4 * kTbStride) + tq;
+#pragma unroll
+      for (int by = 0; by < 4; ++by) dst[by * (kTbStride / 4)] = y[by];
+    }
+    __syncthreads();
+    const uint32_t bit = 0x01010101u << (col & 7);
+    for (int gi = 0; gi < (ns + 31) / 32; ++gi) {
+      const i32x4v av = af[gi * kAfGroup + 33 * kh + col];
+#pragma unroll
+      for (int x = 0; x < WPW; ++x) {
+        const int w = wave + 4 * x;
+        if (w < W) {
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            const uint4 r4 = *reinterpret_cast<const uint4*>(
+                tb + ((size_t)(m * W + w) * 4 + (col >> 3)) * kTbStride + 32 * gi + 16 * kh);
+            const i32x4v bv = {(int)(r4.x & bit), (int)(r4.y & bit), (int)(r4.z & bit), (int)(r4.w & bit)};
+            acc[x][m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[x][m], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- a[j] = unit * sum_P a_P (2 M_P[j] - W) for this lane's coordinate and heads
+  const int e7 = col & 7;
+#pragma unroll
+  for (int x = 0; x < WPW; ++x) {
+    const int w = wave + 4 * x;
+    if (w >= W) continue;
+    const int j = 32 * w + col;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int hh = 2 * q + kh;
+      if (hh >= gq) continue;
+      double tot = 0.0;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        int64_t mv = 0;
+#pragma unroll
+        for (int l = 3; l >= 0; --l) mv = mv * 128 + (int64_t)acc[x][m][4 * q + l];
+        mv = e7 == 7 ? -(mv >> 7) : (mv >> e7);
+        tot += coef[m] * (double)(2 * mv - (int64_t)homega[hh]);
+      }
+      const double unit = (double)hunit[hh] / kFix;
+      a.part[((b * a.Hq + hkv * gq + hh) * a.chunks + c) * (d + 2) + j] = (float)(tot * unit);
+    }
+  }
+  if (tid < gq) {
+    float* out = a.part + ((b * a.Hq + hkv * gq + tid) * a.chunks + c) * (d + 2);
+    out[d] = hm[tid];
+    out[d + 1] = hl[tid];
+  }
+}
+
 struct MergeArgs {
   CodebookArgs vcb;
   const float* part;
@@ -196,6 +484,51 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
 
 int64_t attend_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
 
+namespace {
+
+template <int K, int WPW>
+int launch_attend_mfma(const MfmaPartArgs& pa, int64_t blocks, hipStream_t s) {
+  const size_t lds = attend_lds(pa.gq, pa.vcb.rec_words, 1 << (K - 1), pa.vcb.plane_words).total;
+  static bool attr_set = false;   // idempotent; a race only repeats the call
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_mfma_kernel<K, WPW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 150 * 1024) != hipSuccess)
+      return -10;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((attend_mfma_kernel<K, WPW>), dim3((unsigned)blocks), dim3(kBlock), lds, s, pa);
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+// MFMA partials: Walsh-Hadamard values with k <= 3, head_dim a multiple of 32,
+// an even GQA grouping of at most 8 query heads, and the LDS plan within 150 KB.
+bool attend_mfma_supported(const CodebookArgs& vcb, int64_t Hkv, int64_t Hq) {
+  if (vcb.rotation != kRotHadamard || vcb.k < 1 || vcb.k > 3 || vcb.d < 32 || (vcb.d & 31) != 0) return false;
+  if (Hkv <= 0 || Hq % Hkv != 0 || Hq / Hkv > 8) return false;
+  const int W = vcb.plane_words, masks = 1 << (vcb.k - 1);
+  const int wpw = (W + 3) / 4;
+  if (wpw != 1 && wpw != 2 && wpw != 4) return false;
+  if (masks * wpw > 8) return false;
+  return attend_lds((int)(Hq / Hkv), vcb.rec_words, masks, W).total <= 150 * 1024;
+}
+
+int launch_attend_mfma_k(const MfmaPartArgs& pa, int64_t blocks, hipStream_t s) {
+  const int wpw = (pa.vcb.plane_words + 3) / 4;
+  switch (pa.vcb.k * 8 + wpw) {
+    case 8 + 1: return launch_attend_mfma<1, 1>(pa, blocks, s);
+    case 8 + 2: return launch_attend_mfma<1, 2>(pa, blocks, s);
+    case 8 + 4: return launch_attend_mfma<1, 4>(pa, blocks, s);
+    case 16 + 1: return launch_attend_mfma<2, 1>(pa, blocks, s);
+    case 16 + 2: return launch_attend_mfma<2, 2>(pa, blocks, s);
+    case 16 + 4: return launch_attend_mfma<2, 4>(pa, blocks, s);
+    case 24 + 1: return launch_attend_mfma<3, 1>(pa, blocks, s);
+    case 24 + 2: return launch_attend_mfma<3, 2>(pa, blocks, s);
+  }
+  return -10;
+}
+
+}  // namespace
+
 bool attend_split_supported(const CodebookArgs& vcb) {
   return vcb.rotation == kRotHadamard && vcb.d >= 8 && vcb.d <= kMaxHeadDim && vcb.k >= 1 && vcb.k <= 8;
 }
@@ -204,7 +537,10 @@ int launch_attend_split(const CodebookArgs& vcb, const uint32_t* vrec, const flo
                         int64_t Hkv, int64_t T, int64_t Hq, float* part, float* out, hipStream_t s) {
   if (B * Hq == 0) return 0;
   const int64_t chunks = attend_chunks(T);
-  if (chunks > 0) {
+  if (chunks > 0 && attend_mfma_supported(vcb, Hkv, Hq)) {
+    const MfmaPartArgs pa{vcb, vrec, scores, Hkv, T, Hq, chunks, (int)(Hq / Hkv), part};
+    if (launch_attend_mfma_k(pa, B * Hkv * chunks, s) != 0) return -10;
+  } else if (chunks > 0) {
     PartArgs pa{vcb, vrec, scores, Hkv, T, Hq, chunks, part};
     const dim3 grid((unsigned)(B * Hq * chunks));
     switch (vcb.k) {

@@ -28,6 +28,7 @@ KERNELS = {
     "decode_generic": "decode_generic",
     "attend_part": "attend_part",
     "attend_merge": "attend_merge",
+    "attend_mfma": "attend_mfma",
     "attend": "attend",
     "split256_prep": "split256_prep",
     "split256_kernel": "split256",

@@ -139,6 +139,12 @@ def test_long_context_attend(gpu_lib):
     (256, 4, 1, 256, 1, 1, 2, 1),         # one token
     (8, 2, 3, 16, 1, 1, 1, 2049),         # one lane per token
     (512, 3, 2, 512, 1, 1, 1, 700),
+    # int8-MFMA partials (values k <= 3): GQA 8:1 at k=3, two words per wave,
+    # an odd group of 3 heads, sub-chunk and chunk boundaries
+    (128, 3, 3, 128, 1, 1, 8, 1025),
+    (256, 2, 3, 256, 2, 2, 8, 1300),
+    (32, 2, 1, 32, 1, 1, 3, 257),
+    (64, 3, 2, 64, 1, 2, 4, 1024),
 ])
 def test_attend_shapes(gpu_lib, d, kb, vb, m, B, Hkv, Hq, T):
     import torch
