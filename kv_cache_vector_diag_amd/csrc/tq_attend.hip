@@ -412,8 +412,11 @@ struct MergeArgs {
 
 __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   constexpr int kWTile = 2048;             // chunk weights held in LDS at a time
+  constexpr int kU = 16;                   // chunk rows in flight per thread
   __shared__ float v[kMaxHeadDim];
   __shared__ float wsh[kWTile];
+  __shared__ float lsh[kWTile];
+  __shared__ float part[2 * kBlock];       // [row class][d]: rp * d = 2 * kBlock floats
   __shared__ float red[kBlock / 64];
   const int tid = threadIdx.x;
   const int d = a.vcb.d;
@@ -422,46 +425,72 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   const int64_t g = b * a.Hkv + hq * a.Hkv / a.Hq;
   const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob_of(a.vcb, g) + a.vcb.off_d);
   const float* p = a.part + bh * a.chunks * (d + 2);
+  // chunk maxima (and, for the first tile, the maxima and sums kept in LDS)
   float mx = -INFINITY;
-  for (int64_t c = tid; c < a.chunks; c += kBlock) mx = fmaxf(mx, p[c * (d + 2) + d]);
+  for (int64_t c = tid; c < a.chunks; c += kBlock) {
+    const float2 ml = *reinterpret_cast<const float2*>(p + c * (d + 2) + d);
+    mx = fmaxf(mx, ml.x);
+    if (c < kWTile) {
+      wsh[c] = ml.x;
+      lsh[c] = ml.y;
+    }
+  }
   mx = wave_max_f32(mx);
   if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
+  // thread = (coordinate pair jp, row class cg): rows c = cg, cg + rp, ... of each
+  // tile are summed in order, then the rp classes in order through LDS
+  const int tpr = d / 2, rp = kBlock / tpr;
+  const int jp = tid % tpr, cg = tid / tpr;
   float l = 0.0f;
-  float aj[kMaxHeadDim / kBlock > 0 ? kMaxHeadDim / kBlock : 1] = {};
+  float2 aj = {0.0f, 0.0f};
   for (int64_t c0 = 0; c0 < a.chunks; c0 += kWTile) {
     const int nc = (int)(a.chunks - c0 < kWTile ? a.chunks - c0 : kWTile);
     // rescale factor of each chunk, once
     for (int c = tid; c < nc; c += kBlock) {
-      const float wc = expf(p[(c0 + c) * (d + 2) + d] - mx);
+      float m_c, l_c;
+      if (c0 == 0) {
+        m_c = wsh[c];
+        l_c = lsh[c];
+      } else {
+        const float2 ml = *reinterpret_cast<const float2*>(p + (c0 + c) * (d + 2) + d);
+        m_c = ml.x;
+        l_c = ml.y;
+      }
+      const float wc = expf(m_c - mx);
       wsh[c] = wc;
-      l = fmaf(p[(c0 + c) * (d + 2) + d + 1], wc, l);
+      l = fmaf(l_c, wc, l);
     }
     __syncthreads();
+    for (int c = cg; c < nc; c += rp * kU) {
+      float2 pv[kU];
 #pragma unroll
-    for (int k = 0; k < kMaxHeadDim / kBlock; ++k) {
-      const int j = tid + k * kBlock;
-      if (j < d) {
-        const float* pj = p + c0 * (d + 2) + j;
-        float s0 = 0.0f, s1 = 0.0f;
-        int c = 0;
-        for (; c + 1 < nc; c += 2) {
-          s0 = fmaf(pj[c * (d + 2)], wsh[c], s0);
-          s1 = fmaf(pj[(c + 1) * (d + 2)], wsh[c + 1], s1);
-        }
-        if (c < nc) s0 = fmaf(pj[c * (d + 2)], wsh[c], s0);
-        aj[k] += s0 + s1;
+      for (int u = 0; u < kU; ++u) {
+        const int cc = c + rp * u;
+        pv[u] = cc < nc ? *reinterpret_cast<const float2*>(p + (c0 + cc) * (d + 2) + 2 * jp) : float2{0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int cc = c + rp * u;
+        const float wc = cc < nc ? wsh[cc] : 0.0f;
+        aj.x = fmaf(pv[u].x, wc, aj.x);
+        aj.y = fmaf(pv[u].y, wc, aj.y);
       }
     }
     __syncthreads();
   }
+  part[cg * d + 2 * jp] = aj.x;
+  part[cg * d + 2 * jp + 1] = aj.y;
   l = wave_sum_f32(l);
   if ((tid & 63) == 0) red[tid >> 6] = l;
-#pragma unroll
-  for (int k = 0; k < kMaxHeadDim / kBlock; ++k)
-    if (tid + k * kBlock < d) v[tid + k * kBlock] = aj[k];
+  __syncthreads();
+  for (int j = tid; j < d; j += kBlock) {
+    float t = 0.0f;
+    for (int q = 0; q < rp; ++q) t += part[q * d + j];
+    v[j] = t;
+  }
   __syncthreads();
   l = red[0] + red[1] + red[2] + red[3];
   for (int h = 1; h < d; h <<= 1) {
