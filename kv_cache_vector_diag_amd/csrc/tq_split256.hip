@@ -154,6 +154,7 @@ struct SplitArgs {
   int32_t* status;
   int frags;
   int64_t tiles_per_group, tiles_per_block, blocks_per_group;
+  bool xcd_major;
 };
 
 // Quantize one 32-row result tile (lane half h holds coordinates 16h + r in
@@ -258,253 +259,261 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
   constexpr int NTN = LN / 2 - 1, NTO = LO / 2 - 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, col = lane & 31;
-  const int64_t g = blockIdx.x / a.blocks_per_group;
-  const int64_t chunk = blockIdx.x % a.blocks_per_group;
-  const uint8_t* bn = a.cbn + (g % a.n_cb) * a.stride_n;
-  const uint8_t* bo = a.cbo + (g % a.n_cb) * a.stride_o;
-  if (tid == 0 && a.status) {
-    const BlobHeader* hn = reinterpret_cast<const BlobHeader*>(bn);
-    const BlobHeader* ho = reinterpret_cast<const BlobHeader*>(bo);
-    const bool bad = hn->magic != kBlobMagic || hn->version != kBlobVersion || hn->head_dim != kDn ||
-                     hn->bits != a.bits_n || hn->role != a.role || hn->rotation != (uint32_t)kRotHaar ||
-                     hn->projections != (KEY ? kDn : 0) || ho->magic != kBlobMagic ||
-                     ho->version != kBlobVersion || ho->head_dim != kNo || ho->bits != a.bits_o ||
-                     ho->role != a.role || ho->rotation != (uint32_t)kRotHadamard ||
-                     ho->projections != (KEY ? kNo : 0);
-    if (bad) atomicOr(a.status, TQ_STATUS_BAD_BLOB);
-  }
-  const u32x4* fr = a.frag + (int64_t)g * a.frags * kFragLanes;
-  for (int i = tid; i < (KEY ? kOutFrags : 2 * kKC) * kFragLanes; i += kThreads) ofr[i] = fr[kOffOR * kFragLanes + i];
-  if (tid < LN / 2) consts[tid] = reinterpret_cast<const float*>(bn + a.off_cn)[LN / 2 + tid];
-  if (tid < NTN) consts[8 + tid] = reinterpret_cast<const float*>(bn + a.off_tn)[LN / 2 + tid];
-  if (tid < LO / 2) consts[16 + tid] = reinterpret_cast<const float*>(bo + a.off_co)[LO / 2 + tid];
-  if (tid < NTO) consts[24 + tid] = reinterpret_cast<const float*>(bo + a.off_to)[LO / 2 + tid];
-  __syncthreads();
-  float cpn[LN / 2], tpn[NTN > 0 ? NTN : 1], cpo[LO / 2], tpo[NTO > 0 ? NTO : 1];
-#pragma unroll
-  for (int i = 0; i < LN / 2; ++i) cpn[i] = consts[i];
-#pragma unroll
-  for (int i = 0; i < NTN; ++i) tpn[i] = consts[8 + i];
-#pragma unroll
-  for (int i = 0; i < LO / 2; ++i) cpo[i] = consts[16 + i];
-#pragma unroll
-  for (int i = 0; i < NTO; ++i) tpo[i] = consts[24 + i];
-
-  const int64_t tile0 = chunk * a.tiles_per_block;
-  const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles_per_group);
-  constexpr int kSliceEntries = kSliceR * kFragLanes;   // u32x4 per rotation slice
-  constexpr int kPre = (kSliceEntries + kThreads - 1) / kThreads;
-  for (int64_t base = tile0; base < tile_end; base += kWaves) {
-    // re-derive the fragment base each step (opaque to the compiler), so that
-    // the slice addresses are not hoisted out of the loop into dozens of
-    // 64-bit registers; offsets below are 32-bit, from a uniform base
-    const uint8_t* frb = reinterpret_cast<const uint8_t*>(fr);
-    asm volatile("" : "+s"(frb));
-    const auto frag_at = [&](uint32_t entry) {
-      return *reinterpret_cast<const u32x4*>(frb + (size_t)(entry * 16u));
-    };
-    const int64_t tile = base + wave;
-    const int64_t tok = tile * 32 + col;
-    const bool valid = tile < tile_end && tok < a.N;
-
-    // ---- x: K-chunk c holds channels 16c + 8h .. +7 of token `col` (bf16 pairs);
-    // chunks are loaded kXPre ahead of their use, |x|^2 accumulates as they arrive
-    constexpr int kXPre = 4;
-    const uint32_t* xr = a.x + (g * a.sx_g + (valid ? tok : 0) * a.sx_n) / 2;
-    u32x4 xb[kKC];
-#pragma unroll
-    for (int c = 0; c < kXPre; ++c) xb[c] = *reinterpret_cast<const u32x4*>(xr + 8 * c + 4 * h);
-    double ss = 0.0;
-    __syncthreads();                                     // slice buffers free
-    for (int i = tid; i < kSliceEntries; i += kThreads) slice[i] = frag_at(kOffR * kFragLanes + i);
-
-    // ---- rotation, chunk-outer: u[m] (normal tiles), uo (outlier), xo (outlier gather)
-    f32x16 u[kMT];
-#pragma unroll
-    for (int m = 0; m < kMT; ++m) u[m] = f32x16{};
-    f32x16 uo = {}, xo = {};
-#pragma unroll
-    for (int c = 0; c < kKC; ++c) {
-      __syncthreads();                                   // slice c complete; the other buffer free
-      const u32x4* cur = slice + (c & 1) * kSliceEntries;
-      u32x4* nxt = slice + ((c + 1) & 1) * kSliceEntries;
-      // next slice: rotation chunk c+1, or (keys, after the last) projection slice 0
-      const bool more = c + 1 < kKC || KEY;
-      const int nent = (c + 1 < kKC ? kSliceR : kSliceS) * kFragLanes;
-      const uint32_t nbase = c + 1 < kKC ? (uint32_t)((kOffR + (c + 1) * kSliceR) * kFragLanes)
-                                         : (uint32_t)(kOffS * kFragLanes);
-      u32x4 pre[kPre];
-#pragma unroll
-      for (int i = 0; i < kPre; ++i) {
-        const int idx = tid + i * kThreads;
-        if (more && idx < nent) pre[i] = frag_at(nbase + (uint32_t)idx);
-      }
-      if (c + kXPre < kKC) xb[c + kXPre] = *reinterpret_cast<const u32x4*>(xr + 8 * (c + kXPre) + 4 * h);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) ss += pair_sumsq_bf16(xb[c][q]);
-      const bf16x8 xv = as<bf16x8>(xb[c]);
-#pragma unroll
-      for (int m = 0; m < kMT; ++m) {
-#pragma unroll
-        for (int pc = 0; pc < kRPieces; ++pc)
-          u[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(cur[(m * kRPieces + pc) * kFragLanes + lane]), xv,
-                                                         u[m], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);               // a few fragments live at a time
-      }
-      uo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[c * kFragLanes + lane]), xv, uo, 0, 0, 0);
-      xo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[(kKC + c) * kFragLanes + lane]), xv, xo, 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < kPre; ++i) {
-        const int idx = tid + i * kThreads;
-        if (more && idx < nent) nxt[idx] = pre[i];
-      }
+  // group assignment: XCD-major (workgroup b runs on XCD b % 8 under the usual
+  // round-robin dispatch; all workgroups of one XCD share a group at a time, so
+  // its fragments stay in that XCD's L2), else one group per workgroup range
+  const int64_t g_begin = a.xcd_major ? (int64_t)(blockIdx.x % 8) : blockIdx.x / a.blocks_per_group;
+  const int64_t chunk = a.xcd_major ? (int64_t)(blockIdx.x / 8) : blockIdx.x % a.blocks_per_group;
+  const int64_t g_step = a.xcd_major ? 8 : a.G;
+  for (int64_t g = g_begin; g < a.G; g += g_step) {
+    __syncthreads();                                   // the previous group is done with LDS
+    const uint8_t* bn = a.cbn + (g % a.n_cb) * a.stride_n;
+    const uint8_t* bo = a.cbo + (g % a.n_cb) * a.stride_o;
+    if (tid == 0 && a.status) {
+      const BlobHeader* hn = reinterpret_cast<const BlobHeader*>(bn);
+      const BlobHeader* ho = reinterpret_cast<const BlobHeader*>(bo);
+      const bool bad = hn->magic != kBlobMagic || hn->version != kBlobVersion || hn->head_dim != kDn ||
+                       hn->bits != a.bits_n || hn->role != a.role || hn->rotation != (uint32_t)kRotHaar ||
+                       hn->projections != (KEY ? kDn : 0) || ho->magic != kBlobMagic ||
+                       ho->version != kBlobVersion || ho->head_dim != kNo || ho->bits != a.bits_o ||
+                       ho->role != a.role || ho->rotation != (uint32_t)kRotHadamard ||
+                       ho->projections != (KEY ? kNo : 0);
+      if (bad) atomicOr(a.status, TQ_STATUS_BAD_BLOB);
     }
+    const u32x4* fr = a.frag + (int64_t)g * a.frags * kFragLanes;
+    for (int i = tid; i < (KEY ? kOutFrags : 2 * kKC) * kFragLanes; i += kThreads) ofr[i] = fr[kOffOR * kFragLanes + i];
+    if (tid < LN / 2) consts[tid] = reinterpret_cast<const float*>(bn + a.off_cn)[LN / 2 + tid];
+    if (tid < NTN) consts[8 + tid] = reinterpret_cast<const float*>(bn + a.off_tn)[LN / 2 + tid];
+    if (tid < LO / 2) consts[16 + tid] = reinterpret_cast<const float*>(bo + a.off_co)[LO / 2 + tid];
+    if (tid < NTO) consts[24 + tid] = reinterpret_cast<const float*>(bo + a.off_to)[LO / 2 + tid];
+    __syncthreads();
+    float cpn[LN / 2], tpn[NTN > 0 ? NTN : 1], cpo[LO / 2], tpo[NTO > 0 ? NTO : 1];
+  #pragma unroll
+    for (int i = 0; i < LN / 2; ++i) cpn[i] = consts[i];
+  #pragma unroll
+    for (int i = 0; i < NTN; ++i) tpn[i] = consts[8 + i];
+  #pragma unroll
+    for (int i = 0; i < LO / 2; ++i) cpo[i] = consts[16 + i];
+  #pragma unroll
+    for (int i = 0; i < NTO; ++i) tpo[i] = consts[24 + i];
 
-    // ---- norms (float64): |x|^2 from pair sums, |x_o|^2 from the exact gather
-    double so = 0.0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) so = fma((double)xo[r], (double)xo[r], so);
-    {
-      uint32_t l1 = __double2loint(ss), h1 = __double2hiint(ss), l2 = __double2loint(so), h2 = __double2hiint(so);
-      auto p1 = __builtin_amdgcn_permlane32_swap(l1, l1, false, false);
-      auto q1 = __builtin_amdgcn_permlane32_swap(h1, h1, false, false);
-      auto p2 = __builtin_amdgcn_permlane32_swap(l2, l2, false, false);
-      auto q2 = __builtin_amdgcn_permlane32_swap(h2, h2, false, false);
-      ss += __hiloint2double((int)(h ? q1[0] : q1[1]), (int)(h ? p1[0] : p1[1]));
-      so += __hiloint2double((int)(h ? q2[0] : q2[1]), (int)(h ? p2[0] : p2[1]));
-    }
-    const bool finite = ss <= 3.4028234663852886e38;
-    if (a.status && __ballot(valid && !finite && h == 0) != 0 && lane == 0) atomicOr(a.status, TQ_STATUS_NON_FINITE);
-    double sn = ss - so;
-    sn = sn > 0.0 ? sn : 0.0;
-    const float no32 = (float)sqrt(so), nn32 = (float)sqrt(sn);
-    // powers of two bringing each part's residual to O(1) for the f16 split
-    const auto pow2_scale = [](float n) {
-      const uint32_t e = (__float_as_uint(n) >> 23) & 0xFFu;
-      return (n > 0.0f && e < 253u) ? __uint_as_float((254u - e) << 23) : 1.0f;
-    };
-    const float sco = pow2_scale(no32), scn = pow2_scale(nn32);
+    const int64_t tile0 = chunk * a.tiles_per_block;
+    const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles_per_group);
+    constexpr int kSliceEntries = kSliceR * kFragLanes;   // u32x4 per rotation slice
+    constexpr int kPre = (kSliceEntries + kThreads - 1) / kThreads;
+    for (int64_t base = tile0; base < tile_end; base += kWaves) {
+      // re-derive the fragment base each step (opaque to the compiler), so that
+      // the slice addresses are not hoisted out of the loop into dozens of
+      // 64-bit registers; offsets below are 32-bit, from a uniform base
+      const uint8_t* frb = reinterpret_cast<const uint8_t*>(fr);
+      asm volatile("" : "+s"(frb));
+      const auto frag_at = [&](uint32_t entry) {
+        return *reinterpret_cast<const u32x4*>(frb + (size_t)(entry * 16u));
+      };
+      const int64_t tile = base + wave;
+      const int64_t tok = tile * 32 + col;
+      const bool valid = tile < tile_end && tok < a.N;
 
-    // ---- outlier part: quantize, QJL
-    float tno[NTO > 0 ? NTO : 1];
-#pragma unroll
-    for (int t = 0; t < NTO; ++t) tno[t] = tpo[t] * no32;
-    uint32_t pw_o, tw_o[NTO > 0 ? NTO : 1];
-    u32x4 who[2], wlo_o[2];
-    float wsq_o = 0.0f;
-    quantize_tile<KO, KEY>(uo, no32, cpo, tno, sco, pw_o, tw_o, who, wlo_o, wsq_o);
-    asm volatile("" : "+v"(pw_o));
-#pragma unroll
-    for (int t = 0; t < NTO; ++t) asm volatile("" : "+v"(tw_o[t]));
-    uint32_t sw_o = 0;
-    float gam_o = 0.0f;
-    if (KEY) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 sf = ofr[(2 * kKC + c) * kFragLanes + lane];
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(who[c]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(wlo_o[c]), acc, 0, 0, 0);
+      // ---- x: K-chunk c holds channels 16c + 8h .. +7 of token `col` (bf16 pairs);
+      // chunks are loaded kXPre ahead of their use, |x|^2 accumulates as they arrive
+      constexpr int kXPre = 4;
+      const uint32_t* xr = a.x + (g * a.sx_g + (valid ? tok : 0) * a.sx_n) / 2;
+      u32x4 xb[kKC];
+  #pragma unroll
+      for (int c = 0; c < kXPre; ++c) xb[c] = *reinterpret_cast<const u32x4*>(xr + 8 * c + 4 * h);
+      double ss = 0.0;
+      __syncthreads();                                     // slice buffers free
+      for (int i = tid; i < kSliceEntries; i += kThreads) slice[i] = frag_at(kOffR * kFragLanes + i);
+
+      // ---- rotation, chunk-outer: u[m] (normal tiles), uo (outlier), xo (outlier gather)
+      f32x16 u[kMT];
+  #pragma unroll
+      for (int m = 0; m < kMT; ++m) u[m] = f32x16{};
+      f32x16 uo = {}, xo = {};
+  #pragma unroll
+      for (int c = 0; c < kKC; ++c) {
+        __syncthreads();                                   // slice c complete; the other buffer free
+        const u32x4* cur = slice + (c & 1) * kSliceEntries;
+        u32x4* nxt = slice + ((c + 1) & 1) * kSliceEntries;
+        // next slice: rotation chunk c+1, or (keys, after the last) projection slice 0
+        const bool more = c + 1 < kKC || KEY;
+        const int nent = (c + 1 < kKC ? kSliceR : kSliceS) * kFragLanes;
+        const uint32_t nbase = c + 1 < kKC ? (uint32_t)((kOffR + (c + 1) * kSliceR) * kFragLanes)
+                                           : (uint32_t)(kOffS * kFragLanes);
+        u32x4 pre[kPre];
+  #pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+          const int idx = tid + i * kThreads;
+          if (more && idx < nent) pre[i] = frag_at(nbase + (uint32_t)idx);
+        }
+        if (c + kXPre < kKC) xb[c + kXPre] = *reinterpret_cast<const u32x4*>(xr + 8 * (c + kXPre) + 4 * h);
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) ss += pair_sumsq_bf16(xb[c][q]);
+        const bf16x8 xv = as<bf16x8>(xb[c]);
+        // pieces outer, row tiles inner: consecutive MFMAs use different accumulators
+  #pragma unroll
+        for (int pc = 0; pc < kRPieces; ++pc) {
+  #pragma unroll
+          for (int m = 0; m < kMT; ++m)
+            u[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(cur[(m * kRPieces + pc) * kFragLanes + lane]), xv,
+                                                           u[m], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);               // a few fragments live at a time
+        }
+        uo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[c * kFragLanes + lane]), xv, uo, 0, 0, 0);
+        xo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[(kKC + c) * kFragLanes + lane]), xv, xo, 0, 0, 0);
+  #pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+          const int idx = tid + i * kThreads;
+          if (more && idx < nent) nxt[idx] = pre[i];
+        }
       }
-      sw_o = sign_word(acc);
-      asm volatile("" : "+v"(sw_o));
-      auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq_o), __float_as_uint(wsq_o), false, false);
-      gam_o = sqrtf(__uint_as_float(pg[0]) + __uint_as_float(pg[1])) * 0.17677669529663688f;   // / sqrt(32)
-    }
 
-    // ---- normal part: quantize the 7 row tiles
-    float tnn[NTN > 0 ? NTN : 1];
-#pragma unroll
-    for (int t = 0; t < NTN; ++t) tnn[t] = tpn[t] * nn32;
-    uint32_t pw_n[kMT], tw_n[NTN > 0 ? NTN : 1][kMT];
-    u32x4 whn[KEY ? kQC : 1], wln[KEY ? kQC : 1];
-    float wsq_n = 0.0f;
-#pragma unroll
-    for (int m = 0; m < kMT; ++m) {
-      uint32_t twm[NTN > 0 ? NTN : 1];
-      quantize_tile<KN, KEY>(u[m], nn32, cpn, tnn, scn, pw_n[m], twm, KEY ? &whn[2 * m] : whn,
-                             KEY ? &wln[2 * m] : wln, wsq_n);
-#pragma unroll
-      for (int t = 0; t < NTN; ++t) {
-        tw_n[t][m] = twm[t];
-        asm volatile("" : "+v"(tw_n[t][m]));
+      // ---- norms (float64): |x|^2 from pair sums, |x_o|^2 from the exact gather
+      double so = 0.0;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) so = fma((double)xo[r], (double)xo[r], so);
+      {
+        uint32_t l1 = __double2loint(ss), h1 = __double2hiint(ss), l2 = __double2loint(so), h2 = __double2hiint(so);
+        auto p1 = __builtin_amdgcn_permlane32_swap(l1, l1, false, false);
+        auto q1 = __builtin_amdgcn_permlane32_swap(h1, h1, false, false);
+        auto p2 = __builtin_amdgcn_permlane32_swap(l2, l2, false, false);
+        auto q2 = __builtin_amdgcn_permlane32_swap(h2, h2, false, false);
+        ss += __hiloint2double((int)(h ? q1[0] : q1[1]), (int)(h ? p1[0] : p1[1]));
+        so += __hiloint2double((int)(h ? q2[0] : q2[1]), (int)(h ? p2[0] : p2[1]));
       }
-      asm volatile("" : "+v"(pw_n[m]));
+      const bool finite = ss <= 3.4028234663852886e38;
+      if (a.status && __ballot(valid && !finite && h == 0) != 0 && lane == 0) atomicOr(a.status, TQ_STATUS_NON_FINITE);
+      double sn = ss - so;
+      sn = sn > 0.0 ? sn : 0.0;
+      const float no32 = (float)sqrt(so), nn32 = (float)sqrt(sn);
+      // powers of two bringing each part's residual to O(1) for the f16 split
+      const auto pow2_scale = [](float n) {
+        const uint32_t e = (__float_as_uint(n) >> 23) & 0xFFu;
+        return (n > 0.0f && e < 253u) ? __uint_as_float((254u - e) << 23) : 1.0f;
+      };
+      const float sco = pow2_scale(no32), scn = pow2_scale(nn32);
+
+      // ---- outlier part: quantize, QJL
+      float tno[NTO > 0 ? NTO : 1];
+  #pragma unroll
+      for (int t = 0; t < NTO; ++t) tno[t] = tpo[t] * no32;
+      uint32_t pw_o, tw_o[NTO > 0 ? NTO : 1];
+      u32x4 who[2], wlo_o[2];
+      float wsq_o = 0.0f;
+      quantize_tile<KO, KEY>(uo, no32, cpo, tno, sco, pw_o, tw_o, who, wlo_o, wsq_o);
+      asm volatile("" : "+v"(pw_o));
+  #pragma unroll
+      for (int t = 0; t < NTO; ++t) asm volatile("" : "+v"(tw_o[t]));
+      uint32_t sw_o = 0;
+      float gam_o = 0.0f;
       if (KEY) {
-        asm volatile("" : "+v"(whn[2 * m]), "+v"(whn[2 * m + 1]), "+v"(wln[2 * m]), "+v"(wln[2 * m + 1]));
-      }
-      __builtin_amdgcn_sched_barrier(0);                 // one tile's temporaries at a time
-    }
-
-    // ---- keys: QJL of the normal part, one 32-projection slice at a time
-    uint32_t sw_n[kMT];
-    float gam_n = 0.0f;
-    if (KEY) {
-#pragma unroll
-      for (int mp = 0; mp < kMT; ++mp) {
-        __syncthreads();
-        const u32x4* cur = slice + ((kKC + mp) & 1) * kSliceEntries;
-        u32x4* nxt = slice + ((kKC + mp + 1) & 1) * kSliceEntries;
-        const bool more = mp + 1 < kMT;
-        const uint32_t nbase = (uint32_t)((kOffS + (mp + 1) * kSliceS) * kFragLanes);
-        constexpr int kPreS = (kSliceS * kFragLanes + kThreads - 1) / kThreads;
-        u32x4 pre[kPreS];
-#pragma unroll
-        for (int i = 0; i < kPreS; ++i) {
-          const int idx = tid + i * kThreads;
-          if (more && idx < kSliceS * kFragLanes) pre[i] = frag_at(nbase + (uint32_t)idx);
-        }
         f32x16 acc = {};
-#pragma unroll
-        for (int c = 0; c < kQC; ++c) {
-          const u32x4 sf = cur[c * kFragLanes + lane];
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(whn[c]), acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(wln[c]), acc, 0, 0, 0);
-          if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const u32x4 sf = ofr[(2 * kKC + c) * kFragLanes + lane];
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(who[c]), acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(wlo_o[c]), acc, 0, 0, 0);
         }
-        sw_n[mp] = sign_word(acc);
-        asm volatile("" : "+v"(sw_n[mp]));   // materialise here (not next to the stores)
-#pragma unroll
-        for (int i = 0; i < kPreS; ++i) {
-          const int idx = tid + i * kThreads;
-          if (more && idx < kSliceS * kFragLanes) nxt[idx] = pre[i];
-        }
+        sw_o = sign_word(acc);
+        asm volatile("" : "+v"(sw_o));
+        auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq_o), __float_as_uint(wsq_o), false, false);
+        gam_o = sqrtf(__uint_as_float(pg[0]) + __uint_as_float(pg[1])) * 0.17677669529663688f;   // / sqrt(32)
       }
-      auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq_n), __float_as_uint(wsq_n), false, false);
-      gam_n = sqrtf(__uint_as_float(pg[0]) + __uint_as_float(pg[1])) * 0.06681531047810609f;   // / sqrt(224)
-    }
 
-    // ---- records (built in every lane, stored for valid tokens only: keeping
-    // the computation unconditional stops the compiler from sinking it into
-    // the store branch with all projection accumulators alive)
-    {
-      const int64_t tk = valid ? tok : 0;
-      // normal: KN planes x 7 words, (keys) 7 sign words, n, gamma
-      constexpr int NPN = KN * kMT + (KEY ? kMT : 0);
-      uint32_t part[NPN];
-#pragma unroll
+      // ---- normal part: quantize the 7 row tiles
+      float tnn[NTN > 0 ? NTN : 1];
+  #pragma unroll
+      for (int t = 0; t < NTN; ++t) tnn[t] = tpn[t] * nn32;
+      uint32_t pw_n[kMT], tw_n[NTN > 0 ? NTN : 1][kMT];
+      u32x4 whn[KEY ? kQC : 1], wln[KEY ? kQC : 1];
+      float wsq_n = 0.0f;
+  #pragma unroll
       for (int m = 0; m < kMT; ++m) {
         uint32_t twm[NTN > 0 ? NTN : 1];
-#pragma unroll
-        for (int t = 0; t < NTN; ++t) twm[t] = tw_n[t][m];
-        uint32_t pl[KN];
-        tile_planes<KN>(pw_n[m], twm, pl);
-#pragma unroll
-        for (int p = 0; p < KN; ++p) part[p * kMT + m] = h ? (pl[p] << 16) : (pl[p] & 0xFFFFu);
-        if (KEY) part[KN * kMT + m] = h ? ((~sw_n[m]) << 16) : ((~sw_n[m]) & 0xFFFFu);
+        quantize_tile<KN, KEY>(u[m], nn32, cpn, tnn, scn, pw_n[m], twm, KEY ? &whn[2 * m] : whn,
+                               KEY ? &wln[2 * m] : wln, wsq_n);
+  #pragma unroll
+        for (int t = 0; t < NTN; ++t) {
+          tw_n[t][m] = twm[t];
+          asm volatile("" : "+v"(tw_n[t][m]));
+        }
+        asm volatile("" : "+v"(pw_n[m]));
+        if (KEY) {
+          asm volatile("" : "+v"(whn[2 * m]), "+v"(whn[2 * m + 1]), "+v"(wln[2 * m]), "+v"(wln[2 * m + 1]));
+        }
+        __builtin_amdgcn_sched_barrier(0);                 // one tile's temporaries at a time
       }
-      const uint32_t tail_n[2] = {__float_as_uint(nn32), __float_as_uint(gam_n)};
-      store_record<NPN, KEY ? 2 : 1>(part, tail_n, h, valid, a.rec_n + (g * a.N + tk) * (NPN + (KEY ? 2 : 1)));
-      // outlier: KO planes, (keys) 1 sign word, n, gamma
-      constexpr int NPO = KO + (KEY ? 1 : 0);
-      uint32_t parto[NPO];
-      uint32_t plo[KO];
-      tile_planes<KO>(pw_o, tw_o, plo);
-#pragma unroll
-      for (int p = 0; p < KO; ++p) parto[p] = h ? (plo[p] << 16) : (plo[p] & 0xFFFFu);
-      if (KEY) parto[KO] = h ? ((~sw_o) << 16) : ((~sw_o) & 0xFFFFu);
-      const uint32_t tail_o[2] = {__float_as_uint(no32), __float_as_uint(gam_o)};
-      store_record<NPO, KEY ? 2 : 1>(parto, tail_o, h, valid, a.rec_o + (g * a.N + tk) * (NPO + (KEY ? 2 : 1)));
+
+      // ---- keys: QJL of the normal part, one 32-projection slice at a time
+      uint32_t sw_n[kMT];
+      float gam_n = 0.0f;
+      if (KEY) {
+  #pragma unroll
+        for (int mp = 0; mp < kMT; ++mp) {
+          __syncthreads();
+          const u32x4* cur = slice + ((kKC + mp) & 1) * kSliceEntries;
+          u32x4* nxt = slice + ((kKC + mp + 1) & 1) * kSliceEntries;
+          const bool more = mp + 1 < kMT;
+          const uint32_t nbase = (uint32_t)((kOffS + (mp + 1) * kSliceS) * kFragLanes);
+          constexpr int kPreS = (kSliceS * kFragLanes + kThreads - 1) / kThreads;
+          u32x4 pre[kPreS];
+  #pragma unroll
+          for (int i = 0; i < kPreS; ++i) {
+            const int idx = tid + i * kThreads;
+            if (more && idx < kSliceS * kFragLanes) pre[i] = frag_at(nbase + (uint32_t)idx);
+          }
+          f32x16 acc = {};
+  #pragma unroll
+          for (int c = 0; c < kQC; ++c) {
+            const u32x4 sf = cur[c * kFragLanes + lane];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(whn[c]), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(wln[c]), acc, 0, 0, 0);
+            if ((c & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+          sw_n[mp] = sign_word(acc);
+          asm volatile("" : "+v"(sw_n[mp]));   // materialise here (not next to the stores)
+  #pragma unroll
+          for (int i = 0; i < kPreS; ++i) {
+            const int idx = tid + i * kThreads;
+            if (more && idx < kSliceS * kFragLanes) nxt[idx] = pre[i];
+          }
+        }
+        auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq_n), __float_as_uint(wsq_n), false, false);
+        gam_n = sqrtf(__uint_as_float(pg[0]) + __uint_as_float(pg[1])) * 0.06681531047810609f;   // / sqrt(224)
+      }
+
+      // ---- records (built in every lane, stored for valid tokens only: keeping
+      // the computation unconditional stops the compiler from sinking it into
+      // the store branch with all projection accumulators alive)
+      {
+        const int64_t tk = valid ? tok : 0;
+        // normal: KN planes x 7 words, (keys) 7 sign words, n, gamma
+        constexpr int NPN = KN * kMT + (KEY ? kMT : 0);
+        uint32_t part[NPN];
+  #pragma unroll
+        for (int m = 0; m < kMT; ++m) {
+          uint32_t twm[NTN > 0 ? NTN : 1];
+  #pragma unroll
+          for (int t = 0; t < NTN; ++t) twm[t] = tw_n[t][m];
+          uint32_t pl[KN];
+          tile_planes<KN>(pw_n[m], twm, pl);
+  #pragma unroll
+          for (int p = 0; p < KN; ++p) part[p * kMT + m] = h ? (pl[p] << 16) : (pl[p] & 0xFFFFu);
+          if (KEY) part[KN * kMT + m] = h ? ((~sw_n[m]) << 16) : ((~sw_n[m]) & 0xFFFFu);
+        }
+        const uint32_t tail_n[2] = {__float_as_uint(nn32), __float_as_uint(gam_n)};
+        store_record<NPN, KEY ? 2 : 1>(part, tail_n, h, valid, a.rec_n + (g * a.N + tk) * (NPN + (KEY ? 2 : 1)));
+        // outlier: KO planes, (keys) 1 sign word, n, gamma
+        constexpr int NPO = KO + (KEY ? 1 : 0);
+        uint32_t parto[NPO];
+        uint32_t plo[KO];
+        tile_planes<KO>(pw_o, tw_o, plo);
+  #pragma unroll
+        for (int p = 0; p < KO; ++p) parto[p] = h ? (plo[p] << 16) : (plo[p] & 0xFFFFu);
+        if (KEY) parto[KO] = h ? ((~sw_o) << 16) : ((~sw_o) & 0xFFFFu);
+        const uint32_t tail_o[2] = {__float_as_uint(no32), __float_as_uint(gam_o)};
+        store_record<NPO, KEY ? 2 : 1>(parto, tail_o, h, valid, a.rec_o + (g * a.N + tk) * (NPO + (KEY ? 2 : 1)));
+      }
     }
   }
 }
@@ -518,7 +527,8 @@ int launch_split(SplitArgs a, hipStream_t s) {
       return -10;
     attr_set = true;
   }
-  hipLaunchKernelGGL((split256_kernel<KN, KO, KEY>), dim3((unsigned)(a.G * a.blocks_per_group)), dim3(kThreads),
+  const int64_t grid = a.xcd_major ? 8 * a.blocks_per_group : a.G * a.blocks_per_group;
+  hipLaunchKernelGGL((split256_kernel<KN, KO, KEY>), dim3((unsigned)grid), dim3(kThreads),
                      kLdsBytes, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
@@ -569,14 +579,17 @@ int launch_split256(int role, int bits, const Layout& Ln, const Layout& Lo, cons
   a.status = status;
   a.frags = frags;
   a.tiles_per_group = (N + 31) / 32;
-  // about two workgroups per CU over the launch, whole 8-tile steps
-  int64_t bpg = (512 + G - 1) / G;
+  // Many groups: one workgroup per CU (256), XCD-major, each group's tiles split
+  // over the 32 workgroups of its XCD.  Few groups: about two workgroups per CU
+  // over the launch, each on one group; whole 8-tile steps either way.
+  a.xcd_major = G >= 32;
+  int64_t bpg = a.xcd_major ? 32 : (512 + G - 1) / G;
   if (bpg > a.tiles_per_group) bpg = a.tiles_per_group;
   if (bpg < 1) bpg = 1;
   int64_t per_block = (a.tiles_per_group + bpg - 1) / bpg;
   per_block = (per_block + kWaves - 1) / kWaves * kWaves;
   a.tiles_per_block = per_block;
-  a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
+  a.blocks_per_group = a.xcd_major ? 32 : (a.tiles_per_group + per_block - 1) / per_block;
   if (key) return bits == 2 ? launch_split<1, 2, true>(a, s) : launch_split<2, 3, true>(a, s);
   return bits == 2 ? launch_split<2, 3, false>(a, s) : launch_split<3, 4, false>(a, s);
 }

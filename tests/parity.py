@@ -3,8 +3,11 @@
 Tolerances (the benchmark spec): codes and signs bit-exact except coordinates within
 1e-6 of a decision boundary (z within 1e-6 of a threshold; |(S rho)_i| within
 1e-6 gamma of 0); the number of such mismatches must stay below 1e-5 of all
-coordinates; a vector with an excepted index mismatch is left out of the sign,
-norm and score checks.  Rotated vectors and norms: 1e-5 relative.  Scores and
+coordinates -- a rate, so it is checked over all the coordinates a test encodes
+(check_mismatch_fraction over the reports of its groups), not per group, where
+a single in-band flip among fewer than 1e5 coordinates would already exceed
+it; a vector with an excepted index mismatch is left out of the sign, norm and
+score checks.  Rotated vectors and norms: 1e-5 relative.  Scores and
 decoded values: |gpu - oracle| <= 1e-4 + 1e-3 |oracle|.
 """
 from __future__ import annotations
@@ -30,9 +33,22 @@ class RecordReport:
     excluded_vectors: int
     max_rel_n: float
     max_rel_gamma: float
+    sign_coords: int = 0
 
 
-def compare_records(qz: tq.Quantizer, gpu_rec: np.ndarray, enc: tq.Encoded) -> RecordReport:
+def check_mismatch_fraction(reports) -> None:
+    """In-band mismatches over all the reports' coordinates stay below 1e-5 of them."""
+    idx = sum(r.idx_mismatch_in_band for r in reports)
+    coords = sum(r.coords for r in reports)
+    sgn = sum(r.sign_mismatch_in_band for r in reports)
+    sign_coords = sum(r.sign_coords for r in reports)
+    assert idx <= MISMATCH_FRACTION * coords, f"{idx} in-band index mismatches of {coords}"
+    assert sgn <= MISMATCH_FRACTION * max(sign_coords, 1), f"{sgn} in-band sign mismatches of {sign_coords}"
+
+
+def compare_records(qz: tq.Quantizer, gpu_rec: np.ndarray, enc: tq.Encoded, fraction: bool = True) -> RecordReport:
+    """Band-rule comparison of one group's records; `fraction=False` leaves the
+    mismatch-rate check to check_mismatch_fraction over several groups."""
     gpu_rec = np.ascontiguousarray(gpu_rec).view(np.uint32).reshape(-1, qz.words)
     ok = ~enc.flags
     g = tq.unpack_record(qz, gpu_rec)
@@ -43,7 +59,6 @@ def compare_records(qz: tq.Quantizer, gpu_rec: np.ndarray, enc: tq.Encoded) -> R
     bad = mism & ~(dist < BAND)
     assert not bad.any(), f"{int(bad.sum())} index mismatches outside the 1e-6 band, first at {np.argwhere(bad)[:5]}"
     n_idx = int(mism.sum())
-    assert n_idx <= MISMATCH_FRACTION * mism.size, f"{n_idx} in-band index mismatches of {mism.size}"
     keep = ok & ~mism.any(axis=1)
     rel_n = np.abs(g.n32 - o.n32)[keep] / np.maximum(np.abs(o.n32[keep]), 1e-30)
     assert np.all(rel_n <= 1e-5), f"norm rel err {rel_n.max()}"
@@ -55,13 +70,16 @@ def compare_records(qz: tq.Quantizer, gpu_rec: np.ndarray, enc: tq.Encoded) -> R
         bad = smis & ~(ratio < BAND)
         assert not bad.any(), f"{int(bad.sum())} sign mismatches outside the band, first at {np.argwhere(bad)[:5]}"
         n_sign = int(smis.sum())
-        assert n_sign <= MISMATCH_FRACTION * smis.size
         # unused sign bits are zero on both sides (bit-exact on the sign words of kept vectors)
         rel_g = np.abs(g.gamma32 - o.gamma32)[keep] / np.maximum(np.abs(o.gamma32[keep]), 1e-30)
         small = o.gamma32[keep] < 1e-30
         assert np.all((rel_g <= 1e-5) | small), f"gamma rel err {rel_g.max()}"
-    return RecordReport(gpu_rec.shape[0], int(mism.size), n_idx, n_sign, int((~keep).sum()),
-                        float(rel_n.max(initial=0.0)), float(rel_g.max(initial=0.0)))
+    rep = RecordReport(gpu_rec.shape[0], int(mism.size), n_idx, n_sign, int((~keep).sum()),
+                       float(rel_n.max(initial=0.0)), float(rel_g.max(initial=0.0)),
+                       int(gpu_rec.shape[0] * qz.m) if qz.role == tq.ROLE_KEY else 0)
+    if fraction:
+        check_mismatch_fraction([rep])
+    return rep
 
 
 def assert_close(gpu: np.ndarray, ref: np.ndarray, what: str, atol=ATOL, rtol=RTOL):

@@ -18,7 +18,7 @@ from kv_cache_vector_diag_amd import inputs
 from oracle import split
 from oracle import turboquant as tq
 
-from .parity import assert_close, compare_records, rec_np
+from .parity import assert_close, check_mismatch_fraction, compare_records, rec_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -50,15 +50,17 @@ def test_decode_step_32k_encode_and_scores(gpu_lib):
     del K
     rng = np.random.default_rng(0)
     qv = inputs.exact_values(q)
+    reps = []
     for g in (0, 77, G - 1):
         toks = _sample_tokens(rng, T, 1500)
         X = _bf16_exact(inputs.kv_normal(seed, G, T, d, groups=[g]))[0][toks]
         grec = rec_np(rec[g])[toks]
-        compare_records(qzs[g % Hkv], grec, tq.encode(qzs[g % Hkv], X))
+        reps.append(compare_records(qzs[g % Hkv], grec, tq.encode(qzs[g % Hkv], X), fraction=False))
         bb, h = divmod(g, Hkv)
         ref = tq.scores([qzs[h]], grec[None, None], qv[bb:bb + 1, 4 * h:4 * h + 4])
         got = scores[bb, 4 * h:4 * h + 4][:, torch.from_numpy(toks).to(DEV)].cpu().numpy()[None]
         assert_close(got, ref, f"scores g={g}")
+    check_mismatch_fraction(reps)
 
 
 def test_prefill_encode_full(gpu_lib):
@@ -74,14 +76,16 @@ def test_prefill_encode_full(gpu_lib):
     vrec = b.tq_encode_values(vcb, G, V, d, 4)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
+    reps = []
     for g in (0, 131, G - 1):
         toks = _sample_tokens(rng, T, 800)
         kq = tq.Quantizer(d, 4, 128, seed + g, tq.ROLE_KEY)
         vq = tq.Quantizer(d, 4, 0, seed + g, tq.ROLE_VALUE)
         kx = inputs.exact_values(K[g])[toks]
         vx = inputs.exact_values(V[g])[toks]
-        compare_records(kq, rec_np(krec[g])[toks], tq.encode(kq, kx))
-        compare_records(vq, rec_np(vrec[g])[toks], tq.encode(vq, vx))
+        reps.append(compare_records(kq, rec_np(krec[g])[toks], tq.encode(kq, kx), fraction=False))
+        reps.append(compare_records(vq, rec_np(vrec[g])[toks], tq.encode(vq, vx), fraction=False))
+    check_mismatch_fraction(reps)
     # the inputs the GPU encoded are the generator's, regenerated alone on the CPU
     assert np.array_equal(inputs.exact_values(K[5]), _bf16_exact(inputs.kv_outliers(seed, G, T, d, groups=[5])[0])[0])
 
@@ -118,6 +122,7 @@ def test_mixed_precision_layers_full(gpu_lib):
     s0, s1 = 2 * Hkv, (L - 2) * Hkv
     GS = s1 - s0
     rng = np.random.default_rng(2)
+    reps = []
     for role, stream in ((b.ROLE_KEY, inputs.STREAM_K), (b.ROLE_VALUE, inputs.STREAM_V)):
         X = torch.empty((G, T, d), dtype=torch.bfloat16, device=DEV)
         for l in range(L):
@@ -144,9 +149,11 @@ def test_mixed_precision_layers_full(gpu_lib):
             sq = split.split_quantizer(d, n_out, 3, seed + g, role)
             toks = _sample_tokens(rng, T, 600)
             en, eo = split.encode_split(sq, Xg[toks], ch)
-            compare_records(sq.normal, rec_np(rn[gs])[toks], en)
-            compare_records(sq.outlier, rec_np(ro[gs])[toks], eo)
+            reps.append(compare_records(sq.normal, rec_np(rn[gs])[toks], en, fraction=False))
+            reps.append(compare_records(sq.outlier, rec_np(ro[gs])[toks], eo, fraction=False))
         toks = _sample_tokens(rng, T, 300)
         q8 = tq.Quantizer(d, 8, d if key else 0, seed + 3, role)
-        compare_records(q8, rec_np(r8[3])[toks], tq.encode(q8, inputs.exact_values(X[3])[toks]))
+        reps.append(compare_records(q8, rec_np(r8[3])[toks], tq.encode(q8, inputs.exact_values(X[3])[toks]),
+                                    fraction=False))
         del X
+    check_mismatch_fraction(reps)

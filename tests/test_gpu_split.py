@@ -11,7 +11,7 @@ from kv_cache_vector_diag_amd import inputs
 from oracle import split
 from oracle import turboquant as tq
 
-from .parity import assert_close, compare_records, rec_np
+from .parity import assert_close, check_mismatch_fraction, compare_records, rec_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -87,17 +87,20 @@ def _split_setup(b, role, G, N, d, n_out, bits, seed, n_cb=None, use_workspace=T
 @pytest.mark.parametrize("role", [tq.ROLE_KEY, tq.ROLE_VALUE])
 @pytest.mark.parametrize("G,N,d,n_out,bits,ws", [(3, 333, 256, 32, 3, True), (3, 333, 256, 32, 3, False),
                                                  (2, 300, 256, 32, 2, True), (1, 1, 256, 32, 3, True),
-                                                 (2, 65, 64, 16, 2, True)])
+                                                 (2, 65, 64, 16, 2, True),
+                                                 (40, 70, 256, 32, 3, True)])   # many groups: XCD-major
 def test_split_encode_parity(gpu_lib, role, G, N, d, n_out, bits, ws):
     b = gpu_lib
     X, chan, sqs, _, rn, ro = _split_setup(b, role, G, N, d, n_out, bits, 5, use_workspace=ws)
     xv = inputs.exact_values(X)
     c = chan.cpu().numpy()
+    reps = []
     for g in range(G):
         _chan_ok(xv[g], c[g], n_out)
         en, eo = split.encode_split(sqs[g], xv[g], c[g])      # the oracle on the GPU's channel map
-        compare_records(sqs[g].normal, rec_np(rn)[g], en)
-        compare_records(sqs[g].outlier, rec_np(ro)[g], eo)
+        reps.append(compare_records(sqs[g].normal, rec_np(rn)[g], en, fraction=False))
+        reps.append(compare_records(sqs[g].outlier, rec_np(ro)[g], eo, fraction=False))
+    check_mismatch_fraction(reps)
 
 
 def test_split_scores_parity(gpu_lib):
