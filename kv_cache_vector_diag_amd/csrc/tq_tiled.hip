@@ -165,6 +165,7 @@ __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(TiledArgs a) {
       int q[V][E];
       double ws[V];
       float n32[V];
+      float z[V][E];
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const double nrm = sqrt(ss[i]);
@@ -172,8 +173,20 @@ __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(TiledArgs a) {
         ws[i] = 0.0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float z = nrm > 0.0 ? (float)(u[i][e] / nrm) : 0.0f;
-          q[i][e] = quantize_index(thr, levels, z);
+          z[i][e] = nrm > 0.0 ? (float)(u[i][e] / nrm) : 0.0f;
+          q[i][e] = 0;
+        }
+      }
+      // idx = #{t_i < z} over t[0 .. levels-2]: a branch-free binary search of
+      // log2(levels) steps, the V*E searches interleaved step by step
+#pragma unroll
+      for (int b = 7; b >= 0; --b) {
+        const int st = 1 << b;
+        if (st < levels) {
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+#pragma unroll
+            for (int e = 0; e < E; ++e) q[i][e] += thr[q[i][e] + st - 1] < z[i][e] ? st : 0;
         }
       }
 #pragma unroll
@@ -191,14 +204,15 @@ __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(TiledArgs a) {
         }
         uint32_t* wd = words + vl * RW;
         for (int p = 0; p < k; ++p) {
+          // the plane's W words gathered into lanes 0 .. W-1, one store
+          uint32_t pw = 0;
 #pragma unroll
           for (int e = 0; e < E; ++e) {
             const uint64_t bl = __ballot(live && ((q[i][e] >> p) & 1));
-            if (lane == 0) {
-              wd[p * W + 2 * e] = (uint32_t)bl;
-              if (2 * e + 1 < W) wd[p * W + 2 * e + 1] = (uint32_t)(bl >> 32);
-            }
+            pw = lane == 2 * e ? (uint32_t)bl : pw;
+            pw = lane == 2 * e + 1 ? (uint32_t)(bl >> 32) : pw;
           }
+          if (lane < W) wd[p * W + lane] = pw;
         }
         if (lane == 0) wd[n_off] = __float_as_uint(n32[i]);
       }
