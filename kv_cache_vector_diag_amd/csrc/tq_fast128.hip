@@ -267,6 +267,8 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
     for (int t = 0; t < NT; ++t) tn[t] = tpos[t] * n32;   // thresholds in units of u
     const uint32_t nbits = __float_as_uint(n32);
     uint32_t pw[4], tw[NT > 0 ? NT : 1][4];                // sign-half words, thermometer words
+    constexpr int KB = K - 1;                              // magnitude bits
+    uint32_t mw[KB > 0 ? KB : 1][4];                       // values: magnitude index bits
     u32x4 whi[KEY ? 8 : 1], wlo[KEY ? 8 : 1];
     float wsq = 0.0f;
 #pragma unroll
@@ -275,6 +277,34 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
       uint32_t tacc[NT > 0 ? NT : 1];
 #pragma unroll
       for (int t = 0; t < NT; ++t) tacc[t] = 0;
+      if constexpr (!KEY && KB >= 1 && KB <= 3) {
+        // values need no magnitude for a residual: the magnitude index
+        // m = #{t : |u| > tn_t} by binary search over the sorted thresholds,
+        // its bits shifted straight into words (KB compares instead of 2^KB - 1)
+        uint32_t macc[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) macc[b] = 0;
+#pragma unroll
+        for (int r = 15; r >= 0; --r) {
+          const float uu = u[M][r];
+          pos_bit(pacc, uu);
+          if constexpr (KB == 1) {
+            thr_bit(macc[0], uu, tn[0]);
+          } else if constexpr (KB == 2) {
+            const uint64_t m1 = thr_bit(macc[1], uu, tn[1]);
+            thr_bit(macc[0], uu, sel_mask(m1, tn[2], tn[0]));
+          } else {
+            const uint64_t m2 = thr_bit(macc[2], uu, tn[3]);
+            const uint64_t m1 = thr_bit(macc[1], uu, sel_mask(m2, tn[5], tn[1]));
+            const float ta = sel_mask(m2, tn[6], tn[2]), tb = sel_mask(m2, tn[4], tn[0]);
+            thr_bit(macc[0], uu, sel_mask(m1, ta, tb));
+          }
+        }
+        pw[M] = pacc;
+#pragma unroll
+        for (int b = 0; b < KB; ++b) mw[b][M] = macc[b];
+        continue;
+      }
       float wv[16];
 #pragma unroll
       for (int r = 15; r >= 0; --r) {
@@ -358,11 +388,15 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
       pl[K - 1] = pw[M];
 #pragma unroll
       for (int p = 0; p < K - 1; ++p) {
-        // bit p of cnt = XOR of the thermometer bits [cnt >= j] for j a multiple of 2^p
         uint32_t cb = 0;
+        if constexpr (!KEY && KB <= 3) {
+          cb = mw[p][M];                   // bit p of cnt from the binary search
+        } else {
+          // bit p of cnt = XOR of the thermometer bits [cnt >= j] for j a multiple of 2^p
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (((t + 1) & ((1 << p) - 1)) == 0) cb ^= tw[t][M];
+          for (int t = 0; t < NT; ++t)
+            if (((t + 1) & ((1 << p) - 1)) == 0) cb ^= tw[t][M];
+        }
         pl[p] = ~(cb ^ pw[M]) & 0xFFFFu;   // pos ? cnt_p : ~cnt_p
       }
       for (int p = 0; p < K; ++p) part[p * 4 + M] = h ? (pl[p] << 16) : (pl[p] & 0xFFFFu);

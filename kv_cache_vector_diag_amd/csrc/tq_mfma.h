@@ -97,5 +97,33 @@ __device__ inline void pos_step(uint32_t& acc, float& nsg, float u, uint32_t nbi
       : [u] "v"(u), [sm] "s"(signmask), [nb] "v"(nbits));
 }
 
+// Value quantizer step of a binary search: above = |u| > t; acc = 2*acc + above;
+// returns the lane mask of `above` for choosing the next threshold.
+__device__ inline uint64_t thr_bit(uint32_t& acc, float u, float t) {
+  uint64_t m, c;
+  asm("v_cmp_gt_f32_e64 %[m], |%[u]|, %[t]\n\t"
+      "v_addc_co_u32_e64 %[acc], %[c], %[acc], %[acc], %[m]"
+      : [acc] "+v"(acc), [m] "=&s"(m), [c] "=&s"(c)
+      : [u] "v"(u), [t] "v"(t));
+  return m;
+}
+
+// m ? if_set : if_clear, per lane, for a mask from thr_bit.
+__device__ inline float sel_mask(uint64_t m, float if_set, float if_clear) {
+  float r;
+  asm("v_cndmask_b32_e64 %[r], %[b], %[a], %[m]" : [r] "=v"(r) : [a] "v"(if_set), [b] "v"(if_clear), [m] "s"(m));
+  return r;
+}
+
+// Sign half without the signed norm: pos = u > 0 (top bit of 0 - bits(u), as in
+// pos_step); acc = 2*acc + pos.
+__device__ inline void pos_bit(uint32_t& acc, float u) {
+  uint32_t t;
+  asm("v_sub_u32 %[t], 0, %[u]\n\t"
+      "v_alignbit_b32 %[acc], %[acc], %[t], 31"
+      : [acc] "+v"(acc), [t] "=&v"(t)
+      : [u] "v"(u));
+}
+
 }  // namespace mf
 }  // namespace tq
