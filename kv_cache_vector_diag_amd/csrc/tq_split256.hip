@@ -288,13 +288,13 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
     if (tid < NTO) consts[24 + tid] = reinterpret_cast<const float*>(bo + a.off_to)[LO / 2 + tid];
     __syncthreads();
     float cpn[LN / 2], tpn[NTN > 0 ? NTN : 1], cpo[LO / 2], tpo[NTO > 0 ? NTO : 1];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < LN / 2; ++i) cpn[i] = consts[i];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < NTN; ++i) tpn[i] = consts[8 + i];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < LO / 2; ++i) cpo[i] = consts[16 + i];
-  #pragma unroll
+#pragma unroll
     for (int i = 0; i < NTO; ++i) tpo[i] = consts[24 + i];
 
     const int64_t tile0 = chunk * a.tiles_per_block;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       constexpr int kXPre = 4;
       const uint32_t* xr = a.x + (g * a.sx_g + (valid ? tok : 0) * a.sx_n) / 2;
       u32x4 xb[kKC];
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < kXPre; ++c) xb[c] = *reinterpret_cast<const u32x4*>(xr + 8 * c + 4 * h);
       double ss = 0.0;
       __syncthreads();                                     // slice buffers free
@@ -327,10 +327,10 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
 
       // ---- rotation, chunk-outer: u[m] (normal tiles), uo (outlier), xo (outlier gather)
       f32x16 u[kMT];
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < kMT; ++m) u[m] = f32x16{};
       f32x16 uo = {}, xo = {};
-  #pragma unroll
+#pragma unroll
       for (int c = 0; c < kKC; ++c) {
         __syncthreads();                                   // slice c complete; the other buffer free
         const u32x4* cur = slice + (c & 1) * kSliceEntries;
@@ -341,19 +341,19 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         const uint32_t nbase = c + 1 < kKC ? (uint32_t)((kOffR + (c + 1) * kSliceR) * kFragLanes)
                                            : (uint32_t)(kOffS * kFragLanes);
         u32x4 pre[kPre];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < kPre; ++i) {
           const int idx = tid + i * kThreads;
           if (more && idx < nent) pre[i] = frag_at(nbase + (uint32_t)idx);
         }
         if (c + kXPre < kKC) xb[c + kXPre] = *reinterpret_cast<const u32x4*>(xr + 8 * (c + kXPre) + 4 * h);
-  #pragma unroll
+#pragma unroll
         for (int q = 0; q < 4; ++q) ss += pair_sumsq_bf16(xb[c][q]);
         const bf16x8 xv = as<bf16x8>(xb[c]);
         // pieces outer, row tiles inner: consecutive MFMAs use different accumulators
-  #pragma unroll
+#pragma unroll
         for (int pc = 0; pc < kRPieces; ++pc) {
-  #pragma unroll
+#pragma unroll
           for (int m = 0; m < kMT; ++m)
             u[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(cur[(m * kRPieces + pc) * kFragLanes + lane]), xv,
                                                            u[m], 0, 0, 0);
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         }
         uo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[c * kFragLanes + lane]), xv, uo, 0, 0, 0);
         xo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[(kKC + c) * kFragLanes + lane]), xv, xo, 0, 0, 0);
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < kPre; ++i) {
           const int idx = tid + i * kThreads;
           if (more && idx < nent) nxt[idx] = pre[i];
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
 
       // ---- norms (float64): |x|^2 from pair sums, |x_o|^2 from the exact gather
       double so = 0.0;
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 16; ++r) so = fma((double)xo[r], (double)xo[r], so);
       {
         uint32_t l1 = __double2loint(ss), h1 = __double2hiint(ss), l2 = __double2loint(so), h2 = __double2hiint(so);
@@ -395,20 +395,20 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
 
       // ---- outlier part: quantize, QJL
       float tno[NTO > 0 ? NTO : 1];
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NTO; ++t) tno[t] = tpo[t] * no32;
       uint32_t pw_o, tw_o[NTO > 0 ? NTO : 1];
       u32x4 who[2], wlo_o[2];
       float wsq_o = 0.0f;
       quantize_tile<KO, KEY>(uo, no32, cpo, tno, sco, pw_o, tw_o, who, wlo_o, wsq_o);
       asm volatile("" : "+v"(pw_o));
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NTO; ++t) asm volatile("" : "+v"(tw_o[t]));
       uint32_t sw_o = 0;
       float gam_o = 0.0f;
       if (KEY) {
         f32x16 acc = {};
-  #pragma unroll
+#pragma unroll
         for (int c = 0; c < 2; ++c) {
           const u32x4 sf = ofr[(2 * kKC + c) * kFragLanes + lane];
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(who[c]), acc, 0, 0, 0);
@@ -422,17 +422,17 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
 
       // ---- normal part: quantize the 7 row tiles
       float tnn[NTN > 0 ? NTN : 1];
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < NTN; ++t) tnn[t] = tpn[t] * nn32;
       uint32_t pw_n[kMT], tw_n[NTN > 0 ? NTN : 1][kMT];
       u32x4 whn[KEY ? kQC : 1], wln[KEY ? kQC : 1];
       float wsq_n = 0.0f;
-  #pragma unroll
+#pragma unroll
       for (int m = 0; m < kMT; ++m) {
         uint32_t twm[NTN > 0 ? NTN : 1];
         quantize_tile<KN, KEY>(u[m], nn32, cpn, tnn, scn, pw_n[m], twm, KEY ? &whn[2 * m] : whn,
                                KEY ? &wln[2 * m] : wln, wsq_n);
-  #pragma unroll
+#pragma unroll
         for (int t = 0; t < NTN; ++t) {
           tw_n[t][m] = twm[t];
           asm volatile("" : "+v"(tw_n[t][m]));
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       uint32_t sw_n[kMT];
       float gam_n = 0.0f;
       if (KEY) {
-  #pragma unroll
+#pragma unroll
         for (int mp = 0; mp < kMT; ++mp) {
           __syncthreads();
           const u32x4* cur = slice + ((kKC + mp) & 1) * kSliceEntries;
@@ -457,13 +457,13 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
           const uint32_t nbase = (uint32_t)((kOffS + (mp + 1) * kSliceS) * kFragLanes);
           constexpr int kPreS = (kSliceS * kFragLanes + kThreads - 1) / kThreads;
           u32x4 pre[kPreS];
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < kPreS; ++i) {
             const int idx = tid + i * kThreads;
             if (more && idx < kSliceS * kFragLanes) pre[i] = frag_at(nbase + (uint32_t)idx);
           }
           f32x16 acc = {};
-  #pragma unroll
+#pragma unroll
           for (int c = 0; c < kQC; ++c) {
             const u32x4 sf = cur[c * kFragLanes + lane];
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(whn[c]), acc, 0, 0, 0);
@@ -472,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
           }
           sw_n[mp] = sign_word(acc);
           asm volatile("" : "+v"(sw_n[mp]));   // materialise here (not next to the stores)
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < kPreS; ++i) {
             const int idx = tid + i * kThreads;
             if (more && idx < kSliceS * kFragLanes) nxt[idx] = pre[i];
@@ -490,14 +490,14 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         // normal: KN planes x 7 words, (keys) 7 sign words, n, gamma
         constexpr int NPN = KN * kMT + (KEY ? kMT : 0);
         uint32_t part[NPN];
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < kMT; ++m) {
           uint32_t twm[NTN > 0 ? NTN : 1];
-  #pragma unroll
+#pragma unroll
           for (int t = 0; t < NTN; ++t) twm[t] = tw_n[t][m];
           uint32_t pl[KN];
           tile_planes<KN>(pw_n[m], twm, pl);
-  #pragma unroll
+#pragma unroll
           for (int p = 0; p < KN; ++p) part[p * kMT + m] = h ? (pl[p] << 16) : (pl[p] & 0xFFFFu);
           if (KEY) part[KN * kMT + m] = h ? ((~sw_n[m]) << 16) : ((~sw_n[m]) & 0xFFFFu);
         }
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         uint32_t parto[NPO];
         uint32_t plo[KO];
         tile_planes<KO>(pw_o, tw_o, plo);
-  #pragma unroll
+#pragma unroll
         for (int p = 0; p < KO; ++p) parto[p] = h ? (plo[p] << 16) : (plo[p] & 0xFFFFu);
         if (KEY) parto[KO] = h ? ((~sw_o) << 16) : ((~sw_o) & 0xFFFFu);
         const uint32_t tail_o[2] = {__float_as_uint(no32), __float_as_uint(gam_o)};
