@@ -84,6 +84,7 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   __shared__ float coef[8];                      // a_P
   __shared__ __align__(16) i32x4 afrag[NMF * 64];
   __shared__ int fx[4 * Mk::kMasks * kD];
+  __shared__ uint2 stage[kWaves * 16 * (4 * K + 6)];   // one tile of records per wave
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t grp = blockIdx.x / a.blocks_per_group;      // (b, kv head)
@@ -245,33 +246,36 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   for (int f = 0; f < NMF; ++f) A[f] = afrag[f * 64 + lane];
 
   const int h = lane >> 5, col = lane & 31;
-  const int R = a.rec_words;
   const float kqjl = kQjlConst / (float)kM;
   const float inv_d = 1.0f / (float)kD;
   const int64_t tile0 = chunk * a.tiles_per_block;
   const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles);
-  // Lane half h feeds words ww in {h, h+2} of every bit plane and of the sign
-  // mask.  The raw words of the wave's next kPrefetch tiles are in flight (a ring of
-  // register slots) while it scores the current one.
-  constexpr int NRAW = 2 * K + 2;
+  // A tile's 32 records are contiguous: they are loaded as 8-byte chunks by
+  // consecutive lanes (RW even, so every record is 8-byte aligned and a ragged
+  // tile ends on a chunk boundary), kPrefetch tiles ahead in a register ring,
+  // then passed through this wave's LDS row so that lane (col, h) reads the
+  // words it feeds: words h and h+2 of every bit plane and of the sign mask,
+  // then n and gamma.
+  constexpr int RW = 4 * K + 6;                          // record words (d = m = 128 keys)
+  constexpr int NCH = (16 * RW + 63) / 64;               // 8-byte chunks per lane per tile
   constexpr int kPrefetch = K <= 2 ? 2 : 1;
-  uint32_t raw[kPrefetch][NRAW];
-  float raw_n[kPrefetch], raw_g[kPrefetch];
-  const auto load_raw = [&](int64_t t, uint32_t* rw, float& nn, float& gg) {
-    const int64_t tk = t * 32 + col;
-    const uint32_t* r = a.krec + (grp * a.T + (tk < a.T ? tk : 0)) * R;   // tail lanes read key 0
+  uint2 raw[kPrefetch][NCH];
+  const uint2* grec = reinterpret_cast<const uint2*>(a.krec + grp * a.T * RW);
+  const auto load_raw = [&](int64_t t, uint2* rw) {
+    const int64_t nrec = a.T - t * 32 < 32 ? a.T - t * 32 : 32;
+    const int nvalid = (int)nrec * (RW / 2);
+    const uint2* src = grec + t * 32 * (RW / 2);
 #pragma unroll
-    for (int p = 0; p < K; ++p)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) rw[2 * p + s2] = r[p * 4 + h + 2 * s2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) rw[2 * K + s2] = r[K * 4 + h + 2 * s2];
-    nn = __uint_as_float(r[K * 4 + 4]);
-    gg = __uint_as_float(r[K * 4 + 5]);
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      rw[i] = c < nvalid ? src[c] : make_uint2(0u, 0u);
+    }
   };
+  uint2* st2 = stage + wave * (16 * RW);
+  const uint32_t* st = reinterpret_cast<const uint32_t*>(st2) + col * RW;
 #pragma unroll
   for (int sl = 0; sl < kPrefetch; ++sl)
-    if (tile0 + wave + sl * kWaves < tile_end) load_raw(tile0 + wave + sl * kWaves, raw[sl], raw_n[sl], raw_g[sl]);
+    if (tile0 + wave + sl * kWaves < tile_end) load_raw(tile0 + wave + sl * kWaves, raw[sl]);
   for (int64_t tile_base = tile0 + wave; tile_base < tile_end; tile_base += kPrefetch * kWaves) {
 #pragma unroll
    for (int sl = 0; sl < kPrefetch; ++sl) {
@@ -279,25 +283,30 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
     if (tile >= tile_end) break;
     const int64_t tok = tile * 32 + col;
     const bool valid = tok < a.T;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = lane + 64 * i;
+      if (c < 16 * RW) st2[c] = raw[sl][i];
+    }
+    if (tile + kPrefetch * kWaves < tile_end) load_raw(tile + kPrefetch * kWaves, raw[sl]);
     uint32_t wv[Mk::kWords / 2];
 #pragma unroll
     for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
       const int li = 2 * w2 + h, mask = li >> 2, s2 = (li & 3) >> 1;
       uint32_t word;
       if (mask == Mk::kPlaneMasks) {
-        word = raw[sl][2 * K + s2];
+        word = st[K * 4 + h + 2 * s2];
       } else {
         const int sb = subset_bits<K>(mask);
         word = 0;
 #pragma unroll
         for (int p = 0; p < K; ++p)
-          if ((sb >> p) & 1) word ^= raw[sl][2 * p + s2];
+          if ((sb >> p) & 1) word ^= st[p * 4 + h + 2 * s2];
       }
       wv[w2] = valid ? word : 0u;
     }
-    const float nrm = valid ? raw_n[sl] : 0.0f;
-    const float gam = valid ? raw_g[sl] : 0.0f;
-    if (tile + kPrefetch * kWaves < tile_end) load_raw(tile + kPrefetch * kWaves, raw[sl], raw_n[sl], raw_g[sl]);
+    const float nrm = valid ? __uint_as_float(st[K * 4 + 4]) : 0.0f;
+    const float gam = valid ? __uint_as_float(st[K * 4 + 5]) : 0.0f;
 
     // one accumulation chain (registers are the occupancy limit; the other waves of
     // the SIMD fill the MFMA latency)
@@ -364,8 +373,9 @@ int launch_k(Score128Args a, hipStream_t s) {
 
 }  // namespace
 
-bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq) {
+bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, const void* krec) {
   if (L.d != kD || L.m != kM || L.k < 1 || L.k > 3) return false;
+  if (reinterpret_cast<uintptr_t>(krec) & 7) return false;   // records read as 8-byte chunks
   const int64_t gq = Hq / Hkv;
   return gq == 1 || gq == 2 || gq == 4;
 }

@@ -114,6 +114,29 @@ def test_decode_scoring_gqa(gpu_lib, B, T):
     assert_close(s.cpu().numpy(), ref, "scores")
 
 
+@pytest.mark.parametrize("kbits,gq,T", [(2, 1, 95), (3, 2, 64), (4, 4, 257)])
+def test_scores_fast_path_shapes(gpu_lib, kbits, gq, T):
+    """head_dim 128 scores for 1-3 Lloyd bits and GQA groups of 1, 2, 4 over
+    ragged tiles; the same records at a 4-byte (not 8-byte) aligned address take
+    the generic kernel and must agree too."""
+    import torch
+    b = gpu_lib
+    d, B, Hkv, seed = 128, 2, 2, 21
+    Hq = Hkv * gq
+    K = inputs.to_torch(inputs.kv_normal(seed, B * Hkv, T, d), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    kcb, kq = _codebooks(b, Hkv, d, kbits, 128, seed, tq.ROLE_KEY)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, kbits, 128).view(B, Hkv, T, -1)
+    s = b.tq_scores(kcb, Hkv, krec, q, d, kbits, 128)
+    shifted = torch.empty(krec.numel() + 1, dtype=torch.int32, device=DEV)
+    shifted[1:] = krec.reshape(-1)
+    s2 = b.tq_scores(kcb, Hkv, shifted[1:].view(krec.shape), q, d, kbits, 128)
+    torch.cuda.synchronize()
+    ref = tq.scores(kq, rec_np(krec), inputs.exact_values(q))
+    assert_close(s.cpu().numpy(), ref, "scores")
+    assert_close(s2.cpu().numpy(), ref, "scores (generic kernel)")
+
+
 def test_long_context_attend(gpu_lib):
     """turbo2 keys (b=2) + 2-bit values; scores -> softmax -> weighted sum of
     decoded values, fp32 accumulation (slice: 1 sequence, 8 kv heads, 3000 tokens)."""
