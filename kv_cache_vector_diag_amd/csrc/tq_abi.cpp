@@ -103,7 +103,7 @@ int tq_scores(int head_dim, int bits, int projections, const void* cbs, int64_t 
   if (!cbs || !krec || !q || !scores) return TQ_ERR_NULL;
   if (!dtype_ok(q_dtype)) return TQ_ERR_UNSUPPORTED;
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)head_dim);
-  if (fast128_scores_supported(L, H_kv, H_q, krec))
+  if (fast128_scores_supported(L, H_kv, H_q, T, krec))
     return launch_scores_fast128(L, cbs, n_cb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q,
                                  scale, scores, status, static_cast<hipStream_t>(stream));
   CodebookArgs cb = make_cb_args(cbs, n_cb, L);
@@ -144,7 +144,7 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections, const void*
   CodebookArgs kcb = make_cb_args(kcbs, n_kcb, K);
   CodebookArgs vcb = make_cb_args(vcbs, n_vcb, V);
   if (T > 0) {
-    rc = fast128_scores_supported(K, H_kv, H_q, krec)
+    rc = fast128_scores_supported(K, H_kv, H_q, T, krec)
              ? launch_scores_fast128(K, kcbs, n_kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype,
                                      H_q, scale, sc, status, s)
              : launch_scores_generic(kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype, H_q, scale,

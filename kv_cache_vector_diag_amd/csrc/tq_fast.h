@@ -15,8 +15,9 @@ int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
                           int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
 
 // Scores with the int8-MFMA kernel: head_dim 128, 128 projections, key bits
-// 2..4, 1, 2 or 4 query heads per kv head, 8-byte aligned records.
-bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, const void* krec);
+// 2..4, 1, 2 or 4 query heads per kv head, 8-byte aligned records, and a
+// group's records and scores each under 2^30 bytes (32-bit buffer offsets).
+bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, int64_t T, const void* krec);
 int launch_scores_fast128(const Layout& L, const void* cbs, int64_t n_cb, const uint32_t* krec, int64_t B,
                           int64_t Hkv, int64_t T, const void* q, int q_dtype, int64_t Hq, float scale,
                           float* scores, int32_t* status, hipStream_t s);

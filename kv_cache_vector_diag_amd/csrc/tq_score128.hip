@@ -34,6 +34,9 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kM = 128;
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format; no
+// swizzle, no stride): offsets at or past the resource size read 0 and drop stores.
+constexpr int kRsrcWord3 = 0x00020000;
 // Workgroup size: 16 waves (one workgroup per CU) while the A fragments fit in
 // 128 VGPRs; 8 waves for the 3-plane codebook, whose fragments need more.
 template <int K>
@@ -84,9 +87,11 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   __shared__ float coef[8];                      // a_P
   __shared__ __align__(16) i32x4 afrag[NMF * 64];
   __shared__ int fx[4 * Mk::kMasks * kD];
-  __shared__ uint2 stage[kWaves * 16 * (4 * K + 6)];   // one tile of records per wave
+  constexpr int kStage = 64 * ((16 * (4 * K + 6) + 63) / 64);   // 8-byte chunks per wave: one tile, rounded up
+  __shared__ uint2 stage[kWaves * kStage];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile loops stay scalar
   const int64_t grp = blockIdx.x / a.blocks_per_group;      // (b, kv head)
   const int64_t chunk = blockIdx.x % a.blocks_per_group;
   const int64_t b = grp / a.Hkv, hkv = grp % a.Hkv;
@@ -256,39 +261,54 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   // then passed through this wave's LDS row so that lane (col, h) reads the
   // words it feeds: words h and h+2 of every bit plane and of the sign mask,
   // then n and gamma.
+  // The loads go through a buffer resource that ends at this workgroup's last
+  // record: past it (the ragged tail, prefetches beyond the range) they return
+  // zero without a memory access, so every load is issued unconditionally and
+  // the waits before each tile count exactly the loads and stores still needed
+  // in flight (predicated loads make the compiler drain everything instead).
+  // A zero record scores 0 and is never stored.
   constexpr int RW = 4 * K + 6;                          // record words (d = m = 128 keys)
   constexpr int NCH = (16 * RW + 63) / 64;               // 8-byte chunks per lane per tile
-  constexpr int kPrefetch = K <= 2 ? 2 : 1;
+  constexpr int kPrefetch = 2;
   uint2 raw[kPrefetch][NCH];
-  const uint2* grec = reinterpret_cast<const uint2*>(a.krec + grp * a.T * RW);
+  const int64_t rec_end = min(tile_end * 32, a.T);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.krec + grp * a.T * RW), 0, (int)(rec_end * RW * 4), kRsrcWord3);
   const auto load_raw = [&](int64_t t, uint2* rw) {
-    const int64_t nrec = a.T - t * 32 < 32 ? a.T - t * 32 : 32;
-    const int nvalid = (int)nrec * (RW / 2);
-    const uint2* src = grec + t * 32 * (RW / 2);
+    const uint32_t base = (uint32_t)(t * 32 * RW * 4) + 8u * lane;
 #pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = lane + 64 * i;
-      rw[i] = c < nvalid ? src[c] : make_uint2(0u, 0u);
-    }
+    for (int i = 0; i < NCH; ++i)
+      rw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(krs, base + 512u * i, 0, 0));
   };
-  uint2* st2 = stage + wave * (16 * RW);
+  // scores of this (b, kv head): [gq][T]; stores past the end are dropped
+  const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+      a.scores + (b * a.Hq + hkv * a.gq) * a.T, 0, (int)(a.gq * a.T * 4), kRsrcWord3);
+  uint2* st2 = stage + wave * kStage;
   const uint32_t* st = reinterpret_cast<const uint32_t*>(st2) + col * RW;
+  // Issued in slot order, each followed by two stores past the end of the
+  // scores (dropped by the hardware): on entry the memory operations then stand
+  // in the same order as in the loop (a slot's loads, its two score stores), so
+  // the wait before each slot leaves the later slots' loads in flight.
 #pragma unroll
-  for (int sl = 0; sl < kPrefetch; ++sl)
-    if (tile0 + wave + sl * kWaves < tile_end) load_raw(tile0 + wave + sl * kWaves, raw[sl]);
+  for (int sl = 0; sl < kPrefetch; ++sl) {
+    load_raw(tile0 + wave + sl * kWaves, raw[sl]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0xC0000000u, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0xC0000040u, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   for (int64_t tile_base = tile0 + wave; tile_base < tile_end; tile_base += kPrefetch * kWaves) {
 #pragma unroll
    for (int sl = 0; sl < kPrefetch; ++sl) {
     const int64_t tile = tile_base + sl * kWaves;
-    if (tile >= tile_end) break;
     const int64_t tok = tile * 32 + col;
-    const bool valid = tok < a.T;
+    const bool valid = tok < rec_end;   // a tile past the range reads zeros and stores nothing
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane + 64 * i;
-      if (c < 16 * RW) st2[c] = raw[sl][i];
+      st2[c] = raw[sl][i];
     }
-    if (tile + kPrefetch * kWaves < tile_end) load_raw(tile + kPrefetch * kWaves, raw[sl]);
+    load_raw(tile + kPrefetch * kWaves, raw[sl]);
     uint32_t wv[Mk::kWords / 2];
 #pragma unroll
     for (int w2 = 0; w2 < Mk::kWords / 2; ++w2) {
@@ -303,10 +323,10 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
         for (int p = 0; p < K; ++p)
           if ((sb >> p) & 1) word ^= st[p * 4 + h + 2 * s2];
       }
-      wv[w2] = valid ? word : 0u;
+      wv[w2] = word;
     }
-    const float nrm = valid ? __uint_as_float(st[K * 4 + 4]) : 0.0f;
-    const float gam = valid ? __uint_as_float(st[K * 4 + 5]) : 0.0f;
+    const float nrm = __uint_as_float(st[K * 4 + 4]);
+    const float gam = __uint_as_float(st[K * 4 + 5]);
 
     // one accumulation chain (registers are the occupancy limit; the other waves of
     // the SIMD fill the MFMA latency)
@@ -347,11 +367,10 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
                                 kqjl * gam * (consts[ha][1] * qjl_a - consts[ha][3]));
     const float sb2 = a.scale * ((nrm * inv_d) * (consts[hb][0] * mse_b - consts[hb][2]) +
                                  kqjl * gam * (consts[hb][1] * qjl_b - consts[hb][3]));
-    if (valid) {
-      const int64_t base = (b * a.Hq + hkv * a.gq) * a.T + tok;
-      if (ha < a.gq) a.scores[base + ha * a.T] = sa;
-      if (hb < a.gq) a.scores[base + hb * a.T] = sb2;
-    }
+    // heads ha, hb >= gq land past the end of the resource, as does an invalid token
+    const uint32_t so = valid ? (uint32_t)tok * 4u : 0xC0000000u;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sa), srs, so + (uint32_t)(ha * a.T * 4), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sb2), srs, so + (uint32_t)(hb * a.T * 4), 0, 0);
    }
   }
 }
@@ -373,9 +392,11 @@ int launch_k(Score128Args a, hipStream_t s) {
 
 }  // namespace
 
-bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, const void* krec) {
+bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, int64_t T, const void* krec) {
   if (L.d != kD || L.m != kM || L.k < 1 || L.k > 3) return false;
   if (reinterpret_cast<uintptr_t>(krec) & 7) return false;   // records read as 8-byte chunks
+  // 32-bit buffer offsets: a group's records and its [gq][T] scores stay below 2^30 bytes
+  if (T > (int64_t(1) << 30) / (4 * L.rec_words) || T > (int64_t(1) << 30) / 16) return false;
   const int64_t gq = Hq / Hkv;
   return gq == 1 || gq == 2 || gq == 4;
 }
