@@ -80,18 +80,20 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   constexpr int kWaves = kBlock / 64;
   constexpr int L = 1 << K;
   constexpr int NMF = Mk::kMfma;                 // MFMAs per tile
+  constexpr int kPWaves = 4 * kM / 64;           // waves of the projection step
   __shared__ float qt[4][kD];
   __shared__ float pp[4][kM];
-  __shared__ float vmax[4][2];
+  __shared__ float qstat[4][2];                  // per head: max |qt_j|, sum qt_j
+  __shared__ float pstat[kPWaves][4][2];         // per projection wave and head: max |p_i|, sum p_i
   __shared__ float consts[4][4];                 // per head: delta_mse, delta_qjl, C_mse, C_qjl
   __shared__ float coef[8];                      // a_P
+  __shared__ float cmax;                         // largest centroid
   __shared__ __align__(16) i32x4 afrag[NMF * 64];
-  __shared__ int fx[4 * Mk::kMasks * kD];
   constexpr int kStage = 64 * ((16 * (4 * K + 6) + 63) / 64);   // 8-byte chunks per wave: one tile, rounded up
   __shared__ uint2 stage[kWaves * kStage];
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: tile loops stay scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches on it stay scalar
   const int64_t grp = blockIdx.x / a.blocks_per_group;      // (b, kv head)
   const int64_t chunk = blockIdx.x % a.blocks_per_group;
   const int64_t b = grp / a.Hkv, hkv = grp % a.Hkv;
@@ -106,149 +108,31 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob + a.off_d);
   const _Float16* S = reinterpret_cast<const _Float16*>(blob + a.off_s);
 
-  // ---- prologue: rotated queries, projected queries, fixed-point fragments
+  // ---- query-side loads first: waves 0-3 take head `wave` (coordinates lane
+  // and lane + 64), the projection waves a quarter row of S each, wave 0 the
+  // centroids
+  float q0 = 0.0f, q1 = 0.0f;
+  uint32_t d0 = 0, d1 = 0;
+  if (wave < 4 && wave < a.gq) {
+    const int64_t off = ((b * a.Hq) + hkv * a.gq + wave) * kD + lane;
+    q0 = load_elem(a.q, a.q_dtype, off);
+    q1 = load_elem(a.q, a.q_dtype, off + 64);
+    d0 = dbits[lane >> 5];
+    d1 = dbits[2 + (lane >> 5)];
+  }
+  const int prow = tid >> 2, qtr = tid & 3;      // projection step: row prow, quarter qtr
+  uint4 srow[4];
+  if (wave < kPWaves) {
+    const uint4* row = reinterpret_cast<const uint4*>(S + prow * kD + 32 * qtr);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) srow[v] = row[v];
+  }
+  float cv[L];
   if (tid < Mk::kPlaneMasks) {
-    // a_P = (1/L) sum_v c_v prod_{p in P} sigma_p(v)
-    const int sb = subset_bits<K>(tid);
-    double acc = 0.0;
-    for (int v = 0; v < L; ++v) {
-      const int par = __popc(~v & sb) & 1;       // number of -1 factors
-      acc += par ? -(double)cent[v] : (double)cent[v];
-    }
-    coef[tid] = (float)(acc / L);
-  }
-  for (int e = tid; e < 4 * kD; e += kBlock) {
-    const int hh = e >> 7, j = e & 127;
-    float v = 0.0f;
-    if (hh < a.gq) {
-      const int64_t off = ((b * a.Hq) + hkv * a.gq + hh) * kD + j;
-      v = load_elem(a.q, a.q_dtype, off);
-      if ((dbits[j >> 5] >> (j & 31)) & 1u) v = -v;
-    }
-    qt[hh][j] = v;
-  }
-  __syncthreads();
-  for (int hs = 1; hs < kD; hs <<= 1) {
-    for (int p = tid; p < 4 * kD / 2; p += kBlock) {
-      const int hh = p >> 6, pr = p & 63;
-      const int i = (pr / hs) * 2 * hs + (pr % hs);
-      const float x0 = qt[hh][i], x1 = qt[hh][i + hs];
-      qt[hh][i] = x0 + x1;
-      qt[hh][i + hs] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  if (tid < 4 * kM) {
-    // p = S qt / sqrt(d): threads 4i .. 4i+3 own row i, a quarter of it each (four
-    // 16-byte loads issued together), all four heads; then a 4-lane reduction
-    const int i = tid >> 2, qtr = tid & 3;
-    const uint4* row = reinterpret_cast<const uint4*>(S + i * kD + 32 * qtr);
-    uint4 w[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) w[v] = row[v];
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const uint32_t ww[4] = {w[v].x, w[v].y, w[v].z, w[v].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f16x2 pr = __builtin_bit_cast(f16x2, ww[e]);
-        const int j = 32 * qtr + 8 * v + 2 * e;
-#pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          acc[hh] = fmaf((float)pr[0], qt[hh][j], acc[hh]);
-          acc[hh] = fmaf((float)pr[1], qt[hh][j + 1], acc[hh]);
-        }
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < 4; ++hh) {
-      acc[hh] += __shfl_xor(acc[hh], 1, 64);
-      acc[hh] += __shfl_xor(acc[hh], 2, 64);
-    }
-    pp[qtr][i] = acc[qtr] * 0.08838834764831845f;       // 1/sqrt(128)
+    for (int v = 0; v < L; ++v) cv[v] = cent[v];
   }
-  __syncthreads();
-  if (wave < 4) {
-    // per head: largest |2 a_P qt_j| and |2 p_i|, and the constant terms
-    const int hh = wave;
-    float amax = 0.0f;
-    for (int s = 0; s < Mk::kPlaneMasks; ++s) amax = fmaxf(amax, fabsf(coef[s]));
-    float m1 = 0.0f, m2 = 0.0f, s1 = 0.0f, s2 = 0.0f;
-    for (int j = lane; j < kD; j += 64) {
-      m1 = fmaxf(m1, fabsf(qt[hh][j]));
-      m2 = fmaxf(m2, fabsf(pp[hh][j]));
-      s1 += qt[hh][j];
-      s2 += pp[hh][j];
-    }
-    m1 = wave_max_f32(m1);
-    m2 = wave_max_f32(m2);
-    s1 = wave_sum_f32(s1);
-    s2 = wave_sum_f32(s2);
-    if (lane == 0) {
-      vmax[hh][0] = 2.0f * amax * m1;
-      vmax[hh][1] = 2.0f * m2;
-      consts[hh][2] = cent[L - 1] * s1;          // c_max * sum qt
-      consts[hh][3] = s2;                        // sum p
-    }
-  }
-  __syncthreads();
-  if (tid < 8) {
-    const int hh = tid >> 1, part = tid & 1;
-    const float vm = vmax[hh][part];
-    consts[hh][part] = vm > 0.0f ? vm * (1.0f / 1073741824.0f) : 1.0f;   // value of one unit, 2^30 units max
-  }
-  __syncthreads();
-  // Fixed-point query values, once each: fx[hh][s][j] for mask s (s == kPlaneMasks:
-  // the sign mask, value 2 p_j; else 2 a_s qt_j), in units of consts[hh][part],
-  // pre-divided by 2^(j mod 8) (-128 for j mod 8 == 7: the top bit of a byte).
-  for (int e = tid; e < 4 * Mk::kMasks * kD; e += kBlock) {
-    const int j = e & (kD - 1), sm = (e >> 7) % Mk::kMasks, hh = (e >> 7) / Mk::kMasks;
-    int V = 0;
-    if (hh < a.gq) {
-      const bool sign_mask = sm == Mk::kPlaneMasks;
-      const float val = sign_mask ? 2.0f * pp[hh][j] : 2.0f * coef[sm] * qt[hh][j];
-      const int sh = j & 7;
-      const float div = sh == 7 ? -128.0f : (float)(1 << sh);
-      V = (int)rint((double)val / ((double)consts[hh][sign_mask ? 1 : 0] * (double)div));
-    }
-    fx[(hh * Mk::kMasks + sm) * kD + j] = V;
-  }
-  __syncthreads();
-  // A fragment of MFMA f = 2*w2 + g, lane l: row m = l%32, K = 16(l/32) + 4q + byte.
-  // Lane half hl of MFMA (w2, g) carries list word 2*w2 + hl; bit (8*byte + 4g + q)
-  // of that word.  Row m = 8 hh + 4 part + limb holds signed int8 limb `limb` of
-  // the value (zero where the mask belongs to the other part).
-  for (int idx = tid; idx < NMF * 64 * 4; idx += kBlock) {
-    const int q = idx & 3, ln = (idx >> 2) & 63, f = idx >> 8;
-    const int w2 = f >> 1, g = f & 1;
-    const int m = ln & 31, hl = ln >> 5;
-    const int li = 2 * w2 + hl;                 // list word: mask li/4, word li%4
-    const int mask = li >> 2, ww = li & 3;
-    const int hh = m >> 3, part = (m >> 2) & 1, limb = m & 3;
-    const bool is_sign_mask = mask == Mk::kPlaneMasks;
-    uint32_t packed = 0;
-    if (hh < a.gq && part == (is_sign_mask ? 1 : 0)) {
-#pragma unroll
-      for (int byt = 0; byt < 4; ++byt) {
-        const int jj = 32 * ww + 8 * byt + 4 * g + q;
-        const int V = fx[(hh * Mk::kMasks + mask) * kD + jj];
-        // signed base-256 digits: V = l0 + 256 l1 + 65536 l2 + 2^24 l3
-        int r = V, l = 0;
-        for (int t = 0; t <= limb; ++t) {
-          l = (int)(signed char)(r & 0xFF);
-          r = (r - l) >> 8;
-        }
-        packed |= (uint32_t)(l & 0xFF) << (8 * byt);
-      }
-    }
-    reinterpret_cast<uint32_t*>(afrag)[(f * 64 + ln) * 4 + q] = packed;
-  }
-  __syncthreads();
-
-  i32x4 A[NMF];
-#pragma unroll
-  for (int f = 0; f < NMF; ++f) A[f] = afrag[f * 64 + lane];
+  __builtin_amdgcn_sched_barrier(0);
 
   const int h = lane >> 5, col = lane & 31;
   const float kqjl = kQjlConst / (float)kM;
@@ -285,6 +169,7 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
       a.scores + (b * a.Hq + hkv * a.gq) * a.T, 0, (int)(a.gq * a.T * 4), kRsrcWord3);
   uint2* st2 = stage + wave * kStage;
   const uint32_t* st = reinterpret_cast<const uint32_t*>(st2) + col * RW;
+  // The first tiles' records are in flight while the query side is prepared.
   // Issued in slot order, each followed by two stores past the end of the
   // scores (dropped by the hardware): on entry the memory operations then stand
   // in the same order as in the loop (a slot's loads, its two score stores), so
@@ -297,6 +182,146 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
     __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0xC0000040u, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
+
+  // ---- query side, three barriers
+  // (1) a_P = (1/L) sum_v c_v prod_{p in P} sigma_p(v); qt = H D q per head in
+  //     registers (butterflies of span 1..32 across lanes, then 64 within the
+  //     lane), with max |qt_j| and sum qt_j
+  if (tid < Mk::kPlaneMasks) {
+    const int sb = subset_bits<K>(tid);
+    double acc = 0.0;
+#pragma unroll
+    for (int v = 0; v < L; ++v) {
+      const int par = __popc(~v & sb) & 1;       // number of -1 factors
+      acc += par ? -(double)cv[v] : (double)cv[v];
+    }
+    coef[tid] = (float)(acc / L);
+    if (tid == 0) cmax = cv[L - 1];
+  }
+  if (wave < 4) {
+    float x0 = ((d0 >> (lane & 31)) & 1u) ? -q0 : q0;
+    float x1 = ((d1 >> (lane & 31)) & 1u) ? -q1 : q1;
+#pragma unroll
+    for (int hs = 1; hs < 64; hs <<= 1) {
+      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
+      x0 = (lane & hs) ? o0 - x0 : x0 + o0;
+      x1 = (lane & hs) ? o1 - x1 : x1 + o1;
+    }
+    const float y0 = x0 + x1, y1 = x0 - x1;
+    qt[wave][lane] = y0;
+    qt[wave][lane + 64] = y1;
+    const float m1 = wave_max_f32(fmaxf(fabsf(y0), fabsf(y1)));
+    const float s1 = wave_sum_f32(y0 + y1);
+    if (lane == 0) {
+      qstat[wave][0] = m1;
+      qstat[wave][1] = s1;
+    }
+  }
+  __syncthreads();
+  // (2) p = S qt / sqrt(d): threads 4i .. 4i+3 own row i, a quarter of it each,
+  //     all four heads, then a 4-lane reduction; per wave, max |p_i| and sum p_i
+  if (wave < kPWaves) {
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint32_t ww[4] = {srow[v].x, srow[v].y, srow[v].z, srow[v].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f16x2 pr = __builtin_bit_cast(f16x2, ww[e]);
+        const int j = 32 * qtr + 8 * v + 2 * e;
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+          acc[hh] = fmaf((float)pr[0], qt[hh][j], acc[hh]);
+          acc[hh] = fmaf((float)pr[1], qt[hh][j + 1], acc[hh]);
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      acc[hh] += __shfl_xor(acc[hh], 1, 64);
+      acc[hh] += __shfl_xor(acc[hh], 2, 64);
+      acc[hh] *= 0.08838834764831845f;          // 1/sqrt(128)
+    }
+    pp[qtr][prow] = acc[qtr];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const float pm = wave_max_f32(fabsf(acc[hh]));
+      const float ps = wave_sum_f32(qtr == 0 ? acc[hh] : 0.0f);
+      if (lane == 0) {
+        pstat[wave][hh][0] = pm;
+        pstat[wave][hh][1] = ps;
+      }
+    }
+  }
+  __syncthreads();
+  // (3) per head, the value of one fixed-point unit (2^30 units for the largest
+  //     |2 a_P qt_j| or |2 p_i|) and the constant terms; then the A fragments.
+  // A fragment of MFMA f = 2*w2 + g, lane l: row m = l%32, K = 16(l/32) + 4q + byte.
+  // Lane half hl of MFMA (w2, g) carries list word 2*w2 + hl; bit (8*byte + 4g + q)
+  // of that word.  Row m = 8 hh + 4 part + limb holds signed int8 limb `limb` of
+  // the value (zero where the mask belongs to the other part): the value V of
+  // coordinate j is 2 a_P qt_j (plane masks) or 2 p_j (sign mask) in units,
+  // pre-divided by 2^(j mod 8) (-128 for j mod 8 == 7: the top bit of a byte),
+  // and its signed base-256 digits are the bytes of V + 0x80808080, each minus 128.
+  // A thread's entries all share one row m (kBlock is a multiple of 128).
+  const auto unit_of = [&](int hh, int part) {
+    float vm;
+    if (part == 0) {
+      float amax = 0.0f;
+      for (int s = 0; s < Mk::kPlaneMasks; ++s) amax = fmaxf(amax, fabsf(coef[s]));
+      vm = 2.0f * amax * qstat[hh][0];
+    } else {
+      float m2 = 0.0f;
+      for (int w = 0; w < kPWaves; ++w) m2 = fmaxf(m2, pstat[w][hh][0]);
+      vm = 2.0f * m2;
+    }
+    return vm > 0.0f ? vm * (1.0f / 1073741824.0f) : 1.0f;
+  };
+  if (tid < 16) {
+    const int hh = tid >> 2, c = tid & 3;
+    float v;
+    if (c < 2) {
+      v = unit_of(hh, c);
+    } else if (c == 2) {
+      v = cmax * qstat[hh][1];                   // c_max * sum qt
+    } else {
+      v = 0.0f;
+      for (int w = 0; w < kPWaves; ++w) v += pstat[w][hh][1];   // sum p
+    }
+    consts[hh][c] = v;
+  }
+  {
+    const int m = (tid >> 2) & 31;
+    const int hh = m >> 3, part = (m >> 2) & 1, limb = m & 3;
+    const double inv_unit = 1.0 / (double)unit_of(hh, part);
+    for (int idx = tid; idx < NMF * 64 * 4; idx += kBlock) {
+      const int q = idx & 3, ln = (idx >> 2) & 63, f = idx >> 8;
+      const int w2 = f >> 1, g = f & 1;
+      const int li = 2 * w2 + (ln >> 5);        // list word: mask li/4, word li%4
+      const int mask = li >> 2, ww = li & 3;
+      const bool is_sign_mask = mask == Mk::kPlaneMasks;
+      uint32_t packed = 0;
+      if (hh < a.gq && part == (is_sign_mask ? 1 : 0)) {
+#pragma unroll
+        for (int byt = 0; byt < 4; ++byt) {
+          const int jj = 32 * ww + 8 * byt + 4 * g + q;
+          const float val = is_sign_mask ? 2.0f * pp[hh][jj] : 2.0f * coef[mask] * qt[hh][jj];
+          const int sh = jj & 7;
+          const double inv_div = sh == 7 ? -1.0 / 128.0 : 1.0 / (double)(1 << sh);
+          const int V = (int)rint((double)val * inv_unit * inv_div);
+          const uint32_t digit = (((uint32_t)V + 0x80808080u) >> (8 * limb)) & 0xFFu;
+          packed |= (digit ^ 0x80u) << (8 * byt);
+        }
+      }
+      reinterpret_cast<uint32_t*>(afrag)[(f * 64 + ln) * 4 + q] = packed;
+    }
+  }
+  __syncthreads();
+
+  i32x4 A[NMF];
+#pragma unroll
+  for (int f = 0; f < NMF; ++f) A[f] = afrag[f * 64 + lane];
+
   for (int64_t tile_base = tile0 + wave; tile_base < tile_end; tile_base += kPrefetch * kWaves) {
 #pragma unroll
    for (int sl = 0; sl < kPrefetch; ++sl) {
