@@ -49,7 +49,7 @@ int encode_common(int role, int head_dim, int bits, int projections, const void*
   rc = check_input(L, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n);
   if (rc || G * N == 0) return rc;
   if (!rec) return TQ_ERR_NULL;
-  if (fast128_encode_supported(L, x_dtype, x, sx_g, sx_n))
+  if (fast128_encode_supported(L, x_dtype, x, sx_g, sx_n, N))
     return launch_encode_fast128(L, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
                                  static_cast<hipStream_t>(stream));
   CodebookArgs cb = make_cb_args(cbs, n_cb, L);

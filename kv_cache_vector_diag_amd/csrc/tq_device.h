@@ -108,4 +108,8 @@ __device__ inline int quantize_index(const float* t, int levels, float z) {
 
 constexpr float kQjlConst = 1.2533141373155002512f;  // sqrt(pi/2)
 
+// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format; no
+// swizzle, no stride): offsets at or past the resource size read 0 and drop stores.
+constexpr int kRsrcWord3 = 0x00020000;
+
 }  // namespace tq

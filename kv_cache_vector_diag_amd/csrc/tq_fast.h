@@ -9,8 +9,9 @@
 namespace tq {
 
 // Encode with the MFMA kernel: head_dim 128; keys with 128 projections and
-// 1..3 Lloyd bits; values with 1..4 bits; 16-byte aligned rows.
-bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n);
+// 1..3 Lloyd bits; values with 1..4 bits; 16-byte aligned rows; a group's
+// records under 2^30 bytes (32-bit buffer offsets).
+bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N);
 int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
                           int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
 

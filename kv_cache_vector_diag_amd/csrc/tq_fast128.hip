@@ -147,6 +147,9 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
   const int64_t tile0 = chunk * a.tiles_per_block;
   const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles_per_group);
   const uint32_t* xb16 = reinterpret_cast<const uint32_t*>(a.x);
+  constexpr int RW = KEY ? (K * 4 + 4 + 2) : (K * 4 + 1);
+  const __amdgpu_buffer_rsrc_t rrs =
+      __builtin_amdgcn_make_buffer_rsrc(a.rec + g * a.N * RW, 0, (int)(a.N * RW * 4), kRsrcWord3);
 
   // bf16/f16 inputs: the next tile's rows are loaded while this tile is encoded
   const auto row_ptr = [&](int64_t t) {
@@ -154,10 +157,16 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
     return reinterpret_cast<const u32x4*>(xb16 + (g * a.sx_g + (tk < a.N ? tk : 0) * a.sx_n) / 2);
   };
   u32x4 xr[8];
-  if (DT != 0 && tile0 + wave < tile_end) {
+  if (DT != 0) {
     const u32x4* xp = row_ptr(tile0 + wave);
 #pragma unroll
     for (int c = 0; c < 8; ++c) xr[c] = xp[2 * c + h];   // tail lanes read row 0, never stored
+    // as many dropped stores as a tile stores, so that on entry the memory
+    // operations stand in the loop's order and its first wait is the same
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < (RW + 1) / 2; ++q) __builtin_amdgcn_raw_buffer_store_b32(0u, rrs, 0xC0000000u + 64u * q, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   for (int64_t tile = tile0 + wave; tile < tile_end; tile += kWaves) {
     const int64_t tok = tile * kTile + col;
@@ -419,13 +428,15 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
     } else {
       words[K * 4] = __float_as_uint(n32);
     }
-    if (valid) {
-      uint32_t* out = a.rec + (g * a.N + tok) * R;
+    // every store is issued: one past the group's records (a ragged tail's
+    // token, the odd word of a value record) is dropped by the buffer bounds,
+    // so the next tile's loads never wait for this tile's stores
+    const uint32_t ro = valid ? (uint32_t)(tok * R * 4) : 0xC0000000u;
 #pragma unroll
-      for (int q = 0; q < (R + 1) / 2; ++q) {
-        const int wi = 2 * q + h;
-        if (wi < R) out[wi] = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
-      }
+    for (int q = 0; q < (R + 1) / 2; ++q) {
+      const int wi = 2 * q + h;
+      const uint32_t v = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
+      __builtin_amdgcn_raw_buffer_store_b32(v, rrs, wi < R ? ro + 4u * wi : 0xC0000000u, 0, 0);
     }
   }
 }
@@ -464,8 +475,9 @@ int launch_dt(const Enc128Args& a, int dt, hipStream_t s) {
 
 }  // namespace
 
-bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n) {
+bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N) {
   if (L.d != kD) return false;
+  if (N > (int64_t(1) << 30) / (4 * L.rec_words)) return false;   // 32-bit buffer offsets per group
   if (L.role == TQ_ROLE_KEY && (L.m != kM || L.k < 1 || L.k > 3)) return false;
   if (L.role == TQ_ROLE_VALUE && (L.k < 1 || L.k > 4)) return false;
   const int esz = dtype == TQ_F32 ? 4 : 2;

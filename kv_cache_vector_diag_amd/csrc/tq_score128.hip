@@ -34,9 +34,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;
 constexpr int kM = 128;
-// Word 3 of a raw buffer resource on gfx9-family chips (32-bit data format; no
-// swizzle, no stride): offsets at or past the resource size read 0 and drop stores.
-constexpr int kRsrcWord3 = 0x00020000;
 // Workgroup size: 16 waves (one workgroup per CU) while the A fragments fit in
 // 128 VGPRs; 8 waves for the 3-plane codebook, whose fragments need more.
 template <int K>
