@@ -171,7 +171,11 @@ int tq_scores(int head_dim, int bits, int projections,
  * the fly (never materialised) and summed in the rotated domain, one inverse
  * transform per (b, hq); the softmax is split over chunks of 1024 tokens and
  * merged by log-sum-exp.  `work` is caller scratch of
- * tq_attend_workspace_bytes(...) bytes (scores, then per-chunk partials).  Key
+ * tq_attend_workspace_bytes(...) bytes: the scores (or, where the scores are
+ * computed inside the chunk pass, the prepared query side of each (b, kv head)),
+ * then the per-chunk partials.  At head_dim 128 with 128 projections, key and
+ * value bits giving at most 3 planes each, and 1, 2 or 4 query heads per kv
+ * head, no score is written: one pass per chunk scores the keys on chip.  Key
  * and value codebooks are separate arrays (kcbs, vcbs) with their own n_cb.
  * T == 0 gives o = 0. */
 size_t tq_attend_workspace_bytes(int head_dim, int64_t B, int64_t H_q, int64_t T);

@@ -111,10 +111,13 @@ int tq_scores(int head_dim, int bits, int projections, const void* cbs, int64_t 
                                scores, status, static_cast<hipStream_t>(stream));
 }
 
-// Scratch of tq_attend: the scores [B][H_q][T], then (256-byte aligned) the
-// per-chunk partials [B*H_q][ceil(T/1024)][head_dim + 2] of the split softmax.
+// Scratch of tq_attend: the scores [B][H_q][T] or, on the fused path, the
+// prepared query side of each (b, kv head) (at most B*H_q of them), then
+// (256-byte aligned) the per-chunk partials [B*H_q][ceil(T/1024)][head_dim + 2]
+// of the split softmax.
 static size_t attend_scores_bytes(int64_t B, int64_t H_q, int64_t T) {
-  return ((size_t)(B * H_q * T) * sizeof(float) + 255) / 256 * 256;
+  const size_t sc = (size_t)(B * H_q * T) * sizeof(float), qp = attend_qprep_bytes(B * H_q);
+  return ((sc > qp ? sc : qp) + 255) / 256 * 256;
 }
 
 size_t tq_attend_workspace_bytes(int head_dim, int64_t B, int64_t H_q, int64_t T) {
@@ -143,6 +146,11 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections, const void*
   float* sc = static_cast<float*>(work);
   CodebookArgs kcb = make_cb_args(kcbs, n_kcb, K);
   CodebookArgs vcb = make_cb_args(vcbs, n_vcb, V);
+  if (T > 0 && attend_fused_supported(kcb, vcb, H_kv, H_q, T, krec)) {
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(work) + attend_scores_bytes(B, H_q, T));
+    return launch_attend_fused(kcb, vcb, static_cast<const uint32_t*>(krec), static_cast<const uint32_t*>(vrec), B,
+                               H_kv, T, q, q_dtype, H_q, scale, static_cast<uint8_t*>(work), part, out, status, s);
+  }
   if (T > 0) {
     rc = fast128_scores_supported(K, H_kv, H_q, T, krec)
              ? launch_scores_fast128(K, kcbs, n_kcb, static_cast<const uint32_t*>(krec), B, H_kv, T, q, q_dtype,

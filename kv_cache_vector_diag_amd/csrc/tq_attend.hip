@@ -14,6 +14,7 @@
 
 #include "tq_device.h"
 #include "tq_kernels.h"
+#include "tq_score_core.h"
 
 namespace tq {
 namespace {
@@ -403,6 +404,360 @@ __global__ __launch_bounds__(kBlock) void attend_mfma_kernel(MfmaPartArgs a) {
   }
 }
 
+// ---- fused decode attention at head_dim 128 (keys and values, k <= 3 planes
+// each).  A small kernel prepares the query side of every (sequence, kv head)
+// once (the score kernel's fixed-point MFMA fragments, tq_score_core.h) into
+// the workspace; then one workgroup per (sequence, kv head, chunk of kChunk
+// tokens) issues all of its loads at once (fragments, key tiles, value norms
+// and records), scores the chunk's keys straight into LDS, and runs the chunk
+// softmax and the value MFMA above on them, writing the same per-chunk partials
+// for attend_merge_kernel.  No score reaches memory.
+constexpr int kFBlock = 512;               // 8 waves
+constexpr int kFWaves = kFBlock / 64;
+constexpr size_t kQprepBytes = 20 * 1024 + 256;   // per group: fragments (<= 20 MFMAs x 1 KB), constants
+constexpr int kFSub = 512;                 // tokens per value sub-chunk (two per chunk)
+constexpr int kFRecStride = kFSub + 4;     // as kRecStride and kTbStride, for kFSub tokens
+constexpr int kFTbStride = kFSub + 32;
+
+struct QprepArgs {
+  CodebookArgs kcb;
+  const void* q;
+  int q_dtype;
+  int64_t Hkv, Hq;
+  int gq;
+  uint8_t* qws;          // [groups][kQprepBytes]: i32x4 fragments [NMF][64], then float consts [4][4]
+  int32_t* status;
+};
+
+template <int KK>
+__global__ __launch_bounds__(kFBlock) void attend_qprep_kernel(QprepArgs a) {
+  constexpr int NMF = sc128::Masks<KK>::kMfma;
+  __shared__ sc128::QueryLds<KK> qs;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t g = blockIdx.x, b = g / a.Hkv, hkv = g % a.Hkv;
+  const uint8_t* kblob = blob_of(a.kcb, g);
+  if (tid == 0 && a.status && blob_mismatch(a.kcb, kblob)) atomicOr(a.status, TQ_STATUS_BAD_BLOB);
+  const sc128::QuerySrc src{reinterpret_cast<const float*>(kblob + a.kcb.off_c),
+                            reinterpret_cast<const uint32_t*>(kblob + a.kcb.off_d),
+                            reinterpret_cast<const _Float16*>(kblob + a.kcb.off_s),
+                            a.q, a.q_dtype, ((b * a.Hq) + hkv * a.gq) * sc128::kD, a.gq};
+  sc128::QueryRegs<KK> qr;
+  sc128::query_load<KK>(src, qr, tid, wave, lane);
+  sc128::query_build<KK, kFBlock>(qs, qr, a.gq, tid, wave, lane);
+  uint8_t* out = a.qws + g * kQprepBytes;
+  for (int e = tid; e < NMF * 64; e += kFBlock) reinterpret_cast<sc128::i32x4*>(out)[e] = qs.afrag[e];
+  if (tid < 16) reinterpret_cast<float*>(out + NMF * 1024)[tid] = qs.consts[tid >> 2][tid & 3];
+}
+
+struct FusedArgs {
+  CodebookArgs kcb, vcb;
+  const uint32_t* krec;
+  const uint32_t* vrec;
+  const uint8_t* qws;
+  float scale;
+  int64_t Hkv, T, Hq, chunks;
+  int gq;                // query heads per kv head (1, 2 or 4)
+  float* part;
+  int32_t* status;
+};
+
+// Dynamic LDS of attend_fused_kernel (bytes), shared with its launcher.
+struct FusedLds {
+  size_t wq, rec, tb, af, kst, total;
+};
+
+__host__ __device__ inline FusedLds fused_lds(int gq, int kv_planes, int kk_planes) {
+  const int rwv = 4 * kv_planes + 1, nm = 1 << (kv_planes - 1);
+  const int nch = (16 * (4 * kk_planes + 6) + 63) / 64;
+  FusedLds o;
+  o.wq = 0;                                                   // scores, weights, digit bytes [gq][kChunk]
+  o.rec = a16((size_t)gq * kChunk * 4);                       // value words [rwv][kFRecStride]
+  o.tb = o.rec + a16((size_t)rwv * kFRecStride * 4);          // bytes [nm][4][4][kFTbStride]
+  o.af = o.tb + (size_t)nm * 4 * 4 * kFTbStride;              // i32x4 [kFSub/32][2][33]
+  o.kst = o.af + (size_t)(kFSub / 32) * kAfGroup * 16;        // key tiles: uint2 [kFWaves][64 nch]
+  o.total = o.kst + (size_t)kFWaves * 64 * nch * 8;
+  return o;
+}
+
+template <int KK, int KV>
+__global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
+  using sc128::i32x4;
+  constexpr int NMF = sc128::Masks<KK>::kMfma;
+  constexpr int RWK = sc128::key_words<KK>();
+  constexpr int NCH = (16 * RWK + 63) / 64;       // 8-byte chunks per lane per key tile
+  constexpr int NM = 1 << (KV - 1);               // odd value-plane subsets
+  constexpr int W = 4;                            // value plane words (d = 128)
+  constexpr int RWV = KV * W + 1;                 // value record words
+  constexpr int kTiles = kChunk / 32 / kFWaves;   // key tiles per wave
+  constexpr int kPer = kChunk / kFBlock;          // tokens per thread in the softmax
+  constexpr int kVH = kFBlock / kFSub;            // staging threads per value token
+  constexpr int kVW = (RWV + kVH - 1) / kVH;      // value words per staging thread and sub-chunk
+  constexpr int kNS = kChunk / kFSub;             // value sub-chunks
+  constexpr int d = sc128::kD;
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ float consts[4][4];
+  __shared__ float wred[kFWaves][4][3];           // per wave and head: max score, sum exp, max weight
+  __shared__ double womega[kFWaves][4];           // per wave and head: sum of the fixed-point weights
+  __shared__ double vcoef[NM];
+  __shared__ float hm[4], hl[4], hunit[4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches on it stay scalar
+  const int gq = a.gq;
+  const FusedLds lay = fused_lds(gq, KV, KK);
+  float* wf = reinterpret_cast<float*>(smem + lay.wq);
+  uint32_t* wd = reinterpret_cast<uint32_t*>(smem + lay.wq);   // digit bytes of the codes
+  uint32_t* rec = reinterpret_cast<uint32_t*>(smem + lay.rec);
+  uint8_t* tb = smem + lay.tb;
+  i32x4v* af = reinterpret_cast<i32x4v*>(smem + lay.af);
+  uint2* kst = reinterpret_cast<uint2*>(smem + lay.kst);
+
+  const int64_t g = blockIdx.x / a.chunks, c = blockIdx.x % a.chunks;
+  const int64_t b = g / a.Hkv, hkv = g % a.Hkv;
+  const int64_t t0 = c * kChunk;
+  const int nt = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+  const uint8_t* vblob = blob_of(a.vcb, g);
+  if (tid == 0 && a.status && blob_mismatch(a.vcb, vblob)) atomicOr(a.status, TQ_STATUS_BAD_BLOB);
+  const int h = lane >> 5, col = lane & 31, kh = lane >> 5;
+
+  // ---- every load at once, in the order of use; past T the buffer loads
+  // return zero (such tokens get no weight), so all are issued unconditionally
+  // and each wait counts exactly the loads still needed
+  const uint8_t* qw = a.qws + g * kQprepBytes;
+  i32x4 A[NMF];
+#pragma unroll
+  for (int f = 0; f < NMF; ++f) A[f] = reinterpret_cast<const i32x4*>(qw)[f * 64 + lane];
+  float cst = 0.0f;
+  if (tid < 16) cst = reinterpret_cast<const float*>(qw + NMF * 1024)[tid];
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.krec + g * a.T * RWK), 0, (int)(a.T * RWK * 4), kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(a.vrec + g * a.T * RWV), 0, (int)(a.T * RWV * 4), kRsrcWord3);
+  uint2 raw[kTiles][NCH];                         // wave w: tiles w, w + 8, ... of the chunk
+#pragma unroll
+  for (int k = 0; k < kTiles; ++k) {
+    const uint32_t base = (uint32_t)((t0 + (int64_t)(wave + kFWaves * k) * 32) * RWK * 4) + 8u * lane;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      raw[k][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(krs, base + 512u * i, 0, 0));
+  }
+  float nrm[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    nrm[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+        vrs, (uint32_t)((t0 + tid + i * kFBlock) * RWV * 4) + 4u * (KV * W), 0, 0));
+  const int vtok = tid % kFSub, vhalf = tid / kFSub;   // value staging: token, first word
+  uint32_t vr[kNS][kVW];
+#pragma unroll
+  for (int sc = 0; sc < kNS; ++sc) {
+    const uint32_t tok_off = (uint32_t)((t0 + sc * kFSub + vtok) * RWV * 4);
+#pragma unroll
+    for (int i = 0; i < kVW; ++i) {
+      const int wi = vhalf + kVH * i;
+      vr[sc][i] = __builtin_amdgcn_raw_buffer_load_b32(vrs, wi < RWV ? tok_off + 4u * wi : 0xC0000000u, 0, 0);
+    }
+  }
+  if (tid < NM) {
+    // value codebook in the sign basis: a_P = (1/L) sum_v c_v prod_{p in P} sigma_p(v)
+    const float* cent = reinterpret_cast<const float*>(vblob + a.vcb.off_c);
+    const int sb = odd_subset<KV>(tid);
+    double acc = 0.0;
+    for (int v = 0; v < (1 << KV); ++v) acc += (__popc(~v & sb) & 1) ? -(double)cent[v] : (double)cent[v];
+    vcoef[tid] = acc / (1 << KV);
+  }
+  for (int e = tid; e < (kFSub / 32) * kAfGroup; e += kFBlock) af[e] = i32x4v{0, 0, 0, 0};   // rows of absent heads
+  if (tid < 16) consts[tid >> 2][tid & 3] = cst;
+  __syncthreads();
+
+  // ---- (S) scores of the chunk's keys into wf[head][token]
+  uint2* st2 = kst + wave * 64 * NCH;
+  const uint32_t* st = reinterpret_cast<const uint32_t*>(st2) + col * RWK;
+#pragma unroll
+  for (int k = 0; k < kTiles; ++k) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) st2[lane + 64 * i] = raw[k][i];
+    float sa, sb;
+    sc128::score_tile<KK>(A, st, consts, a.scale, h, sa, sb);
+    const int tt = (wave + kFWaves * k) * 32 + col;
+    if (2 * h < gq) wf[(2 * h) * kChunk + tt] = sa;
+    if (2 * h + 1 < gq) wf[(2 * h + 1) * kChunk + tt] = sb;
+  }
+  __syncthreads();
+
+  // ---- (W) weights of all heads at once, two barriers: chunk max; then exp,
+  // sum and the largest weight; then the fixed-point codes, whose sum stays in
+  // per-wave partials until the finalize
+  {
+    float sv[4][kPer], mloc[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      mloc[hh] = -INFINITY;
+      if (hh < gq) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int t = tid + i * kFBlock;
+          sv[hh][i] = t < nt ? wf[hh * kChunk + t] : -INFINITY;
+          mloc[hh] = fmaxf(mloc[hh], sv[hh][i]);
+        }
+        mloc[hh] = wave_max_f32(mloc[hh]);
+        if (lane == 0) wred[wave][hh][0] = mloc[hh];
+      }
+    }
+    __syncthreads();
+    float mx[4];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      if (hh >= gq) continue;
+      mx[hh] = wred[0][hh][0];
+#pragma unroll
+      for (int w = 1; w < kFWaves; ++w) mx[hh] = fmaxf(mx[hh], wred[w][hh][0]);
+      float esl = 0.0f, oml = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int t = tid + i * kFBlock;
+        const float e = t < nt ? expf(sv[hh][i] - mx[hh]) : 0.0f;
+        esl += e;
+        sv[hh][i] = e * nrm[i];                     // the weight
+        oml = fmaxf(oml, sv[hh][i]);
+      }
+      esl = wave_sum_f32(esl);
+      oml = wave_max_f32(oml);
+      if (lane == 0) {
+        wred[wave][hh][1] = esl;
+        wred[wave][hh][2] = oml;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      if (hh >= gq) continue;
+      float es = 0.0f, om = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kFWaves; ++w) {
+        es += wred[w][hh][1];
+        om = fmaxf(om, wred[w][hh][2]);
+      }
+      const double fs = kFix / (double)(om > 0.0f ? om : 1.0f);
+      double tot = 0.0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int t = tid + i * kFBlock;
+        const uint32_t v = (uint32_t)rint((double)sv[hh][i] * fs);   // <= 2^27
+        tot += (double)v;                           // integers: exact in any order
+        wd[hh * kChunk + t] = (v & 0x7Fu) | ((v << 1) & 0x7F00u) | ((v << 2) & 0x7F0000u) | ((v << 3) & 0x7F000000u);
+      }
+      tot = wave_sum_f64(tot);
+      if (lane == 0) womega[wave][hh] = tot;
+      if (tid == 0) {
+        hm[hh] = mx[hh];
+        hl[hh] = es;
+        hunit[hh] = om > 0.0f ? om : 1.0f;
+      }
+    }
+  }
+
+  // ---- (V) value MFMA over sub-chunks of kFSub tokens; all 8 waves: wave w
+  // takes word w % 4 and the 32-token groups of parity w / 4
+  i32x16v acc[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = i32x16v{};
+  const int vw = wave & 3, vpar = wave >> 2;
+#pragma unroll
+  for (int sc = 0; sc < kNS; ++sc) {
+    const int s0 = sc * kFSub;
+    if (s0 >= nt) break;
+    const int ns = nt - s0 < kFSub ? nt - s0 : kFSub;
+#pragma unroll
+    for (int i = 0; i < kVW; ++i) {
+      const int wi = vhalf + kVH * i;
+      if (wi < RWV) rec[wi * kFRecStride + vtok] = vr[sc][i];
+    }
+    __syncthreads();                              // records, codes in; last sub-chunk's fragments consumed
+    // A fragments: head hh, tokens 4 qd .. 4 qd + 3 -> dword q of lanes (row 8(hh/2) + 4(hh%2) + l, half)
+    for (int e = tid; e < gq * (kFSub / 4); e += kFBlock) {
+      const int hh = e / (kFSub / 4), qd = e % (kFSub / 4);
+      const int gi = qd >> 3, half = (qd >> 2) & 1, q = qd & 3;
+      const uint4 x4 = *reinterpret_cast<const uint4*>(wd + hh * kChunk + s0 + 4 * qd);
+      const uint32_t x[4] = {x4.x, x4.y, x4.z, x4.w};
+      uint32_t y[4];
+      transpose4x4(x, y);
+      const int row0 = 8 * (hh >> 1) + 4 * (hh & 1);
+#pragma unroll
+      for (int l = 0; l < 4; ++l) reinterpret_cast<uint32_t*>(af + gi * kAfGroup + 33 * half + row0 + l)[q] = y[l];
+    }
+    // byte transpose of the mask words: tb[m][w][byte][token]
+    for (int e = tid; e < NM * W * (kFSub / 4); e += kFBlock) {
+      const int tq = e % (kFSub / 4), mw = e / (kFSub / 4), w = mw % W, m = mw / W;
+      const int sb = odd_subset<KV>(m);
+      uint32_t x[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int p = 0; p < KV; ++p)
+        if ((sb >> p) & 1) {
+          const uint4 r4 = *reinterpret_cast<const uint4*>(rec + (p * W + w) * kFRecStride + 4 * tq);
+          x[0] ^= r4.x; x[1] ^= r4.y; x[2] ^= r4.z; x[3] ^= r4.w;
+        }
+      uint32_t y[4];
+      transpose4x4(x, y);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(tb + (size_t)(m * W + w) * 4 * kFTbStride) + tq;
+#pragma unroll
+      for (int by = 0; by < 4; ++by) dst[by * (kFTbStride / 4)] = y[by];
+    }
+    __syncthreads();
+    const uint32_t bit = 0x01010101u << (col & 7);
+    for (int gi = vpar; gi < (ns + 31) / 32; gi += 2) {
+      const i32x4v av = af[gi * kAfGroup + 33 * kh + col];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const uint4 r4 = *reinterpret_cast<const uint4*>(
+            tb + ((size_t)(m * W + vw) * 4 + (col >> 3)) * kFTbStride + 32 * gi + 16 * kh);
+        const i32x4v bv = {(int)(r4.x & bit), (int)(r4.y & bit), (int)(r4.z & bit), (int)(r4.w & bit)};
+        acc[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, bv, acc[m], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- (F) waves 4-7 hand their sums to waves 0-3 through LDS (from the
+  // value records' area on, free now); a[j] = unit * sum_P a_P (2 M_P[j] - W)
+  __syncthreads();
+  int* xch = reinterpret_cast<int*>(smem + lay.rec);   // [4 waves][NM][8 regs][64 lanes]
+  if (wave >= 4) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) xch[((vw * NM + m) * 8 + r) * 64 + lane] = acc[m][r];
+  }
+  __syncthreads();
+  if (wave < 4) {
+    const int e7 = col & 7;
+    const int j = 32 * vw + col;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int hh = 2 * q + kh;
+      if (hh >= gq) continue;
+      double omega = 0.0;
+#pragma unroll
+      for (int w = 0; w < kFWaves; ++w) omega += womega[w][hh];
+      double tot = 0.0;
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        int64_t mv = 0;
+#pragma unroll
+        for (int l = 3; l >= 0; --l)
+          mv = mv * 128 + (int64_t)acc[m][4 * q + l] + (int64_t)xch[((vw * NM + m) * 8 + 4 * q + l) * 64 + lane];
+        mv = e7 == 7 ? -(mv >> 7) : (mv >> e7);
+        tot += vcoef[m] * (double)(2 * mv - (int64_t)omega);
+      }
+      const double unit = (double)hunit[hh] / kFix;
+      a.part[((b * a.Hq + hkv * gq + hh) * a.chunks + c) * (d + 2) + j] = (float)(tot * unit);
+    }
+  }
+  if (tid < gq) {
+    float* out = a.part + ((b * a.Hq + hkv * gq + tid) * a.chunks + c) * (d + 2);
+    out[d] = hm[tid];
+    out[d + 1] = hl[tid];
+  }
+}
+
 struct MergeArgs {
   CodebookArgs vcb;
   const float* part;
@@ -557,6 +912,96 @@ int launch_attend_mfma_k(const MfmaPartArgs& pa, int64_t blocks, hipStream_t s) 
 }
 
 }  // namespace
+
+namespace {
+
+template <int KK, int KV>
+int launch_fused(const FusedArgs& fa, int64_t blocks, hipStream_t s) {
+  const size_t lds = fused_lds(fa.gq, KV, KK).total;
+  static bool attr_set = false;   // idempotent; a race only repeats the call
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&attend_fused_kernel<KK, KV>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 120 * 1024) != hipSuccess)
+      return -10;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((attend_fused_kernel<KK, KV>), dim3((unsigned)blocks), dim3(kFBlock), lds, s, fa);
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+}  // namespace
+
+size_t attend_qprep_bytes(int64_t groups) { return (size_t)groups * kQprepBytes; }
+
+// Fused path: head_dim 128, 128 projections, Walsh-Hadamard rotations, key and
+// value codebooks of k <= 3 planes, 1, 2 or 4 query heads per kv head, 8-byte
+// aligned key records, and a group's key and value records under 2^30 bytes
+// (32-bit buffer offsets).
+bool attend_fused_supported(const CodebookArgs& kcb, const CodebookArgs& vcb, int64_t Hkv, int64_t Hq, int64_t T,
+                            const void* krec) {
+  if (kcb.d != 128 || kcb.m != 128 || kcb.rotation != kRotHadamard || kcb.k < 1 || kcb.k > 3) return false;
+  if (vcb.d != 128 || vcb.rotation != kRotHadamard || vcb.k < 1 || vcb.k > 3) return false;
+  if (reinterpret_cast<uintptr_t>(krec) & 7) return false;
+  if (T + kChunk > (int64_t(1) << 30) / (4 * (kcb.rec_words > vcb.rec_words ? kcb.rec_words : vcb.rec_words)))
+    return false;
+  if (Hkv <= 0 || Hq % Hkv != 0) return false;
+  const int64_t gq = Hq / Hkv;
+  if (gq != 1 && gq != 2 && gq != 4) return false;
+  const FusedLds lay = fused_lds((int)gq, vcb.k, kcb.k);
+  // the finalize hands partial sums over through the LDS from the value records on
+  const size_t xch = (size_t)4 * (1 << (vcb.k - 1)) * 8 * 64 * 4;
+  return lay.total <= 120 * 1024 && lay.total - lay.rec >= xch;
+}
+
+int launch_attend_fused(const CodebookArgs& kcb, const CodebookArgs& vcb, const uint32_t* krec,
+                        const uint32_t* vrec, int64_t B, int64_t Hkv, int64_t T, const void* q, int q_dtype,
+                        int64_t Hq, float scale, uint8_t* qws, float* part, float* out, int32_t* status,
+                        hipStream_t s) {
+  if (B * Hq == 0) return 0;
+  const int64_t chunks = attend_chunks(T);
+  const int64_t groups = B * Hkv;
+  const int gq = (int)(Hq / Hkv);
+  if (chunks > 0) {
+    QprepArgs qa{kcb, q, q_dtype, Hkv, Hq, gq, qws, status};
+    switch (kcb.k) {
+      case 1: hipLaunchKernelGGL(attend_qprep_kernel<1>, dim3((unsigned)groups), dim3(kFBlock), 0, s, qa); break;
+      case 2: hipLaunchKernelGGL(attend_qprep_kernel<2>, dim3((unsigned)groups), dim3(kFBlock), 0, s, qa); break;
+      case 3: hipLaunchKernelGGL(attend_qprep_kernel<3>, dim3((unsigned)groups), dim3(kFBlock), 0, s, qa); break;
+      default: return -13;
+    }
+    if (hipGetLastError() != hipSuccess) return -10;
+    FusedArgs fa;
+    fa.kcb = kcb;
+    fa.vcb = vcb;
+    fa.krec = krec;
+    fa.vrec = vrec;
+    fa.qws = qws;
+    fa.scale = scale;
+    fa.Hkv = Hkv; fa.T = T; fa.Hq = Hq;
+    fa.chunks = chunks;
+    fa.gq = gq;
+    fa.part = part;
+    fa.status = status;
+    const int64_t blocks = groups * chunks;       // one workgroup per (sequence, kv head, chunk)
+    int rc;
+    switch (kcb.k * 4 + vcb.k) {
+      case 4 + 1: rc = launch_fused<1, 1>(fa, blocks, s); break;
+      case 4 + 2: rc = launch_fused<1, 2>(fa, blocks, s); break;
+      case 4 + 3: rc = launch_fused<1, 3>(fa, blocks, s); break;
+      case 8 + 1: rc = launch_fused<2, 1>(fa, blocks, s); break;
+      case 8 + 2: rc = launch_fused<2, 2>(fa, blocks, s); break;
+      case 8 + 3: rc = launch_fused<2, 3>(fa, blocks, s); break;
+      case 12 + 1: rc = launch_fused<3, 1>(fa, blocks, s); break;
+      case 12 + 2: rc = launch_fused<3, 2>(fa, blocks, s); break;
+      case 12 + 3: rc = launch_fused<3, 3>(fa, blocks, s); break;
+      default: rc = -13;
+    }
+    if (rc) return rc;
+  }
+  MergeArgs ma{vcb, part, Hkv, Hq, chunks, out};
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kBlock), 0, s, ma);
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
 
 bool attend_split_supported(const CodebookArgs& vcb) {
   return vcb.rotation == kRotHadamard && vcb.d >= 8 && vcb.d <= kMaxHeadDim && vcb.k >= 1 && vcb.k <= 8;

@@ -30,6 +30,17 @@ int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t 
 // Split-token attention output (any power-of-two d in [8, 512], value k <= 8):
 // per-chunk partials in `part` ([B*Hq][attend_chunks(T)][d + 2] floats), then a merge.
 int64_t attend_chunks(int64_t T);
+// Fused attention (d = m = 128, k <= 3 for keys and values): the query side of
+// each (b, kv head) into `qws` (attend_qprep_bytes(B * Hkv) bytes), then scores
+// straight from the key records into the chunk partials, then the merge; `part`
+// as above.
+size_t attend_qprep_bytes(int64_t groups);
+bool attend_fused_supported(const CodebookArgs& kcb, const CodebookArgs& vcb, int64_t Hkv, int64_t Hq, int64_t T,
+                            const void* krec);
+int launch_attend_fused(const CodebookArgs& kcb, const CodebookArgs& vcb, const uint32_t* krec,
+                        const uint32_t* vrec, int64_t B, int64_t Hkv, int64_t T, const void* q, int q_dtype,
+                        int64_t Hq, float scale, uint8_t* qws, float* part, float* out, int32_t* status,
+                        hipStream_t s);
 bool attend_split_supported(const CodebookArgs& vcb);
 int launch_attend_split(const CodebookArgs& vcb, const uint32_t* vrec, const float* scores, int64_t B,
                         int64_t Hkv, int64_t T, int64_t Hq, float* part, float* out, hipStream_t s);

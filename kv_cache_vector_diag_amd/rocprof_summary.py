@@ -29,6 +29,8 @@ KERNELS = {
     "attend_part": "attend_part",
     "attend_merge": "attend_merge",
     "attend_mfma": "attend_mfma",
+    "attend_fused": "attend_fused",
+    "attend_qprep": "attend_qprep",
     "attend": "attend",
     "split256_prep": "split256_prep",
     "split256_kernel": "split256",
@@ -45,7 +47,8 @@ ROLE_KERNELS = {"encode128_kernel": ("encode", 1), "encode_tiled_kernel": ("tile
 _COMMON = ["tq_device.h", "tq_layout.h", "tq_mfma.h", "tq_fast.h", "../../include/tq.h"]
 KERNEL_SOURCES = {
     "encode_keys": ["tq_fast128.hip"] + _COMMON,
-    "score": ["tq_score128.hip"] + _COMMON,
+    "score": ["tq_score128.hip", "tq_score_core.h"] + _COMMON,
+    "attend_fused": ["tq_attend.hip", "tq_score_core.h", "tq_kernels.h"] + _COMMON,
 }
 
 

@@ -169,6 +169,15 @@ def test_long_context_attend(gpu_lib):
     (256, 2, 3, 256, 2, 2, 8, 1300),
     (32, 2, 1, 32, 1, 1, 3, 257),
     (64, 3, 2, 64, 1, 2, 4, 1024),
+    # fused path (head_dim 128, k <= 3 for keys and values, 1, 2 or 4 query heads
+    # per kv head): every key/value plane count, ragged chunks and tiles, one token
+    (128, 2, 2, 128, 1, 3, 3, 1025),
+    (128, 3, 3, 128, 2, 2, 8, 2100),
+    (128, 4, 1, 128, 1, 2, 4, 300),
+    (128, 3, 2, 128, 1, 1, 2, 1),
+    (128, 4, 3, 128, 1, 1, 4, 4097),
+    (128, 2, 1, 128, 2, 1, 2, 1100),
+    (128, 4, 2, 128, 1, 2, 2, 777),
 ])
 def test_attend_shapes(gpu_lib, d, kb, vb, m, B, Hkv, Hq, T):
     import torch
@@ -185,6 +194,30 @@ def test_attend_shapes(gpu_lib, d, kb, vb, m, B, Hkv, Hq, T):
     torch.cuda.synchronize()
     ref = tq.attend(kq, rec_np(krec), vq, rec_np(vrec), inputs.exact_values(q))
     assert_close(o.cpu().numpy(), ref, "attend")
+
+
+def test_attend_fused_chunk_runs(gpu_lib):
+    """64 (sequence, kv head) groups of 9000 tokens: each fused workgroup takes a
+    run of several chunks; sampled groups against the oracle."""
+    import torch
+    b = gpu_lib
+    d, B, Hkv, Hq, T, seed = 128, 8, 8, 16, 9000, 12
+    K = inputs.to_torch(inputs.kv_normal(seed, B * Hkv, T, d, inputs.STREAM_K), "bf16", DEV)
+    V = inputs.to_torch(inputs.kv_normal(seed, B * Hkv, T, d, inputs.STREAM_V), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    kcb, kq = _codebooks(b, Hkv, d, 3, 128, seed, tq.ROLE_KEY)
+    vcb, vq = _codebooks(b, Hkv, d, 2, 0, seed + 1, tq.ROLE_VALUE)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, 3, 128).view(B, Hkv, T, -1)
+    vrec = b.tq_encode_values(vcb, Hkv, V, d, 2).view(B, Hkv, T, -1)
+    del K, V
+    o = b.tq_attend(kcb, Hkv, vcb, Hkv, krec, vrec, q, d, 3, 2, 128)
+    torch.cuda.synchronize()
+    qv = inputs.exact_values(q)
+    gq = Hq // Hkv
+    for bb, h in ((0, 0), (5, 3), (7, 7)):
+        ref = tq.attend([kq[h]], rec_np(krec[bb, h])[None, None], [vq[h]], rec_np(vrec[bb, h])[None, None],
+                        qv[bb:bb + 1, h * gq:(h + 1) * gq])
+        assert_close(o[bb, h * gq:(h + 1) * gq].cpu().numpy()[None], ref, f"attend b={bb} h={h}")
 
 
 def test_attend_empty_context_gives_zero(gpu_lib):

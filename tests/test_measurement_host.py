@@ -24,6 +24,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     ("void tq::(anonymous namespace)::score128_kernel<2>(tq::(anonymous namespace)::Score128Args)", "score"),
     ("void tq::(anonymous namespace)::split256_prep_kernel(tq::(anonymous namespace)::PrepArgs)",
      "split256_prep"),
+    ("void tq::(anonymous namespace)::attend_fused_kernel<1, 2>(tq::(anonymous namespace)::FusedArgs)",
+     "attend_fused"),
+    ("void tq::(anonymous namespace)::attend_qprep_kernel<1>(tq::(anonymous namespace)::QprepArgs)",
+     "attend_qprep"),
+    ("void tq::(anonymous namespace)::attend_merge_kernel(tq::(anonymous namespace)::MergeArgs)",
+     "attend_merge"),
     ("__amd_rocclr_copyBuffer", "copy"),
 ])
 def test_short_names(name, short):
