@@ -185,6 +185,43 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections,
               const void* q, int q_dtype, int64_t H_q, float scale,
               float* out, void* work, size_t work_bytes, int32_t* status, void* stream);
 
+/* Rotation-named forms of the five compute calls above (README "Architecture"
+ * step 1 and "Modules" rotation: the random rotation is Haar via QR, or the fast
+ * Walsh-Hadamard transform).  Arguments, layouts and errors as in the plain
+ * forms, which are these with rotation = TQ_ROT_HADAMARD; `rotation` names the
+ * rotation the codebooks were made with (tq_make_codebook_ex) and must match
+ * the blob headers (else the status word gets the blob-mismatch bit).  With
+ * TQ_ROT_HAAR, head_dim is any value in [2, 512]; R = sqrt(head_dim) Q takes the
+ * place of H D everywhere (u = R x, x^ = (n/head_dim) R^T c[idx], qt = R q), and
+ * attention applies R^T once per (b, hq) to the rotated-domain sum.  Haar
+ * encodes and scores run on the float64 per-vector kernels; the attention's
+ * value partials run on the same MFMA kernels as for Walsh-Hadamard codebooks
+ * when head_dim is a multiple of 32. */
+int tq_encode_keys_ex(int head_dim, int bits, int projections, int rotation,
+                      const void* cbs, int64_t n_cb,
+                      const void* x, int x_dtype, int64_t G, int64_t N,
+                      int64_t sx_g, int64_t sx_n,
+                      void* rec, int32_t* status, void* stream);
+int tq_encode_values_ex(int head_dim, int bits, int rotation,
+                        const void* cbs, int64_t n_cb,
+                        const void* x, int x_dtype, int64_t G, int64_t N,
+                        int64_t sx_g, int64_t sx_n,
+                        void* rec, int32_t* status, void* stream);
+int tq_decode_values_ex(int head_dim, int bits, int rotation,
+                        const void* cbs, int64_t n_cb,
+                        const void* rec, int64_t G, int64_t N,
+                        float* out, int32_t* status, void* stream);
+int tq_scores_ex(int head_dim, int bits, int projections, int rotation,
+                 const void* cbs, int64_t n_cb,
+                 const void* krec, int64_t B, int64_t H_kv, int64_t T,
+                 const void* q, int q_dtype, int64_t H_q, float scale,
+                 float* scores, int32_t* status, void* stream);
+int tq_attend_ex(int head_dim, int k_bits, int v_bits, int projections, int rotation,
+                 const void* kcbs, int64_t n_kcb, const void* vcbs, int64_t n_vcb,
+                 const void* krec, const void* vrec, int64_t B, int64_t H_kv, int64_t T,
+                 const void* q, int q_dtype, int64_t H_q, float scale,
+                 float* out, void* work, size_t work_bytes, int32_t* status, void* stream);
+
 /* Test hook: u = H(D x) (unnormalised rotation) and n = |x| for every vector,
  * with the D of the group's codebook.  u [G][N][head_dim] f32, norms [G][N] f32. */
 int tq_rotate(int head_dim, int bits, int projections, int role,

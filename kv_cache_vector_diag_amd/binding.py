@@ -29,7 +29,8 @@ EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encod
            "tq_encode_values", "tq_decode_values", "tq_scores", "tq_attend_workspace_bytes",
            "tq_attend", "tq_rotate", "tq_memory_stats", "tq_status_string", "tq_codebook_bytes_ex",
            "tq_record_bytes_ex", "tq_make_codebook_ex", "tq_outlier_workspace_bytes", "tq_outlier_channels",
-           "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes"]
+           "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes",
+           "tq_encode_keys_ex", "tq_encode_values_ex", "tq_decode_values_ex", "tq_scores_ex", "tq_attend_ex"]
 
 _lib = None
 
@@ -85,6 +86,17 @@ def load() -> ctypes.CDLL:
                                     c_void_p, c_void_p, c_void_p]),
         "tq_decode_values_split": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
                                            c_void_p, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_encode_keys_ex": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int, c_int64,
+                                      c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_encode_values_ex": (c_int, [c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int, c_int64, c_int64,
+                                        c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_decode_values_ex": (c_int, [c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int64,
+                                        c_void_p, c_void_p, c_void_p]),
+        "tq_scores_ex": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int64,
+                                 c_int64, c_void_p, c_int, c_int64, c_float, c_void_p, c_void_p, c_void_p]),
+        "tq_attend_ex": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64,
+                                 c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float,
+                                 c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -183,39 +195,56 @@ def _groups(x, head_dim):
     return x.shape[0], x.shape[1], x.stride(0), x.stride(1)
 
 
-def tq_encode_keys(cbs, n_cb, x, head_dim, bits, projections, rec=None, status=None):
+# A `rotation` other than ROT_HADAMARD calls the rotation-named (_ex) entry point.
+def tq_encode_keys(cbs, n_cb, x, head_dim, bits, projections, rec=None, status=None, rotation=ROT_HADAMARD):
     import torch
     G, N, sg, sn = _groups(x, head_dim)
-    words = tq_record_bytes(head_dim, bits, projections, ROLE_KEY) // 4
+    words = tq_record_bytes_ex(head_dim, bits, projections, ROLE_KEY, rotation) // 4
     if rec is None:
         rec = torch.empty((G, N, words), dtype=torch.int32, device=x.device)
-    _check(load().tq_encode_keys(head_dim, bits, projections, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N,
-                                 sg, sn, _ptr(rec), _ptr(status), _stream(x)), "tq_encode_keys")
+    if rotation == ROT_HADAMARD:
+        rc = load().tq_encode_keys(head_dim, bits, projections, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N,
+                                   sg, sn, _ptr(rec), _ptr(status), _stream(x))
+    else:
+        rc = load().tq_encode_keys_ex(head_dim, bits, projections, rotation, _ptr(cbs), n_cb, _ptr(x),
+                                      _dtype_code(x), G, N, sg, sn, _ptr(rec), _ptr(status), _stream(x))
+    _check(rc, "tq_encode_keys")
     return rec
 
 
-def tq_encode_values(cbs, n_cb, x, head_dim, bits, rec=None, status=None):
+def tq_encode_values(cbs, n_cb, x, head_dim, bits, rec=None, status=None, rotation=ROT_HADAMARD):
     import torch
     G, N, sg, sn = _groups(x, head_dim)
-    words = tq_record_bytes(head_dim, bits, 0, ROLE_VALUE) // 4
+    words = tq_record_bytes_ex(head_dim, bits, 0, ROLE_VALUE, rotation) // 4
     if rec is None:
         rec = torch.empty((G, N, words), dtype=torch.int32, device=x.device)
-    _check(load().tq_encode_values(head_dim, bits, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N, sg, sn,
-                                   _ptr(rec), _ptr(status), _stream(x)), "tq_encode_values")
+    if rotation == ROT_HADAMARD:
+        rc = load().tq_encode_values(head_dim, bits, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N, sg, sn,
+                                     _ptr(rec), _ptr(status), _stream(x))
+    else:
+        rc = load().tq_encode_values_ex(head_dim, bits, rotation, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N,
+                                        sg, sn, _ptr(rec), _ptr(status), _stream(x))
+    _check(rc, "tq_encode_values")
     return rec
 
 
-def tq_decode_values(cbs, n_cb, rec, head_dim, bits, out=None, status=None):
+def tq_decode_values(cbs, n_cb, rec, head_dim, bits, out=None, status=None, rotation=ROT_HADAMARD):
     import torch
     G, N = rec.shape[0], rec.shape[1]
     if out is None:
         out = torch.empty((G, N, head_dim), dtype=torch.float32, device=rec.device)
-    _check(load().tq_decode_values(head_dim, bits, _ptr(cbs), n_cb, _ptr(rec), G, N, _ptr(out), _ptr(status),
-                                   _stream(rec)), "tq_decode_values")
+    if rotation == ROT_HADAMARD:
+        rc = load().tq_decode_values(head_dim, bits, _ptr(cbs), n_cb, _ptr(rec), G, N, _ptr(out), _ptr(status),
+                                     _stream(rec))
+    else:
+        rc = load().tq_decode_values_ex(head_dim, bits, rotation, _ptr(cbs), n_cb, _ptr(rec), G, N, _ptr(out),
+                                        _ptr(status), _stream(rec))
+    _check(rc, "tq_decode_values")
     return out
 
 
-def tq_scores(cbs, n_cb, krec, q, head_dim, bits, projections, scale=0.0, out=None, status=None):
+def tq_scores(cbs, n_cb, krec, q, head_dim, bits, projections, scale=0.0, out=None, status=None,
+              rotation=ROT_HADAMARD):
     """krec [B][H_kv][T][words] (int32 view of uint32), q [B][H_q][head_dim] -> [B][H_q][T] float32."""
     import torch
     B, Hkv, T = krec.shape[0], krec.shape[1], krec.shape[2]
@@ -224,13 +253,18 @@ def tq_scores(cbs, n_cb, krec, q, head_dim, bits, projections, scale=0.0, out=No
         raise ValueError("q must be contiguous [B][H_q][head_dim]")
     if out is None:
         out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
-    _check(load().tq_scores(head_dim, bits, projections, _ptr(cbs), n_cb, _ptr(krec), B, Hkv, T, _ptr(q),
-                            _dtype_code(q), Hq, scale, _ptr(out), _ptr(status), _stream(q)), "tq_scores")
+    if rotation == ROT_HADAMARD:
+        rc = load().tq_scores(head_dim, bits, projections, _ptr(cbs), n_cb, _ptr(krec), B, Hkv, T, _ptr(q),
+                              _dtype_code(q), Hq, scale, _ptr(out), _ptr(status), _stream(q))
+    else:
+        rc = load().tq_scores_ex(head_dim, bits, projections, rotation, _ptr(cbs), n_cb, _ptr(krec), B, Hkv, T,
+                                 _ptr(q), _dtype_code(q), Hq, scale, _ptr(out), _ptr(status), _stream(q))
+    _check(rc, "tq_scores")
     return out
 
 
 def tq_attend(kcbs, n_kcb, vcbs, n_vcb, krec, vrec, q, head_dim, k_bits, v_bits, projections, scale=0.0,
-              out=None, work=None, status=None):
+              out=None, work=None, status=None, rotation=ROT_HADAMARD):
     import torch
     B, Hkv, T = krec.shape[0], krec.shape[1], krec.shape[2]
     Hq = q.shape[1]
@@ -239,9 +273,13 @@ def tq_attend(kcbs, n_kcb, vcbs, n_vcb, krec, vrec, q, head_dim, k_bits, v_bits,
     need = int(load().tq_attend_workspace_bytes(head_dim, B, Hq, T))
     if work is None:
         work = torch.empty(need, dtype=torch.uint8, device=q.device)
-    _check(load().tq_attend(head_dim, k_bits, v_bits, projections, _ptr(kcbs), n_kcb, _ptr(vcbs), n_vcb,
-                            _ptr(krec), _ptr(vrec), B, Hkv, T, _ptr(q), _dtype_code(q), Hq, scale, _ptr(out),
-                            _ptr(work), work.numel(), _ptr(status), _stream(q)), "tq_attend")
+    args = (_ptr(kcbs), n_kcb, _ptr(vcbs), n_vcb, _ptr(krec), _ptr(vrec), B, Hkv, T, _ptr(q), _dtype_code(q), Hq,
+            scale, _ptr(out), _ptr(work), work.numel(), _ptr(status), _stream(q))
+    if rotation == ROT_HADAMARD:
+        rc = load().tq_attend(head_dim, k_bits, v_bits, projections, *args)
+    else:
+        rc = load().tq_attend_ex(head_dim, k_bits, v_bits, projections, rotation, *args)
+    _check(rc, "tq_attend")
     return out
 
 

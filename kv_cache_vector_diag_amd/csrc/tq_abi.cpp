@@ -40,11 +40,11 @@ int split_layouts(int role, int head_dim, int n_outlier, int bits, Layout* Ln, L
   return make_layout(n_outlier, bits + 1, key ? n_outlier : 0, role, Lo, kRotHadamard);
 }
 
-int encode_common(int role, int head_dim, int bits, int projections, const void* cbs, int64_t n_cb,
+int encode_common(int role, int head_dim, int bits, int projections, int rotation, const void* cbs, int64_t n_cb,
                   const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec,
                   int32_t* status, void* stream) {
   Layout L;
-  int rc = make_layout(head_dim, bits, projections, role, &L);
+  int rc = make_layout(head_dim, bits, projections, role, &L, rotation);
   if (rc) return rc;
   rc = check_input(L, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n);
   if (rc || G * N == 0) return rc;
@@ -64,24 +64,43 @@ int encode_common(int role, int head_dim, int bits, int projections, const void*
 
 extern "C" {
 
+int tq_encode_keys_ex(int head_dim, int bits, int projections, int rotation, const void* cbs, int64_t n_cb,
+                      const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec,
+                      int32_t* status, void* stream) {
+  return encode_common(TQ_ROLE_KEY, head_dim, bits, projections, rotation, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n,
+                       rec, status, stream);
+}
+
 int tq_encode_keys(int head_dim, int bits, int projections, const void* cbs, int64_t n_cb, const void* x,
                    int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec, int32_t* status,
                    void* stream) {
-  return encode_common(TQ_ROLE_KEY, head_dim, bits, projections, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, rec,
+  return tq_encode_keys_ex(head_dim, bits, projections, kRotHadamard, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, rec,
+                           status, stream);
+}
+
+int tq_encode_values_ex(int head_dim, int bits, int rotation, const void* cbs, int64_t n_cb, const void* x,
+                        int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec, int32_t* status,
+                        void* stream) {
+  return encode_common(TQ_ROLE_VALUE, head_dim, bits, 0, rotation, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, rec,
                        status, stream);
 }
 
 int tq_encode_values(int head_dim, int bits, const void* cbs, int64_t n_cb, const void* x, int x_dtype,
                      int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec, int32_t* status,
                      void* stream) {
-  return encode_common(TQ_ROLE_VALUE, head_dim, bits, 0, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, rec, status,
-                       stream);
+  return tq_encode_values_ex(head_dim, bits, kRotHadamard, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, rec, status,
+                             stream);
 }
 
 int tq_decode_values(int head_dim, int bits, const void* cbs, int64_t n_cb, const void* rec, int64_t G,
                      int64_t N, float* out, int32_t* status, void* stream) {
+  return tq_decode_values_ex(head_dim, bits, kRotHadamard, cbs, n_cb, rec, G, N, out, status, stream);
+}
+
+int tq_decode_values_ex(int head_dim, int bits, int rotation, const void* cbs, int64_t n_cb, const void* rec,
+                        int64_t G, int64_t N, float* out, int32_t* status, void* stream) {
   Layout L;
-  int rc = make_layout(head_dim, bits, 0, TQ_ROLE_VALUE, &L);
+  int rc = make_layout(head_dim, bits, 0, TQ_ROLE_VALUE, &L, rotation);
   if (rc) return rc;
   if (n_cb <= 0 || G < 0 || N < 0) return TQ_ERR_EMPTY_INPUT;
   if (G * N == 0) return TQ_OK;
@@ -94,8 +113,15 @@ int tq_decode_values(int head_dim, int bits, const void* cbs, int64_t n_cb, cons
 int tq_scores(int head_dim, int bits, int projections, const void* cbs, int64_t n_cb, const void* krec,
               int64_t B, int64_t H_kv, int64_t T, const void* q, int q_dtype, int64_t H_q, float scale,
               float* scores, int32_t* status, void* stream) {
+  return tq_scores_ex(head_dim, bits, projections, kRotHadamard, cbs, n_cb, krec, B, H_kv, T, q, q_dtype, H_q, scale,
+                      scores, status, stream);
+}
+
+int tq_scores_ex(int head_dim, int bits, int projections, int rotation, const void* cbs, int64_t n_cb,
+                 const void* krec, int64_t B, int64_t H_kv, int64_t T, const void* q, int q_dtype, int64_t H_q,
+                 float scale, float* scores, int32_t* status, void* stream) {
   Layout L;
-  int rc = make_layout(head_dim, bits, projections, TQ_ROLE_KEY, &L);
+  int rc = make_layout(head_dim, bits, projections, TQ_ROLE_KEY, &L, rotation);
   if (rc) return rc;
   if (n_cb <= 0 || B < 0 || H_kv <= 0 || T < 0 || H_q <= 0) return TQ_ERR_EMPTY_INPUT;
   if (H_q % H_kv) return TQ_ERR_DIMENSION_MISMATCH;
@@ -130,10 +156,18 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections, const void*
               const void* vcbs, int64_t n_vcb, const void* krec, const void* vrec, int64_t B, int64_t H_kv,
               int64_t T, const void* q, int q_dtype, int64_t H_q, float scale, float* out, void* work,
               size_t work_bytes, int32_t* status, void* stream) {
+  return tq_attend_ex(head_dim, k_bits, v_bits, projections, kRotHadamard, kcbs, n_kcb, vcbs, n_vcb, krec, vrec, B,
+                      H_kv, T, q, q_dtype, H_q, scale, out, work, work_bytes, status, stream);
+}
+
+int tq_attend_ex(int head_dim, int k_bits, int v_bits, int projections, int rotation, const void* kcbs,
+                 int64_t n_kcb, const void* vcbs, int64_t n_vcb, const void* krec, const void* vrec, int64_t B,
+                 int64_t H_kv, int64_t T, const void* q, int q_dtype, int64_t H_q, float scale, float* out,
+                 void* work, size_t work_bytes, int32_t* status, void* stream) {
   Layout K, V;
-  int rc = make_layout(head_dim, k_bits, projections, TQ_ROLE_KEY, &K);
+  int rc = make_layout(head_dim, k_bits, projections, TQ_ROLE_KEY, &K, rotation);
   if (rc) return rc;
-  rc = make_layout(head_dim, v_bits, 0, TQ_ROLE_VALUE, &V);
+  rc = make_layout(head_dim, v_bits, 0, TQ_ROLE_VALUE, &V, rotation);
   if (rc) return rc;
   if (n_kcb <= 0 || n_vcb <= 0 || B < 0 || H_kv <= 0 || T < 0 || H_q <= 0) return TQ_ERR_EMPTY_INPUT;
   if (H_q % H_kv) return TQ_ERR_DIMENSION_MISMATCH;

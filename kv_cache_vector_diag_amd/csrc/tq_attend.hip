@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kBlock) void attend_part_kernel(PartArgs a) {
   __syncthreads();
 
   const int lpt = d >> 3;                 // lanes per token
-  const int slots = kBlock / lpt;
+  const int slots = kBlock / lpt;         // threads past slots * lpt (d not dividing 2048) take no token
   const int slot = tid / lpt, sub = tid % lpt;
   const int word = sub >> 2, shift = (sub & 3) * 8;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -75,8 +75,9 @@ __global__ __launch_bounds__(kBlock) void attend_part_kernel(PartArgs a) {
     nn = __uint_as_float(r[K * W]);
     ns = s[t];
   };
-  if (t0 + slot < t1) load_tok(t0 + slot);
-  for (int64_t t = t0 + slot; t < t1; t += slots) {
+  const int64_t tbeg = slot < slots ? t0 + slot : t1;
+  if (tbeg < t1) load_tok(tbeg);
+  for (int64_t t = tbeg; t < t1; t += slots) {
     uint32_t by[K];
 #pragma unroll
     for (int p = 0; p < K; ++p) by[p] = nw[p] >> shift;
@@ -778,7 +779,7 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / a.Hq, hq = bh % a.Hq;
   const int64_t g = b * a.Hkv + hq * a.Hkv / a.Hq;
-  const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob_of(a.vcb, g) + a.vcb.off_d);
+  const uint8_t* blob = blob_of(a.vcb, g);
   const float* p = a.part + bh * a.chunks * (d + 2);
   // chunk maxima (and, for the first tile, the maxima and sums kept in LDS)
   float mx = -INFINITY;
@@ -796,9 +797,10 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   // thread = (coordinate pair jp, row class cg): rows c = cg, cg + rp, ... of each
-  // tile are summed in order, then the rp classes in order through LDS
+  // tile are summed in order, then the rp classes in order through LDS (threads
+  // past rp classes, where d does not divide 2 kBlock, take no rows)
   const int tpr = d / 2, rp = kBlock / tpr;
-  const int jp = tid % tpr, cg = tid / tpr;
+  const int jp = tid % tpr, cg = tid / tpr < rp ? tid / tpr : kWTile;
   float l = 0.0f;
   float2 aj = {0.0f, 0.0f};
   for (int64_t c0 = 0; c0 < a.chunks; c0 += kWTile) {
@@ -836,8 +838,10 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
     }
     __syncthreads();
   }
-  part[cg * d + 2 * jp] = aj.x;
-  part[cg * d + 2 * jp + 1] = aj.y;
+  if (cg < rp) {
+    part[cg * d + 2 * jp] = aj.x;
+    part[cg * d + 2 * jp + 1] = aj.y;
+  }
   l = wave_sum_f32(l);
   if ((tid & 63) == 0) red[tid >> 6] = l;
   __syncthreads();
@@ -848,6 +852,18 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   }
   __syncthreads();
   l = red[0] + red[1] + red[2] + red[3];
+  const float norm = l > 0.0f ? 1.0f / ((float)d * l) : 0.0f;
+  if (a.vcb.rotation == kRotHaar) {
+    // x^ = (n/d) R^T c: o_j = sum_i R[i][j] a_i / (d l), R row-major at off_d
+    const float* R = reinterpret_cast<const float*>(blob + a.vcb.off_d);
+    for (int j = tid; j < d; j += kBlock) {
+      float o = 0.0f;
+      for (int i = 0; i < d; ++i) o = fmaf(R[i * d + j], v[i], o);
+      a.out[bh * d + j] = o * norm;
+    }
+    return;
+  }
+  const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob + a.vcb.off_d);
   for (int h = 1; h < d; h <<= 1) {
     for (int q = tid; q < d / 2; q += kBlock) {
       int i = (q / h) * 2 * h + (q % h);
@@ -857,7 +873,6 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
     }
     __syncthreads();
   }
-  const float norm = l > 0.0f ? 1.0f / ((float)d * l) : 0.0f;
   for (int j = tid; j < d; j += kBlock) {
     const float o = v[j] * norm;
     a.out[bh * d + j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -o : o;
@@ -884,10 +899,11 @@ int launch_attend_mfma(const MfmaPartArgs& pa, int64_t blocks, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
-// MFMA partials: Walsh-Hadamard values with k <= 3, head_dim a multiple of 32,
-// an even GQA grouping of at most 8 query heads, and the LDS plan within 150 KB.
+// MFMA partials (in the rotated domain, so for either rotation): values with
+// k <= 3, head_dim a multiple of 32, an even GQA grouping of at most 8 query
+// heads, and the LDS plan within 150 KB.
 bool attend_mfma_supported(const CodebookArgs& vcb, int64_t Hkv, int64_t Hq) {
-  if (vcb.rotation != kRotHadamard || vcb.k < 1 || vcb.k > 3 || vcb.d < 32 || (vcb.d & 31) != 0) return false;
+  if (vcb.k < 1 || vcb.k > 3 || vcb.d < 32 || (vcb.d & 31) != 0) return false;
   if (Hkv <= 0 || Hq % Hkv != 0 || Hq / Hkv > 8) return false;
   const int W = vcb.plane_words, masks = 1 << (vcb.k - 1);
   const int wpw = (W + 3) / 4;
@@ -1003,8 +1019,12 @@ int launch_attend_fused(const CodebookArgs& kcb, const CodebookArgs& vcb, const 
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
+// Chunk partials and merge: eight coordinates per lane in the partials, pairs
+// in the merge, so head_dim a multiple of 8 (any power of two from 8 for the
+// Walsh-Hadamard rotation).
 bool attend_split_supported(const CodebookArgs& vcb) {
-  return vcb.rotation == kRotHadamard && vcb.d >= 8 && vcb.d <= kMaxHeadDim && vcb.k >= 1 && vcb.k <= 8;
+  return (vcb.rotation == kRotHadamard || vcb.rotation == kRotHaar) && vcb.d >= 8 && vcb.d % 8 == 0 &&
+         vcb.d <= kMaxHeadDim && vcb.k >= 1 && vcb.k <= 8;
 }
 
 int launch_attend_split(const CodebookArgs& vcb, const uint32_t* vrec, const float* scores, int64_t B,

@@ -126,7 +126,7 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
   if (threadIdx.x == 0 && a.status) {
     const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(blob);
     if (hd->magic != kBlobMagic || hd->version != kBlobVersion || hd->head_dim != kD || hd->bits != a.bits ||
-        hd->role != a.role || hd->projections != (KEY ? kM : 0))
+        hd->role != a.role || hd->projections != (KEY ? kM : 0) || (int)hd->rotation != kRotHadamard)
       atomicOr(a.status, TQ_STATUS_BAD_BLOB);
   }
   build_hfrag<DT == 2>(hfrag, reinterpret_cast<const uint32_t*>(blob + a.off_d));
@@ -476,7 +476,7 @@ int launch_dt(const Enc128Args& a, int dt, hipStream_t s) {
 }  // namespace
 
 bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N) {
-  if (L.d != kD) return false;
+  if (L.d != kD || L.rotation != kRotHadamard) return false;
   if (N > (int64_t(1) << 30) / (4 * L.rec_words)) return false;   // 32-bit buffer offsets per group
   if (L.role == TQ_ROLE_KEY && (L.m != kM || L.k < 1 || L.k > 3)) return false;
   if (L.role == TQ_ROLE_VALUE && (L.k < 1 || L.k > 4)) return false;

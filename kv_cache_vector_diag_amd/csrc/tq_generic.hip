@@ -437,6 +437,17 @@ __global__ __launch_bounds__(kAttendBlock) void attend_generic_kernel(AttendArgs
     acc[j] = aj;
   }
   __syncthreads();
+  const float norm = esum > 0.0f ? 1.0f / ((float)d * esum) : 0.0f;  // T == 0 gives 0
+  if (a.vcb.rotation == kRotHaar) {
+    // x^ = (n/d) R^T c: o_j = sum_i R[i][j] acc_i / (d esum), R row-major at off_d
+    const float* R = reinterpret_cast<const float*>(blob + a.vcb.off_d);
+    for (int j = tid; j < d; j += kAttendBlock) {
+      float o = 0.0f;
+      for (int i = 0; i < d; ++i) o = fmaf(R[i * d + j], acc[i], o);
+      a.out[(b * a.Hq + hq) * d + j] = o * norm;
+    }
+    return;
+  }
   for (int hh = 1; hh < d; hh <<= 1) {
     for (int pp = tid; pp < d / 2; pp += kAttendBlock) {
       int i = (pp / hh) * 2 * hh + (pp % hh);
@@ -446,7 +457,6 @@ __global__ __launch_bounds__(kAttendBlock) void attend_generic_kernel(AttendArgs
     }
     __syncthreads();
   }
-  const float norm = esum > 0.0f ? 1.0f / ((float)d * esum) : 0.0f;  // T == 0 gives 0
   for (int j = tid; j < d; j += kAttendBlock) {
     float v = acc[j] * norm;
     a.out[(b * a.Hq + hq) * d + j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -v : v;

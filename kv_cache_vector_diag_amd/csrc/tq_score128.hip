@@ -156,7 +156,7 @@ int launch_k(Score128Args a, hipStream_t s) {
 }  // namespace
 
 bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, int64_t T, const void* krec) {
-  if (L.d != kD || L.m != kM || L.k < 1 || L.k > 3) return false;
+  if (L.d != kD || L.m != kM || L.rotation != kRotHadamard || L.k < 1 || L.k > 3) return false;
   if (reinterpret_cast<uintptr_t>(krec) & 7) return false;   // records read as 8-byte chunks
   // 32-bit buffer offsets: a group's records and its [gq][T] scores stay below 2^30 bytes
   if (T > (int64_t(1) << 30) / (4 * L.rec_words) || T > (int64_t(1) << 30) / 16) return false;
