@@ -12,8 +12,9 @@ Inputs are resident in HBM before timing.  Buffers rotate (2 input caches,
 cache still holds from the previous launch.  Kernel durations come from HIP
 events on the stream the kernels are launched on.
 
-Prints ONE JSON line.  `--config c2|c4` measures the prefill-encode and the
-long-context attend rows instead (also one line each).
+Prints ONE JSON line.  `--config c2|c4|c5|haar` measures the prefill-encode, the
+long-context attend, the mixed-precision layer and the Haar-rotation rows
+instead (also one line each).
 """
 from __future__ import annotations
 
@@ -354,12 +355,72 @@ def bench_c5(args, torch, b):
                          "traffic": _traffic("encode_c5", kb), "kernel": "encode_keys (all layers)"}}
 
 
+FP64_VECTOR_PEAK_TFLOPS = 78.6     # MI355X fp64 vector: 256 CUs x 2.4 GHz x 128 flop/clk/CU
+
+
+def bench_haar(args, torch, b):
+    """Haar-QR rotation (dense R = sqrt(d) Q): encode turbo3 keys + score, d=128,
+    on a 4K-context slice of the decode-step shape.  Haar codebooks run on the
+    float64 per-vector kernels; the encode's arithmetic (rotation R x and
+    projection S rho, 2 d^2 + 2 m d flops) bounds it."""
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    B, Hkv, Hq, T, d, bits, m, seed = 16, 8, 32, 4096, 128, 3, 128, 3
+    G = B * Hkv
+    rot = b.ROT_HAAR
+    words = b.tq_record_bytes_ex(d, bits, m, b.ROLE_KEY, rot) // 4
+    kcb = b.make_codebooks(Hkv, d, bits, m, seed, b.ROLE_KEY, device=dev, rotation=rot)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d), "bf16", dev)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", dev)
+    recs = [torch.empty((G, T, words), dtype=torch.int32, device=dev) for _ in range(2)]
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    b.tq_encode_keys(kcb, Hkv, K, d, bits, m, rec=recs[1], status=status, rotation=rot)
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_encode_keys(kcb, Hkv, K, d, bits, m, rec=recs[i % 2], status=status, rotation=rot)
+        if ev:
+            ev[1].record()
+        b.tq_scores(kcb, Hkv, recs[(i + 1) % 2].view(B, Hkv, T, words), q, d, bits, m, out=scores, rotation=rot)
+        if ev:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [_events(torch, 3) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0
+    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    flops = G * T * (2 * d * d + 2 * m * d)
+    tflops = flops / (enc_ms * 1e-3) / 1e12
+    enc_bytes = G * T * (d * 2 + words * 4) + kcb.numel()
+    return {"metric": "Haar-rotation encode + score tokens/s", "value": B * T / (ms_step * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+            "data": "synthetic",
+            "config": {"workload": "Haar-QR rotation: 16 seq x 8 kv heads x 4096 tokens, d=128, bf16 N(0,1) "
+                                   "keys b=3 (128 projections), 32 query heads"},
+            "encode_ms": enc_ms, "encode_GBps": enc_bytes / (enc_ms * 1e-3) / 1e9, "score_ms": sc_ms,
+            "roofline": {"bound": "alu", "achieved": tflops, "peak": FP64_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / FP64_VECTOR_PEAK_TFLOPS, "traffic": None, "kernel": "encode_generic",
+                         "algorithmic_flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5", "haar"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -392,7 +453,7 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": reps + 1,
                                                "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}}))
         return
-    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5}[args.config]
+    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5, "haar": bench_haar}[args.config]
     line = fn(args, torch, b)
     if args.config == "c3":
         line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_c3()
