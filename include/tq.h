@@ -82,6 +82,7 @@ enum tq_status {
 #define TQ_STATUS_NON_FINITE 1
 #define TQ_STATUS_BAD_BLOB 2
 #define TQ_STATUS_BAD_CHANNEL 4   /* a channel map entry outside [0, head_dim) */
+#define TQ_STATUS_BAD_PAGE 8      /* a position or page-table entry outside the pool */
 
 enum tq_role {
   TQ_ROLE_KEY = 0,    /* TurboQuant: (bits-1)-bit Lloyd-Max + 1-bit QJL of the residual */
@@ -221,6 +222,40 @@ int tq_attend_ex(int head_dim, int k_bits, int v_bits, int projections, int rota
                  const void* krec, const void* vrec, int64_t B, int64_t H_kv, int64_t T,
                  const void* q, int q_dtype, int64_t H_q, float scale,
                  float* out, void* work, size_t work_bytes, int32_t* status, void* stream);
+
+/* ---- Streaming append into a paged compressed cache ----------------------
+ * page "fib-quant 0.1.0-beta.4 README", "Streaming KV encoder": the encoded KV
+ * tensor is built one token at a time, pages are complete when they reach
+ * tokens_per_page, and the result equals the batch encode of the same input;
+ * page "bitpolar 0.3.3 src/kv_cache.rs", MultiHeadKvCache::push_token: one
+ * token's key and value for every head at once.
+ *
+ * Pools hold pages of tokens_per_page tokens of one sequence, all H_kv heads:
+ *   kpool [num_pages][H_kv][tokens_per_page][key record words]   (uint32)
+ *   vpool [num_pages][H_kv][tokens_per_page][value record words]
+ * so that one (sequence, kv head) has its records of a page contiguous.
+ * page_table [B][max_pages] (int32, device): the pool page of each page index
+ * of sequence b; the caller maps a fresh page whenever a sequence's length
+ * reaches a multiple of tokens_per_page.  pos [B] (int32, device): the position
+ * the new token takes in sequence b.
+ *
+ * tq_append_kv encodes k_new and v_new [B][H_kv][head_dim] (contiguous; dtype
+ * as for tq_encode_keys) and writes record (b, h) to page
+ * page_table[b][pos[b] / tokens_per_page], slot pos[b] % tokens_per_page.  The
+ * records are bit-identical to tq_encode_keys / tq_encode_values on the same
+ * vectors (same kernels); codebook of (b, h) as there: (b*H_kv + h) mod n_cb.
+ * A negative position, one at or past max_pages * tokens_per_page, or a page
+ * outside [0, num_pages) writes nothing for that sequence and sets
+ * TQ_STATUS_BAD_PAGE.  `work`: caller scratch of tq_append_workspace_bytes(...)
+ * bytes.  Walsh-Hadamard codebooks. */
+size_t tq_append_workspace_bytes(int head_dim, int k_bits, int v_bits, int projections, int64_t B, int64_t H_kv);
+int tq_append_kv(int head_dim, int k_bits, int v_bits, int projections,
+                 const void* kcbs, int64_t n_kcb, const void* vcbs, int64_t n_vcb,
+                 const void* k_new, const void* v_new, int x_dtype, int64_t B, int64_t H_kv,
+                 const int32_t* pos, const int32_t* page_table, int64_t max_pages,
+                 int tokens_per_page, int64_t num_pages,
+                 void* kpool, void* vpool, void* work, size_t work_bytes,
+                 int32_t* status, void* stream);
 
 /* Test hook: u = H(D x) (unnormalised rotation) and n = |x| for every vector,
  * with the D of the group's codebook.  u [G][N][head_dim] f32, norms [G][N] f32. */

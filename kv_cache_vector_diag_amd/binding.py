@@ -30,7 +30,8 @@ EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encod
            "tq_attend", "tq_rotate", "tq_memory_stats", "tq_status_string", "tq_codebook_bytes_ex",
            "tq_record_bytes_ex", "tq_make_codebook_ex", "tq_outlier_workspace_bytes", "tq_outlier_channels",
            "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes",
-           "tq_encode_keys_ex", "tq_encode_values_ex", "tq_decode_values_ex", "tq_scores_ex", "tq_attend_ex"]
+           "tq_encode_keys_ex", "tq_encode_values_ex", "tq_decode_values_ex", "tq_scores_ex", "tq_attend_ex",
+           "tq_append_workspace_bytes", "tq_append_kv"]
 
 _lib = None
 
@@ -97,6 +98,10 @@ def load() -> ctypes.CDLL:
         "tq_attend_ex": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64,
                                  c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float,
                                  c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
+        "tq_append_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int64, c_int64]),
+        "tq_append_kv": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                 c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int, c_int64,
+                                 c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -281,6 +286,23 @@ def tq_attend(kcbs, n_kcb, vcbs, n_vcb, krec, vrec, q, head_dim, k_bits, v_bits,
         rc = load().tq_attend_ex(head_dim, k_bits, v_bits, projections, rotation, *args)
     _check(rc, "tq_attend")
     return out
+
+
+def tq_append_kv(kcbs, n_kcb, vcbs, n_vcb, k_new, v_new, head_dim, k_bits, v_bits, projections, pos, page_table,
+                 tokens_per_page, kpool, vpool, work=None, status=None):
+    """One new token per sequence, all kv heads: k_new, v_new [B][H_kv][head_dim]; pos [B] int32;
+    page_table [B][max_pages] int32; pools [num_pages][H_kv][tokens_per_page][record words] int32."""
+    import torch
+    B, Hkv = k_new.shape[0], k_new.shape[1]
+    if not (k_new.is_contiguous() and v_new.is_contiguous()) or k_new.shape[2] != head_dim:
+        raise ValueError("k_new, v_new must be contiguous [B][H_kv][head_dim]")
+    need = int(load().tq_append_workspace_bytes(head_dim, k_bits, v_bits, projections, B, Hkv))
+    if work is None:
+        work = torch.empty(max(need, 1), dtype=torch.uint8, device=k_new.device)
+    _check(load().tq_append_kv(head_dim, k_bits, v_bits, projections, _ptr(kcbs), n_kcb, _ptr(vcbs), n_vcb,
+                               _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, Hkv, _ptr(pos), _ptr(page_table),
+                               page_table.shape[1], tokens_per_page, kpool.shape[0], _ptr(kpool), _ptr(vpool),
+                               _ptr(work), work.numel(), _ptr(status), _stream(k_new)), "tq_append_kv")
 
 
 def split_codebooks(n_cb: int, head_dim: int, n_outlier: int, bits: int, seed: int, role: int, device=None):

@@ -200,6 +200,59 @@ int tq_attend_ex(int head_dim, int k_bits, int v_bits, int projections, int rota
   return launch_attend_generic(vcb, static_cast<const uint32_t*>(vrec), sc, B, H_kv, T, H_q, out, s);
 }
 
+// Scratch of tq_append_kv: the new keys' records, then (256-byte aligned) the
+// new values' records, B*H_kv of each.
+static size_t append_stage_bytes(const Layout& L, int64_t B, int64_t H_kv) {
+  return ((size_t)(B * H_kv * L.rec_words) * 4 + 255) / 256 * 256;
+}
+
+size_t tq_append_workspace_bytes(int head_dim, int k_bits, int v_bits, int projections, int64_t B, int64_t H_kv) {
+  Layout K, V;
+  if (make_layout(head_dim, k_bits, projections, TQ_ROLE_KEY, &K) ||
+      make_layout(head_dim, v_bits, 0, TQ_ROLE_VALUE, &V) || B < 0 || H_kv < 0)
+    return 0;
+  return append_stage_bytes(K, B, H_kv) + append_stage_bytes(V, B, H_kv);
+}
+
+int tq_append_kv(int head_dim, int k_bits, int v_bits, int projections, const void* kcbs, int64_t n_kcb,
+                 const void* vcbs, int64_t n_vcb, const void* k_new, const void* v_new, int x_dtype, int64_t B,
+                 int64_t H_kv, const int32_t* pos, const int32_t* page_table, int64_t max_pages,
+                 int tokens_per_page, int64_t num_pages, void* kpool, void* vpool, void* work, size_t work_bytes,
+                 int32_t* status, void* stream) {
+  Layout K, V;
+  int rc = make_layout(head_dim, k_bits, projections, TQ_ROLE_KEY, &K);
+  if (rc) return rc;
+  rc = make_layout(head_dim, v_bits, 0, TQ_ROLE_VALUE, &V);
+  if (rc) return rc;
+  if (n_kcb <= 0 || n_vcb <= 0 || B < 0 || H_kv <= 0 || num_pages < 0) return TQ_ERR_EMPTY_INPUT;
+  if (B == 0) return TQ_OK;
+  if (tokens_per_page <= 0 || max_pages <= 0) return TQ_ERR_DIMENSION_MISMATCH;
+  if (!kcbs || !vcbs || !k_new || !v_new || !pos || !page_table || !kpool || !vpool || !work) return TQ_ERR_NULL;
+  if (!dtype_ok(x_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (work_bytes < tq_append_workspace_bytes(head_dim, k_bits, v_bits, projections, B, H_kv))
+    return TQ_ERR_DIMENSION_MISMATCH;
+  uint32_t* kst = static_cast<uint32_t*>(work);
+  uint32_t* vst = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work) + append_stage_bytes(K, B, H_kv));
+  // When the codebook of (b, h) is that of h for every b (n_cb divides H_kv),
+  // the new vectors are encoded as H_kv groups of B tokens (head-major), so the
+  // batch of sequences fills the encode kernel's tiles; else one group per vector.
+  const bool head_major = H_kv % n_kcb == 0 && H_kv % n_vcb == 0;
+  const int64_t G = head_major ? H_kv : B * H_kv, N = head_major ? B : 1;
+  const int64_t sx_g = head_dim, sx_n = head_major ? H_kv * head_dim : head_dim;
+  rc = encode_common(TQ_ROLE_KEY, head_dim, k_bits, projections, kRotHadamard, kcbs, n_kcb, k_new, x_dtype, G, N,
+                     sx_g, sx_n, kst, status, stream);
+  if (rc) return rc;
+  rc = encode_common(TQ_ROLE_VALUE, head_dim, v_bits, 0, kRotHadamard, vcbs, n_vcb, v_new, x_dtype, G, N, sx_g,
+                     sx_n, vst, status, stream);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = launch_page_scatter(kst, head_major, B, H_kv, K.rec_words, pos, page_table, max_pages, tokens_per_page,
+                           num_pages, static_cast<uint32_t*>(kpool), status, s);
+  if (rc) return rc;
+  return launch_page_scatter(vst, head_major, B, H_kv, V.rec_words, pos, page_table, max_pages, tokens_per_page,
+                             num_pages, static_cast<uint32_t*>(vpool), status, s);
+}
+
 int tq_rotate(int head_dim, int bits, int projections, int role, const void* cbs, int64_t n_cb, const void* x,
               int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, float* u, float* norms,
               void* stream) {

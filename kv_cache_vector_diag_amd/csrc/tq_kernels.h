@@ -35,6 +35,12 @@ int64_t attend_chunks(int64_t T);
 // straight from the key records into the chunk partials, then the merge; `part`
 // as above.
 size_t attend_qprep_bytes(int64_t groups);
+// Paged pools: record (b, h) of `staged` ([Hkv][B] records when head_major, else
+// [B][Hkv]) to page page_table[b][pos[b] / tpp], slot pos[b] % tpp of
+// pool [num_pages][Hkv][tpp][rw]; bad positions or pages set TQ_STATUS_BAD_PAGE.
+int launch_page_scatter(const uint32_t* staged, bool head_major, int64_t B, int64_t Hkv, int rw,
+                        const int32_t* pos, const int32_t* page_table, int64_t max_pages, int tpp,
+                        int64_t num_pages, uint32_t* pool, int32_t* status, hipStream_t s);
 bool attend_fused_supported(const CodebookArgs& kcb, const CodebookArgs& vcb, int64_t Hkv, int64_t Hq, int64_t T,
                             const void* krec);
 int launch_attend_fused(const CodebookArgs& kcb, const CodebookArgs& vcb, const uint32_t* krec,
