@@ -257,6 +257,22 @@ int tq_append_kv(int head_dim, int k_bits, int v_bits, int projections,
                  void* kpool, void* vpool, void* work, size_t work_bytes,
                  int32_t* status, void* stream);
 
+/* Scores (as tq_scores) from a paged key pool filled by tq_append_kv: token t
+ * of sequence b, kv head h, is record (page_table[b][t / tokens_per_page], h,
+ * t % tokens_per_page) of kpool; every sequence has T tokens.  Scores equal
+ * tq_scores on the same records gathered in token order.  Needs head_dim 128,
+ * 128 projections, bits 2..4, 1, 2 or 4 query heads per kv head, and
+ * tokens_per_page a multiple of 32 (else TQ_ERR_UNSUPPORTED /
+ * TQ_ERR_DIMENSION_MISMATCH).  A page outside [0, num_pages) reads as zero
+ * records and sets TQ_STATUS_BAD_PAGE. */
+int tq_scores_paged(int head_dim, int bits, int projections,
+                    const void* cbs, int64_t n_cb,
+                    const void* kpool, const int32_t* page_table, int64_t max_pages,
+                    int tokens_per_page, int64_t num_pages,
+                    int64_t B, int64_t H_kv, int64_t T,
+                    const void* q, int q_dtype, int64_t H_q, float scale,
+                    float* scores, int32_t* status, void* stream);
+
 /* Test hook: u = H(D x) (unnormalised rotation) and n = |x| for every vector,
  * with the D of the group's codebook.  u [G][N][head_dim] f32, norms [G][N] f32. */
 int tq_rotate(int head_dim, int bits, int projections, int role,

@@ -31,7 +31,7 @@ EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encod
            "tq_record_bytes_ex", "tq_make_codebook_ex", "tq_outlier_workspace_bytes", "tq_outlier_channels",
            "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes",
            "tq_encode_keys_ex", "tq_encode_values_ex", "tq_decode_values_ex", "tq_scores_ex", "tq_attend_ex",
-           "tq_append_workspace_bytes", "tq_append_kv"]
+           "tq_append_workspace_bytes", "tq_append_kv", "tq_scores_paged"]
 
 _lib = None
 
@@ -99,6 +99,9 @@ def load() -> ctypes.CDLL:
                                  c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float,
                                  c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
         "tq_append_workspace_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int64, c_int64]),
+        "tq_scores_paged": (c_int, [c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_int,
+                                    c_int64, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float, c_void_p,
+                                    c_void_p, c_void_p]),
         "tq_append_kv": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
                                  c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int, c_int64,
                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
@@ -303,6 +306,21 @@ def tq_append_kv(kcbs, n_kcb, vcbs, n_vcb, k_new, v_new, head_dim, k_bits, v_bit
                                _ptr(k_new), _ptr(v_new), _dtype_code(k_new), B, Hkv, _ptr(pos), _ptr(page_table),
                                page_table.shape[1], tokens_per_page, kpool.shape[0], _ptr(kpool), _ptr(vpool),
                                _ptr(work), work.numel(), _ptr(status), _stream(k_new)), "tq_append_kv")
+
+
+def tq_scores_paged(cbs, n_cb, kpool, page_table, tokens_per_page, T, q, head_dim, bits, projections, scale=0.0,
+                    out=None, status=None):
+    """kpool [num_pages][H_kv][tokens_per_page][words], page_table [B][max_pages] -> scores [B][H_q][T]."""
+    import torch
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv = kpool.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    _check(load().tq_scores_paged(head_dim, bits, projections, _ptr(cbs), n_cb, _ptr(kpool), _ptr(page_table),
+                                  page_table.shape[1], tokens_per_page, kpool.shape[0], B, Hkv, T, _ptr(q),
+                                  _dtype_code(q), Hq, scale, _ptr(out), _ptr(status), _stream(q)),
+           "tq_scores_paged")
+    return out
 
 
 def split_codebooks(n_cb: int, head_dim: int, n_outlier: int, bits: int, seed: int, role: int, device=None):

@@ -200,6 +200,26 @@ int tq_attend_ex(int head_dim, int k_bits, int v_bits, int projections, int rota
   return launch_attend_generic(vcb, static_cast<const uint32_t*>(vrec), sc, B, H_kv, T, H_q, out, s);
 }
 
+int tq_scores_paged(int head_dim, int bits, int projections, const void* cbs, int64_t n_cb, const void* kpool,
+                    const int32_t* page_table, int64_t max_pages, int tokens_per_page, int64_t num_pages, int64_t B,
+                    int64_t H_kv, int64_t T, const void* q, int q_dtype, int64_t H_q, float scale, float* scores,
+                    int32_t* status, void* stream) {
+  Layout L;
+  int rc = make_layout(head_dim, bits, projections, TQ_ROLE_KEY, &L);
+  if (rc) return rc;
+  if (n_cb <= 0 || B < 0 || H_kv <= 0 || T < 0 || H_q <= 0 || num_pages < 0) return TQ_ERR_EMPTY_INPUT;
+  if (H_q % H_kv) return TQ_ERR_DIMENSION_MISMATCH;
+  if (B * T == 0) return TQ_OK;
+  if (tokens_per_page <= 0 || tokens_per_page % 32 || max_pages <= 0) return TQ_ERR_DIMENSION_MISMATCH;
+  if (!cbs || !kpool || !page_table || !q || !scores) return TQ_ERR_NULL;
+  if (!dtype_ok(q_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (!fast128_scores_supported(L, H_kv, H_q, T, kpool)) return TQ_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)head_dim);
+  return launch_scores_fast128(L, cbs, n_cb, static_cast<const uint32_t*>(kpool), B, H_kv, T, q, q_dtype, H_q, scale,
+                               scores, status, static_cast<hipStream_t>(stream), page_table, max_pages,
+                               tokens_per_page, num_pages);
+}
+
 // Scratch of tq_append_kv: the new keys' records, then (256-byte aligned) the
 // new values' records, B*H_kv of each.
 static size_t append_stage_bytes(const Layout& L, int64_t B, int64_t H_kv) {

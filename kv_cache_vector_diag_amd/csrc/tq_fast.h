@@ -21,6 +21,7 @@ int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
 bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, int64_t T, const void* krec);
 int launch_scores_fast128(const Layout& L, const void* cbs, int64_t n_cb, const uint32_t* krec, int64_t B,
                           int64_t Hkv, int64_t T, const void* q, int q_dtype, int64_t Hq, float scale,
-                          float* scores, int32_t* status, hipStream_t s);
+                          float* scores, int32_t* status, hipStream_t s, const int32_t* page_table = nullptr,
+                          int64_t max_pages = 0, int tpp = 0, int64_t num_pages = 0);
 
 }  // namespace tq

@@ -9,6 +9,13 @@
 #include "tq_score_core.h"
 
 namespace tq {
+
+// Scalar load through a buffer resource (s_buffer_load_dword): the page id of a
+// wave's tile is uniform, and a scalar load keeps it out of the vector memory
+// counter that orders the record loads.
+typedef int i32x4r __attribute__((ext_vector_type(4)));
+__device__ int32_t s_buffer_load_i32(i32x4r rsrc, int32_t offset, int32_t aux) __asm("llvm.amdgcn.s.buffer.load.i32");
+
 namespace {
 
 using sc128::i32x4;
@@ -34,9 +41,14 @@ struct Score128Args {
   int bits, rec_words, gq;   // gq = query heads per kv head (1, 2 or 4)
   uint32_t off_c, off_d, off_s;
   int64_t tiles, tiles_per_block, blocks_per_group;
+  // paged keys (page_table not null): krec is the pool [num_pages][Hkv][tpp][rec],
+  // token t of (b, h) in page page_table[b * max_pages + t / tpp], slot t % tpp
+  const int32_t* page_table;
+  int64_t max_pages, num_pages;
+  int tpp;
 };
 
-template <int K>
+template <int K, bool PAGED>
 __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Args a) {
   using Mk = Masks<K>;
   constexpr int kBlock = block_threads<K>();
@@ -86,9 +98,31 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   constexpr int kPrefetch = 2;
   uint2 raw[kPrefetch][NCH];
   const int64_t rec_end = min(tile_end * 32, a.T);
+  bool bad_page = false;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(a.krec + grp * a.T * RW), 0, (int)(rec_end * RW * 4), kRsrcWord3);
+  // paged: this sequence's row of the page table as a scalar buffer
+  const uint64_t ptab = reinterpret_cast<uint64_t>(a.page_table + b * a.max_pages);
+  const i32x4r prow = {(int)(uint32_t)ptab, (int)((uint32_t)(ptab >> 32) & 0xFFFFu), (int)(a.max_pages * 4),
+                       kRsrcWord3};
   const auto load_raw = [&](int64_t t, uint2* rw) {
+    if constexpr (PAGED) {
+      // a tile lies in one page (tpp a multiple of 32): a resource per tile,
+      // ending at the tile's last valid record; a bad page reads nothing
+      const int64_t tok = t * 32;
+      const int64_t nrec = rec_end - tok < 0 ? 0 : (rec_end - tok < 32 ? rec_end - tok : 32);
+      const int64_t pi = tok / a.tpp;
+      const int64_t page = nrec > 0 && pi < a.max_pages ? s_buffer_load_i32(prow, (int)(pi * 4), 0) : 0;
+      const bool ok = page >= 0 && page < a.num_pages;
+      bad_page |= !ok && nrec > 0;                 // reported once, at the end
+      const uint32_t* base = a.krec + ((ok ? page : 0) * a.Hkv + hkv) * a.tpp * RW + (tok % a.tpp) * RW;
+      const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint32_t*>(base), 0, ok ? (int)(nrec * RW * 4) : 0, kRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        rw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(prs, 8u * lane + 512u * i, 0, 0));
+      return;
+    }
     const uint32_t base = (uint32_t)(t * 32 * RW * 4) + 8u * lane;
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
@@ -136,10 +170,12 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sb2), srs, so + (uint32_t)(hb * a.T * 4), 0, 0);
     }
   }
+  if (bad_page && lane == 0 && a.status) atomicOr(a.status, TQ_STATUS_BAD_PAGE);
 }
 
 template <int K>
 int launch_k(Score128Args a, hipStream_t s) {
+  const auto kern = a.page_table ? score128_kernel<K, true> : score128_kernel<K, false>;
   constexpr int kWaves = block_threads<K>() / 64;
   // about one workgroup of 16 waves per CU, at least 16 tiles per wave
   const int64_t groups = a.B * a.Hkv;
@@ -149,7 +185,7 @@ int launch_k(Score128Args a, hipStream_t s) {
   a.tiles_per_block = per_block;
   a.blocks_per_group = (a.tiles + per_block - 1) / per_block;
   const int64_t blocks = groups * a.blocks_per_group;
-  hipLaunchKernelGGL(score128_kernel<K>, dim3((unsigned)blocks), dim3(block_threads<K>()), 0, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(block_threads<K>()), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
@@ -166,8 +202,13 @@ bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, int64_t 
 
 int launch_scores_fast128(const Layout& L, const void* cbs, int64_t n_cb, const uint32_t* krec, int64_t B,
                           int64_t Hkv, int64_t T, const void* q, int q_dtype, int64_t Hq, float scale,
-                          float* scores, int32_t* status, hipStream_t s) {
+                          float* scores, int32_t* status, hipStream_t s, const int32_t* page_table, int64_t max_pages,
+                          int tpp, int64_t num_pages) {
   Score128Args a;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.num_pages = num_pages;
+  a.tpp = tpp;
   a.cbs = static_cast<const uint8_t*>(cbs);
   a.stride = L.total;
   a.n_cb = n_cb;

@@ -10,7 +10,7 @@ import pytest
 from kv_cache_vector_diag_amd import inputs
 from oracle import turboquant as tq
 
-from .parity import check_mismatch_fraction, compare_records, rec_np
+from .parity import assert_close, check_mismatch_fraction, compare_records
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -105,3 +105,32 @@ def test_append_bad_position_or_page_is_flagged(gpu_lib):
         allowed = {int(table[bb, pos_list[bb] // P]) for bb in range(B)
                    if 0 <= pos_list[bb] < 2 * P and 0 <= int(table[bb, pos_list[bb] // P]) < 5}
         assert set(changed) <= allowed
+
+
+@pytest.mark.parametrize("kb,B,Hkv,Hq,T,P", [(3, 3, 4, 8, 300, 64), (2, 2, 2, 2, 97, 32), (4, 1, 2, 8, 1100, 256)])
+def test_scores_from_paged_pool_equal_contiguous(gpu_lib, kb, B, Hkv, Hq, T, P):
+    """tq_scores_paged over the streamed pool gives the scores of tq_scores over
+    the batch-encoded records (the same kernel, addressed through the pages)."""
+    import torch
+    b = gpu_lib
+    d = 128
+    K, V, kg, vg, kbatch, vbatch, kpool, table = _stream(b, d, kb, 2, 128, B, Hkv, T, P, Hkv, Hkv, "bf16", seed=41)
+    assert np.array_equal(kg.view(np.uint32), kbatch.view(np.uint32))
+    kcb = b.make_codebooks(Hkv, d, kb, 128, 41, b.ROLE_KEY, device=DEV)
+    q = inputs.to_torch(inputs.queries(41, B, Hq, d), "bf16", DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    sp = b.tq_scores_paged(kcb, Hkv, kpool, table, P, T, q, d, kb, 128, status=st)
+    sc = b.tq_scores(kcb, Hkv, torch.from_numpy(kbatch).to(DEV), q, d, kb, 128)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(sp, sc)
+    ref = tq.scores([tq.Quantizer(d, kb, 128, 41 + h, tq.ROLE_KEY) for h in range(Hkv)], kbatch.view(np.uint32),
+                    inputs.exact_values(q))
+    assert_close(sp.cpu().numpy(), ref, "paged scores")
+    # a page outside the pool: flagged, its tokens read as zero records
+    bad = table.clone()
+    bad[0, 0] = kpool.shape[0] + 5
+    st.zero_()
+    b.tq_scores_paged(kcb, Hkv, kpool, bad, P, T, q, d, kb, 128, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 8
