@@ -12,9 +12,9 @@ Inputs are resident in HBM before timing.  Buffers rotate (2 input caches,
 cache still holds from the previous launch.  Kernel durations come from HIP
 events on the stream the kernels are launched on.
 
-Prints ONE JSON line.  `--config c2|c4|c5|haar` measures the prefill-encode, the
-long-context attend, the mixed-precision layer and the Haar-rotation rows
-instead (also one line each).
+Prints ONE JSON line.  `--config c2|c4|c5|haar|paged` measures the
+prefill-encode, the long-context attend, the mixed-precision layer, the
+Haar-rotation and the paged-cache decode rows instead (also one line each).
 """
 from __future__ import annotations
 
@@ -355,6 +355,79 @@ def bench_c5(args, torch, b):
                          "traffic": _traffic("encode_c5", kb), "kernel": "encode_keys (all layers)"}}
 
 
+def bench_paged(args, torch, b):
+    """Paged decode step at the 32K-context shape: append one token (key and
+    value, every kv head of every sequence) into pages of 256 tokens, then score
+    32 query heads against the 32768 paged keys of each sequence."""
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    B, Hkv, Hq, T, d, kb, vb, m, P, seed = 16, 8, 32, 32768, 128, 3, 3, 128, 256, 3
+    G = B * Hkv
+    kw = b.tq_record_bytes(d, kb, m, b.ROLE_KEY) // 4
+    vw = b.tq_record_bytes(d, vb, 0, b.ROLE_VALUE) // 4
+    kcb = b.make_codebooks(Hkv, d, kb, m, seed, b.ROLE_KEY, device=dev)
+    vcb = b.make_codebooks(Hkv, d, vb, 0, seed + 1, b.ROLE_VALUE, device=dev)
+    max_pages = T // P + 1
+    num_pages = B * max_pages
+    # pool pages in a shuffled order; the cached keys placed by batch encode (set-up, untimed)
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+    table = perm.view(B, max_pages).to(dev)
+    # two pools, alternated, so that the memory-side cache cannot serve one step from the previous
+    kpools = [torch.empty((num_pages, Hkv, P, kw), dtype=torch.int32, device=dev) for _ in range(2)]
+    vpools = [torch.empty((num_pages, Hkv, P, vw), dtype=torch.int32, device=dev) for _ in range(2)]
+    for i in range(2):
+        K = inputs.to_torch(inputs.kv_normal(seed + i, G, T, d), "bf16", dev)
+        krec = b.tq_encode_keys(kcb, Hkv, K, d, kb, m).view(B, Hkv, T // P, P, kw)
+        del K
+        kpools[i][table[:, : T // P].reshape(-1).long()] = krec.permute(0, 2, 1, 3, 4).reshape(-1, Hkv, P, kw)
+        del krec
+    kn = inputs.to_torch(inputs.kv_normal(seed + 5, B, Hkv, d), "bf16", dev).contiguous()
+    vn = inputs.to_torch(inputs.kv_normal(seed + 6, B, Hkv, d), "bf16", dev).contiguous()
+    pos = torch.full((B,), T, dtype=torch.int32, device=dev)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", dev)
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    work = torch.empty(b.load().tq_append_workspace_bytes(d, kb, vb, m, B, Hkv), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_append_kv(kcb, Hkv, vcb, Hkv, kn, vn, d, kb, vb, m, pos, table, P, kpools[i % 2], vpools[i % 2],
+                       work=work, status=status)
+        if ev:
+            ev[1].record()
+        b.tq_scores_paged(kcb, Hkv, kpools[i % 2], table, P, T, q, d, kb, m, out=scores, status=status)
+        if ev:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [_events(torch, 3) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0
+    ap_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    sc_bytes = G * T * kw * 4 + B * Hq * T * 4 + q.numel() * 2 + kcb.numel()
+    ap_bytes = G * (2 * d * 2 + (kw + vw) * 4) * 2        # vectors in, records staged out and in, pool writes
+    return {"metric": "paged decode step tokens/s (append one token per sequence + score the paged 32K context)",
+            "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "paged cache: 16 seq x 8 kv heads x 32768 tokens in pages of 256, d=128, turbo3 "
+                                   "keys + 3-bit values appended, 32 bf16 query heads scored"},
+            "append_us": ap_ms * 1e3, "append_tokens_per_s": G / (ap_ms * 1e-3), "append_bytes": ap_bytes,
+            "score_ms": sc_ms,
+            "roofline": {"bound": "hbm", "achieved": sc_bytes / (sc_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": sc_bytes / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
+                         "kernel": "score (paged)", "algorithmic_bytes_per_launch": sc_bytes}}
+
+
 FP64_VECTOR_PEAK_TFLOPS = 78.6     # MI355X fp64 vector: 256 CUs x 2.4 GHz x 128 flop/clk/CU
 
 
@@ -420,7 +493,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5", "haar"])
+    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5", "haar", "paged"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -453,7 +526,8 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": reps + 1,
                                                "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}}))
         return
-    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5, "haar": bench_haar}[args.config]
+    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5, "haar": bench_haar,
+          "paged": bench_paged}[args.config]
     line = fn(args, torch, b)
     if args.config == "c3":
         line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_c3()
