@@ -442,7 +442,9 @@ __global__ __launch_bounds__(kFBlock) void attend_qprep_kernel(QprepArgs a) {
   const sc128::QuerySrc src{reinterpret_cast<const float*>(kblob + a.kcb.off_c),
                             reinterpret_cast<const uint32_t*>(kblob + a.kcb.off_d),
                             reinterpret_cast<const _Float16*>(kblob + a.kcb.off_s),
-                            a.q, a.q_dtype, ((b * a.Hq) + hkv * a.gq) * sc128::kD, a.gq};
+                            a.q, a.q_dtype, ((b * a.Hq) + hkv * a.gq) * sc128::kD, a.gq,
+                            a.kcb.rotation == kRotHaar ? reinterpret_cast<const float*>(kblob + a.kcb.off_d)
+                                                       : nullptr};
   sc128::QueryRegs<KK> qr;
   sc128::query_load<KK>(src, qr, tid, wave, lane);
   sc128::query_build<KK, kFBlock>(qs, qr, a.gq, tid, wave, lane);
@@ -949,14 +951,15 @@ int launch_fused(const FusedArgs& fa, int64_t blocks, hipStream_t s) {
 
 size_t attend_qprep_bytes(int64_t groups) { return (size_t)groups * kQprepBytes; }
 
-// Fused path: head_dim 128, 128 projections, Walsh-Hadamard rotations, key and
+// Fused path: head_dim 128, 128 projections, Walsh-Hadamard or Haar rotations, key and
 // value codebooks of k <= 3 planes, 1, 2 or 4 query heads per kv head, 8-byte
 // aligned key records, and a group's key and value records under 2^30 bytes
 // (32-bit buffer offsets).
 bool attend_fused_supported(const CodebookArgs& kcb, const CodebookArgs& vcb, int64_t Hkv, int64_t Hq, int64_t T,
                             const void* krec) {
-  if (kcb.d != 128 || kcb.m != 128 || kcb.rotation != kRotHadamard || kcb.k < 1 || kcb.k > 3) return false;
-  if (vcb.d != 128 || vcb.rotation != kRotHadamard || vcb.k < 1 || vcb.k > 3) return false;
+  const auto rot_ok = [](int r) { return r == kRotHadamard || r == kRotHaar; };
+  if (kcb.d != 128 || kcb.m != 128 || !rot_ok(kcb.rotation) || kcb.k < 1 || kcb.k > 3) return false;
+  if (vcb.d != 128 || !rot_ok(vcb.rotation) || vcb.k < 1 || vcb.k > 3) return false;
   if (reinterpret_cast<uintptr_t>(krec) & 7) return false;
   if (T + kChunk > (int64_t(1) << 30) / (4 * (kcb.rec_words > vcb.rec_words ? kcb.rec_words : vcb.rec_words)))
     return false;

@@ -39,9 +39,9 @@ constexpr int kD = 128;
 constexpr int kM = 128;
 // Waves per workgroup (one workgroup per CU): 12 (three per SIMD) where the
 // kernel fits in 168 VGPRs, else 8 (two per SIMD, up to 256 VGPRs).
-template <int K, bool KEY, int DT>
+template <int K, bool KEY, int DT, bool HAAR>
 constexpr int waves_for() {
-  return (DT == 0 || (KEY && (K == 3 || (K == 2 && DT == 2)))) ? 8 : 12;
+  return (DT == 0 || (HAAR && DT == 2) || (KEY && (K == 3 || (K == 2 && DT == 2)))) ? 8 : 12;
 }
 constexpr int kTile = 32;
 
@@ -87,6 +87,57 @@ __device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
   }
 }
 
+// bf16 round-to-nearest-even of a float (bit pattern in the low 16 bits).
+__device__ inline uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Haar rotation (R = sqrt(d) Q, float32 in the blob): u = R x as 96 MFMA products
+// per 32-key tile.  R is split into three 16-bit terms so that every product
+// with an exact 16-bit input is exact and the fp32 sums carry R to 24 bits or
+// more.  bf16 (bf16 inputs): R = t0 + t1 + t2, each term the bf16 rounding of
+// what is left.  f16 (f16 inputs): R = t0 + 2^-12 (t1 + t2), the two low terms
+// scaled up by 2^12 to stay clear of the f16 subnormals; their products go to
+// a second accumulator that is scaled back once per output block.
+// Fragment (t, M, c), lane l: A[rho][k] = t_t of R[32M + tile_row_index(rho)][16c + 8(l/32) + e].
+template <bool F16>
+__device__ uint32_t r_term(float r, int t) {
+  if (F16) {
+    const _Float16 h0 = (_Float16)r;
+    const float e1 = r - (float)h0;                        // exact
+    const _Float16 h1 = (_Float16)(e1 * 4096.0f);
+    const float e2 = e1 - (float)h1 * (1.0f / 4096.0f);    // exact
+    const _Float16 h2 = (_Float16)(e2 * 4096.0f);
+    const _Float16 hv = t == 0 ? h0 : (t == 1 ? h1 : h2);
+    return __builtin_bit_cast(uint16_t, hv);
+  }
+  const uint32_t b0 = f32_to_bf16_rne(r);
+  const float e1 = r - __uint_as_float(b0 << 16);
+  const uint32_t b1 = f32_to_bf16_rne(e1);
+  const uint32_t b2 = f32_to_bf16_rne(e1 - __uint_as_float(b1 << 16));
+  return t == 0 ? b0 : (t == 1 ? b1 : b2);
+}
+
+template <bool F16>
+__device__ void build_rfrag(u32x4* rfrag, const float* R) {
+  for (int f = threadIdx.x; f < 96 * 64; f += blockDim.x) {
+    const int lane = f & 63, c = (f >> 6) & 7, M = (f >> 9) & 3, t = f >> 11;
+    const int row = 32 * M + tile_row_index(lane & 31);
+    u32x4 v;
+    for (int q = 0; q < 4; ++q) {
+      uint32_t word = 0;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;
+        word |= r_term<F16>(R[row * kD + col], t) << (16 * hh);
+      }
+      v[q] = word;
+    }
+    rfrag[f] = v;
+  }
+}
+
 // S fragments (A operand of MFMA#2): fragment (Mp, c), lane l: row rho = l%32 is
 // projection 32Mp + tile_row_index(rho); element e: S[proj][qjl_coord(c, l/32, e)].
 __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
@@ -103,20 +154,20 @@ __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
   }
 }
 
-// bf16 round-to-nearest-even of a float (bit pattern in the low 16 bits).
-__device__ inline uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
-template <int K, bool KEY, int DT>
-__global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kernel(Enc128Args a) {
-  constexpr int kWaves = waves_for<K, KEY, DT>();
+// LDS of encode128_kernel: rotation fragments, S fragments (keys), constants.
+template <bool KEY, bool HAAR>
+constexpr size_t enc_lds_bytes() { return (HAAR ? 98304 : 32768) + (KEY ? 32768 : 0) + 128; }
+
+template <int K, bool KEY, int DT, bool HAAR>
+__global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode128_kernel(Enc128Args a) {
+  constexpr int kWaves = waves_for<K, KEY, DT, HAAR>();
+  constexpr int kRotBytes = HAAR ? 98304 : 32768;
+  static_assert(!HAAR || DT != 0, "the Haar rotation takes 16-bit inputs");
   extern __shared__ __align__(16) uint8_t smem[];
-  u32x4* hfrag = reinterpret_cast<u32x4*>(smem);                // 32 KB
-  u32x4* sfrag = reinterpret_cast<u32x4*>(smem + 32768);        // 32 KB (keys)
-  float* consts = reinterpret_cast<float*>(smem + (KEY ? 65536 : 32768));
+  u32x4* hfrag = reinterpret_cast<u32x4*>(smem);                // rotation: 8 (Hadamard) or 96 (Haar) fragments
+  u32x4* sfrag = reinterpret_cast<u32x4*>(smem + kRotBytes);    // 32 KB (keys)
+  float* consts = reinterpret_cast<float*>(smem + kRotBytes + (KEY ? 32768 : 0));
 
   constexpr int L = 1 << K;
   constexpr int NT = L / 2 - 1;  // positive thresholds
@@ -126,10 +177,14 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
   if (threadIdx.x == 0 && a.status) {
     const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(blob);
     if (hd->magic != kBlobMagic || hd->version != kBlobVersion || hd->head_dim != kD || hd->bits != a.bits ||
-        hd->role != a.role || hd->projections != (KEY ? kM : 0) || (int)hd->rotation != kRotHadamard)
+        hd->role != a.role || hd->projections != (KEY ? kM : 0) ||
+        (int)hd->rotation != (HAAR ? kRotHaar : kRotHadamard))
       atomicOr(a.status, TQ_STATUS_BAD_BLOB);
   }
-  build_hfrag<DT == 2>(hfrag, reinterpret_cast<const uint32_t*>(blob + a.off_d));
+  if constexpr (HAAR)
+    build_rfrag<DT == 2>(hfrag, reinterpret_cast<const float*>(blob + a.off_d));
+  else
+    build_hfrag<DT == 2>(hfrag, reinterpret_cast<const uint32_t*>(blob + a.off_d));
   if (KEY) build_sfrag(sfrag, reinterpret_cast<const uint16_t*>(blob + a.off_s));
   if (threadIdx.x < L / 2) consts[threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_c)[L / 2 + threadIdx.x];
   if (threadIdx.x < NT) consts[16 + threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_t)[L / 2 + threadIdx.x];
@@ -219,8 +274,36 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
     f32x16 u[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) u[p] = f32x16{};
+    if constexpr (HAAR) {
+      // u[M] = sum over K-chunks c and terms t of fragment (t, M, c) x chunk c
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
+      for (int M = 0; M < 4; ++M) {
+        f32x16 lo{};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+#pragma unroll
+          for (int t = 0; t < 3; ++t) {
+            const u32x4 rf = hfrag[((t * 4 + M) * 8 + c) * 64 + lane];
+            if (DT == 2) {
+              if (t == 0)
+                u[M] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(rf), as<f16x8>(xb[c]), u[M], 0, 0, 0);
+              else
+                lo = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(rf), as<f16x8>(xb[c]), lo, 0, 0, 0);
+            } else {
+              u[M] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(rf), as<bf16x8>(xb[c]), u[M], 0, 0, 0);
+            }
+          }
+          // keep the compiler from hoisting all fragment reads ahead of the products
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (DT == 2) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) u[M][r] = fmaf(lo[r], 1.0f / 4096.0f, u[M][r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c2 = 0; c2 < (HAAR ? 0 : 2); ++c2) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int c = 2 * p + c2;
@@ -237,7 +320,7 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
       }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < (HAAR ? 0 : 16); ++r) {
       const float a0 = u[0][r] + u[1][r], b0 = u[0][r] - u[1][r];
       const float a1 = u[2][r] + u[3][r], b1 = u[2][r] - u[3][r];
       u[0][r] = a0 + a1;    // M = 0: + + + +
@@ -441,9 +524,9 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT>())) void encode128_kern
   }
 }
 
-template <int K, bool KEY, int DT>
+template <int K, bool KEY, int DT, bool HAAR>
 int launch_one(Enc128Args a, hipStream_t s) {
-  constexpr int kWaves = waves_for<K, KEY, DT>();
+  constexpr int kWaves = waves_for<K, KEY, DT, HAAR>();
   // ~256 workgroups (one per CU) in total, at least 8 tiles per wave, never more
   // than the group holds; a multiple of the wave count
   int64_t per_block = (a.tiles_per_group * a.G + 255) / 256;
@@ -452,31 +535,34 @@ int launch_one(Enc128Args a, hipStream_t s) {
   if (per_block > a.tiles_per_group) per_block = (a.tiles_per_group + kWaves - 1) / kWaves * kWaves;
   a.tiles_per_block = per_block;
   a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
-  const size_t lds = (KEY ? 65536 : 32768) + 128;
+  const size_t lds = enc_lds_bytes<KEY, HAAR>();
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_kernel<K, KEY, DT>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_kernel<K, KEY, DT, HAAR>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return -10;
     attr_set = true;
   }
   const int64_t blocks = a.G * a.blocks_per_group;
-  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT>), dim3((unsigned)blocks), dim3(64 * waves_for<K, KEY, DT>()), lds,
-                     s, a);
+  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT, HAAR>), dim3((unsigned)blocks),
+                     dim3(64 * waves_for<K, KEY, DT, HAAR>()), lds, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
 template <int K, bool KEY>
-int launch_dt(const Enc128Args& a, int dt, hipStream_t s) {
-  if (dt == TQ_BF16) return launch_one<K, KEY, 1>(a, s);
-  if (dt == TQ_F16) return launch_one<K, KEY, 2>(a, s);
-  return launch_one<K, KEY, 0>(a, s);
+int launch_dt(const Enc128Args& a, int dt, bool haar, hipStream_t s) {
+  if (haar) return dt == TQ_F16 ? launch_one<K, KEY, 2, true>(a, s) : launch_one<K, KEY, 1, true>(a, s);
+  if (dt == TQ_BF16) return launch_one<K, KEY, 1, false>(a, s);
+  if (dt == TQ_F16) return launch_one<K, KEY, 2, false>(a, s);
+  return launch_one<K, KEY, 0, false>(a, s);
 }
 
 }  // namespace
 
 bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N) {
-  if (L.d != kD || L.rotation != kRotHadamard) return false;
+  if (L.d != kD) return false;
+  // Haar: 16-bit inputs (their products with 16-bit terms of R are exact)
+  if (L.rotation != kRotHadamard && !(L.rotation == kRotHaar && dtype != TQ_F32)) return false;
   if (N > (int64_t(1) << 30) / (4 * L.rec_words)) return false;   // 32-bit buffer offsets per group
   if (L.role == TQ_ROLE_KEY && (L.m != kM || L.k < 1 || L.k > 3)) return false;
   if (L.role == TQ_ROLE_VALUE && (L.k < 1 || L.k > 4)) return false;
@@ -499,14 +585,15 @@ int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
   a.off_c = L.off_c; a.off_t = L.off_t; a.off_d = L.off_d; a.off_s = L.off_s;
   a.tiles_per_group = (N + kTile - 1) / kTile;
   const bool key = L.role == TQ_ROLE_KEY;
+  const bool haar = L.rotation == kRotHaar;
   switch (L.k * 2 + (key ? 1 : 0)) {
-    case 1 * 2 + 1: return launch_dt<1, true>(a, dtype, s);
-    case 2 * 2 + 1: return launch_dt<2, true>(a, dtype, s);
-    case 3 * 2 + 1: return launch_dt<3, true>(a, dtype, s);
-    case 1 * 2: return launch_dt<1, false>(a, dtype, s);
-    case 2 * 2: return launch_dt<2, false>(a, dtype, s);
-    case 3 * 2: return launch_dt<3, false>(a, dtype, s);
-    case 4 * 2: return launch_dt<4, false>(a, dtype, s);
+    case 1 * 2 + 1: return launch_dt<1, true>(a, dtype, haar, s);
+    case 2 * 2 + 1: return launch_dt<2, true>(a, dtype, haar, s);
+    case 3 * 2 + 1: return launch_dt<3, true>(a, dtype, haar, s);
+    case 1 * 2: return launch_dt<1, false>(a, dtype, haar, s);
+    case 2 * 2: return launch_dt<2, false>(a, dtype, haar, s);
+    case 3 * 2: return launch_dt<3, false>(a, dtype, haar, s);
+    case 4 * 2: return launch_dt<4, false>(a, dtype, haar, s);
     default: return -13;
   }
 }

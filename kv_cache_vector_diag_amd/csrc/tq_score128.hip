@@ -39,6 +39,7 @@ struct Score128Args {
   float* scores;
   int32_t* status;
   int bits, rec_words, gq;   // gq = query heads per kv head (1, 2 or 4)
+  int rotation;              // kRotHadamard or kRotHaar
   uint32_t off_c, off_d, off_s;
   int64_t tiles, tiles_per_block, blocks_per_group;
   // paged keys (page_table not null): krec is the pool [num_pages][Hkv][tpp][rec],
@@ -68,13 +69,14 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   if (tid == 0 && a.status) {
     const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(blob);
     if (hd->magic != kBlobMagic || hd->version != kBlobVersion || hd->head_dim != kD || hd->bits != a.bits ||
-        hd->role != TQ_ROLE_KEY || hd->projections != kM || (int)hd->rotation != kRotHadamard)
+        hd->role != TQ_ROLE_KEY || hd->projections != kM || (int)hd->rotation != a.rotation)
       atomicOr(a.status, TQ_STATUS_BAD_BLOB);
   }
   const sc128::QuerySrc src{reinterpret_cast<const float*>(blob + a.off_c),
                             reinterpret_cast<const uint32_t*>(blob + a.off_d),
                             reinterpret_cast<const _Float16*>(blob + a.off_s),
-                            a.q, a.q_dtype, ((b * a.Hq) + hkv * a.gq) * kD, a.gq};
+                            a.q, a.q_dtype, ((b * a.Hq) + hkv * a.gq) * kD, a.gq,
+                            a.rotation == kRotHaar ? reinterpret_cast<const float*>(blob + a.off_d) : nullptr};
   sc128::QueryRegs<K> qr;
   sc128::query_load<K>(src, qr, tid, wave, lane);
   __builtin_amdgcn_sched_barrier(0);
@@ -192,7 +194,8 @@ int launch_k(Score128Args a, hipStream_t s) {
 }  // namespace
 
 bool fast128_scores_supported(const Layout& L, int64_t Hkv, int64_t Hq, int64_t T, const void* krec) {
-  if (L.d != kD || L.m != kM || L.rotation != kRotHadamard || L.k < 1 || L.k > 3) return false;
+  if (L.d != kD || L.m != kM || L.k < 1 || L.k > 3) return false;
+  if (L.rotation != kRotHadamard && L.rotation != kRotHaar) return false;
   if (reinterpret_cast<uintptr_t>(krec) & 7) return false;   // records read as 8-byte chunks
   // 32-bit buffer offsets: a group's records and its [gq][T] scores stay below 2^30 bytes
   if (T > (int64_t(1) << 30) / (4 * L.rec_words) || T > (int64_t(1) << 30) / 16) return false;
@@ -220,6 +223,7 @@ int launch_scores_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
   a.status = status;
   a.bits = L.bits; a.rec_words = L.rec_words; a.gq = (int)(Hq / Hkv);
   a.off_c = L.off_c; a.off_d = L.off_d; a.off_s = L.off_s;
+  a.rotation = L.rotation;
   a.tiles = (T + 31) / 32;
   switch (L.k) {
     case 1: return launch_k<1>(a, s);

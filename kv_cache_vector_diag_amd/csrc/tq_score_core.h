@@ -7,7 +7,7 @@
 // 1/sqrt(head_dim); page "turboquant-plus-rs 0.1.0 README", "Architecture":
 // MSE stage + QJL residual correction):
 //   s = scale * ( (n_t/d) sum_j qt_j c[idx_tj] + sqrt(pi/2)/m gamma_t sum_i p_i (2 s_ti - 1) ),
-//   qt = H(D q), p = S qt / sqrt(d).
+//   qt = H(D q) (Haar codebooks: qt = R q), p = S qt / sqrt(d).
 // No key is decoded.  The Lloyd-Max codebook is symmetric, so with
 // sigma_p = 2 b_p - 1 (b_p = bit-plane p of idx)
 //   c[idx] = sum over odd subsets P of planes of a_P * prod_{p in P} sigma_p,
@@ -81,6 +81,7 @@ struct QuerySrc {
   int q_dtype;
   int64_t q_off;                       // element offset of the group's first query head
   int gq;                              // query heads of the group (1, 2 or 4)
+  const float* R;                      // Haar codebooks: R = sqrt(d) Q [d][d] (dbits unused); else null
 };
 
 // Query-side loads, issued first: waves 0-3 take head `wave` (coordinates lane
@@ -90,6 +91,7 @@ template <int K>
 struct QueryRegs {
   float q0 = 0.0f, q1 = 0.0f;
   uint32_t d0 = 0, d1 = 0;
+  const float* R = nullptr;
   uint4 srow[4];
   float cv[1 << K];
 };
@@ -100,9 +102,12 @@ __device__ inline void query_load(const QuerySrc& src, QueryRegs<K>& r, int tid,
     const int64_t off = src.q_off + (int64_t)wave * kD + lane;
     r.q0 = load_elem(src.q, src.q_dtype, off);
     r.q1 = load_elem(src.q, src.q_dtype, off + 64);
-    r.d0 = src.dbits[lane >> 5];
-    r.d1 = src.dbits[2 + (lane >> 5)];
+    if (!src.R) {
+      r.d0 = src.dbits[lane >> 5];
+      r.d1 = src.dbits[2 + (lane >> 5)];
+    }
   }
+  r.R = src.R;
   if (wave < kPWaves) {
     const int prow = tid >> 2, qtr = tid & 3;
     const uint4* row = reinterpret_cast<const uint4*>(src.S + prow * kD + 32 * qtr);
@@ -138,7 +143,50 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
     s.coef[tid] = (float)(acc / L);
     if (tid == 0) s.cmax = r.cv[L - 1];
   }
-  if (wave < 4) {
+  if (r.R) {
+    // Haar: qt = R q as a dense product.  The queries pass through s.pp (free
+    // until step 2); threads 4i .. 4i+3 own row i of R, a quarter of it each,
+    // all four heads, then a 4-lane reduction as in step 2.
+    if (wave < 4) {
+      s.pp[wave][lane] = r.q0;
+      s.pp[wave][lane + 64] = r.q1;
+    }
+    const int row = tid >> 2, qtr = tid & 3;
+    float4 rv[8];
+    if (tid < 4 * kD) {
+      const float4* rp = reinterpret_cast<const float4*>(r.R + row * kD + 32 * qtr);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) rv[v] = rp[v];
+    }
+    __syncthreads();
+    if (tid < 4 * kD) {
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const float rr[4] = {rv[v].x, rv[v].y, rv[v].z, rv[v].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int hh = 0; hh < 4; ++hh) acc[hh] = fmaf(rr[e], s.pp[hh][32 * qtr + 4 * v + e], acc[hh]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        acc[hh] += __shfl_xor(acc[hh], 1, 64);
+        acc[hh] += __shfl_xor(acc[hh], 2, 64);
+      }
+      s.qt[qtr][row] = acc[qtr];
+    }
+    __syncthreads();
+    if (wave < 4) {
+      const float y0 = s.qt[wave][lane], y1 = s.qt[wave][lane + 64];
+      const float m1 = wave_max_f32(fmaxf(fabsf(y0), fabsf(y1)));
+      const float s1 = wave_sum_f32(y0 + y1);
+      if (lane == 0) {
+        s.qstat[wave][0] = m1;
+        s.qstat[wave][1] = s1;
+      }
+    }
+  } else if (wave < 4) {
     float x0 = ((r.d0 >> (lane & 31)) & 1u) ? -r.q0 : r.q0;
     float x1 = ((r.d1 >> (lane & 31)) & 1u) ? -r.q1 : r.q1;
 #pragma unroll

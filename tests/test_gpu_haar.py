@@ -78,3 +78,74 @@ def test_haar_blob_through_hadamard_call_is_flagged(gpu_lib):
     b.tq_encode_keys(cb, 1, x, d, 3, 128, rec=rec, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & 2
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("kb,vb", [(2, 1), (3, 2), (4, 3), (4, 4)])
+def test_haar_mfma_encode_d128(gpu_lib, dtype, kb, vb):
+    """At head_dim 128 with 16-bit inputs the Haar rotation runs on the matrix
+    cores (R in three exact 16-bit terms): records against the oracle, for every
+    key and value width, with groups that span several blocks and a ragged tail."""
+    import torch
+    b = gpu_lib
+    d, m, G, N, seed = 128, 128, 3, 2 * 1024 + 77, 61
+    K = inputs.to_torch(inputs.kv_normal(seed, G, N, d, inputs.STREAM_K), dtype, DEV)
+    V = inputs.to_torch(inputs.kv_normal(seed, G, N, d, inputs.STREAM_V), dtype, DEV)
+    kcb, kq = _haar(b, 2, d, kb, m, seed, tq.ROLE_KEY)
+    vcb, vq = _haar(b, 2, d, vb, 0, seed + 9, tq.ROLE_VALUE)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    krec = b.tq_encode_keys(kcb, 2, K, d, kb, m, status=st, rotation=b.ROT_HAAR)
+    vrec = b.tq_encode_values(vcb, 2, V, d, vb, status=st, rotation=b.ROT_HAAR)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    kx, vx = inputs.exact_values(K), inputs.exact_values(V)
+    kr, vr = rec_np(krec), rec_np(vrec)
+    reps = []
+    for g in range(G):
+        reps.append(compare_records(kq[g % 2], kr[g], tq.encode(kq[g % 2], kx[g]), fraction=False))
+        reps.append(compare_records(vq[g % 2], vr[g], tq.encode(vq[g % 2], vx[g]), fraction=False))
+    check_mismatch_fraction(reps)
+
+
+@pytest.mark.parametrize("kb,Hkv,Hq,T", [(2, 2, 2, 300), (3, 2, 4, 1100), (4, 1, 4, 2049), (3, 4, 16, 77)])
+def test_haar_scores_d128(gpu_lib, kb, Hkv, Hq, T):
+    """At head_dim 128 (128 projections) the compressed-key score kernel takes
+    Haar codebooks: the query is rotated by the dense R, the rest of the score
+    is rotation-agnostic.  Scores against the oracle for every key width and
+    query-group size, over several tiles with a ragged tail."""
+    import torch
+    b = gpu_lib
+    d, m, B, seed = 128, 128, 2, 71
+    G = B * Hkv
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_K), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    kcb, kq = _haar(b, Hkv, d, kb, m, seed, tq.ROLE_KEY)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, kb, m, status=st, rotation=b.ROT_HAAR).view(B, Hkv, T, -1)
+    s = b.tq_scores(kcb, Hkv, krec, q, d, kb, m, status=st, rotation=b.ROT_HAAR)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert_close(s.cpu().numpy(), tq.scores(kq, rec_np(krec), inputs.exact_values(q)), "scores")
+
+
+@pytest.mark.parametrize("kb,vb,B,Hkv,Hq,T", [(2, 1, 2, 2, 2, 1500), (4, 3, 1, 2, 8, 1030), (3, 3, 1, 1, 4, 40)])
+def test_haar_fused_attend_d128(gpu_lib, kb, vb, B, Hkv, Hq, T):
+    """At head_dim 128 the fused attention path takes Haar codebooks (query
+    rotated by R in the query preparation, R^T applied once in the merge):
+    outputs against the oracle over several chunks with a ragged tail."""
+    import torch
+    b = gpu_lib
+    d, m, seed = 128, 128, 83
+    G = B * Hkv
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_K), "bf16", DEV)
+    V = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_V), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    kcb, kq = _haar(b, Hkv, d, kb, m, seed, tq.ROLE_KEY)
+    vcb, vq = _haar(b, Hkv, d, vb, 0, seed + 50, tq.ROLE_VALUE)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, kb, m, status=st, rotation=b.ROT_HAAR).view(B, Hkv, T, -1)
+    vrec = b.tq_encode_values(vcb, Hkv, V, d, vb, status=st, rotation=b.ROT_HAAR).view(B, Hkv, T, -1)
+    o = b.tq_attend(kcb, Hkv, vcb, Hkv, krec, vrec, q, d, kb, vb, m, status=st, rotation=b.ROT_HAAR)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert_close(o.cpu().numpy(), tq.attend(kq, rec_np(krec), vq, rec_np(vrec), inputs.exact_values(q)), "attend")
