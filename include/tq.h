@@ -194,10 +194,13 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections,
  * the blob headers (else the status word gets the blob-mismatch bit).  With
  * TQ_ROT_HAAR, head_dim is any value in [2, 512]; R = sqrt(head_dim) Q takes the
  * place of H D everywhere (u = R x, x^ = (n/head_dim) R^T c[idx], qt = R q), and
- * attention applies R^T once per (b, hq) to the rotated-domain sum.  Haar
- * encodes and scores run on the float64 per-vector kernels; the attention's
- * value partials run on the same MFMA kernels as for Walsh-Hadamard codebooks
- * when head_dim is a multiple of 32. */
+ * attention applies R^T once per (b, hq) to the rotated-domain sum.  At
+ * head_dim 128, encodes of bf16/f16 inputs run R x on the matrix cores (R in
+ * three exact 16-bit terms), and scores and the fused attention (128
+ * projections) rotate the query by R; other Haar encodes and scores run on the
+ * float64 per-vector kernels.  The attention's value partials run on the same
+ * MFMA kernels as for Walsh-Hadamard codebooks when head_dim is a multiple of
+ * 32. */
 int tq_encode_keys_ex(int head_dim, int bits, int projections, int rotation,
                       const void* cbs, int64_t n_cb,
                       const void* x, int x_dtype, int64_t G, int64_t N,

@@ -10,6 +10,11 @@ SeedSequence([seed, stream, group]).
   * kv_channel_std: N(0,1) times a per-(group, channel) std drawn
                     log-uniformly in [lo, hi].
   * queries:        N(0,1) query heads [B][H_q][d].
+  * block_codebook: N codewords of dimension k, i.i.d. N(0, 1/d) per
+                    coordinate (the scale of a k-block of a unit vector in R^d).
+  * sign_bits:      ceil(d/32) uint32 words of fair random bits.
+  * block_codes:    uniform indices in [0, N) [M][nb] and norms [M] drawn as
+                    |N(0, I_d)| (chi with d degrees of freedom), float32.
 bf16 inputs are the float32 draws rounded to nearest-even by torch.
 """
 from __future__ import annotations
@@ -20,6 +25,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 STREAM_K, STREAM_V, STREAM_Q, STREAM_OUTLIER, STREAM_SIGMA = 1, 2, 3, 4, 5
+STREAM_CODEBOOK, STREAM_SIGNS, STREAM_CODES = 6, 7, 8
 
 
 def _rng(seed: int, *keys: int) -> np.random.Generator:
@@ -76,6 +82,21 @@ def kv_channel_std(seed: int, G: int, N: int, d: int, lo: float = 0.5, hi: float
 
 def queries(seed: int, B: int, Hq: int, d: int) -> np.ndarray:
     return _rng(seed, STREAM_Q).standard_normal((B, Hq, d), dtype=np.float32)
+
+
+def block_codebook(seed: int, N: int, k: int, d: int) -> np.ndarray:
+    return (_rng(seed, STREAM_CODEBOOK).standard_normal((N, k)) / math.sqrt(d)).astype(np.float32)
+
+
+def sign_bits(seed: int, d: int) -> np.ndarray:
+    return _rng(seed, STREAM_SIGNS).integers(0, 1 << 32, (d + 31) // 32, dtype=np.uint64).astype(np.uint32)
+
+
+def block_codes(seed: int, M: int, nb: int, N: int, d: int, stream: int = STREAM_CODES):
+    r = _rng(seed, stream)
+    idx = r.integers(0, N, (M, nb), dtype=np.int64)
+    norms = np.sqrt(r.chisquare(d, M)).astype(np.float32)
+    return idx, norms
 
 
 def to_torch(a: np.ndarray, dtype: str = "bf16", device=None):

@@ -1,4 +1,5 @@
-"""CPU oracle for the TurboQuant KV-cache codec (test infrastructure only).
+"""CPU oracle for the TurboQuant KV-cache codec and the Gram-table scorer of
+block-codebook codes (test infrastructure only).
 
 This package is the slow, obviously-correct reference that the HIP path is
 checked against.  It is plain Python + NumPy in float64, uses dense matrices
@@ -13,7 +14,9 @@ Pages cited in docstrings (the method statement and the API evidence):
     "Compression formats", "Modules", "Usage";
   * "bitpolar 0.3.3 src/kv_cache.rs" (docs.rs), ``KvCacheConfig``,
     ``KvCacheCompressor::{push, attention_scores, decode_values,
-    compression_ratio}``, ``MultiHeadKvCache::new``.
+    compression_ratio}``, ``MultiHeadKvCache::new``;
+  * "fib-quant 0.1.0-beta.4 README" (docs.rs), "What's in the box" (Codec,
+    Rotation, Scoring) and "New modules", Scoring (``oracle/gram.py``).
 
 Parity status per function is listed in the header of each module.
 """
