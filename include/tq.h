@@ -76,6 +76,7 @@ enum tq_status {
   TQ_ERR_INVALID_PROJECTIONS = -12,/* projections > 1024                               */
   TQ_ERR_UNSUPPORTED = -13,        /* dtype or alignment not supported                 */
   TQ_ERR_INVALID_ROTATION = -14,   /* rotation not TQ_ROT_HADAMARD / TQ_ROT_HAAR       */
+  TQ_ERR_INVALID_CODEBOOK = -15,   /* Gram codec: codebook size not a power of two in [2, 256] */
 };
 
 /* Device status bits (OR-ed into *status). */
@@ -354,6 +355,46 @@ int tq_decode_values_split(int head_dim, int n_outlier, int bits,
  * (1.0 when empty).  Host only. */
 int tq_memory_stats(int head_dim, int k_bits, int v_bits, int projections,
                     int64_t seq_len, int64_t layers, int64_t kv_heads, double out[4]);
+
+/* ---- Gram-table scoring of block-codebook codes --------------------------
+ * Page "fib-quant 0.1.0-beta.4 README": a vector is cut into blocks, each
+ * block is stored as the index of a codeword of a small codebook ("What's in
+ * the box", Codec; rotated first by the fast Walsh-Hadamard transform,
+ * Rotation), and inner products with stored codes are estimated from the Gram
+ * table G[i][j] = <c_i, c_j> without decoding them ("New modules", Scoring).
+ *   head_dim d  : a power of two in [2, 512] (else TQ_ERR_BAD_DIMENSION);
+ *   block_dim k : 1, 2, 4 or 8, at most d (else TQ_ERR_BAD_DIMENSION);
+ *   codebook_size N : a power of two in [2, 256], w = log2 N bits per index
+ *                 (else TQ_ERR_INVALID_CODEBOOK);
+ *   codebook    : float32 [N][k], device, caller-made (any contents);
+ *   signs       : ceil(d/32) uint32 words, device; bit j set negates
+ *                 coordinate j before the transform (the diagonal D).
+ * Record: the d/k indices, index b at bits [b w, (b+1) w) of the little-endian
+ * words (LSB first; an index may straddle two words), ceil(d w / (k 32))
+ * words, then float32 |x|.  Encode: n = |x| (float64, stored as float32),
+ * u = H(D x) / (sqrt(d) n) (u = 0 for a zero vector), block b = u[b k, b k + k)
+ * takes the nearest codeword (Euclidean; the lowest index on ties; decided in
+ * float32).  Scores (the query encoded alike):
+ *   s[b][hq][t] = scale * n_q * n_t * sum_blocks G[cq_blk][ct_blk]
+ * with query head hq reading kv head floor(hq * H_kv / H_q); scale <= 0 means
+ * 1/sqrt(d).  No data errors exist for scores (indices are masked to w bits). */
+size_t tq_gram_record_bytes(int head_dim, int block_dim, int codebook_size);
+
+/* G[i][j] = <c_i, c_j>, float32 [N][N] (device), summed in float32 by fma. */
+int tq_gram_table(int block_dim, int codebook_size, const float* codebook, float* table, void* stream);
+
+/* Records [G][N][tq_gram_record_bytes/4] of x [G][N][head_dim] (strides as for
+ * tq_encode_keys; TQ_F32/TQ_BF16/TQ_F16).  Non-finite input, or a squared
+ * norm past the float32 range, sets TQ_STATUS_NON_FINITE (record unspecified). */
+int tq_gram_encode(int head_dim, int block_dim, int codebook_size, const float* codebook, const uint32_t* signs,
+                   const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n,
+                   void* rec, int32_t* status, void* stream);
+
+/* scores [B][H_q][T] float32 from query records qrec [B][H_q][words] and key
+ * records krec [B][H_kv][T][words], with the table of tq_gram_table. */
+int tq_gram_scores(int head_dim, int block_dim, int codebook_size, const float* table,
+                   const void* qrec, const void* krec, int64_t B, int64_t H_kv, int64_t T, int64_t H_q,
+                   float scale, float* scores, void* stream);
 
 /* Human-readable name of a return code. */
 const char* tq_status_string(int code);

@@ -31,7 +31,8 @@ EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encod
            "tq_record_bytes_ex", "tq_make_codebook_ex", "tq_outlier_workspace_bytes", "tq_outlier_channels",
            "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes",
            "tq_encode_keys_ex", "tq_encode_values_ex", "tq_decode_values_ex", "tq_scores_ex", "tq_attend_ex",
-           "tq_append_workspace_bytes", "tq_append_kv", "tq_scores_paged"]
+           "tq_append_workspace_bytes", "tq_append_kv", "tq_scores_paged", "tq_gram_record_bytes", "tq_gram_table",
+           "tq_gram_encode", "tq_gram_scores"]
 
 _lib = None
 
@@ -105,6 +106,12 @@ def load() -> ctypes.CDLL:
         "tq_append_kv": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
                                  c_void_p, c_int, c_int64, c_int64, c_void_p, c_void_p, c_int64, c_int, c_int64,
                                  c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
+        "tq_gram_record_bytes": (c_size_t, [c_int, c_int, c_int]),
+        "tq_gram_table": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p]),
+        "tq_gram_encode": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int64,
+                                   c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_gram_scores": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_int64,
+                                   c_int64, c_float, c_void_p, c_void_p]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -417,3 +424,54 @@ def tq_rotate(cbs, n_cb, x, head_dim, bits, projections, role):
     _check(load().tq_rotate(head_dim, bits, projections, role, _ptr(cbs), n_cb, _ptr(x), _dtype_code(x), G, N,
                             sg, sn, _ptr(u), _ptr(norms), _stream(x)), "tq_rotate")
     return u, norms
+
+
+# ---- Gram-table scoring of block-codebook codes
+def tq_gram_record_bytes(head_dim: int, block_dim: int, codebook_size: int) -> int:
+    return int(load().tq_gram_record_bytes(head_dim, block_dim, codebook_size))
+
+
+def tq_gram_table(codebook, out=None):
+    """codebook [N][k] float32 (device) -> G [N][N] float32."""
+    import torch
+    N, k = codebook.shape
+    if codebook.dtype != torch.float32 or not codebook.is_contiguous():
+        raise ValueError("codebook must be contiguous float32 [N][k]")
+    if out is None:
+        out = torch.empty((N, N), dtype=torch.float32, device=codebook.device)
+    _check(load().tq_gram_table(k, N, _ptr(codebook), _ptr(out), _stream(codebook)), "tq_gram_table")
+    return out
+
+
+def tq_gram_encode(codebook, signs, x, head_dim, rec=None, status=None):
+    """x [G][N][head_dim] -> records [G][N][words] (int32 view of uint32)."""
+    import torch
+    N_cb, k = codebook.shape
+    G, N, sg, sn = _groups(x, head_dim)
+    words = tq_gram_record_bytes(head_dim, k, N_cb) // 4
+    if words == 0:
+        raise ValueError("bad Gram codec shape")
+    if rec is None:
+        rec = torch.empty((G, N, words), dtype=torch.int32, device=x.device)
+    rc = load().tq_gram_encode(head_dim, k, N_cb, _ptr(codebook), _ptr(signs), _ptr(x), _dtype_code(x), G, N, sg,
+                               sn, _ptr(rec), _ptr(status), _stream(x))
+    _check(rc, "tq_gram_encode")
+    return rec
+
+
+def tq_gram_scores(table, qrec, krec, head_dim, block_dim, scale=0.0, out=None):
+    """qrec [B][H_q][words], krec [B][H_kv][T][words] -> [B][H_q][T] float32."""
+    import torch
+    N_cb = table.shape[0]
+    B, Hkv, T = krec.shape[0], krec.shape[1], krec.shape[2]
+    Hq = qrec.shape[1]
+    words = tq_gram_record_bytes(head_dim, block_dim, N_cb) // 4
+    if qrec.shape != (B, Hq, words) or krec.shape[3] != words or not (qrec.is_contiguous() and krec.is_contiguous()):
+        raise ValueError("records must be contiguous [B][H_q][words] and [B][H_kv][T][words]")
+    if out is None:
+        out = torch.empty((B, Hq, T), dtype=torch.float32, device=krec.device)
+    rc = load().tq_gram_scores(head_dim, block_dim, N_cb, _ptr(table), _ptr(qrec), _ptr(krec), B, Hkv, T, Hq, scale,
+                               _ptr(out), _stream(krec))
+    _check(rc, "tq_gram_scores")
+    return out
+

@@ -12,7 +12,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["tq_host.cpp", "tq_abi.cpp", "tq_generic.hip", "tq_fast128.hip", "tq_score128.hip", "tq_split.hip", "tq_attend.hip", "tq_split256.hip", "tq_tiled.hip", "tq_paged.hip"]
+SOURCES = ["tq_host.cpp", "tq_abi.cpp", "tq_generic.hip", "tq_fast128.hip", "tq_score128.hip", "tq_split.hip", "tq_attend.hip", "tq_split256.hip", "tq_tiled.hip", "tq_paged.hip", "tq_gram.hip"]
 
 # Packed-FP32 VALU forms are disabled for every device pass; the host pass
 # warns that it does not know the feature, which is harmless.  MFMA results

@@ -382,4 +382,82 @@ int tq_decode_values_split(int head_dim, int n_outlier, int bits, const void* cb
                                N, out, status, s, head_dim, ChannelMap{chan, head_dim, 0, head_dim});
 }
 
+// ---- Gram-table scoring of block-codebook codes
+
+static int gram_check(int head_dim, int block_dim, int codebook_size, int* W) {
+  if (head_dim == 0) return TQ_ERR_ZERO_DIMENSION;
+  if (head_dim < 2 || head_dim > kMaxHeadDim || (head_dim & (head_dim - 1))) return TQ_ERR_BAD_DIMENSION;
+  if ((block_dim != 1 && block_dim != 2 && block_dim != 4 && block_dim != 8) || block_dim > head_dim)
+    return TQ_ERR_BAD_DIMENSION;
+  if (codebook_size < 2 || codebook_size > 256 || (codebook_size & (codebook_size - 1)))
+    return TQ_ERR_INVALID_CODEBOOK;
+  int w = 0;
+  while ((1 << w) < codebook_size) ++w;
+  *W = w;
+  return TQ_OK;
+}
+
+static int gram_words(int head_dim, int block_dim, int W) { return ((head_dim / block_dim) * W + 31) / 32 + 1; }
+
+size_t tq_gram_record_bytes(int head_dim, int block_dim, int codebook_size) {
+  int W;
+  if (gram_check(head_dim, block_dim, codebook_size, &W)) return 0;
+  return (size_t)gram_words(head_dim, block_dim, W) * 4;
+}
+
+int tq_gram_table(int block_dim, int codebook_size, const float* codebook, float* table, void* stream) {
+  int W;
+  int rc = gram_check(kMaxHeadDim, block_dim, codebook_size, &W);
+  if (rc) return rc;
+  if (!codebook || !table) return TQ_ERR_NULL;
+  return launch_gram_table(codebook, codebook_size, block_dim, table, static_cast<hipStream_t>(stream));
+}
+
+int tq_gram_encode(int head_dim, int block_dim, int codebook_size, const float* codebook, const uint32_t* signs,
+                   const void* x, int x_dtype, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n, void* rec,
+                   int32_t* status, void* stream) {
+  int W;
+  int rc = gram_check(head_dim, block_dim, codebook_size, &W);
+  if (rc) return rc;
+  if (G < 0 || N < 0) return TQ_ERR_EMPTY_INPUT;
+  if (G * N == 0) return TQ_OK;
+  if (!codebook || !signs || !x || !rec) return TQ_ERR_NULL;
+  if (!dtype_ok(x_dtype)) return TQ_ERR_UNSUPPORTED;
+  if ((N > 1 && sx_n < head_dim) || (G > 1 && sx_g < head_dim) || sx_n < 0 || sx_g < 0)
+    return TQ_ERR_DIMENSION_MISMATCH;
+  GramEncArgs a;
+  a.C = codebook;
+  a.N = codebook_size; a.k = block_dim; a.W = W; a.d = head_dim; a.nb = head_dim / block_dim;
+  a.rw = gram_words(head_dim, block_dim, W);
+  a.signs = signs;
+  a.x = x; a.dtype = x_dtype;
+  a.G = G; a.Nv = N; a.sx_g = sx_g; a.sx_n = sx_n;
+  a.rec = static_cast<uint32_t*>(rec);
+  a.status = status;
+  return launch_gram_encode(a, static_cast<hipStream_t>(stream));
+}
+
+int tq_gram_scores(int head_dim, int block_dim, int codebook_size, const float* table, const void* qrec,
+                   const void* krec, int64_t B, int64_t H_kv, int64_t T, int64_t H_q, float scale, float* scores,
+                   void* stream) {
+  int W;
+  int rc = gram_check(head_dim, block_dim, codebook_size, &W);
+  if (rc) return rc;
+  if (B < 0 || H_kv <= 0 || T < 0 || H_q <= 0) return TQ_ERR_EMPTY_INPUT;
+  if (H_q % H_kv) return TQ_ERR_DIMENSION_MISMATCH;
+  if (B * T == 0) return TQ_OK;
+  if (!table || !qrec || !krec || !scores) return TQ_ERR_NULL;
+  if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)head_dim);
+  GramScoreArgs a;
+  a.G = table;
+  a.qrec = static_cast<const uint32_t*>(qrec);
+  a.krec = static_cast<const uint32_t*>(krec);
+  a.B = B; a.Hkv = H_kv; a.T = T; a.Hq = H_q;
+  a.scale = scale;
+  a.scores = scores;
+  a.chunks = 0;
+  return launch_gram_scores(a, W, head_dim / block_dim, gram_words(head_dim, block_dim, W),
+                            static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -382,6 +382,7 @@ const char* tq_status_string(int code) {
     case TQ_ERR_INVALID_PROJECTIONS: return "InvalidProjections: projections must be <= 1024";
     case TQ_ERR_UNSUPPORTED: return "Unsupported dtype or alignment";
     case TQ_ERR_INVALID_ROTATION: return "InvalidRotation: rotation must be TQ_ROT_HADAMARD or TQ_ROT_HAAR";
+    case TQ_ERR_INVALID_CODEBOOK: return "InvalidCodebook: codebook size must be a power of two in [2, 256]";
     default: return "unknown status";
   }
 }

@@ -67,4 +67,30 @@ int launch_outlier_channels(const void* x, int dtype, int64_t G, int64_t N, int6
 int launch_attend_generic(const CodebookArgs& vcb, const uint32_t* vrec, const float* scores, int64_t B,
                           int64_t Hkv, int64_t T, int64_t Hq, float* out, hipStream_t s);
 
+// Gram-table scoring of block-codebook codes (tq_gram.hip).  Shapes are
+// validated by the caller: d a power of two in [2, 512], k in {1, 2, 4, 8},
+// N = 2^W in [2, 256]; records of rw = ceil(d W / (k 32)) + 1 words.
+struct GramEncArgs {
+  const float* C;            // [N][k] codebook
+  int N, k, W, d, nb, rw;    // nb = d / k
+  const uint32_t* signs;     // ceil(d/32) words, bit j set: coordinate j negated
+  const void* x;
+  int dtype;
+  int64_t G, Nv, sx_g, sx_n;
+  uint32_t* rec;             // [G][Nv][rw]
+  int32_t* status;
+};
+struct GramScoreArgs {
+  const float* G;            // [N][N] Gram table
+  const uint32_t* qrec;      // [B][Hq][rw]
+  const uint32_t* krec;      // [B][Hkv][T][rw]
+  int64_t B, Hkv, T, Hq;
+  float scale;
+  float* scores;             // [B][Hq][T]
+  int64_t chunks;            // set by the launcher
+};
+int launch_gram_table(const float* C, int N, int k, float* G, hipStream_t s);
+int launch_gram_encode(const GramEncArgs& a, hipStream_t s);
+int launch_gram_scores(GramScoreArgs a, int W, int nb, int rw, hipStream_t s);
+
 }  // namespace tq

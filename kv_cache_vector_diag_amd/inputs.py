@@ -92,8 +92,8 @@ def sign_bits(seed: int, d: int) -> np.ndarray:
     return _rng(seed, STREAM_SIGNS).integers(0, 1 << 32, (d + 31) // 32, dtype=np.uint64).astype(np.uint32)
 
 
-def block_codes(seed: int, M: int, nb: int, N: int, d: int, stream: int = STREAM_CODES):
-    r = _rng(seed, stream)
+def block_codes(seed: int, M: int, nb: int, N: int, d: int, stream: int = STREAM_CODES, group: int = 0):
+    r = _rng(seed, stream, group)
     idx = r.integers(0, N, (M, nb), dtype=np.int64)
     norms = np.sqrt(r.chisquare(d, M)).astype(np.float32)
     return idx, norms

@@ -172,3 +172,26 @@ def test_device_calls_validate_before_touching_the_gpu():
     assert lib.tq_encode_values(128, 9, None, 1, None, 0, 1, 1, 128, 128, None, None, None) == -3
     assert lib.tq_scores(128, 3, 128, None, 1, None, 1, 3, 10, None, 0, 4, 0.0, None, None, None) == -5
     assert lib.tq_decode_values(128, 3, None, 1, None, 0, 10, None, None, None) == 0
+
+
+def test_gram_calls_validate_before_touching_the_gpu():
+    """Gram-table codec: sizes agree with the oracle, bad shapes are refused on
+    the host before any HIP call."""
+    from oracle import gram
+    lib = b.load()
+    for d, k, N in ((128, 4, 32), (64, 4, 32), (512, 1, 256), (2, 1, 2), (16, 8, 4), (256, 2, 64)):
+        assert b.tq_gram_record_bytes(d, k, N) == 4 * gram.record_words(d, k, N)
+    for d, k, N, code in ((96, 4, 32, -2), (0, 4, 32, -1), (128, 3, 32, -2), (4, 8, 32, -2), (128, 4, 24, -15),
+                          (128, 4, 512, -15), (128, 4, 1, -15)):
+        assert lib.tq_gram_record_bytes(d, k, N) == 0
+        assert lib.tq_gram_encode(d, k, N, None, None, None, 0, 1, 1, 128, 128, None, None, None) == code
+        assert lib.tq_gram_scores(d, k, N, None, None, None, 1, 1, 1, 1, 0.0, None, None) == code
+    assert lib.tq_gram_table(3, 32, None, None, None) == -2
+    assert lib.tq_gram_table(4, 32, None, None, None) == -8
+    assert lib.tq_gram_encode(128, 4, 32, None, None, None, 0, 0, 5, 128, 128, None, None, None) == 0
+    assert lib.tq_gram_encode(128, 4, 32, None, None, None, 0, 2, 5, 128, 128, None, None, None) == -8
+    assert lib.tq_gram_encode(128, 4, 32, None, None, None, 0, -1, 5, 128, 128, None, None, None) == -7
+    assert lib.tq_gram_scores(128, 4, 32, None, None, None, 1, 3, 10, 4, 0.0, None, None) == -5
+    assert lib.tq_gram_scores(128, 4, 32, None, None, None, 0, 2, 10, 4, 0.0, None, None) == 0
+    assert lib.tq_gram_scores(128, 4, 32, None, None, None, 1, 2, 10, 4, 0.0, None, None) == -8
+    assert "InvalidCodebook" in lib.tq_status_string(-15).decode()
