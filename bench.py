@@ -12,9 +12,10 @@ Inputs are resident in HBM before timing.  Buffers rotate (2 input caches,
 cache still holds from the previous launch.  Kernel durations come from HIP
 events on the stream the kernels are launched on.
 
-Prints ONE JSON line.  `--config c2|c4|c5|haar|paged` measures the
+Prints ONE JSON line.  `--config c2|c4|c5|haar|paged|gram` measures the
 prefill-encode, the long-context attend, the mixed-precision layer, the
-Haar-rotation and the paged-cache decode rows instead (also one line each).
+Haar-rotation, the paged-cache decode and the Gram-table scoring rows instead
+(also one line each).
 """
 from __future__ import annotations
 
@@ -494,12 +495,71 @@ def bench_haar(args, torch, b):
                          "algorithmic_flops_per_launch": flops}}
 
 
+def bench_gram(args, torch, b):
+    """Gram-table scoring of block-codebook codes at the 32K-context decode
+    shape: head_dim 128 cut into blocks of 4, a 32-codeword codebook (5-bit
+    indices, 24-byte records).  The key cache is encoded once before timing;
+    one step = encode the 32 query heads of every sequence + score them against
+    the whole cache from the Gram table.  Three record caches rotate so that no
+    launch reads what the memory-side cache kept from the previous one."""
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    B, Hkv, Hq, T, d, k, N, seed = 16, 8, 32, 32768, 128, 4, 32, 3
+    G = B * Hkv
+    words = b.tq_gram_record_bytes(d, k, N) // 4
+    C = torch.from_numpy(inputs.block_codebook(seed, N, k, d)).to(dev)
+    signs = torch.from_numpy(inputs.sign_bits(seed, d).view("int32")).to(dev)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d), "bf16", dev)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    krec = b.tq_gram_encode(C, signs, K, d, status=status)
+    recs = [krec.view(B, Hkv, T, words)] + [krec.clone().view(B, Hkv, T, words) for _ in range(2)]
+    del K
+    table = b.tq_gram_table(C)
+    qrec = torch.empty((B, Hq, words), dtype=torch.int32, device=dev)
+    scores = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+
+    def step(i, ev=None):
+        b.tq_gram_encode(C, signs, q, d, rec=qrec, status=status)
+        if ev:
+            ev[0].record()
+        b.tq_gram_scores(table, qrec, recs[i % 3], d, k, out=scores)
+        if ev:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    evs = [_events(torch, 2) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(status.item()) == 0
+    sc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    sc_bytes = G * T * words * 4 + B * Hq * T * 4 + qrec.numel() * 4 + table.numel() * 4
+    sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
+    return {"metric": "Gram-table score tokens/s (block-codebook codes, no decode)", "value": B * T / (ms_step * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "Gram-table scoring: 16 seq x 8 kv heads x 32768 tokens, d=128, blocks of 4, "
+                                   "32 codewords (24-byte records), 32 bf16 query heads encoded per step"},
+            "score_ms": sc_ms, "score_GBps": sc_gbps, "score_tokens_per_s": B * T / (sc_ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": sc_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": sc_gbps / HBM_PEAK_GBPS, "traffic": _traffic("score_gram", sc_bytes),
+                         "kernel": "gram_scores", "algorithmic_bytes_per_launch": sc_bytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5", "haar", "paged"])
+    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5", "haar", "paged", "gram"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -533,7 +593,7 @@ def main():
                                                "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}}))
         return
     fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5, "haar": bench_haar,
-          "paged": bench_paged}[args.config]
+          "paged": bench_paged, "gram": bench_gram}[args.config]
     line = fn(args, torch, b)
     if args.config == "c3":
         line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_c3()

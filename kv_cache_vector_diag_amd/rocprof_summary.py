@@ -21,6 +21,10 @@ import os
 import sys
 
 KERNELS = {
+    "gram_scores_fast": "gram_scores",
+    "gram_scores_generic": "gram_scores_generic",
+    "gram_encode": "gram_encode",
+    "gram_table": "gram_table",
     "encode128_kernel": "encode",
     "score128_kernel": "score",
     "encode_generic": "encode_generic",
@@ -49,6 +53,7 @@ KERNEL_SOURCES = {
     "encode_keys": ["tq_fast128.hip"] + _COMMON,
     "score": ["tq_score128.hip", "tq_score_core.h"] + _COMMON,
     "attend_fused": ["tq_attend.hip", "tq_score_core.h", "tq_kernels.h"] + _COMMON,
+    "gram_scores": ["tq_gram.hip", "tq_kernels.h"] + _COMMON,
 }
 
 

@@ -157,3 +157,56 @@ def test_mixed_precision_layers_full(gpu_lib):
                                     fraction=False))
         del X
     check_mismatch_fraction(reps)
+
+
+def test_gram_scoring_32k_full_size(gpu_lib):
+    """Gram-table scoring at the decode-step shape (16 x 8 kv heads x 32768
+    tokens, d=128, blocks of 4, 32 codewords, 32 query heads), the keys and
+    queries encoded on the GPU: sampled tokens of three groups against the
+    oracle's encode, and their scores where the codes agree."""
+    import math
+
+    import torch
+    from oracle import gram
+
+    from .test_gpu_gram import U, _check_codes
+    b = gpu_lib
+    B, Hkv, Hq, T, d, k, N, seed = 16, 8, 32, 32768, 128, 4, 32, 3
+    G = B * Hkv
+    C = inputs.block_codebook(seed, N, k, d)
+    s = inputs.sign_bits(seed, d)
+    Ct = torch.from_numpy(C).to(DEV)
+    st = torch.from_numpy(s.view(np.int32)).to(DEV)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    krec = b.tq_gram_encode(Ct, st, K, d, status=status)
+    qrec = b.tq_gram_encode(Ct, st, q, d, status=status)
+    sc = b.tq_gram_scores(b.tq_gram_table(Ct), qrec, krec.view(B, Hkv, T, -1), d, k)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    del K
+    qref, _, qdist = gram.encode(C, s, inputs.exact_values(q).reshape(-1, d), d, k)
+    _check_codes(rec_np(qrec).reshape(B * Hq, -1), qref, qdist, d, k, N, "queries")
+    qref = qref.reshape(B, Hq, -1)
+    same_q = np.all(rec_np(qrec) == qref, axis=2)
+    Gmax = float(np.max(np.abs(gram.gram_table(C))))
+    rng = np.random.default_rng(1)
+    for g in (0, 77, G - 1):
+        toks = _sample_tokens(rng, T, 1500)
+        X = _bf16_exact(inputs.kv_normal(seed, G, T, d, groups=[g]))[0][toks]
+        kref, _, kdist = gram.encode(C, s, X, d, k)
+        grec = rec_np(krec[g])[toks]
+        _check_codes(grec, kref, kdist, d, k, N, f"keys g={g}")
+        bb, h = divmod(g, Hkv)
+        rows = list(range(4 * h, 4 * h + 4))
+        ref = gram.scores(C, qref[bb:bb + 1, rows], kref[None, None], d, k)[0]
+        got = sc[bb, 4 * h:4 * h + 4].cpu().numpy().astype(np.float64)[:, toks]
+        same_k = np.all(grec == kref, axis=1)
+        _, kn = gram.unpack_record(kref, d, k, N)
+        for i, hq in enumerate(rows):
+            if not same_q[bb, hq]:
+                continue
+            _, qn = gram.unpack_record(qref[bb, hq][None, :], d, k, N)
+            bound = (d // k + k + 4) * U / math.sqrt(d) * qn[0] * kn * (d // k) * Gmax
+            assert np.all(np.abs(got[i] - ref[i])[same_k] <= bound[same_k])

@@ -30,6 +30,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
      "attend_qprep"),
     ("void tq::(anonymous namespace)::attend_merge_kernel(tq::(anonymous namespace)::MergeArgs)",
      "attend_merge"),
+    ("void tq::(anonymous namespace)::gram_scores_fast_kernel<5, 32, 4>(tq::GramScoreArgs)", "gram_scores"),
+    ("tq::(anonymous namespace)::gram_scores_generic_kernel(tq::GramScoreArgs, int, int, int, long)",
+     "gram_scores_generic"),
+    ("tq::(anonymous namespace)::gram_encode_kernel(tq::GramEncArgs)", "gram_encode"),
     ("__amd_rocclr_copyBuffer", "copy"),
 ])
 def test_short_names(name, short):
