@@ -88,7 +88,8 @@ def test_encode_recovers_exact_codewords():
 
 def test_encode_picks_the_nearest_codeword_brute_force():
     """Each block's index minimises the squared distance over all codewords
-    (plain loops), the lowest index on ties."""
+    (plain loops on the float32-rounded rotated coordinates), the lowest index
+    on ties."""
     d, k, N = 16, 4, 8
     C = inputs.block_codebook(2, N, k, d).astype(np.float64)
     s = inputs.sign_bits(2, d)
@@ -101,7 +102,8 @@ def test_encode_picks_the_nearest_codeword_brute_force():
         nrm = math.sqrt(math.fsum(X[r] * X[r]))
         assert n[r] == np.float32(nrm)
         n32 = float(np.float32(nrm))
-        u = [math.fsum(H[i, j] * dv[j] * X[r, j] for j in range(d)) / (math.sqrt(d) * n32) for i in range(d)]
+        u = [float(np.float32(math.fsum(H[i, j] * dv[j] * X[r, j] for j in range(d)) / (math.sqrt(d) * n32)))
+             for i in range(d)]
         for b in range(d // k):
             dist = [math.fsum((u[b * k + e] - C[i, e]) ** 2 for e in range(k)) for i in range(N)]
             best = min(range(N), key=lambda i: (dist[i], i))
