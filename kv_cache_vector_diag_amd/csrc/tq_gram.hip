@@ -7,7 +7,8 @@
 // from the codebook's Gram table G[i][j] = <c_i, c_j> with no decode ("New
 // modules", Scoring).  Here:
 //   encode: n = |x|, u = H(D x) / (sqrt(d) n); block b (k coordinates) takes
-//           the nearest codeword in Euclidean distance, the lowest on ties;
+//           the nearest codeword in Euclidean distance, the lowest on ties,
+//           decided on u rounded to float32 with float64 squared distances;
 //   record: d/k indices of w = log2 N bits, LSB first at bit b w of the
 //           little-endian words (an index may straddle two words), then
 //           float32 n;
@@ -36,20 +37,29 @@ __global__ void gram_table_kernel(const float* C, int N, int k, float* G) {
 }
 
 // ---- encode: one wave per vector, four vectors per workgroup step.  Lane l
-// holds coordinates l + 64 p (p < d/64; for d < 64 lane l < d holds l); the
-// transform runs spans 1..32 across lanes, larger ones within the lane.  The
-// rotated vector then goes through LDS so that lane b owns block b.
+// holds coordinates l + 64 p (p < P = d/64; for d < 64 lane l < d holds l).
+// The transform runs in float64 (exact sums of the float32 inputs): spans
+// 1..32 across lanes, larger ones within the lane.  u = y / (sqrt(d) n32) is
+// rounded to float32 and goes through LDS so that lanes own blocks; each block's
+// squared distances to the codewords (float64, codebook in LDS, read as
+// broadcasts) pick the nearest, the lowest index on ties.  With at most 32
+// blocks, lanes b and b + 32 search the lower and upper half of the codebook.
 constexpr int kEncWaves = 4;
 constexpr int kMaxWords = 512 * 8 / 32;   // d/k indices of up to 8 bits: at most 128 words
 
+template <int K, int P>
 __global__ __launch_bounds__(64 * kEncWaves) void gram_encode_kernel(GramEncArgs a) {
-  __shared__ float cb[256 * 8];
-  __shared__ float ub[kEncWaves][512];
+  __shared__ double cb[256 * K];
+  __shared__ float ub[kEncWaves][64 * P];
   __shared__ uint32_t wb[kEncWaves][kMaxWords];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < a.N * a.k; e += blockDim.x) cb[e] = a.C[e];
-  const int P = a.d >= 64 ? a.d / 64 : 1;
+  for (int e = tid; e < a.N * K; e += blockDim.x) cb[e] = (double)a.C[e];
   const int nw = a.rw - 1;
+  const int nb = a.d / K;
+  const bool halves = nb <= 32;
+  const int hb = lane & 31, half = lane >> 5;
+  const int i_lo = halves ? half * (a.N >> 1) : 0;
+  const int i_hi = halves ? i_lo + (a.N >> 1) : a.N;
   const int64_t total = a.G * a.Nv;
   const double rsd = 1.0 / sqrt((double)a.d);
   // every wave runs the same number of steps, so the workgroup barriers match
@@ -58,15 +68,15 @@ __global__ __launch_bounds__(64 * kEncWaves) void gram_encode_kernel(GramEncArgs
     const bool live = v < total;
     const int64_t g = live ? v / a.Nv : 0, t = live ? v - g * a.Nv : 0;
     const int64_t base = g * a.sx_g + t * a.sx_n;
-    float y[8];
+    double y[P];
     double ss = 0.0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < P; ++p) {
       const int j = lane + 64 * p;
-      float xv = 0.0f;
-      if (live && p < P && j < a.d) {
-        xv = load_elem(a.x, a.dtype, base + j);
-        ss = fma((double)xv, (double)xv, ss);
+      double xv = 0.0;
+      if (live && j < a.d) {
+        xv = (double)load_elem(a.x, a.dtype, base + j);
+        ss = fma(xv, xv, ss);
         if ((a.signs[j >> 5] >> (j & 31)) & 1u) xv = -xv;
       }
       y[p] = xv;
@@ -76,18 +86,18 @@ __global__ __launch_bounds__(64 * kEncWaves) void gram_encode_kernel(GramEncArgs
     for (int h = 1; h < 64; h <<= 1) {
       if (h < a.d) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const float o = __shfl_xor(y[p], h, 64);
+        for (int p = 0; p < P; ++p) {
+          const double o = __shfl_xor(y[p], h, 64);
           y[p] = (lane & h) ? o - y[p] : y[p] + o;
         }
       }
     }
 #pragma unroll
-    for (int h2 = 1; h2 < 8; h2 <<= 1) {
+    for (int h2 = 1; h2 < P; h2 <<= 1) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        if (h2 < P && !(p & h2)) {
-          const float a0 = y[p], b0 = y[p + h2];
+      for (int p = 0; p < P; ++p) {
+        if (!(p & h2)) {
+          const double a0 = y[p], b0 = y[p + h2];
           y[p] = a0 + b0;
           y[p + h2] = a0 - b0;
         }
@@ -96,37 +106,45 @@ __global__ __launch_bounds__(64 * kEncWaves) void gram_encode_kernel(GramEncArgs
     const bool finite = ss <= 3.4028234663852886e38;
     if (live && !finite && lane == 0 && a.status) atomicOr(a.status, TQ_STATUS_NON_FINITE);
     const float n32 = (float)sqrt(ss);
-    const float sc = (finite && n32 > 0.0f) ? (float)(rsd / (double)n32) : 0.0f;
+    const double sc = (finite && n32 > 0.0f) ? rsd / (double)n32 : 0.0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < P; ++p) {
       const int j = lane + 64 * p;
-      if (p < P && j < a.d) ub[wave][j] = y[p] * sc;
+      if (j < a.d) ub[wave][j] = (float)(y[p] * sc);
     }
     for (int w = lane; w < nw; w += 64) wb[wave][w] = 0u;
     __syncthreads();
-    for (int b = lane; b < a.nb; b += 64) {
-      float u[8];
+    for (int b0 = 0; b0 < nb; b0 += halves ? 32 : 64) {
+      const int b = b0 + (halves ? hb : lane);
+      const bool own = b < nb;
+      double u[K];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) u[e] = e < a.k ? ub[wave][b * a.k + e] : 0.0f;
-      int best = 0;
-      float bd = __builtin_inff();
-      for (int i = 0; i < a.N; ++i) {
-        float dd = 0.0f;
+      for (int e = 0; e < K; ++e) u[e] = own ? (double)ub[wave][b * K + e] : 0.0;
+      int best = i_lo;
+      double bd = __builtin_inf();
+      for (int i = i_lo; i < i_hi; ++i) {
+        double dd = 0.0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (e < a.k) {
-            const float df = u[e] - cb[i * a.k + e];
-            dd = fmaf(df, df, dd);
-          }
+        for (int e = 0; e < K; ++e) {
+          const double df = u[e] - cb[i * K + e];
+          dd = fma(df, df, dd);
         }
         if (dd < bd) {
           bd = dd;
           best = i;
         }
       }
-      const int pos = b * a.W, wi = pos >> 5, sh = pos & 31;
-      atomicOr(&wb[wave][wi], (uint32_t)best << sh);
-      if (sh + a.W > 32) atomicOr(&wb[wave][wi + 1], (uint32_t)best >> (32 - sh));
+      if (halves) {
+        // the upper half wins only when strictly nearer: ties keep the lower index
+        const double od = __shfl_xor(bd, 32, 64);
+        const int oi = __shfl_xor(best, 32, 64);
+        if (od < bd) best = oi;
+      }
+      if (own && (!halves || half == 0)) {
+        const int pos = b * a.W, wi = pos >> 5, sh = pos & 31;
+        atomicOr(&wb[wave][wi], (uint32_t)best << sh);
+        if (sh + a.W > 32) atomicOr(&wb[wave][wi + 1], (uint32_t)best >> (32 - sh));
+      }
     }
     __syncthreads();
     if (live) {
@@ -135,6 +153,25 @@ __global__ __launch_bounds__(64 * kEncWaves) void gram_encode_kernel(GramEncArgs
       if (lane == 0) r[nw] = __float_as_uint(n32);
     }
     __syncthreads();   // ub and wb are rewritten by the next step
+  }
+}
+
+template <int K, int P>
+int launch_encode_kp(const GramEncArgs& a, hipStream_t s) {
+  const int64_t steps = (a.G * a.Nv + kEncWaves - 1) / kEncWaves;
+  const int64_t blocks = steps < 8192 ? steps : 8192;
+  hipLaunchKernelGGL((gram_encode_kernel<K, P>), dim3((unsigned)blocks), dim3(64 * kEncWaves), 0, s, a);
+  return hipGetLastError() == hipSuccess ? 0 : TQ_ERR_HIP;
+}
+
+template <int K>
+int launch_encode_k(const GramEncArgs& a, hipStream_t s) {
+  switch (a.d <= 64 ? 1 : a.d / 64) {
+    case 1: return launch_encode_kp<K, 1>(a, s);
+    case 2: return launch_encode_kp<K, 2>(a, s);
+    case 4: return launch_encode_kp<K, 4>(a, s);
+    case 8: return launch_encode_kp<K, 8>(a, s);
+    default: return TQ_ERR_UNSUPPORTED;
   }
 }
 
@@ -262,10 +299,13 @@ int launch_gram_table(const float* C, int N, int k, float* G, hipStream_t s) {
 }
 
 int launch_gram_encode(const GramEncArgs& a, hipStream_t s) {
-  const int64_t steps = (a.G * a.Nv + kEncWaves - 1) / kEncWaves;
-  const int64_t blocks = steps < 4096 ? steps : 4096;
-  hipLaunchKernelGGL(gram_encode_kernel, dim3((unsigned)blocks), dim3(64 * kEncWaves), 0, s, a);
-  return hipGetLastError() == hipSuccess ? 0 : TQ_ERR_HIP;
+  switch (a.k) {
+    case 1: return launch_encode_k<1>(a, s);
+    case 2: return launch_encode_k<2>(a, s);
+    case 4: return launch_encode_k<4>(a, s);
+    case 8: return launch_encode_k<8>(a, s);
+    default: return TQ_ERR_UNSUPPORTED;
+  }
 }
 
 int launch_gram_scores(GramScoreArgs a, int W, int nb, int rw, hipStream_t s) {

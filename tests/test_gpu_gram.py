@@ -7,10 +7,12 @@ Tolerances come from the float32 arithmetic of the kernels:
   * table: k products summed by fma, |G32 - G| <= k u sum_e |c_ie c_je|;
   * scores: the table entry times scale n_q (2 roundings), nb additions and
     the product by n_t, so |s32 - s| <= (nb + k + 4) u scale n_q n_t nb max|G|;
-  * encode: the indices are decided in float32 after a float32 transform, so
-    an index may differ from the oracle's only where the oracle's two squared
-    distances are within a band (1e-5 of the mean distance); norms are the
-    float32 rounding of a float64 sum and must agree bit for bit.
+  * encode: both sides decide on the rotated coordinates rounded to float32
+    (from a float64 transform) with float64 squared distances, so an index may
+    differ only where a coordinate sits on a float32 rounding boundary or two
+    distances tie to float64 rounding: the oracle's two distances must then be
+    within 1e-6 of the mean distance, and such blocks stay below 1e-5 of all;
+    norms are the float32 rounding of a float64 sum and agree bit for bit.
 with u = 2^-24.
 """
 import math
@@ -49,11 +51,11 @@ def _check_codes(gpu_rec, ref_rec, dist, d, k, N, what):
     oi, on = gram.unpack_record(ref_rec, d, k, N)
     assert np.array_equal(gn.astype(np.float32), on.astype(np.float32)), f"{what}: norms"
     bad = np.argwhere(gi != oi)
-    band = 1e-5 * float(np.mean(dist))
+    band = 1e-6 * float(np.mean(dist))
     for r, blk in bad:
         gap = dist[r, blk, gi[r, blk]] - dist[r, blk, oi[r, blk]]
         assert 0.0 <= gap <= band, (what, int(r), int(blk), gap, band)
-    assert len(bad) <= max(2, gi.size // 1000), (what, len(bad), gi.size)
+    assert len(bad) <= max(1, gi.size // 100000), (what, len(bad), gi.size)
 
 
 @pytest.mark.parametrize("d,k,N,dtype,G,Nv", [
