@@ -259,13 +259,23 @@ int tq_append_kv(int head_dim, int k_bits, int v_bits, int projections, const vo
   const bool head_major = H_kv % n_kcb == 0 && H_kv % n_vcb == 0;
   const int64_t G = head_major ? H_kv : B * H_kv, N = head_major ? B : 1;
   const int64_t sx_g = head_dim, sx_n = head_major ? H_kv * head_dim : head_dim;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // The MFMA encode writes each record straight into its page slot.
+  if (fast128_encode_supported(K, x_dtype, k_new, sx_g, sx_n, N) &&
+      fast128_encode_supported(V, x_dtype, v_new, sx_g, sx_n, N)) {
+    const PagedOut po{page_table, pos, max_pages, num_pages, H_kv, tokens_per_page, head_major};
+    rc = launch_encode_fast128(K, kcbs, n_kcb, k_new, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(kpool),
+                               status, s, &po);
+    if (rc) return rc;
+    return launch_encode_fast128(V, vcbs, n_vcb, v_new, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(vpool),
+                                 status, s, &po);
+  }
   rc = encode_common(TQ_ROLE_KEY, head_dim, k_bits, projections, kRotHadamard, kcbs, n_kcb, k_new, x_dtype, G, N,
                      sx_g, sx_n, kst, status, stream);
   if (rc) return rc;
   rc = encode_common(TQ_ROLE_VALUE, head_dim, v_bits, 0, kRotHadamard, vcbs, n_vcb, v_new, x_dtype, G, N, sx_g,
                      sx_n, vst, status, stream);
   if (rc) return rc;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   rc = launch_page_scatter(kst, head_major, B, H_kv, K.rec_words, pos, page_table, max_pages, tokens_per_page,
                            num_pages, static_cast<uint32_t*>(kpool), status, s);
   if (rc) return rc;

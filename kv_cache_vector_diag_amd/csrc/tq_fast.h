@@ -11,9 +11,23 @@ namespace tq {
 // Encode with the MFMA kernel: head_dim 128; keys with 128 projections and
 // 1..3 Lloyd bits; values with 1..4 bits; 16-byte aligned rows; a group's
 // records under 2^30 bytes (32-bit buffer offsets).
+// With `po` (paged output, Walsh-Hadamard codebooks), rec is a pool
+// [num_pages][Hkv][tpp][rec_words]: the record of token t of group g goes to page
+// page_table[b][pos[b] / tpp], slot pos[b] % tpp, kv head h, where (b, h) =
+// (t, g) when head_major (groups are kv heads, tokens are sequences), else
+// (g / Hkv, g % Hkv); a position or page outside the table or pool stores
+// nothing and sets TQ_STATUS_BAD_PAGE.
+struct PagedOut {
+  const int32_t* page_table;
+  const int32_t* pos;
+  int64_t max_pages, num_pages, Hkv;
+  int tpp;
+  bool head_major;
+};
 bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N);
 int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
-                          int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
+                          int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
+                          const PagedOut* po = nullptr);
 
 // Scores with the int8-MFMA kernel: head_dim 128, 128 projections, key bits
 // 2..4, 1, 2 or 4 query heads per kv head, 8-byte aligned records, and a

@@ -58,6 +58,7 @@ struct Enc128Args {
   int64_t tiles_per_group;   // ceil(N / 32)
   int64_t tiles_per_block;
   int64_t blocks_per_group;
+  PagedOut po;               // paged output (the PAGED kernels): rec is the pool
 };
 
 // H_128 = H_4 (x) H_32 (Sylvester order): with row r = 32M + r', column
@@ -159,7 +160,19 @@ __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
 template <bool KEY, bool HAAR>
 constexpr size_t enc_lds_bytes() { return (HAAR ? 98304 : 32768) + (KEY ? 32768 : 0) + 128; }
 
-template <int K, bool KEY, int DT, bool HAAR>
+// The page slot of token tok of group g for paged output, or null (the status
+// word flagged) when the position or its page lies outside the table or pool.
+__device__ inline uint32_t* paged_slot(const Enc128Args& a, int64_t g, int64_t tok, int rw) {
+  const PagedOut& po = a.po;
+  const int64_t b = po.head_major ? tok : g / po.Hkv, hd = po.head_major ? g : g % po.Hkv;
+  const int32_t p = po.pos[b];
+  const int64_t pi = p >= 0 ? p / po.tpp : po.max_pages;
+  const int32_t page = pi < po.max_pages ? po.page_table[b * po.max_pages + pi] : -1;
+  if (page < 0 || page >= po.num_pages) return nullptr;
+  return a.rec + ((page * po.Hkv + hd) * po.tpp + p % po.tpp) * rw;
+}
+
+template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
 __global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode128_kernel(Enc128Args a) {
   constexpr int kWaves = waves_for<K, KEY, DT, HAAR>();
   constexpr int kRotBytes = HAAR ? 98304 : 32768;
@@ -203,8 +216,10 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode12
   const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles_per_group);
   const uint32_t* xb16 = reinterpret_cast<const uint32_t*>(a.x);
   constexpr int RW = KEY ? (K * 4 + 4 + 2) : (K * 4 + 1);
+  // (paged output stores through per-lane page slots; its resource is empty)
   const __amdgpu_buffer_rsrc_t rrs =
-      __builtin_amdgcn_make_buffer_rsrc(a.rec + g * a.N * RW, 0, (int)(a.N * RW * 4), kRsrcWord3);
+      __builtin_amdgcn_make_buffer_rsrc(PAGED ? a.rec : a.rec + g * a.N * RW, 0, PAGED ? 0 : (int)(a.N * RW * 4),
+                                        kRsrcWord3);
 
   // bf16/f16 inputs: the next tile's rows are loaded while this tile is encoded
   const auto row_ptr = [&](int64_t t) {
@@ -514,17 +529,29 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode12
     // every store is issued: one past the group's records (a ragged tail's
     // token, the odd word of a value record) is dropped by the buffer bounds,
     // so the next tile's loads never wait for this tile's stores
-    const uint32_t ro = valid ? (uint32_t)(tok * R * 4) : 0xC0000000u;
+    if constexpr (PAGED) {
+      uint32_t* dst = valid ? paged_slot(a, g, tok, R) : nullptr;
+      if (valid && !dst && h == 0 && a.status) atomicOr(a.status, TQ_STATUS_BAD_PAGE);
+      if (dst) {
 #pragma unroll
-    for (int q = 0; q < (R + 1) / 2; ++q) {
-      const int wi = 2 * q + h;
-      const uint32_t v = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
-      __builtin_amdgcn_raw_buffer_store_b32(v, rrs, wi < R ? ro + 4u * wi : 0xC0000000u, 0, 0);
+        for (int q = 0; q < (R + 1) / 2; ++q) {
+          const int wi = 2 * q + h;
+          if (wi < R) dst[wi] = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
+        }
+      }
+    } else {
+      const uint32_t ro = valid ? (uint32_t)(tok * R * 4) : 0xC0000000u;
+#pragma unroll
+      for (int q = 0; q < (R + 1) / 2; ++q) {
+        const int wi = 2 * q + h;
+        const uint32_t v = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
+        __builtin_amdgcn_raw_buffer_store_b32(v, rrs, wi < R ? ro + 4u * wi : 0xC0000000u, 0, 0);
+      }
     }
   }
 }
 
-template <int K, bool KEY, int DT, bool HAAR>
+template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
 int launch_one(Enc128Args a, hipStream_t s) {
   constexpr int kWaves = waves_for<K, KEY, DT, HAAR>();
   // ~256 workgroups (one per CU) in total, at least 8 tiles per wave, never more
@@ -538,23 +565,29 @@ int launch_one(Enc128Args a, hipStream_t s) {
   const size_t lds = enc_lds_bytes<KEY, HAAR>();
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_kernel<K, KEY, DT, HAAR>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_kernel<K, KEY, DT, HAAR, PAGED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return -10;
     attr_set = true;
   }
   const int64_t blocks = a.G * a.blocks_per_group;
-  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT, HAAR>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT, HAAR, PAGED>), dim3((unsigned)blocks),
                      dim3(64 * waves_for<K, KEY, DT, HAAR>()), lds, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
 template <int K, bool KEY>
-int launch_dt(const Enc128Args& a, int dt, bool haar, hipStream_t s) {
-  if (haar) return dt == TQ_F16 ? launch_one<K, KEY, 2, true>(a, s) : launch_one<K, KEY, 1, true>(a, s);
-  if (dt == TQ_BF16) return launch_one<K, KEY, 1, false>(a, s);
-  if (dt == TQ_F16) return launch_one<K, KEY, 2, false>(a, s);
-  return launch_one<K, KEY, 0, false>(a, s);
+int launch_dt(const Enc128Args& a, int dt, bool haar, bool paged, hipStream_t s) {
+  if (paged) {
+    if (haar) return -13;
+    if (dt == TQ_BF16) return launch_one<K, KEY, 1, false, true>(a, s);
+    if (dt == TQ_F16) return launch_one<K, KEY, 2, false, true>(a, s);
+    return launch_one<K, KEY, 0, false, true>(a, s);
+  }
+  if (haar) return dt == TQ_F16 ? launch_one<K, KEY, 2, true, false>(a, s) : launch_one<K, KEY, 1, true, false>(a, s);
+  if (dt == TQ_BF16) return launch_one<K, KEY, 1, false, false>(a, s);
+  if (dt == TQ_F16) return launch_one<K, KEY, 2, false, false>(a, s);
+  return launch_one<K, KEY, 0, false, false>(a, s);
 }
 
 }  // namespace
@@ -572,8 +605,10 @@ bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t
 }
 
 int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
-                          int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s) {
+                          int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
+                          const PagedOut* po) {
   Enc128Args a;
+  a.po = po ? *po : PagedOut{};
   a.cbs = static_cast<const uint8_t*>(cbs);
   a.stride = L.total;
   a.n_cb = n_cb;
@@ -587,13 +622,13 @@ int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
   const bool key = L.role == TQ_ROLE_KEY;
   const bool haar = L.rotation == kRotHaar;
   switch (L.k * 2 + (key ? 1 : 0)) {
-    case 1 * 2 + 1: return launch_dt<1, true>(a, dtype, haar, s);
-    case 2 * 2 + 1: return launch_dt<2, true>(a, dtype, haar, s);
-    case 3 * 2 + 1: return launch_dt<3, true>(a, dtype, haar, s);
-    case 1 * 2: return launch_dt<1, false>(a, dtype, haar, s);
-    case 2 * 2: return launch_dt<2, false>(a, dtype, haar, s);
-    case 3 * 2: return launch_dt<3, false>(a, dtype, haar, s);
-    case 4 * 2: return launch_dt<4, false>(a, dtype, haar, s);
+    case 1 * 2 + 1: return launch_dt<1, true>(a, dtype, haar, po != nullptr, s);
+    case 2 * 2 + 1: return launch_dt<2, true>(a, dtype, haar, po != nullptr, s);
+    case 3 * 2 + 1: return launch_dt<3, true>(a, dtype, haar, po != nullptr, s);
+    case 1 * 2: return launch_dt<1, false>(a, dtype, haar, po != nullptr, s);
+    case 2 * 2: return launch_dt<2, false>(a, dtype, haar, po != nullptr, s);
+    case 3 * 2: return launch_dt<3, false>(a, dtype, haar, po != nullptr, s);
+    case 4 * 2: return launch_dt<4, false>(a, dtype, haar, po != nullptr, s);
     default: return -13;
   }
 }
