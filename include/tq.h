@@ -251,7 +251,8 @@ int tq_attend_ex(int head_dim, int k_bits, int v_bits, int projections, int rota
  * A negative position, one at or past max_pages * tokens_per_page, or a page
  * outside [0, num_pages) writes nothing for that sequence and sets
  * TQ_STATUS_BAD_PAGE.  `work`: caller scratch of tq_append_workspace_bytes(...)
- * bytes.  Walsh-Hadamard codebooks. */
+ * bytes (staging for shapes the head_dim-128 kernels do not take; at head_dim
+ * 128 the records go straight to their page slots).  Walsh-Hadamard codebooks. */
 size_t tq_append_workspace_bytes(int head_dim, int k_bits, int v_bits, int projections, int64_t B, int64_t H_kv);
 int tq_append_kv(int head_dim, int k_bits, int v_bits, int projections,
                  const void* kcbs, int64_t n_kcb, const void* vcbs, int64_t n_vcb,
