@@ -415,7 +415,7 @@ def bench_paged(args, torch, b):
     sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
     ms_step = wall * 1e3 / args.steps
     sc_bytes = G * T * kw * 4 + B * Hq * T * 4 + q.numel() * 2 + kcb.numel()
-    ap_bytes = G * (2 * d * 2 + (kw + vw) * 4) * 2        # vectors in, records staged out and in, pool writes
+    ap_bytes = G * (2 * d * 2 + (kw + vw) * 4)            # vectors in, records written into their page slots
     return {"metric": "paged decode step tokens/s (append one token per sequence + score the paged 32K context)",
             "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",

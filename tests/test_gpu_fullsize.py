@@ -10,7 +10,9 @@ sampled groups and tokens, regenerating exactly those inputs on the CPU.
     (seed 4); attention output of sampled (sequence, head) pairs.
   * mixed-precision layers: 32 layers x 8 kv heads x 16384 tokens, d=256, per-
     channel std log-uniform in [0.5, 8] (seed 5); boundary layers b=8, others
-    split (32 outliers at 4 bits, 224 channels at 3 bits, Haar)."""
+    split (32 outliers at 4 bits, 224 channels at 3 bits, Haar).
+  * Gram-table scoring, the paged decode step and the Haar-rotation step at
+    their bench shapes (below)."""
 import numpy as np
 import pytest
 
@@ -210,3 +212,90 @@ def test_gram_scoring_32k_full_size(gpu_lib):
             _, qn = gram.unpack_record(qref[bb, hq][None, :], d, k, N)
             bound = (d // k + k + 4) * U / math.sqrt(d) * qn[0] * kn * (d // k) * Gmax
             assert np.all(np.abs(got[i] - ref[i])[same_k] <= bound[same_k])
+
+
+def test_paged_decode_step_full_size(gpu_lib):
+    """The paged decode step at its bench shape (16 x 8 kv heads x 32768 cached
+    tokens in shuffled pages of 256, turbo3 keys and 3-bit values, 32 query
+    heads): one token appended per sequence, then the 32769 paged keys scored.
+    The appended slots equal the batch encode of the new vectors, the paged
+    scores equal tq_scores over the contiguous records bit for bit, and sampled
+    rows match the oracle's scores of those records."""
+    import torch
+    b = gpu_lib
+    B, Hkv, Hq, T, d, kb, vb, m, P, seed = 16, 8, 32, 32768, 128, 3, 3, 128, 256, 3
+    G = B * Hkv
+    kw = b.tq_record_bytes(d, kb, m, b.ROLE_KEY) // 4
+    vw = b.tq_record_bytes(d, vb, 0, b.ROLE_VALUE) // 4
+    kcb = b.make_codebooks(Hkv, d, kb, m, seed, b.ROLE_KEY, device=DEV)
+    vcb = b.make_codebooks(Hkv, d, vb, 0, seed + 1, b.ROLE_VALUE, device=DEV)
+    max_pages = T // P + 1
+    num_pages = B * max_pages
+    perm = torch.randperm(num_pages, generator=torch.Generator().manual_seed(seed)).to(torch.int32)
+    table = perm.view(B, max_pages).to(DEV)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d), "bf16", DEV)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, kb, m).view(B, Hkv, T, kw)
+    del K
+    kpool = torch.full((num_pages, Hkv, P, kw), -1, dtype=torch.int32, device=DEV)
+    vpool = torch.full((num_pages, Hkv, P, vw), -1, dtype=torch.int32, device=DEV)
+    kpool[table[:, : T // P].reshape(-1).long()] = krec.view(B, Hkv, T // P, P, kw).permute(0, 2, 1, 3, 4).reshape(
+        -1, Hkv, P, kw)
+    kn = inputs.to_torch(inputs.kv_normal(seed + 5, B, Hkv, d), "bf16", DEV).contiguous()
+    vn = inputs.to_torch(inputs.kv_normal(seed + 6, B, Hkv, d), "bf16", DEV).contiguous()
+    pos = torch.full((B,), T, dtype=torch.int32, device=DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    b.tq_append_kv(kcb, Hkv, vcb, Hkv, kn, vn, d, kb, vb, m, pos, table, P, kpool, vpool, status=st)
+    sp = b.tq_scores_paged(kcb, Hkv, kpool, table, P, T + 1, q, d, kb, m, status=st)
+    knew = b.tq_encode_keys(kcb, Hkv, kn.transpose(0, 1).contiguous(), d, kb, m)      # [H_kv][B] records
+    vnew = b.tq_encode_values(vcb, Hkv, vn.transpose(0, 1).contiguous(), d, vb)
+    full = torch.cat([krec, knew.transpose(0, 1).unsqueeze(2)], dim=2).contiguous()
+    sc = b.tq_scores(kcb, Hkv, full, q, d, kb, m)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    last = table[:, T // P].long()
+    assert torch.equal(kpool[last, :, 0], knew.transpose(0, 1))
+    assert torch.equal(vpool[last, :, 0], vnew.transpose(0, 1))
+    assert torch.equal(sp, sc)
+    qzs = tq.quantizers(Hkv, d, kb, m, seed, tq.ROLE_KEY)
+    qv = inputs.exact_values(q)
+    rng = np.random.default_rng(2)
+    for bb, h in ((0, 0), (7, 3), (B - 1, Hkv - 1)):
+        toks = _sample_tokens(rng, T + 1, 1500)
+        grec = rec_np(full[bb, h])[toks]
+        ref = tq.scores([qzs[h]], grec[None, None], qv[bb:bb + 1, 4 * h:4 * h + 4])
+        assert_close(sp[bb:bb + 1, 4 * h:4 * h + 4].cpu().numpy()[:, :, toks], ref, f"paged scores b={bb} h={h}")
+
+
+def test_haar_encode_and_scores_full_size(gpu_lib):
+    """Haar-rotation codebooks at their bench shape (16 x 8 kv heads x 4096
+    tokens, d=128, bf16 keys b=3 with 128 projections, 32 query heads), on the
+    matrix-core encode and the score kernel: sampled tokens of three groups
+    against the oracle, records and scores."""
+    import torch
+    b = gpu_lib
+    B, Hkv, Hq, T, d, bits, m, seed = 16, 8, 32, 4096, 128, 3, 128, 3
+    G = B * Hkv
+    kcb = b.make_codebooks(Hkv, d, bits, m, seed, b.ROLE_KEY, device=DEV, rotation=b.ROT_HAAR)
+    qzs = [tq.Quantizer(d, bits, m, seed + h, tq.ROLE_KEY, rotation=tq.ROT_HAAR) for h in range(Hkv)]
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rec = b.tq_encode_keys(kcb, Hkv, K, d, bits, m, status=st, rotation=b.ROT_HAAR)
+    scores = b.tq_scores(kcb, Hkv, rec.view(B, Hkv, T, -1), q, d, bits, m, status=st, rotation=b.ROT_HAAR)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    del K
+    rng = np.random.default_rng(3)
+    qv = inputs.exact_values(q)
+    reps = []
+    for g in (0, 45, G - 1):
+        toks = _sample_tokens(rng, T, 1000)
+        X = _bf16_exact(inputs.kv_normal(seed, G, T, d, groups=[g]))[0][toks]
+        grec = rec_np(rec[g])[toks]
+        reps.append(compare_records(qzs[g % Hkv], grec, tq.encode(qzs[g % Hkv], X), fraction=False))
+        bb, h = divmod(g, Hkv)
+        ref = tq.scores([qzs[h]], grec[None, None], qv[bb:bb + 1, 4 * h:4 * h + 4])
+        got = scores[bb, 4 * h:4 * h + 4][:, torch.from_numpy(toks).to(DEV)].cpu().numpy()[None]
+        assert_close(got, ref, f"Haar scores g={g}")
+    check_mismatch_fraction(reps)
