@@ -18,7 +18,10 @@
 //    wave; the bf16 row is the B operand as it is, in natural channel order.
 //    The contraction runs chunk-outer: for each 16-channel chunk, its slice of
 //    fragments (all row tiles) is staged in LDS (double buffered) and shared by
-//    the 8 waves, and the 7 + 2 row-tile accumulators stay in registers.
+//    the 8 waves, and the 7 + 2 row-tile accumulators stay in registers.  The
+//    next slice goes straight from memory into LDS (buffer loads to LDS) while
+//    the current one feeds the matrix cores; the two buffers are distinct
+//    arrays, so reading one never waits for the loads into the other.
 //  * Norms: |x|^2 in float64 from pair sums; |x_o|^2 exactly from the gathered
 //    outlier channels; |x_n|^2 = |x|^2 - |x_o|^2.
 #include <hip/hip_runtime.h>
@@ -57,7 +60,7 @@ constexpr int kOutFrags = 2 * kKC + 2;            // outlier fragments kept in L
 
 constexpr size_t kLdsOut = (size_t)kOutFrags * kFragLanes * 16;     // 34 KB
 constexpr size_t kLdsSlice = (size_t)kSliceR * kFragLanes * 16;     // 21 KB
-constexpr size_t kLdsBytes = kLdsOut + 2 * kLdsSlice + 256;
+constexpr size_t kLdsBytes = kLdsOut + 256;   // the two slice buffers are static arrays
 
 struct PrepArgs {
   const uint8_t* cbn;
@@ -249,12 +252,17 @@ __device__ inline void store_record(const uint32_t* part, const uint32_t* tail, 
   }
 }
 
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
 template <int KN, int KO, bool KEY>
 __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
+  // slice buffers: two distinct arrays, so that a DMA into one never makes the
+  // reads of the other wait for it
+  __shared__ __align__(16) u32x4 slice_a[kSliceR * kFragLanes];
+  __shared__ __align__(16) u32x4 slice_b[kSliceR * kFragLanes];
   u32x4* ofr = reinterpret_cast<u32x4*>(smem);
-  u32x4* slice = reinterpret_cast<u32x4*>(smem + kLdsOut);
-  float* consts = reinterpret_cast<float*>(smem + kLdsOut + 2 * kLdsSlice);
+  float* consts = reinterpret_cast<float*>(smem + kLdsOut);
   constexpr int LN = 1 << KN, LO = 1 << KO;
   constexpr int NTN = LN / 2 - 1, NTO = LO / 2 - 1;
 
@@ -310,6 +318,21 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       const auto frag_at = [&](uint32_t entry) {
         return *reinterpret_cast<const u32x4*>(frb + (size_t)(entry * 16u));
       };
+      (void)frag_at;
+      const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(frb), 0, a.frags * kFragLanes * 16, kRsrcWord3);
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      // fragments nbase .. nbase + nent of the group straight into an LDS slice
+      // buffer, 64 entries (1 KB) per wave and round
+      const auto dma = [&](u32x4* dst, uint32_t nbase, int nent) {
+#pragma unroll
+        for (int i = 0; i < (kSliceEntries + kThreads - 1) / kThreads; ++i) {
+          const int e0 = i * kThreads + wv * 64;
+          if (e0 < nent)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(frs, (lds_u32*)(dst + e0), 16, (nbase + (uint32_t)(e0 + lane)) * 16u,
+                                                     0, 0, 0);
+        }
+      };
       const int64_t tile = base + wave;
       const int64_t tok = tile * 32 + col;
       const bool valid = tile < tile_end && tok < a.N;
@@ -323,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       for (int c = 0; c < kXPre; ++c) xb[c] = *reinterpret_cast<const u32x4*>(xr + 8 * c + 4 * h);
       double ss = 0.0;
       __syncthreads();                                     // slice buffers free
-      for (int i = tid; i < kSliceEntries; i += kThreads) slice[i] = frag_at(kOffR * kFragLanes + i);
+      dma(slice_a, kOffR * kFragLanes, kSliceEntries);
 
       // ---- rotation, chunk-outer: u[m] (normal tiles), uo (outlier), xo (outlier gather)
       f32x16 u[kMT];
@@ -332,20 +355,20 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       f32x16 uo = {}, xo = {};
 #pragma unroll
       for (int c = 0; c < kKC; ++c) {
+        // this wave's slice DMA has landed: it was issued before the one x chunk
+        // load of the previous chunk (if any), and loads complete in order
+        if (c >= 1 && c - 1 + kXPre < kKC) __builtin_amdgcn_s_waitcnt(0x0F71);   // vmcnt(1)
+        else __builtin_amdgcn_s_waitcnt(0x0F70);                                // vmcnt(0)
         __syncthreads();                                   // slice c complete; the other buffer free
-        const u32x4* cur = slice + (c & 1) * kSliceEntries;
-        u32x4* nxt = slice + ((c + 1) & 1) * kSliceEntries;
+        const u32x4* cur = (c & 1) ? slice_b : slice_a;
+        u32x4* nxt = (c & 1) ? slice_a : slice_b;
         // next slice: rotation chunk c+1, or (keys, after the last) projection slice 0
         const bool more = c + 1 < kKC || KEY;
         const int nent = (c + 1 < kKC ? kSliceR : kSliceS) * kFragLanes;
         const uint32_t nbase = c + 1 < kKC ? (uint32_t)((kOffR + (c + 1) * kSliceR) * kFragLanes)
                                            : (uint32_t)(kOffS * kFragLanes);
-        u32x4 pre[kPre];
-#pragma unroll
-        for (int i = 0; i < kPre; ++i) {
-          const int idx = tid + i * kThreads;
-          if (more && idx < nent) pre[i] = frag_at(nbase + (uint32_t)idx);
-        }
+        if (more) dma(nxt, nbase, nent);
+        __builtin_amdgcn_sched_barrier(0);                 // the DMA before the x chunk load
         if (c + kXPre < kKC) xb[c + kXPre] = *reinterpret_cast<const u32x4*>(xr + 8 * (c + kXPre) + 4 * h);
 #pragma unroll
         for (int q = 0; q < 4; ++q) ss += pair_sumsq_bf16(xb[c][q]);
@@ -361,11 +384,6 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         }
         uo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[c * kFragLanes + lane]), xv, uo, 0, 0, 0);
         xo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[(kKC + c) * kFragLanes + lane]), xv, xo, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < kPre; ++i) {
-          const int idx = tid + i * kThreads;
-          if (more && idx < nent) nxt[idx] = pre[i];
-        }
       }
 
       // ---- norms (float64): |x|^2 from pair sums, |x_o|^2 from the exact gather
@@ -450,18 +468,13 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       if (KEY) {
 #pragma unroll
         for (int mp = 0; mp < kMT; ++mp) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): this wave's slice DMA has landed
           __syncthreads();
-          const u32x4* cur = slice + ((kKC + mp) & 1) * kSliceEntries;
-          u32x4* nxt = slice + ((kKC + mp + 1) & 1) * kSliceEntries;
+          const u32x4* cur = ((kKC + mp) & 1) ? slice_b : slice_a;
+          u32x4* nxt = ((kKC + mp) & 1) ? slice_a : slice_b;
           const bool more = mp + 1 < kMT;
           const uint32_t nbase = (uint32_t)((kOffS + (mp + 1) * kSliceS) * kFragLanes);
-          constexpr int kPreS = (kSliceS * kFragLanes + kThreads - 1) / kThreads;
-          u32x4 pre[kPreS];
-#pragma unroll
-          for (int i = 0; i < kPreS; ++i) {
-            const int idx = tid + i * kThreads;
-            if (more && idx < kSliceS * kFragLanes) pre[i] = frag_at(nbase + (uint32_t)idx);
-          }
+          if (more) dma(nxt, nbase, kSliceS * kFragLanes);
           f32x16 acc = {};
 #pragma unroll
           for (int c = 0; c < kQC; ++c) {
@@ -472,11 +485,6 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
           }
           sw_n[mp] = sign_word(acc);
           asm volatile("" : "+v"(sw_n[mp]));   // materialise here (not next to the stores)
-#pragma unroll
-          for (int i = 0; i < kPreS; ++i) {
-            const int idx = tid + i * kThreads;
-            if (more && idx < kSliceS * kFragLanes) nxt[idx] = pre[i];
-          }
         }
         auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq_n), __float_as_uint(wsq_n), false, false);
         gam_n = sqrtf(__uint_as_float(pg[0]) + __uint_as_float(pg[1])) * 0.06681531047810609f;   // / sqrt(224)
