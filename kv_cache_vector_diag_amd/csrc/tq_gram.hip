@@ -322,6 +322,7 @@ int launch_gram_scores(GramScoreArgs a, int W, int nb, int rw, hipStream_t s) {
     return launch_fast_gq<6, 32>(a, (int)gq, blocks, s);
   }
   const int64_t tblocks = (a.T + 255) / 256;
+  if (a.B * a.Hq * tblocks > 0x7FFFFFFF) return TQ_ERR_UNSUPPORTED;   // one-dimensional grid
   hipLaunchKernelGGL(gram_scores_generic_kernel, dim3((unsigned)(a.B * a.Hq * tblocks)), dim3(256), 0, s, a, W, nb,
                      rw, tblocks);
   return hipGetLastError() == hipSuccess ? 0 : TQ_ERR_HIP;
