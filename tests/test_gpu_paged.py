@@ -134,3 +134,53 @@ def test_scores_from_paged_pool_equal_contiguous(gpu_lib, kb, B, Hkv, Hq, T, P):
     b.tq_scores_paged(kcb, Hkv, kpool, bad, P, T, q, d, kb, 128, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & 8
+
+
+def test_paged_step_in_a_graph_equals_eager(gpu_lib):
+    """The decode step (append + paged scores) captured in a HIP graph: every
+    replay, with eager work and synchronisations between the replays, gives the
+    eager step's pools and scores (the calls enqueue kernels only: no
+    allocation, copy or memset on the stream)."""
+    import torch
+    b = gpu_lib
+    d, kb, vb, m, B, Hkv, Hq, T, P = 128, 3, 3, 128, 3, 4, 8, 300, 64
+    K, V, kg, vg, kbatch, vbatch, kpool, table = _stream(b, d, kb, vb, m, B, Hkv, T, P, Hkv, Hkv, "bf16", seed=53)
+    kcb = b.make_codebooks(Hkv, d, kb, m, 53, b.ROLE_KEY, device=DEV)
+    vcb = b.make_codebooks(Hkv, d, vb, 0, 60, b.ROLE_VALUE, device=DEV)
+    vpool = torch.zeros((kpool.shape[0], Hkv, P, b.tq_record_bytes(d, vb, 0, b.ROLE_VALUE) // 4), dtype=torch.int32,
+                        device=DEV)
+    kn = inputs.to_torch(inputs.kv_normal(54, B, Hkv, d), "bf16", DEV).contiguous()
+    vn = inputs.to_torch(inputs.kv_normal(55, B, Hkv, d), "bf16", DEV).contiguous()
+    q = inputs.to_torch(inputs.queries(53, B, Hq, d), "bf16", DEV)
+    pos = torch.full((B,), T, dtype=torch.int32, device=DEV)
+    work = torch.empty(b.load().tq_append_workspace_bytes(d, kb, vb, m, B, Hkv), dtype=torch.uint8, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.empty((B, Hq, T + 1), dtype=torch.float32, device=DEV)
+
+    def step():
+        b.tq_append_kv(kcb, Hkv, vcb, Hkv, kn, vn, d, kb, vb, m, pos, table, P, kpool, vpool, work=work, status=st)
+        b.tq_scores_paged(kcb, Hkv, kpool, table, P, T + 1, q, d, kb, m, out=out, status=st)
+
+    step()
+    torch.cuda.synchronize()
+    ref_s, ref_k, ref_v = out.clone(), kpool.clone(), vpool.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                       # warm-up on the side stream before capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        kpool[table[:, T // P].long(), :, T % P] = -1
+        vpool[table[:, T // P].long(), :, T % P] = -1
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_s), f"replay {r}: scores"
+        assert torch.equal(kpool, ref_k) and torch.equal(vpool, ref_v), f"replay {r}: pools"
+        _ = (out.sum() + 1.0).item()   # eager work between the replays
+    assert int(st.item()) == 0
