@@ -189,3 +189,44 @@ def test_gram_end_to_end_encode_then_score(gpu_lib):
             assert np.all(np.abs(got[bb, hq] - ref[bb, hq])[m] <= bound[m])
             checked += int(m.sum())
     assert checked >= 0.99 * B * Hq * T
+
+
+def test_gram_step_in_a_graph_equals_eager(gpu_lib):
+    """Query encode + Gram scores captured in a HIP graph: every replay, with
+    eager work between the replays, equals the eager step."""
+    import torch
+    b = gpu_lib
+    d, k, N, B, Hkv, Hq, T, seed = 128, 4, 32, 2, 2, 8, 2100, 91
+    C = _t(inputs.block_codebook(seed, N, k, d))
+    sg = _t(inputs.sign_bits(seed, d).view(np.int32))
+    K = inputs.to_torch(inputs.kv_normal(seed, B * Hkv, T, d), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    krec = b.tq_gram_encode(C, sg, K, d).view(B, Hkv, T, -1)
+    table = b.tq_gram_table(C)
+    qrec = torch.empty((B, Hq, krec.shape[-1]), dtype=torch.int32, device=DEV)
+    out = torch.empty((B, Hq, T), dtype=torch.float32, device=DEV)
+
+    def step():
+        b.tq_gram_encode(C, sg, q, d, rec=qrec)
+        b.tq_gram_scores(table, qrec, krec, d, k, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref_q, ref_s = qrec.clone(), out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        qrec.zero_()
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(qrec, ref_q) and torch.equal(out, ref_s), f"replay {r}"
+        _ = (out.sum() + 1.0).item()
