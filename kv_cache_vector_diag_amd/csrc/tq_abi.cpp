@@ -264,6 +264,9 @@ int tq_append_kv(int head_dim, int k_bits, int v_bits, int projections, const vo
   if (fast128_encode_supported(K, x_dtype, k_new, sx_g, sx_n, N) &&
       fast128_encode_supported(V, x_dtype, v_new, sx_g, sx_n, N)) {
     const PagedOut po{page_table, pos, max_pages, num_pages, H_kv, tokens_per_page, head_major};
+    rc = launch_append_fast128(K, V, kcbs, n_kcb, vcbs, n_vcb, k_new, v_new, x_dtype, G, N, sx_g, sx_n,
+                               static_cast<uint32_t*>(kpool), static_cast<uint32_t*>(vpool), status, s, po);
+    if (rc != 1) return rc;
     rc = launch_encode_fast128(K, kcbs, n_kcb, k_new, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(kpool),
                                status, s, &po);
     if (rc) return rc;

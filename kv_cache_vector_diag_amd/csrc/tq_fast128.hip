@@ -172,8 +172,10 @@ __device__ inline uint32_t* paged_slot(const Enc128Args& a, int64_t g, int64_t t
   return a.rec + ((page * po.Hkv + hd) * po.tpp + p % po.tpp) * rw;
 }
 
+// The encode of workgroup `bid` of a launch over a's groups (the kernels below
+// run it for their own workgroup index).
 template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
-__global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode128_kernel(Enc128Args a) {
+__device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid) {
   constexpr int kWaves = waves_for<K, KEY, DT, HAAR>();
   constexpr int kRotBytes = HAAR ? 98304 : 32768;
   static_assert(!HAAR || DT != 0, "the Haar rotation takes 16-bit inputs");
@@ -184,8 +186,8 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode12
 
   constexpr int L = 1 << K;
   constexpr int NT = L / 2 - 1;  // positive thresholds
-  const int64_t g = blockIdx.x / a.blocks_per_group;
-  const int64_t chunk = blockIdx.x % a.blocks_per_group;
+  const int64_t g = bid / a.blocks_per_group;
+  const int64_t chunk = bid % a.blocks_per_group;
   const uint8_t* blob = a.cbs + (g % a.n_cb) * a.stride;
   if (threadIdx.x == 0 && a.status) {
     const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(blob);
@@ -552,16 +554,38 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode12
 }
 
 template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
-int launch_one(Enc128Args a, hipStream_t s) {
-  constexpr int kWaves = waves_for<K, KEY, DT, HAAR>();
-  // ~256 workgroups (one per CU) in total, at least 8 tiles per wave, never more
-  // than the group holds; a multiple of the wave count
+__global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode128_kernel(Enc128Args a) {
+  encode128_body<K, KEY, DT, HAAR, PAGED>(a, blockIdx.x);
+}
+
+// Keys and values of an append in one launch (paged output): the first
+// ka.G * ka.blocks_per_group workgroups encode the keys, the rest the values.
+// Both roles run the same wave count, and the LDS is the keys' (the larger).
+template <int KK, int KV, int DT>
+__global__ __launch_bounds__((64 * waves_for<KK, true, DT, false>())) void encode128_pair_kernel(Enc128Args ka,
+                                                                                                 Enc128Args va) {
+  static_assert(waves_for<KK, true, DT, false>() == waves_for<KV, false, DT, false>(), "one workgroup shape");
+  const int64_t nk = ka.G * ka.blocks_per_group;
+  if ((int64_t)blockIdx.x < nk)
+    encode128_body<KK, true, DT, false, true>(ka, blockIdx.x);
+  else
+    encode128_body<KV, false, DT, false, true>(va, (int64_t)blockIdx.x - nk);
+}
+
+// ~256 workgroups (one per CU) in total, at least 8 tiles per wave, never more
+// than the group holds; a multiple of the wave count.
+inline void split_tiles(Enc128Args& a, int waves) {
   int64_t per_block = (a.tiles_per_group * a.G + 255) / 256;
-  per_block = per_block < kWaves * 8 ? kWaves * 8 : per_block;
-  per_block = (per_block + kWaves - 1) / kWaves * kWaves;
-  if (per_block > a.tiles_per_group) per_block = (a.tiles_per_group + kWaves - 1) / kWaves * kWaves;
+  per_block = per_block < waves * 8 ? waves * 8 : per_block;
+  per_block = (per_block + waves - 1) / waves * waves;
+  if (per_block > a.tiles_per_group) per_block = (a.tiles_per_group + waves - 1) / waves * waves;
   a.tiles_per_block = per_block;
   a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
+}
+
+template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
+int launch_one(Enc128Args a, hipStream_t s) {
+  split_tiles(a, waves_for<K, KEY, DT, HAAR>());
   const size_t lds = enc_lds_bytes<KEY, HAAR>();
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
@@ -604,9 +628,10 @@ bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t
   return true;
 }
 
-int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
-                          int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
-                          const PagedOut* po) {
+namespace {
+
+Enc128Args make_args(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int64_t G, int64_t N,
+                     int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, const PagedOut* po) {
   Enc128Args a;
   a.po = po ? *po : PagedOut{};
   a.cbs = static_cast<const uint8_t*>(cbs);
@@ -619,6 +644,58 @@ int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const 
   a.bits = L.bits; a.role = L.role; a.rec_words = L.rec_words;
   a.off_c = L.off_c; a.off_t = L.off_t; a.off_d = L.off_d; a.off_s = L.off_s;
   a.tiles_per_group = (N + kTile - 1) / kTile;
+  return a;
+}
+
+template <int KK, int KV, int DT>
+int launch_pair(Enc128Args ka, Enc128Args va, hipStream_t s) {
+  constexpr int W = waves_for<KK, true, DT, false>();
+  split_tiles(ka, W);
+  split_tiles(va, W);
+  const size_t lds = enc_lds_bytes<true, false>();
+  static bool attr_set = false;   // idempotent; a race only repeats the call
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_pair_kernel<KK, KV, DT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return -10;
+    attr_set = true;
+  }
+  const int64_t blocks = ka.G * ka.blocks_per_group + va.G * va.blocks_per_group;
+  hipLaunchKernelGGL((encode128_pair_kernel<KK, KV, DT>), dim3((unsigned)blocks), dim3(64 * W), lds, s, ka, va);
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+template <int KK, int DT>
+int launch_pair_v(const Enc128Args& ka, const Enc128Args& va, int kv, hipStream_t s) {
+  switch (kv) {
+    case 1: return launch_pair<KK, 1, DT>(ka, va, s);
+    case 2: return launch_pair<KK, 2, DT>(ka, va, s);
+    case 3: return launch_pair<KK, 3, DT>(ka, va, s);
+    case 4: return launch_pair<KK, 4, DT>(ka, va, s);
+    default: return 1;
+  }
+}
+
+}  // namespace
+
+int launch_append_fast128(const Layout& K, const Layout& V, const void* kcbs, int64_t n_kcb, const void* vcbs,
+                          int64_t n_vcb, const void* k, const void* v, int dtype, int64_t G, int64_t N, int64_t sx_g,
+                          int64_t sx_n, uint32_t* kpool, uint32_t* vpool, int32_t* status, hipStream_t s,
+                          const PagedOut& po) {
+  if (K.rotation != kRotHadamard || V.rotation != kRotHadamard) return 1;
+  const Enc128Args ka = make_args(K, kcbs, n_kcb, k, G, N, sx_g, sx_n, kpool, status, &po);
+  const Enc128Args va = make_args(V, vcbs, n_vcb, v, G, N, sx_g, sx_n, vpool, status, &po);
+  // the pairs whose key and value kernels take the same workgroup shape
+  if (dtype == TQ_BF16 && K.k == 1) return launch_pair_v<1, 1>(ka, va, V.k, s);
+  if (dtype == TQ_BF16 && K.k == 2) return launch_pair_v<2, 1>(ka, va, V.k, s);
+  if (dtype == TQ_F16 && K.k == 1) return launch_pair_v<1, 2>(ka, va, V.k, s);
+  return 1;
+}
+
+int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
+                          int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
+                          const PagedOut* po) {
+  const Enc128Args a = make_args(L, cbs, n_cb, x, G, N, sx_g, sx_n, rec, status, po);
   const bool key = L.role == TQ_ROLE_KEY;
   const bool haar = L.rotation == kRotHaar;
   switch (L.k * 2 + (key ? 1 : 0)) {

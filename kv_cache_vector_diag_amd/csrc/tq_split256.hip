@@ -59,7 +59,6 @@ constexpr int kSliceS = kQC;                      // fragments per projection sl
 constexpr int kOutFrags = 2 * kKC + 2;            // outlier fragments kept in LDS (34)
 
 constexpr size_t kLdsOut = (size_t)kOutFrags * kFragLanes * 16;     // 34 KB
-constexpr size_t kLdsSlice = (size_t)kSliceR * kFragLanes * 16;     // 21 KB
 constexpr size_t kLdsBytes = kLdsOut + 256;   // the two slice buffers are static arrays
 
 struct PrepArgs {
@@ -308,17 +307,12 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
     const int64_t tile0 = chunk * a.tiles_per_block;
     const int64_t tile_end = min(tile0 + a.tiles_per_block, a.tiles_per_group);
     constexpr int kSliceEntries = kSliceR * kFragLanes;   // u32x4 per rotation slice
-    constexpr int kPre = (kSliceEntries + kThreads - 1) / kThreads;
     for (int64_t base = tile0; base < tile_end; base += kWaves) {
       // re-derive the fragment base each step (opaque to the compiler), so that
       // the slice addresses are not hoisted out of the loop into dozens of
       // 64-bit registers; offsets below are 32-bit, from a uniform base
       const uint8_t* frb = reinterpret_cast<const uint8_t*>(fr);
       asm volatile("" : "+s"(frb));
-      const auto frag_at = [&](uint32_t entry) {
-        return *reinterpret_cast<const u32x4*>(frb + (size_t)(entry * 16u));
-      };
-      (void)frag_at;
       const __amdgpu_buffer_rsrc_t frs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint8_t*>(frb), 0, a.frags * kFragLanes * 16, kRsrcWord3);
       const int wv = __builtin_amdgcn_readfirstlane(wave);
