@@ -230,3 +230,50 @@ def test_gram_step_in_a_graph_equals_eager(gpu_lib):
         torch.cuda.synchronize()
         assert torch.equal(qrec, ref_q) and torch.equal(out, ref_s), f"replay {r}"
         _ = (out.sum() + 1.0).item()
+
+
+def _gram_cases(n=12, seed=77):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(r.choice([2, 8, 32, 64, 128, 128, 256, 512]))
+        k = int(r.choice([x for x in (1, 2, 4, 8) if x <= d]))
+        N = int(r.choice([2, 4, 16, 32, 32, 64, 256]))
+        Hkv = int(r.choice([1, 2, 4]))
+        gq = int(r.choice([1, 2, 3, 4]))
+        out.append((i, d, k, N, str(r.choice(["bf16", "f16", "f32"])), int(r.integers(1, 3)), Hkv, Hkv * gq,
+                    int(r.integers(1, 2500))))
+    return out
+
+
+@pytest.mark.parametrize("i,d,k,N,dtype,B,Hkv,Hq,T", _gram_cases())
+def test_gram_sweep(gpu_lib, i, d, k, N, dtype, B, Hkv, Hq, T):
+    """Seeded shapes across both score kernels: GPU encode of keys and queries
+    against the oracle's codes, then the GPU scores of the oracle's records
+    against the oracle's scores."""
+    import torch
+    b = gpu_lib
+    seed = 500 + i
+    C = inputs.block_codebook(seed, N, k, d)
+    s = inputs.sign_bits(seed, d)
+    K = inputs.to_torch(inputs.kv_normal(seed, B * Hkv, T, d), dtype, DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), dtype, DEV)
+    Ct, st = _t(C), _t(s.view(np.int32))
+    krec = b.tq_gram_encode(Ct, st, K, d)
+    qrec = b.tq_gram_encode(Ct, st, q, d)
+    torch.cuda.synchronize()
+    kref, _, kdist = gram.encode(C, s, inputs.exact_values(K).reshape(-1, d), d, k)
+    qref, _, qdist = gram.encode(C, s, inputs.exact_values(q).reshape(-1, d), d, k)
+    _check_codes(rec_np(krec).reshape(-1, krec.shape[-1]), kref, kdist, d, k, N, f"keys case {i}")
+    _check_codes(rec_np(qrec).reshape(-1, qrec.shape[-1]), qref, qdist, d, k, N, f"queries case {i}")
+    w = kref.shape[-1]
+    sc = b.tq_gram_scores(b.tq_gram_table(Ct), _t(qref.reshape(B, Hq, w).view(np.int32)),
+                          _t(kref.reshape(B, Hkv, T, w).view(np.int32)), d, k)
+    ref = gram.scores(C, qref.reshape(B, Hq, w), kref.reshape(B, Hkv, T, w), d, k)
+    _, qn = gram.unpack_record(qref, d, k, N)
+    _, kn = gram.unpack_record(kref, d, k, N)
+    nb = d // k
+    Gmax = float(np.max(np.abs(gram.gram_table(C))))
+    kv = kn.reshape(B, Hkv, T)[:, np.arange(Hq) * Hkv // Hq, :]
+    bound = (nb + k + 4) * U / math.sqrt(d) * qn.reshape(B, Hq, 1) * kv * nb * Gmax + 1e-30
+    assert np.all(np.abs(sc.cpu().numpy().astype(np.float64) - ref) <= bound), f"scores case {i}"
