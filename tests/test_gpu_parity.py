@@ -379,3 +379,45 @@ def test_bad_blob_flag(gpu_lib):
     b.tq_encode_keys(big, 1, X, d, 3, 128, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & 2
+
+
+def test_attend_in_a_graph_equals_eager(gpu_lib):
+    """tq_attend (query side, fused chunk pass, merge) captured in a HIP graph:
+    every replay, with eager work between the replays, equals the eager call."""
+    import torch
+    b = gpu_lib
+    d, B, Hkv, Hq, T, seed = 128, 2, 2, 8, 3000, 12
+    G = B * Hkv
+    kcb = b.make_codebooks(Hkv, d, 2, 128, seed, b.ROLE_KEY, device=DEV)
+    vcb = b.make_codebooks(Hkv, d, 2, 0, seed, b.ROLE_VALUE, device=DEV)
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_K), "bf16", DEV)
+    V = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_V), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, 2, 128).view(B, Hkv, T, -1)
+    vrec = b.tq_encode_values(vcb, Hkv, V, d, 2).view(B, Hkv, T, -1)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=DEV)
+    work = torch.empty(b.load().tq_attend_workspace_bytes(d, B, Hq, T), dtype=torch.uint8, device=DEV)
+
+    def step():
+        b.tq_attend(kcb, Hkv, vcb, Hkv, krec, vrec, q, d, 2, 2, 128, out=out, work=work)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        work.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {r}"
+        _ = (out.sum() + 1.0).item()
