@@ -34,6 +34,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     ("tq::(anonymous namespace)::gram_scores_generic_kernel(tq::GramScoreArgs, int, int, int, long)",
      "gram_scores_generic"),
     ("tq::(anonymous namespace)::gram_encode_kernel(tq::GramEncArgs)", "gram_encode"),
+    ("void tq::(anonymous namespace)::encode128_pair_kernel<2, 3, 1>(tq::(anonymous namespace)::Enc128Args, "
+     "tq::(anonymous namespace)::Enc128Args)", "append_pair"),
     ("__amd_rocclr_copyBuffer", "copy"),
 ])
 def test_short_names(name, short):
