@@ -374,8 +374,9 @@ int tq_memory_stats(int head_dim, int k_bits, int v_bits, int projections,
  * words (LSB first; an index may straddle two words), ceil(d w / (k 32))
  * words, then float32 |x|.  Encode: n = |x| (float64, stored as float32),
  * u = H(D x) / (sqrt(d) n) (u = 0 for a zero vector), block b = u[b k, b k + k)
- * takes the nearest codeword (Euclidean; the lowest index on ties; decided in
- * float32).  Scores (the query encoded alike):
+ * takes the nearest codeword (Euclidean; the lowest index on ties; decided on
+ * u rounded to float32 from a float64 transform, with float64 squared
+ * distances to the float32 codewords).  Scores (the query encoded alike):
  *   s[b][hq][t] = scale * n_q * n_t * sum_blocks G[cq_blk][ct_blk]
  * with query head hq reading kv head floor(hq * H_kv / H_q); scale <= 0 means
  * 1/sqrt(d).  No data errors exist for scores (indices are masked to w bits). */
