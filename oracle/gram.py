@@ -25,10 +25,12 @@ Readings where the pages are silent (each also listed in the design doc):
       n32) with the sign diagonal D given as bits (bit j set: coordinate j
       negated) and H the Sylvester-Hadamard matrix; block b = u[b k : (b+1) k]
       takes the index of the nearest codeword in Euclidean distance, the
-      lowest index on ties.  A zero vector has u = 0.  The decision is taken
-      on u rounded to float32 against the float32 codewords, the squared
-      distances in float64 (exact up to the last add), so that both sides of
-      a parity check decide in the same precision.
+      lowest index on ties.  A zero vector has u = 0.  The decision is the
+      plain definition, the nearest codeword of the exact (float64) u, with
+      float64 distances to the float32 codewords.  The pages fix no working
+      precision; a kernel that rounds u may differ only for blocks whose u
+      lies within that rounding of the boundary between two codewords, which
+      the parity band absorbs.
   G3  record: the d/k indices of w = log2(N) bits each, LSB first, index b at
       bit offset b w of the little-endian 32-bit words (an index may straddle
       two words), ceil(d w / (k 32)) words, then float32 n32.
@@ -130,9 +132,8 @@ def encode(codebook: np.ndarray, signs: np.ndarray, X, d: int, k: int):
     n = n32.astype(np.float64)
     U = Xs @ rotation_matrix(signs, d).T
     U = np.where(n[:, None] > 0, U / np.where(n > 0, n, 1.0)[:, None], 0.0)
-    U32 = U.astype(np.float32).astype(np.float64)
     nb = d // k
-    blocks = U32.reshape(-1, nb, k)
+    blocks = U.reshape(-1, nb, k)
     dist = np.sum((blocks[:, :, None, :] - C[None, None, :, :]) ** 2, axis=3)   # (M, nb, N)
     idx = np.argmin(dist, axis=2)        # first minimum: the lowest index on ties
     return pack_record(idx, n32, d, k, N), flags, dist

@@ -23,8 +23,11 @@ product estimate times 1/sqrt(head_dim), before softmax; ``decode_values``;
 Readings where the pages are silent (each also listed in the design doc):
   R1  rotation Pi = H D / sqrt(d), D applied first, Sylvester order; z =
       H(D x)/|x| so that z ~ N(0, 1) per coordinate.
-  R2  quantizer index idx_j = #{i : t_i < z_j} (ties go to the lower cell);
-      the decision is taken on float32 z against float32 thresholds.
+  R2  quantizer index idx_j = #{i : t_i < z_j} (ties go to the lower cell),
+      the plain definition: the exact (float64) z against the stored float32
+      thresholds.  The pages fix no working precision; a kernel that decides
+      on a rounded z may differ only where z lies within its rounding of a
+      threshold, which the parity band absorbs.
   R3  the stored norm is n32 = float32(|x|); reconstruction and the
       residual both use n32 (the residual is exactly what a decoder holding
       the record cannot rebuild).
@@ -216,7 +219,7 @@ def _words_f32(w: np.ndarray) -> np.ndarray:
 class Encoded:
     records: np.ndarray        # (N, words) uint32
     idx: np.ndarray            # (N, d) int
-    z: np.ndarray              # (N, d) float64 (exact z, before the float32 decision)
+    z: np.ndarray              # (N, d) float64: the exact z the decision is taken on
     n: np.ndarray              # (N,) float64
     flags: np.ndarray          # (N,) bool: rejected input
     gamma: np.ndarray | None = None   # (N,) float64
@@ -252,8 +255,7 @@ def encode(qz: Quantizer, X) -> Encoded:
     U = _rotate(qz, Xs)
     safe_n = np.where(n > 0, n, 1.0)
     z = np.where(n[:, None] > 0, U / safe_n[:, None], 0.0)
-    z32 = z.astype(np.float32).astype(np.float64)
-    idx = np.searchsorted(qz.t32, z32.ravel(), side="left").reshape(N, qz.d)
+    idx = np.searchsorted(qz.t32, z.ravel(), side="left").reshape(N, qz.d)
 
     parts = [pack_bits((idx >> p) & 1) for p in range(qz.k)]
     gamma = proj = None

@@ -189,7 +189,7 @@ def test_gram_scoring_32k_full_size(gpu_lib):
     assert int(status.item()) == 0
     del K
     qref, _, qdist = gram.encode(C, s, inputs.exact_values(q).reshape(-1, d), d, k)
-    _check_codes(rec_np(qrec).reshape(B * Hq, -1), qref, qdist, d, k, N, "queries")
+    _check_codes(rec_np(qrec).reshape(B * Hq, -1), qref, qdist, d, k, N, "queries", C)
     qref = qref.reshape(B, Hq, -1)
     same_q = np.all(rec_np(qrec) == qref, axis=2)
     Gmax = float(np.max(np.abs(gram.gram_table(C))))
@@ -199,7 +199,7 @@ def test_gram_scoring_32k_full_size(gpu_lib):
         X = _bf16_exact(inputs.kv_normal(seed, G, T, d, groups=[g]))[0][toks]
         kref, _, kdist = gram.encode(C, s, X, d, k)
         grec = rec_np(krec[g])[toks]
-        _check_codes(grec, kref, kdist, d, k, N, f"keys g={g}")
+        _check_codes(grec, kref, kdist, d, k, N, f"keys g={g}", C)
         bb, h = divmod(g, Hkv)
         rows = list(range(4 * h, 4 * h + 4))
         ref = gram.scores(C, qref[bb:bb + 1, rows], kref[None, None], d, k)[0]

@@ -7,12 +7,14 @@ Tolerances come from the float32 arithmetic of the kernels:
   * table: k products summed by fma, |G32 - G| <= k u sum_e |c_ie c_je|;
   * scores: the table entry times scale n_q (2 roundings), nb additions and
     the product by n_t, so |s32 - s| <= (nb + k + 4) u scale n_q n_t nb max|G|;
-  * encode: both sides decide on the rotated coordinates rounded to float32
-    (from a float64 transform) with float64 squared distances, so an index may
-    differ only where a coordinate sits on a float32 rounding boundary or two
-    distances tie to float64 rounding: the oracle's two distances must then be
-    within 1e-6 of the mean distance, and such blocks stay below 1e-5 of all;
-    norms are the float32 rounding of a float64 sum and agree bit for bit.
+  * encode: the oracle takes the nearest codeword of the exact (float64)
+    rotated block; the kernel decides on the block rounded to float32.  An
+    index may differ only where the exact block lies within 1e-6 of the
+    boundary between the two codewords (the bisecting hyperplane), in units of
+    the coordinate scale 1/sqrt(d) of the normalised rotated vector (the same
+    band as the scalar quantizer's 1e-6 on z ~ N(0, 1)), and such blocks stay
+    below 1e-5 of all; norms are the float32 rounding of a float64 sum and
+    agree bit for bit.
 with u = 2^-24.
 """
 import math
@@ -46,14 +48,17 @@ def test_gram_table(gpu_lib, N, k):
     assert np.all(np.abs(G - want) <= bound)
 
 
-def _check_codes(gpu_rec, ref_rec, dist, d, k, N, what):
+def _check_codes(gpu_rec, ref_rec, dist, d, k, N, what, C):
     gi, gn = gram.unpack_record(gpu_rec, d, k, N)
     oi, on = gram.unpack_record(ref_rec, d, k, N)
     assert np.array_equal(gn.astype(np.float32), on.astype(np.float32)), f"{what}: norms"
     bad = np.argwhere(gi != oi)
-    band = 1e-6 * float(np.mean(dist))
+    band = 1e-6 / math.sqrt(d)
+    Cd = np.asarray(C, dtype=np.float64)
     for r, blk in bad:
-        gap = dist[r, blk, gi[r, blk]] - dist[r, blk, oi[r, blk]]
+        a, o = gi[r, blk], oi[r, blk]
+        # distance of the exact block to the hyperplane equidistant from codewords a and o
+        gap = (dist[r, blk, a] - dist[r, blk, o]) / (2.0 * np.linalg.norm(Cd[a] - Cd[o]))
         assert 0.0 <= gap <= band, (what, int(r), int(blk), gap, band)
     assert len(bad) <= max(1, gi.size // 100000), (what, len(bad), gi.size)
 
@@ -76,7 +81,7 @@ def test_gram_encode(gpu_lib, d, k, N, dtype, G, Nv):
     assert int(st.item()) == 0
     ref, flags, dist = gram.encode(C, s, inputs.exact_values(x).reshape(-1, d), d, k)
     assert not flags.any()
-    _check_codes(rec_np(rec).reshape(G * Nv, -1), ref, dist, d, k, N, f"encode d={d} k={k} N={N}")
+    _check_codes(rec_np(rec).reshape(G * Nv, -1), ref, dist, d, k, N, f"encode d={d} k={k} N={N}", C)
 
 
 def test_gram_encode_zero_and_non_finite(gpu_lib):
@@ -168,8 +173,8 @@ def test_gram_end_to_end_encode_then_score(gpu_lib):
     torch.cuda.synchronize()
     kref, _, kdist = gram.encode(C, s, inputs.exact_values(K).reshape(-1, d), d, k)
     qref, _, qdist = gram.encode(C, s, inputs.exact_values(q).reshape(-1, d), d, k)
-    _check_codes(rec_np(krec).reshape(-1, krec.shape[-1]), kref, kdist, d, k, N, "keys")
-    _check_codes(rec_np(qrec).reshape(-1, qrec.shape[-1]), qref, qdist, d, k, N, "queries")
+    _check_codes(rec_np(krec).reshape(-1, krec.shape[-1]), kref, kdist, d, k, N, "keys", C)
+    _check_codes(rec_np(qrec).reshape(-1, qrec.shape[-1]), qref, qdist, d, k, N, "queries", C)
     ref = gram.scores(C, qref.reshape(B, Hq, -1), kref.reshape(B, Hkv, T, -1), d, k)
     same_k = np.all(rec_np(krec).reshape(-1, krec.shape[-1]) == kref, axis=1).reshape(B, Hkv, T)
     same_q = np.all(rec_np(qrec).reshape(-1, qrec.shape[-1]) == qref, axis=1).reshape(B, Hq)
@@ -264,8 +269,8 @@ def test_gram_sweep(gpu_lib, i, d, k, N, dtype, B, Hkv, Hq, T):
     torch.cuda.synchronize()
     kref, _, kdist = gram.encode(C, s, inputs.exact_values(K).reshape(-1, d), d, k)
     qref, _, qdist = gram.encode(C, s, inputs.exact_values(q).reshape(-1, d), d, k)
-    _check_codes(rec_np(krec).reshape(-1, krec.shape[-1]), kref, kdist, d, k, N, f"keys case {i}")
-    _check_codes(rec_np(qrec).reshape(-1, qrec.shape[-1]), qref, qdist, d, k, N, f"queries case {i}")
+    _check_codes(rec_np(krec).reshape(-1, krec.shape[-1]), kref, kdist, d, k, N, f"keys case {i}", C)
+    _check_codes(rec_np(qrec).reshape(-1, qrec.shape[-1]), qref, qdist, d, k, N, f"queries case {i}", C)
     w = kref.shape[-1]
     sc = b.tq_gram_scores(b.tq_gram_table(Ct), _t(qref.reshape(B, Hq, w).view(np.int32)),
                           _t(kref.reshape(B, Hkv, T, w).view(np.int32)), d, k)

@@ -70,8 +70,7 @@ def test_index_is_nearest_centroid(bits, role):
     qz = tq.Quantizer(64, bits, 64, 5, role)
     x = np.random.default_rng(2).standard_normal((300, 64))
     enc = tq.encode(qz, x)
-    z32 = enc.z.astype(np.float32).astype(np.float64)
-    dist = np.abs(z32[..., None] - qz.c32[None, None, :])
+    dist = np.abs(enc.z[..., None] - qz.c32[None, None, :])
     brute = np.argmin(dist, axis=-1)
     srt = np.sort(dist, axis=-1)
     clear = (srt[..., 1] - srt[..., 0]) > 1e-9

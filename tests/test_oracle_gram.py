@@ -86,10 +86,33 @@ def test_encode_recovers_exact_codewords():
             assert n[0] == np.float32(3.5)
 
 
+def test_decode_inverts_the_rotation():
+    """decode(encode(x)) = x for x = n D H c / sqrt(d) whose blocks are codewords,
+    with D and H written out here by loops, not taken from the oracle: the
+    decoder applies the inverse rotation Pi^T = D H / sqrt(d).  Applying Pi =
+    H D / sqrt(d) instead gives a different vector whenever D is not the
+    identity (checked), so the direction is pinned, not only inner products."""
+    d, k, N = 8, 4, 4
+    C = np.eye(4) / math.sqrt(2.0)
+    s = inputs.sign_bits(9, d)
+    dv = [-1.0 if (int(s[j // 32]) >> (j % 32)) & 1 else 1.0 for j in range(d)]
+    assert min(dv) < 0 < max(dv)
+    H = [[(-1.0) ** bin(i & j).count("1") for j in range(d)] for i in range(d)]
+    for i0, i1, nrm in ((0, 3, 3.5), (2, 2, 0.75), (1, 0, 12.0)):
+        c = list(C[i0]) + list(C[i1])
+        x = np.array([nrm * dv[i] * math.fsum(H[i][j] * c[j] for j in range(d)) / math.sqrt(d) for i in range(d)])
+        rec, flags, _ = gram.encode(C, s, x[None, :], d, k)
+        assert not flags[0]
+        back = gram.decode(C, s, rec, d, k)[0]
+        assert np.max(np.abs(back - x)) < 1e-12 * nrm
+        wrong = np.array([nrm * math.fsum(H[i][j] * dv[j] * c[j] for j in range(d)) / math.sqrt(d) for i in range(d)])
+        assert np.max(np.abs(wrong - x)) > 0.1 * nrm
+
+
 def test_encode_picks_the_nearest_codeword_brute_force():
     """Each block's index minimises the squared distance over all codewords
-    (plain loops on the float32-rounded rotated coordinates), the lowest index
-    on ties."""
+    (plain loops on the exact rotated coordinates), the lowest index on
+    ties."""
     d, k, N = 16, 4, 8
     C = inputs.block_codebook(2, N, k, d).astype(np.float64)
     s = inputs.sign_bits(2, d)
@@ -102,8 +125,7 @@ def test_encode_picks_the_nearest_codeword_brute_force():
         nrm = math.sqrt(math.fsum(X[r] * X[r]))
         assert n[r] == np.float32(nrm)
         n32 = float(np.float32(nrm))
-        u = [float(np.float32(math.fsum(H[i, j] * dv[j] * X[r, j] for j in range(d)) / (math.sqrt(d) * n32)))
-             for i in range(d)]
+        u = [math.fsum(H[i, j] * dv[j] * X[r, j] for j in range(d)) / (math.sqrt(d) * n32) for i in range(d)]
         for b in range(d // k):
             dist = [math.fsum((u[b * k + e] - C[i, e]) ** 2 for e in range(k)) for i in range(N)]
             best = min(range(N), key=lambda i: (dist[i], i))

@@ -28,10 +28,15 @@ def test_fixed_point_conditions_and_symmetry(k):
     assert np.array_equal(t, 0.5 * (c[:-1] + c[1:]))
     assert np.array_equal(c, -c[::-1])
     edges = np.concatenate([[-np.inf], t, [np.inf]])
-    # conditional means computed with scipy's normal law, independent of the solver's helpers
+    # conditional means computed with scipy's normal law, independent of the
+    # solver's helpers; each cell mass is taken from the tail it lies in (sf in
+    # the upper tail, cdf in the lower), so that no tail cell loses digits to
+    # cancellation and the fixed point is checked to float64 evaluation
     a, b = edges[:-1], edges[1:]
-    means = (norm.pdf(a) - norm.pdf(b)) / (norm.sf(a) - norm.sf(b))
-    assert np.max(np.abs(means - c)) < 1e-9 * max(1.0, 4.0 ** (k - 4))
+    mass = np.where(a >= 0.0, norm.sf(a) - norm.sf(b),
+                    np.where(b <= 0.0, norm.cdf(b) - norm.cdf(a), 1.0 - norm.sf(b) - norm.cdf(a)))
+    means = (norm.pdf(a) - norm.pdf(b)) / mass
+    assert np.max(np.abs(means - c)) < 1e-12
     if k >= 1:
         assert t[len(t) // 2] == 0.0
 

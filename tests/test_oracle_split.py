@@ -114,8 +114,7 @@ def test_haar_lattice_round_trip():
     enc = tq.encode(qz, X)
     # the lattice point has z_j = sqrt(d) c_j / |c| which lands in the cell of c_j only
     # when |c| ~ sqrt(d) (true on average); compare against the brute-force nearest cell
-    z32 = enc.z.astype(np.float32).astype(np.float64)
-    brute = np.array([[int(np.sum(qz.t32 < v)) for v in row] for row in z32])
+    brute = np.array([[int(np.sum(qz.t32 < v)) for v in row] for row in enc.z])
     assert np.array_equal(enc.idx, brute)
     assert np.allclose(enc.n, np.linalg.norm(X, axis=1), rtol=1e-15)
 
