@@ -64,13 +64,26 @@ def compare_records(qz: tq.Quantizer, gpu_rec: np.ndarray, enc: tq.Encoded, frac
     assert np.all(rel_n <= 1e-5), f"norm rel err {rel_n.max()}"
     n_sign = 0
     rel_g = np.zeros(0)
+    # raw plane and sign words of kept vectors, bit for bit: this also holds
+    # the unused high bits of each plane word (d < 32) and of the last sign
+    # word at zero, as the canonical record fixes them
+    nraw = qz.k * ((qz.d + 31) // 32)
+    allowed = np.zeros((gpu_rec.shape[0], nraw), dtype=np.uint32)
     if qz.role == tq.ROLE_KEY:
         smis = (g.signs != o.signs) & keep[:, None]
         ratio = np.abs(enc.proj) / (math.sqrt(qz.d) * np.maximum(enc.gamma, 1e-300))[:, None]
         bad = smis & ~(ratio < BAND)
         assert not bad.any(), f"{int(bad.sum())} sign mismatches outside the band, first at {np.argwhere(bad)[:5]}"
         n_sign = int(smis.sum())
-        # unused sign bits are zero on both sides (bit-exact on the sign words of kept vectors)
+        nsw = (qz.m + 31) // 32
+        allowed = np.concatenate([allowed, tq.pack_bits(smis)], axis=1)   # in-band sign flips only
+        nraw += nsw
+    diff = (gpu_rec[:, :nraw] ^ np.asarray(enc.records, dtype=np.uint32)[:, :nraw]) & ~allowed
+    stray = diff[keep]
+    assert not stray.any(), (f"record words differ beyond the band (unused bits included) in "
+                             f"{int(np.count_nonzero(stray.any(axis=1)))} vectors, first "
+                             f"{np.argwhere(diff & keep[:, None])[:3].tolist()}")
+    if qz.role == tq.ROLE_KEY:
         rel_g = np.abs(g.gamma32 - o.gamma32)[keep] / np.maximum(np.abs(o.gamma32[keep]), 1e-30)
         small = o.gamma32[keep] < 1e-30
         assert np.all((rel_g <= 1e-5) | small), f"gamma rel err {rel_g.max()}"
