@@ -93,10 +93,17 @@ enum tq_role {
 enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 };
 
 /* Byte size of one codebook blob (multiple of 256; also the stride between
- * blobs).  0 when the parameters are invalid.  Host only. */
+ * blobs): the quantizer state that (head_dim, bits, projections, seed) fixes
+ * (page "bitpolar 0.3.3 src/kv_cache.rs", KvCacheConfig; page
+ * "turboquant-plus-rs 0.1.0 README", "Modules" codebook, rotation and qjl).
+ * 0 when the parameters are invalid.  Host only. */
 size_t tq_codebook_bytes(int head_dim, int bits, int projections, int role);
 
-/* Byte size of one record (multiple of 4).  0 when the parameters are invalid. */
+/* Byte size of one record (multiple of 4): the bit-packed indices, signs and
+ * norms of one head vector (README "Modules" utils, bit packing and the
+ * memory-footprint calculation; "Compression formats" gives the bits per
+ * value, e.g. 56 bytes = 3.5 bits/value for turbo3 keys at head_dim 128).
+ * 0 when the parameters are invalid.  Host only. */
 size_t tq_record_bytes(int head_dim, int bits, int projections, int role);
 
 /* Build the quantizer state for (head_dim, bits, projections, seed, role) into
@@ -278,8 +285,11 @@ int tq_scores_paged(int head_dim, int bits, int projections,
                     const void* q, int q_dtype, int64_t H_q, float scale,
                     float* scores, int32_t* status, void* stream);
 
-/* Test hook: u = H(D x) (unnormalised rotation) and n = |x| for every vector,
- * with the D of the group's codebook.  u [G][N][head_dim] f32, norms [G][N] f32. */
+/* Test hook: the first half of README "Architecture" step 1 (random rotation,
+ * with "Modules" polar_quant's norm extraction): u = H(D x) (unnormalised
+ * rotation) and n = |x| for every vector, with the D of the group's codebook.
+ * u [G][N][head_dim] f32, norms [G][N] f32 (caller-owned); argument errors as
+ * for tq_encode_keys. */
 int tq_rotate(int head_dim, int bits, int projections, int role,
               const void* cbs, int64_t n_cb,
               const void* x, int x_dtype, int64_t G, int64_t N,
@@ -301,6 +311,22 @@ int tq_rotate(int head_dim, int bits, int projections, int role,
  * codebook array (n_cb blobs each, group g uses blob g mod n_cb).  Keys: bits in
  * [2, 8]; values: bits in [1, 7].  A map entry outside [0, head_dim) sets
  * TQ_STATUS_BAD_CHANNEL and reads channel 0. */
+
+/* Codebooks of the two parts of one (layer, kv-head) group whose head seed is
+ * `seed` (the seed tq_make_codebook would take for the unsplit head):
+ *   part 0, normal : head_dim - n_outlier coordinates, TQ_ROT_HAAR, `bits`,
+ *                    seeded `seed`;
+ *   part 1, outlier: n_outlier coordinates, TQ_ROT_HADAMARD, bits + 1, seeded
+ *                    seed XOR 0x9E3779B97F4A7C15 (the 64-bit golden-ratio
+ *                    constant), so that the parts draw independent D and S;
+ *   keys project each part onto as many signs as it has coordinates.
+ * The pages give one seed per head and no rule for sub-quantizers; this is the
+ * rule every split call assumes.  tq_split_codebook_bytes gives the byte size
+ * (and blob stride) of part 0 or 1, 0 on invalid parameters; blobs are written
+ * to the caller's HOST buffers as by tq_make_codebook_ex.  Host only. */
+size_t tq_split_codebook_bytes(int role, int head_dim, int n_outlier, int bits, int part);
+int tq_make_split_codebooks(int role, int head_dim, int n_outlier, int bits, uint64_t seed,
+                            void* normal_blob, size_t normal_bytes, void* outlier_blob, size_t outlier_bytes);
 
 /* Scratch for tq_outlier_channels: G * chunks * head_dim * 16 bytes, chunks =
  * clamp(ceil(N/512), 1, 64).  0 on invalid sizes. */
@@ -374,9 +400,12 @@ int tq_memory_stats(int head_dim, int k_bits, int v_bits, int projections,
  * words (LSB first; an index may straddle two words), ceil(d w / (k 32))
  * words, then float32 |x|.  Encode: n = |x| (float64, stored as float32),
  * u = H(D x) / (sqrt(d) n) (u = 0 for a zero vector), block b = u[b k, b k + k)
- * takes the nearest codeword (Euclidean; the lowest index on ties; decided on
- * u rounded to float32 from a float64 transform, with float64 squared
- * distances to the float32 codewords).  Scores (the query encoded alike):
+ * takes the nearest codeword (Euclidean; the lowest index on ties).  The
+ * kernel decides on u rounded to float32 from a float64 transform, with
+ * float64 squared distances to the float32 codewords, so it can differ from
+ * the nearest codeword of the exact u only for a block lying within that
+ * rounding of the boundary between two codewords.  Scores (the query encoded
+ * alike):
  *   s[b][hq][t] = scale * n_q * n_t * sum_blocks G[cq_blk][ct_blk]
  * with query head hq reading kv head floor(hq * H_kv / H_q); scale <= 0 means
  * 1/sqrt(d).  No data errors exist for scores (indices are masked to w bits). */
@@ -398,7 +427,9 @@ int tq_gram_scores(int head_dim, int block_dim, int codebook_size, const float* 
                    const void* qrec, const void* krec, int64_t B, int64_t H_kv, int64_t T, int64_t H_q,
                    float scale, float* scores, void* stream);
 
-/* Human-readable name of a return code. */
+/* Human-readable name of a return code; the names follow the error enum of
+ * page "bitpolar 0.3.3 src/kv_cache.rs" where one exists.  A static string,
+ * never NULL ("unknown status" for codes outside enum tq_status). */
 const char* tq_status_string(int code);
 
 #ifdef __cplusplus

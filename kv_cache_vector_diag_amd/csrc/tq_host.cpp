@@ -282,6 +282,38 @@ int tq_make_codebook_ex(int head_dim, int bits, int projections, uint64_t seed, 
   return make_codebook(head_dim, bits, projections, seed, role, rotation, blob, blob_bytes);
 }
 
+// The two parts of a split head vector: normal part of head_dim - n_outlier
+// channels (Haar, bits), outlier part of n_outlier channels (Walsh-Hadamard,
+// bits + 1); keys project each part onto as many signs as it has coordinates.
+static int split_part(int role, int head_dim, int n_outlier, int bits, int part, int* d, int* b, int* m, int* rot) {
+  if (role != TQ_ROLE_KEY && role != TQ_ROLE_VALUE) return TQ_ERR_INVALID_ROLE;
+  if (head_dim == 0) return TQ_ERR_ZERO_DIMENSION;
+  if (head_dim < 2 || head_dim > kMaxHeadDim) return TQ_ERR_BAD_DIMENSION;
+  if (n_outlier <= 0 || n_outlier >= head_dim || (part != 0 && part != 1)) return TQ_ERR_DIMENSION_MISMATCH;
+  *d = part == 0 ? head_dim - n_outlier : n_outlier;
+  *b = part == 0 ? bits : bits + 1;
+  *m = role == TQ_ROLE_KEY ? *d : 0;
+  *rot = part == 0 ? TQ_ROT_HAAR : TQ_ROT_HADAMARD;
+  return TQ_OK;
+}
+
+size_t tq_split_codebook_bytes(int role, int head_dim, int n_outlier, int bits, int part) {
+  int d, b, m, rot;
+  if (split_part(role, head_dim, n_outlier, bits, part, &d, &b, &m, &rot)) return 0;
+  return tq_codebook_bytes_ex(d, b, m, role, rot);
+}
+
+int tq_make_split_codebooks(int role, int head_dim, int n_outlier, int bits, uint64_t seed, void* normal_blob,
+                            size_t normal_bytes, void* outlier_blob, size_t outlier_bytes) {
+  int d, b, m, rot;
+  int rc = split_part(role, head_dim, n_outlier, bits, 0, &d, &b, &m, &rot);
+  if (rc) return rc;
+  rc = make_codebook(d, b, m, seed, role, rot, normal_blob, normal_bytes);
+  if (rc) return rc;
+  split_part(role, head_dim, n_outlier, bits, 1, &d, &b, &m, &rot);
+  return make_codebook(d, b, m, seed ^ kOutlierSeedXor, role, rot, outlier_blob, outlier_bytes);
+}
+
 }  // extern "C"
 
 namespace tq {

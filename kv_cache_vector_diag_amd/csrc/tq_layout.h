@@ -13,6 +13,10 @@ constexpr int kMaxHeadDim = 512;
 constexpr int kMaxProjections = 1024;
 constexpr int kRotHadamard = 0;
 constexpr int kRotHaar = 1;
+// Seed of the outlier part of a split head vector: the head's seed XOR this
+// (the 64-bit golden-ratio constant), so that the two parts draw independent
+// D and S from one per-head seed.
+constexpr uint64_t kOutlierSeedXor = 0x9E3779B97F4A7C15ull;
 
 // 64-byte header at the start of every blob.
 struct BlobHeader {
