@@ -91,6 +91,12 @@ __device__ inline float wave_max_f32(float v) {
   return v;
 }
 
+// z = u/|x| (float64) rounded toward +infinity.  For every float32 threshold t,
+// t < z_up exactly when t < z, the comparison the quantizer's definition asks
+// for: if z > t then z_up >= z > t; if z <= t then z_up <= t, because t is a
+// float32 value at or above z and z_up is the least such value.
+__device__ inline float z_up(double u, double nrm) { return nrm > 0.0 ? __double2float_ru(u / nrm) : 0.0f; }
+
 // Number of thresholds strictly below z (lower_bound over t[0 .. L-2]).
 __device__ inline int quantize_index(const float* t, int levels, float z) {
   int lo = 0, n = levels - 1;

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64) void encode_generic_kernel(EncodeArgs a) {
     double ws = 0.0;
     for (int j = lane; j < d; j += kWave) {
       double uj = u[j];
-      float z = nrm > 0.0 ? (float)(uj / nrm) : 0.0f;
+      const float z = z_up(uj, nrm);
       int q = quantize_index(thr, a.cb.levels, z);
       idx[j] = q;
       if (a.cb.role == TQ_ROLE_KEY) {

@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void encode_tiled_kernel(TiledArgs a) {
         ws[i] = 0.0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          z[i][e] = nrm > 0.0 ? (float)(u[i][e] / nrm) : 0.0f;
+          z[i][e] = z_up(u[i][e], nrm);
           q[i][e] = 0;
         }
       }
