@@ -77,6 +77,7 @@ enum tq_status {
   TQ_ERR_UNSUPPORTED = -13,        /* dtype or alignment not supported                 */
   TQ_ERR_INVALID_ROTATION = -14,   /* rotation not TQ_ROT_HADAMARD / TQ_ROT_HAAR       */
   TQ_ERR_INVALID_CODEBOOK = -15,   /* Gram codec: codebook size not a power of two in [2, 256] */
+  TQ_ERR_SCRATCH_LIMIT = -16,      /* tq_attend_static: the call needs more than the static scratch */
 };
 
 /* Device status bits (OR-ed into *status). */
@@ -193,6 +194,30 @@ int tq_attend(int head_dim, int k_bits, int v_bits, int projections,
               const void* krec, const void* vrec, int64_t B, int64_t H_kv, int64_t T,
               const void* q, int q_dtype, int64_t H_q, float scale,
               float* out, void* work, size_t work_bytes, int32_t* status, void* stream);
+
+/* Allocation-free form of tq_attend_ex, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, results and errors as tq_attend_ex
+ * (rotation as there; TQ_ROT_HADAMARD gives tq_attend), without `work`: the
+ * scratch is a library-owned device array of TQ_ATTEND_STATIC_SCRATCH_BYTES
+ * (32 MiB) per GPU, held until the process ends.  A call whose
+ * tq_attend_workspace_bytes(head_dim, B, H_q, T) exceeds it returns
+ * TQ_ERR_SCRATCH_LIMIT with nothing enqueued (e.g. the long-context step of 4
+ * sequences x 8 query heads x 131072 tokens needs 18.9 MB).  The call itself allocates nothing (no hipMalloc,
+ * no hipFree).  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind; nothing in it needs to start at zero.  Calls that overlap on
+ * one GPU (two streams, or two host threads) race on the array and give
+ * undefined results: serialise them.  The first call on a device looks up the
+ * array's device address (hipGetSymbolAddress), so make one such call outside
+ * any graph capture first.  tq_attend_static_scratch_bytes() returns the
+ * array's size. */
+#define TQ_ATTEND_STATIC_SCRATCH_BYTES (32u << 20)
+size_t tq_attend_static_scratch_bytes(void);
+int tq_attend_static(int head_dim, int k_bits, int v_bits, int projections, int rotation,
+                     const void* kcbs, int64_t n_kcb, const void* vcbs, int64_t n_vcb,
+                     const void* krec, const void* vrec, int64_t B, int64_t H_kv, int64_t T,
+                     const void* q, int q_dtype, int64_t H_q, float scale,
+                     float* out, int32_t* status, void* stream);
 
 /* Rotation-named forms of the five compute calls above (README "Architecture"
  * step 1 and "Modules" rotation: the random rotation is Haar via QR, or the fast

@@ -31,7 +31,8 @@ EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encod
            "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes",
            "tq_encode_keys_ex", "tq_encode_values_ex", "tq_decode_values_ex", "tq_scores_ex", "tq_attend_ex",
            "tq_append_workspace_bytes", "tq_append_kv", "tq_scores_paged", "tq_gram_record_bytes", "tq_gram_table",
-           "tq_gram_encode", "tq_gram_scores", "tq_split_codebook_bytes", "tq_make_split_codebooks"]
+           "tq_gram_encode", "tq_gram_scores", "tq_split_codebook_bytes", "tq_make_split_codebooks",
+           "tq_attend_static_scratch_bytes", "tq_attend_static"]
 
 _lib = None
 
@@ -109,6 +110,10 @@ def load() -> ctypes.CDLL:
         "tq_split_codebook_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
         "tq_make_split_codebooks": (c_int, [c_int, c_int, c_int, c_int, c_uint64, c_void_p, c_size_t, c_void_p,
                                             c_size_t]),
+        "tq_attend_static_scratch_bytes": (c_size_t, []),
+        "tq_attend_static": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64,
+                                     c_void_p, c_void_p, c_int64, c_int64, c_int64, c_void_p, c_int, c_int64, c_float,
+                                     c_void_p, c_void_p, c_void_p]),
         "tq_gram_table": (c_int, [c_int, c_int, c_void_p, c_void_p, c_void_p]),
         "tq_gram_encode": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int64,
                                    c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
@@ -442,6 +447,32 @@ def tq_attend(kcbs, n_kcb, vcbs, n_vcb, krec, vrec, q, head_dim, k_bits, v_bits,
     else:
         rc = load().tq_attend_ex(head_dim, k_bits, v_bits, projections, rotation, *args)
     _check(rc, "tq_attend")
+    return out
+
+
+def tq_attend_static(kcbs, n_kcb, vcbs, n_vcb, krec, vrec, q, head_dim, k_bits, v_bits, projections, scale=0.0,
+                     out=None, status=None, rotation=ROT_HADAMARD):
+    """tq_attend without a workspace: the library's static device scratch (the
+    allocation-free entry point; `out` is allocated here only when None)."""
+    import torch
+    kw = _words(tq_record_bytes_ex(head_dim, k_bits, projections, ROLE_KEY, rotation), "key records")
+    vw = _words(tq_record_bytes_ex(head_dim, v_bits, 0, ROLE_VALUE, rotation), "value records")
+    B, Hkv, T = _key_cache(krec, "krec", kw)
+    dev = krec.device
+    _shaped(vrec, "vrec", dev, (B, Hkv, T, vw), _i32())
+    Hq = _query(q, B, head_dim)
+    _tensor(q, "q", dev)
+    _codebooks(kcbs, "kcbs", dev, n_kcb, tq_codebook_bytes_ex(head_dim, k_bits, projections, ROLE_KEY, rotation))
+    _codebooks(vcbs, "vcbs", dev, n_vcb, tq_codebook_bytes_ex(head_dim, v_bits, 0, ROLE_VALUE, rotation))
+    if out is not None:
+        _shaped(out, "out", dev, (B, Hq, head_dim), torch.float32)
+    _status(status, dev)
+    _on_gpu(dev)
+    if out is None:
+        out = torch.empty((B, Hq, head_dim), dtype=torch.float32, device=dev)
+    _check(load().tq_attend_static(head_dim, k_bits, v_bits, projections, rotation, _ptr(kcbs), n_kcb, _ptr(vcbs),
+                                   n_vcb, _ptr(krec), _ptr(vrec), B, Hkv, T, _ptr(q), _dtype_code(q), Hq, scale,
+                                   _ptr(out), _ptr(status), _stream(q)), "tq_attend_static")
     return out
 
 
