@@ -10,12 +10,15 @@ Lloyd-Max + 128 QJL signs, 56-byte records), 32 bf16 query heads (grouped
 Inputs are resident in HBM before timing.  Buffers rotate (2 input caches,
 3 record caches) so that neither kernel reads data the 256 MB memory-side
 cache still holds from the previous launch.  Kernel durations come from HIP
-events on the stream the kernels are launched on.
+events on the stream the kernels are launched on: 20 untimed warm-up steps,
+then 100 timed steps by default, reported as mean and median.  A plain
+device copy is timed in the same run, and each kernel's bandwidth is also
+given as a fraction of it.
 
-Prints ONE JSON line.  `--config c2|c4|c5|haar|paged|gram` measures the
-prefill-encode, the long-context attend, the mixed-precision layer, the
-Haar-rotation, the paged-cache decode and the Gram-table scoring rows instead
-(also one line each).
+Prints ONE JSON line.  `--config c1|c2|c4|c5|haar|paged|gram` measures the
+single-head latency, the prefill-encode, the long-context attend, the
+mixed-precision layer, the Haar-rotation, the paged-cache decode and the
+Gram-table scoring rows instead (also one line each).
 """
 from __future__ import annotations
 
@@ -23,6 +26,7 @@ import argparse
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -39,53 +43,162 @@ def _kernel_sources_sha(kernel: str) -> str:
     return kernel_sources_sha(ROOT, kernel)
 
 
-def _traffic(kernel_key: str, launches_bytes: float):
-    """HBM bytes per launch from the committed counter summary, or None when the
-    kernel's sources changed since the counters were taken."""
+def _profile_entry(kernel_key: str):
     path = os.path.join(PROFILES, "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        data = json.load(open(path))
-        ent = data[kernel_key]
+        return json.load(open(path))[kernel_key]
     except (KeyError, ValueError):
         return None
-    if "kernel" not in ent or ent.get("source_sha") != _kernel_sources_sha(ent["kernel"]):
+
+
+def _traffic(kernel_key: str, launches_bytes: float):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel's sources changed since the counters were taken."""
+    ent = _profile_entry(kernel_key)
+    if not ent or "kernel" not in ent or "source_sha" not in ent:
+        return None
+    if ent["source_sha"] != _kernel_sources_sha(ent["kernel"]):
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+def _busy(kernel_key: str):
+    """VALU and MFMA busy (percent) from the committed counter summary, or None
+    when the kernel's sources changed since the counters were taken."""
+    ent = _profile_entry(kernel_key)
+    if not ent or "busy_kernel" not in ent or ent.get("busy_source_sha") != _kernel_sources_sha(ent["busy_kernel"]):
+        return None
+    return {"valu_busy_pct": ent["valu_busy_pct"], "mfma_util_pct": ent["mfma_util_pct"]}
 
 
 def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def cpu_baseline_c3(budget_s: float = 15.0) -> dict:
-    """The oracle (as it stands) on a bounded sample of the same workload:
-    whole (sequence, kv-head) groups of 32768 keys, encode + score of the 4
-    query heads of each group, single thread (BLAS limited to 1)."""
+def _run_timed(torch, step, steps, nseg, first=0):
+    """`steps` calls of step(i, ev) after a synchronize, each recording nseg + 1
+    events on the launch stream; returns (wall ms per step, per-segment lists of
+    event ms, per-step event ms)."""
+    evs = [_events(torch, nseg + 1) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(first + i, evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    segs = [[e[s].elapsed_time(e[s + 1]) for e in evs] for s in range(nseg)]
+    whole = [e[0].elapsed_time(e[nseg]) for e in evs]
+    return wall, segs, whole
+
+
+def _stat(v):
+    return {"mean": statistics.fmean(v), "median": statistics.median(v)}
+
+
+def copy_gbps(torch, reps: int = 20) -> float:
+    """Read + write bandwidth of a plain 1 GiB device copy on this GPU (median of
+    `reps` timed copies), the practical ceiling beside the 8 TB/s peak."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        ev = _events(torch, 2)
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / (statistics.median(times) * 1e-3) / 1e9
+
+
+def _roofline(achieved_gbps, algorithmic_bytes, kernel, traffic_key, copy, mean_ms, median_ms):
+    r = {"bound": "hbm", "achieved": achieved_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+         "frac": achieved_gbps / HBM_PEAK_GBPS, "traffic": _traffic(traffic_key, algorithmic_bytes) if traffic_key
+         else None, "kernel": kernel, "algorithmic_bytes_per_launch": algorithmic_bytes,
+         "launch_ms_mean": mean_ms, "launch_ms_median": median_ms,
+         "frac_of_measured_copy": achieved_gbps / copy if copy else None}
+    busy = _busy(traffic_key) if traffic_key else None
+    if busy:
+        r.update(busy)
+    return r
+
+
+C3_T, C3_D, C3_HKV, C3_HQ_PER, C3_GROUPS = 32768, 128, 8, 4, 128
+
+
+def _oracle_c3_group(g: int) -> tuple[int, float]:
+    """Oracle encode of one (sequence, kv-head) group of the 32K-context cache
+    (32768 keys) and the scores of its 4 query heads, single-threaded; returns
+    (process id, seconds spent in the oracle, input generation excluded)."""
     from threadpoolctl import threadpool_limits
 
     from kv_cache_vector_diag_amd import inputs
     from oracle import turboquant as tq
-    T, d, Hkv, Hq_per = 32768, 128, 8, 4
     with threadpool_limits(1):
-        qzs = tq.quantizers(Hkv, d, 3, 128, 3, tq.ROLE_KEY)
-        q = inputs.exact_values(inputs.to_torch(inputs.queries(3, 16, 32, d), "bf16"))
-        done = 0
-        spent = 0.0
-        while done < 128 and spent < budget_s:
-            g = done
-            K = inputs.exact_values(inputs.to_torch(inputs.kv_normal(3, 128, T, d, groups=[g]), "bf16"))[0]
-            t0 = time.perf_counter()
-            enc = tq.encode(qzs[g % Hkv], K)
-            b, h = divmod(g, Hkv)
-            tq.scores([qzs[g % Hkv]], enc.records[None, None], q[b:b + 1, h * Hq_per:(h + 1) * Hq_per])
-            spent += time.perf_counter() - t0
-            done += 1
-    tokens = done / Hkv * T   # sequence positions fully processed (all kv heads of a position)
-    return {"value": tokens / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of 128 (sequence, kv-head) groups x {T} keys: encode + score of 4 query "
-                      f"heads each, float64 NumPy, 1 thread, {spent:.1f} s"}
+        qz = tq.quantizers(C3_HKV, C3_D, 3, 128, 3, tq.ROLE_KEY)[g % C3_HKV]
+        q = inputs.exact_values(inputs.to_torch(inputs.queries(3, 16, 32, C3_D), "bf16"))
+        K = inputs.exact_values(inputs.to_torch(inputs.kv_normal(3, C3_GROUPS, C3_T, C3_D, groups=[g]), "bf16"))[0]
+        t0 = time.perf_counter()
+        enc = tq.encode(qz, K)
+        b, h = divmod(g, C3_HKV)
+        tq.scores([qz], enc.records[None, None], q[b:b + 1, h * C3_HQ_PER:(h + 1) * C3_HQ_PER])
+        return os.getpid(), time.perf_counter() - t0
+
+
+def cpu_baseline_c3(budget_s: float = 12.0) -> dict:
+    """The oracle (as it stands) on bounded samples of the same workload, before
+    the GPU is touched: whole (sequence, kv-head) groups of 32768 keys, encode +
+    score of the 4 query heads of each group.  Leg 1: one process, BLAS limited
+    to one thread, groups in order for about `budget_s`.  Leg 2: the groups
+    fanned out over all the host's cores (one single-threaded process each,
+    forked before any GPU use) for about `budget_s` of wall time; its time is
+    the largest oracle time any one process spent (input generation left out,
+    as in leg 1).  Rates are sequence positions (all kv heads of a position)
+    per second."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    done, spent = 0, 0.0
+    while done < C3_GROUPS and spent < budget_s:
+        spent += _oracle_c3_group(done)[1]
+        done += 1
+    one = {"value": done / C3_HKV * C3_T / spent, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} of {C3_GROUPS} (sequence, kv-head) groups x {C3_T} keys: encode + score of 4 query "
+                     f"heads each, float64 NumPy, 1 thread, {spent:.1f} s"}
+    ncpu = os.cpu_count() or 1
+    workers = max(1, min(ncpu, 16))     # at most the host share a GPU job gets
+    t0 = time.perf_counter()
+    n_all = 0
+    per_proc: dict[int, float] = {}
+    with cf.ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork")) as ex:
+        pending = set()
+        nxt = 0
+        while nxt < C3_GROUPS and nxt < workers:
+            pending.add(ex.submit(_oracle_c3_group, nxt))
+            nxt += 1
+        while pending:
+            fin, pending = cf.wait(pending, return_when=cf.FIRST_COMPLETED)
+            for f in fin:
+                pid, sec = f.result()
+                per_proc[pid] = per_proc.get(pid, 0.0) + sec
+                n_all += 1
+                if nxt < C3_GROUPS and time.perf_counter() - t0 < budget_s:
+                    pending.add(ex.submit(_oracle_c3_group, nxt))
+                    nxt += 1
+    wall = time.perf_counter() - t0
+    busiest = max(per_proc.values())
+    return {"value": n_all / C3_HKV * C3_T / busiest, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "os_cpu_count": ncpu,
+            "sample": f"{n_all} of {C3_GROUPS} (sequence, kv-head) groups x {C3_T} keys: encode + score of 4 query "
+                      f"heads each, float64 NumPy, {workers} single-threaded processes ({len(per_proc)} used), "
+                      f"busiest process {busiest:.1f} s of oracle time, {wall:.1f} s wall",
+            "single_core": one}
 
 
 def bench_c3(args, torch, b):
@@ -119,48 +232,39 @@ def bench_c3(args, torch, b):
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [_events(torch, 3) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_step, (enc_l, sc_l), whole = _run_timed(torch, step, args.steps, 2, first=args.warmup)
     assert int(status.item()) == 0
-    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_step = wall * 1e3 / args.steps
+    enc, sc = _stat(enc_l), _stat(sc_l)
+    enc_ms, sc_ms = enc["mean"], sc["mean"]
 
     enc_bytes = G * T * d * 2 + G * T * words * 4 + kcb.numel()           # 312 B per key + codebooks
     sc_bytes = G * T * words * 4 + B * Hq * T * 4 + q.numel() * 2 + kcb.numel()  # 56 B + 4 scores per key
     enc_gbps = enc_bytes / (enc_ms * 1e-3) / 1e9
     sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
     tokens = B * T
+    cp = args.copy_gbps
+    r_enc = _roofline(enc_gbps, enc_bytes, "encode", "encode_c3", cp, enc["mean"], enc["median"])
+    r_sc = _roofline(sc_gbps, sc_bytes, "score", "score_c3", cp, sc["mean"], sc["median"])
     dominant = "encode" if enc_ms >= sc_ms else "score"
-    dom_gbps, dom_bytes = (enc_gbps, enc_bytes) if dominant == "encode" else (sc_gbps, sc_bytes)
-    tr = _traffic(f"{dominant}_c3", dom_bytes)
     line = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms_step,
+        "ms_per_step": ms_step, "ms_per_step_median": statistics.median(whole),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": "32K-context decode step: encode turbo3 keys + score from compressed keys",
                    "batch": B, "kv_heads": Hkv, "q_heads": Hq, "ctx": T, "head_dim": d, "key_bits": bits,
                    "projections": m, "input": "bf16 N(0,1), seed 3", "record_bytes": words * 4},
-        "encode_ms": enc_ms, "encode_GBps": enc_gbps, "encode_frac_hbm": enc_gbps / HBM_PEAK_GBPS,
-        "encode_keys_per_s": G * T / (enc_ms * 1e-3),
-        "score_ms": sc_ms, "score_GBps": sc_gbps, "score_frac_hbm": sc_gbps / HBM_PEAK_GBPS,
-        "score_tokens_per_s": tokens / (sc_ms * 1e-3),
-        "roofline": {"bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": dom_gbps / HBM_PEAK_GBPS, "traffic": tr, "kernel": dominant,
-                     "algorithmic_bytes_per_launch": dom_bytes},
-        "roofline_score": {"bound": "hbm", "achieved": sc_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                           "frac": sc_gbps / HBM_PEAK_GBPS, "traffic": _traffic("score_c3", sc_bytes),
-                           "algorithmic_bytes_per_launch": sc_bytes},
+        "copy_GBps": cp,
+        "encode_ms": enc_ms, "encode_ms_median": enc["median"], "encode_GBps": enc_gbps,
+        "encode_frac_hbm": enc_gbps / HBM_PEAK_GBPS, "encode_keys_per_s": G * T / (enc_ms * 1e-3),
+        "score_ms": sc_ms, "score_ms_median": sc["median"], "score_GBps": sc_gbps,
+        "score_frac_hbm": sc_gbps / HBM_PEAK_GBPS, "score_tokens_per_s": tokens / (sc_ms * 1e-3),
+        "score_records_per_s": G * T / (sc_ms * 1e-3), "score_scores_per_s": B * Hq * T / (sc_ms * 1e-3),
+        "roofline": r_enc if dominant == "encode" else r_sc,
+        "roofline_score" if dominant == "encode" else "roofline_encode": r_sc if dominant == "encode" else r_enc,
     }
     return line
 
@@ -192,29 +296,26 @@ def bench_c2(args, torch, b):
 
     for i in range(args.warmup):
         step(i)
-    evs = [_events(torch, 3) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    k_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    v_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_step = wall * 1e3 / args.steps
+    ms_step, (k_l, v_l), whole = _run_timed(torch, step, args.steps, 2)
+    ks, vs = _stat(k_l), _stat(v_l)
+    k_ms, v_ms = ks["mean"], vs["mean"]
     kb = G * T * (d * 2 + kw * 4) + kcb.numel()
     vb = G * T * (d * 2 + vw * 4) + vcb.numel()
+    cp = args.copy_gbps
     return {"metric": "prefill encode GB/s (K turbo4 + V 4-bit)", "value": (kb + vb) / (ms_step * 1e-3) / 1e9,
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+            "ms_per_step_median": statistics.median(whole),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic",
             "config": {"workload": "prefill encode: 32 layers x 8 kv heads x 4096 tokens, d=128, bf16 with "
                                    "4 outlier channels x8, K b=4 + V 4-bit"},
-            "encode_keys_ms": k_ms, "encode_keys_GBps": kb / (k_ms * 1e-3) / 1e9,
-            "encode_values_ms": v_ms, "encode_values_GBps": vb / (v_ms * 1e-3) / 1e9,
-            "roofline": {"bound": "hbm", "achieved": kb / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": kb / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                         "traffic": _traffic("encode_c2", kb), "kernel": "encode_keys"}}
+            "copy_GBps": cp,
+            "encode_keys_ms": k_ms, "encode_keys_ms_median": ks["median"], "encode_keys_GBps": kb / (k_ms * 1e-3) / 1e9,
+            "encode_values_ms": v_ms, "encode_values_ms_median": vs["median"],
+            "encode_values_GBps": vb / (v_ms * 1e-3) / 1e9,
+            "roofline": _roofline(kb / (k_ms * 1e-3) / 1e9, kb, "encode_keys", "encode_c2", cp, k_ms, ks["median"]),
+            "roofline_values": _roofline(vb / (v_ms * 1e-3) / 1e9, vb, "encode_values", "encode_values_c2", cp, v_ms,
+                                         vs["median"])}
 
 
 def bench_c4(args, torch, b):
@@ -235,22 +336,17 @@ def bench_c4(args, torch, b):
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     work = torch.empty(b.load().tq_attend_workspace_bytes(d, B, Hq, T), dtype=torch.uint8, device=dev)
 
-    def step(i):
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
         b.tq_attend(kcb, Hkv, vcb, Hkv, krecs[i % 2], vrecs[i % 2], q, d, 2, 2, 128, out=out, work=work)
+        if ev:
+            ev[1].record()
 
     for i in range(args.warmup):
         step(i)
-    ev = _events(torch, 2)
-    torch.cuda.synchronize()
-    ev[0].record()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    ev[1].record()
-    torch.cuda.synchronize()
-    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
-    ms_eager_dev = ev[0].elapsed_time(ev[1]) / args.steps
-    # the call's three launches captured in a HIP graph per cache and replayed
+    ms_eager, (eager_l,), _ = _run_timed(torch, step, args.steps, 1)
+    # the call's launches captured in a HIP graph per cache and replayed
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -264,27 +360,29 @@ def bench_c4(args, torch, b):
             step(i)
     for i in range(args.warmup):
         graphs[i % 2].replay()
-    torch.cuda.synchronize()
-    ev[0].record()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
+
+    def replay(i, ev):
+        ev[0].record()
         graphs[i % 2].replay()
-    ev[1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = ev[0].elapsed_time(ev[1]) / args.steps
+        ev[1].record()
+
+    wall, (graph_l,), _ = _run_timed(torch, replay, args.steps, 1)
+    gs, es = _stat(graph_l), _stat(eager_l)
+    ms = gs["mean"]
     fused_bytes = G * T * (kw + vw) * 4 + q.numel() * 2 + out.numel() * 4
+    cp = args.copy_gbps
     return {"metric": "long-context decode step tokens/s (scores -> softmax -> V from compressed K, V)",
             "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "warmup": args.warmup, "ms_per_step": wall, "ms_per_step_median": gs["median"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "long-context step: B=4, 8 kv heads, 8 q heads, 131072 tokens, d=128, "
                                    "turbo2 K + 2-bit V",
                        "launch": "HIP graph per step (eager launches: ms_per_step_eager)"},
-            "ms_per_step_eager": ms_eager, "ms_per_step_eager_device": ms_eager_dev,
-            "roofline": {"bound": "hbm", "achieved": fused_bytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": fused_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                         "traffic": _traffic("attend_c4", fused_bytes), "kernel": "attend"}}
+            "copy_GBps": cp, "ms_per_step_device": ms,
+            "ms_per_step_eager": ms_eager, "ms_per_step_eager_device": es["mean"],
+            "ms_per_step_eager_device_median": es["median"],
+            "roofline": _roofline(fused_bytes / (ms * 1e-3) / 1e9, fused_bytes, "attend (step)", "attend_c4", cp,
+                                  ms, gs["median"])}
 
 
 def bench_c5(args, torch, b):
@@ -331,7 +429,7 @@ def bench_c5(args, torch, b):
                         device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
 
-    def step(ev=None):
+    def step(i=0, ev=None):
         if ev:
             ev[0].record()
         b.tq_outlier_channels(Kd[s0:s1], d, n_out, chan=kchan, work=work)
@@ -350,17 +448,10 @@ def bench_c5(args, torch, b):
 
     for _ in range(args.warmup):
         step()
-    evs = [_events(torch, 3) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_step, (k_l, v_l), whole = _run_timed(torch, step, args.steps, 2)
     assert int(status.item()) == 0
-    k_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    v_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_step = wall * 1e3 / args.steps
+    ks, vs = _stat(k_l), _stat(v_l)
+    k_ms, v_ms = ks["mean"], vs["mean"]
     GB = G - GS
     row = T * d * 2
     cbk = sum(c.numel() for c in kcb8) + kcbn.numel() + kcbo.numel()
@@ -368,17 +459,22 @@ def bench_c5(args, torch, b):
     # algorithmic bytes: boundary layers read once; split layers read twice (variance pass + encode)
     kb = GB * row + 2 * GS * row + GB * T * kw8 * 4 + GS * T * (kwn + kwo) * 4 + cbk
     vb = GB * row + 2 * GS * row + GB * T * vw8 * 4 + GS * T * (vwn + vwo) * 4 + cbv
+    cp = args.copy_gbps
     return {"metric": "mixed-precision encode GB/s (K and V, 32 layers)", "value": (kb + vb) / (ms_step * 1e-3) / 1e9,
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+            "ms_per_step_median": statistics.median(whole),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "mixed-precision layers: 32 layers x 8 kv heads x 16384 tokens, d=256, bf16 "
                                    "with per-channel std log-U[0.5,8]; layers 0,1,30,31 b=8; others b=3 with 32 "
                                    "outlier channels at 4 bits (Walsh-Hadamard) + 224 at 3 bits (Haar)"},
-            "encode_keys_ms": k_ms, "encode_keys_GBps": kb / (k_ms * 1e-3) / 1e9,
-            "encode_values_ms": v_ms, "encode_values_GBps": vb / (v_ms * 1e-3) / 1e9,
-            "roofline": {"bound": "hbm", "achieved": kb / (k_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": kb / (k_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                         "traffic": _traffic("encode_c5", kb), "kernel": "encode_keys (all layers)"}}
+            "dtype_note": "split layers: exact bf16/f16 matrix products with fp32 sums; boundary layers "
+                          "(b=8): float64 rotation and residual",
+            "copy_GBps": cp,
+            "encode_keys_ms": k_ms, "encode_keys_ms_median": ks["median"], "encode_keys_GBps": kb / (k_ms * 1e-3) / 1e9,
+            "encode_values_ms": v_ms, "encode_values_ms_median": vs["median"],
+            "encode_values_GBps": vb / (v_ms * 1e-3) / 1e9,
+            "roofline": _roofline(kb / (k_ms * 1e-3) / 1e9, kb, "encode_keys (all layers)", None, cp, k_ms,
+                                  ks["median"])}
 
 
 def bench_paged(args, torch, b):
@@ -430,17 +526,10 @@ def bench_paged(args, torch, b):
 
     for i in range(args.warmup):
         step(i)
-    evs = [_events(torch, 3) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_eager, (ap_l, sc_l), _ = _run_timed(torch, step, args.steps, 2, first=args.warmup)
     assert int(status.item()) == 0
-    ap_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_eager = wall * 1e3 / args.steps
+    aps, scs = _stat(ap_l), _stat(sc_l)
+    ap_ms, sc_ms = aps["mean"], scs["mean"]
     # the step as a decode loop runs it: captured once per pool in a HIP graph
     # and replayed, so the launches cost no host time between kernels
     side = torch.cuda.Stream()
@@ -456,12 +545,13 @@ def bench_paged(args, torch, b):
             step(i)
     for i in range(args.warmup):
         graphs[i % 2].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
+
+    def replay(i, ev):
+        ev[0].record()
         graphs[i % 2].replay()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        ev[1].record()
+
+    ms_step, (g_l,), _ = _run_timed(torch, replay, args.steps, 1)
     assert int(status.item()) == 0
     sc_bytes = G * T * kw * 4 + B * Hq * T * 4 + q.numel() * 2 + kcb.numel()
     ap_bytes = G * (2 * d * 2 + (kw + vw) * 4)            # vectors in, records written into their page slots
@@ -472,12 +562,12 @@ def bench_paged(args, torch, b):
             "config": {"workload": "paged cache: 16 seq x 8 kv heads x 32768 tokens in pages of 256, d=128, turbo3 "
                                    "keys + 3-bit values appended, 32 bf16 query heads scored",
                        "launch": "HIP graph per step (eager launches: ms_per_step_eager)"},
-            "ms_per_step_eager": ms_eager,
-            "append_us": ap_ms * 1e3, "append_tokens_per_s": G / (ap_ms * 1e-3), "append_bytes": ap_bytes,
-            "score_ms": sc_ms,
-            "roofline": {"bound": "hbm", "achieved": sc_bytes / (sc_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": sc_bytes / (sc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, "traffic": None,
-                         "kernel": "score (paged)", "algorithmic_bytes_per_launch": sc_bytes}}
+            "ms_per_step_median": statistics.median(g_l), "ms_per_step_eager": ms_eager, "copy_GBps": args.copy_gbps,
+            "append_us": ap_ms * 1e3, "append_us_median": aps["median"] * 1e3,
+            "append_tokens_per_s": G / (ap_ms * 1e-3), "append_bytes": ap_bytes,
+            "score_ms": sc_ms, "score_ms_median": scs["median"],
+            "roofline": _roofline(sc_bytes / (sc_ms * 1e-3) / 1e9, sc_bytes, "score (paged)", None, args.copy_gbps,
+                                  sc_ms, scs["median"])}
 
 
 BF16_MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix-core peak
@@ -517,17 +607,10 @@ def bench_haar(args, torch, b):
 
     for i in range(args.warmup):
         step(i)
-    evs = [_events(torch, 3) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_step, (enc_l, sc_l), whole = _run_timed(torch, step, args.steps, 2)
     assert int(status.item()) == 0
-    enc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    sc_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    ms_step = wall * 1e3 / args.steps
+    es, ss = _stat(enc_l), _stat(sc_l)
+    enc_ms, sc_ms = es["mean"], ss["mean"]
     flops = G * T * (2 * d * d + 2 * m * d)
     tflops = flops / (enc_ms * 1e-3) / 1e12
     enc_bytes = G * T * (d * 2 + words * 4) + kcb.numel()
@@ -538,12 +621,16 @@ def bench_haar(args, torch, b):
             "data": "synthetic",
             "config": {"workload": "Haar-QR rotation: 16 seq x 8 kv heads x 4096 tokens, d=128, bf16 N(0,1) "
                                    "keys b=3 (128 projections), 32 query heads"},
-            "encode_ms": enc_ms, "encode_GBps": enc_bytes / (enc_ms * 1e-3) / 1e9,
-            "encode_keys_per_s": G * T / (enc_ms * 1e-3), "score_ms": sc_ms,
+            "ms_per_step_median": statistics.median(whole), "copy_GBps": args.copy_gbps,
+            "encode_ms": enc_ms, "encode_ms_median": es["median"], "encode_GBps": enc_bytes / (enc_ms * 1e-3) / 1e9,
+            "encode_keys_per_s": G * T / (enc_ms * 1e-3), "score_ms": sc_ms, "score_ms_median": ss["median"],
             "score_GBps": sc_bytes / (sc_ms * 1e-3) / 1e9,
-            "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": "encode",
-                         "algorithmic_flops_per_launch": flops}}
+            # the binding bound of the encode is HBM (its MFMA share is reported beside it)
+            "roofline": _roofline(enc_bytes / (enc_ms * 1e-3) / 1e9, enc_bytes, "encode (Haar)", None,
+                                  args.copy_gbps, enc_ms, es["median"]),
+            "roofline_mfma": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "kernel": "encode (Haar)",
+                              "algorithmic_flops_per_launch": flops}}
 
 
 def bench_gram(args, torch, b):
@@ -582,16 +669,10 @@ def bench_gram(args, torch, b):
 
     for i in range(args.warmup):
         step(i)
-    evs = [_events(torch, 2) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i, evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    ms_eager, (sc_l,), _ = _run_timed(torch, step, args.steps, 1, first=args.warmup)
     assert int(status.item()) == 0
-    sc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    ms_eager = wall * 1e3 / args.steps
+    scs = _stat(sc_l)
+    sc_ms = scs["mean"]
     # the step captured in a HIP graph per record cache and replayed
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -606,12 +687,13 @@ def bench_gram(args, torch, b):
             step(i)
     for i in range(args.warmup):
         graphs[i % 3].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
+
+    def replay(i, ev):
+        ev[0].record()
         graphs[i % 3].replay()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        ev[1].record()
+
+    ms_step, (g_l,), _ = _run_timed(torch, replay, args.steps, 1)
     assert int(status.item()) == 0
     sc_bytes = G * T * words * 4 + B * Hq * T * 4 + qrec.numel() * 4 + table.numel() * 4
     sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
@@ -621,18 +703,94 @@ def bench_gram(args, torch, b):
             "config": {"workload": "Gram-table scoring: 16 seq x 8 kv heads x 32768 tokens, d=128, blocks of 4, "
                                    "32 codewords (24-byte records), 32 bf16 query heads encoded per step",
                        "launch": "HIP graph per step (eager launches: ms_per_step_eager)"},
-            "ms_per_step_eager": ms_eager, "score_ms": sc_ms, "score_GBps": sc_gbps, "score_tokens_per_s": B * T / (sc_ms * 1e-3),
-            "roofline": {"bound": "hbm", "achieved": sc_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": sc_gbps / HBM_PEAK_GBPS, "traffic": _traffic("score_gram", sc_bytes),
-                         "kernel": "gram_scores", "algorithmic_bytes_per_launch": sc_bytes}}
+            "ms_per_step_median": statistics.median(g_l), "ms_per_step_eager": ms_eager, "copy_GBps": args.copy_gbps,
+            "score_ms": sc_ms, "score_ms_median": scs["median"], "score_GBps": sc_gbps,
+            "score_tokens_per_s": B * T / (sc_ms * 1e-3),
+            "roofline": _roofline(sc_gbps, sc_bytes, "gram_scores", "score_gram", args.copy_gbps, sc_ms,
+                                  scs["median"])}
+
+
+def bench_c1(args, torch, b):
+    """Single head: 1024 fp32 N(0,1) keys and values (seed 42), head_dim 128,
+    keys b=3 (128 projections), values 3 bits, one fp32 query.  One step =
+    encode K, encode V, score the query, decode V: a latency-bound shape (four
+    launches of a few workgroups), timed as a HIP graph replay and eagerly."""
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    d, N, seed = 128, 1024, 42
+    K = inputs.to_torch(inputs.kv_normal(seed, 1, N, d, inputs.STREAM_K), "f32", dev)
+    V = inputs.to_torch(inputs.kv_normal(seed, 1, N, d, inputs.STREAM_V), "f32", dev)
+    q = inputs.to_torch(inputs.queries(seed, 1, 1, d), "f32", dev)
+    kcb = b.make_codebooks(1, d, 3, 128, seed, b.ROLE_KEY, device=dev)
+    vcb = b.make_codebooks(1, d, 3, 0, seed, b.ROLE_VALUE, device=dev)
+    kw = b.tq_record_bytes(d, 3, 128, b.ROLE_KEY) // 4
+    vw = b.tq_record_bytes(d, 3, 0, b.ROLE_VALUE) // 4
+    krec = torch.empty((1, N, kw), dtype=torch.int32, device=dev)
+    vrec = torch.empty((1, N, vw), dtype=torch.int32, device=dev)
+    scores = torch.empty((1, 1, N), dtype=torch.float32, device=dev)
+    dec = torch.empty((1, N, d), dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_encode_keys(kcb, 1, K, d, 3, 128, rec=krec, status=status)
+        if ev:
+            ev[1].record()
+        b.tq_encode_values(vcb, 1, V, d, 3, rec=vrec, status=status)
+        if ev:
+            ev[2].record()
+        b.tq_scores(kcb, 1, krec.view(1, 1, N, kw), q, d, 3, 128, out=scores, status=status)
+        if ev:
+            ev[3].record()
+        b.tq_decode_values(vcb, 1, vrec, d, 3, out=dec, status=status)
+        if ev:
+            ev[4].record()
+
+    for i in range(args.warmup):
+        step(i)
+    ms_eager, segs, whole = _run_timed(torch, step, args.steps, 4)
+    assert int(status.item()) == 0
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(0)
+    for _ in range(args.warmup):
+        graph.replay()
+
+    def replay(i, ev):
+        ev[0].record()
+        graph.replay()
+        ev[1].record()
+
+    ms_step, (g_l,), _ = _run_timed(torch, replay, args.steps, 1)
+    assert int(status.item()) == 0
+    gs = _stat(g_l)
+    names = ["encode_keys", "encode_values", "score", "decode_values"]
+    return {"metric": "single-head step latency (encode K + V, score, decode V)", "value": gs["median"] * 1e3,
+            "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+            "ms_per_step_median": gs["median"], "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "single head: 1024 tokens, d=128, fp32 N(0,1) K and V (seed 42), K b=3 "
+                                   "(128 projections), V 3-bit, one fp32 query",
+                       "launch": "HIP graph per step (value: median replay, device events)"},
+            "step_us_mean": gs["mean"] * 1e3, "step_us_eager_median": statistics.median(whole) * 1e3,
+            "ms_per_step_eager": ms_eager,
+            "kernels_us_median_eager": {n: statistics.median(v) * 1e3 for n, v in zip(names, segs)},
+            "roofline": None}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3", choices=["c2", "c3", "c4", "c5", "haar", "paged", "gram"])
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "haar", "paged", "gram"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -641,6 +799,11 @@ def main():
         print(f"bench.py measures one GPU only (this path runs on a single MI355X); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+    # the oracle legs run first: the all-core leg forks worker processes, which
+    # must happen before anything initialises the GPU
+    cpu = None
+    if args.config == "c3" and not args.no_cpu_baseline and not args.copy_calibration:
+        cpu = cpu_baseline_c3()
     import torch
 
     from kv_cache_vector_diag_amd import binding as b
@@ -665,11 +828,12 @@ def main():
         print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": reps + 1,
                                                "ms_per_copy": ms, "GBps_read_plus_write": 2 * n / (ms * 1e-3) / 1e9}}))
         return
-    fn = {"c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5, "haar": bench_haar,
+    args.copy_gbps = copy_gbps(torch)
+    fn = {"c1": bench_c1, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5, "haar": bench_haar,
           "paged": bench_paged, "gram": bench_gram}[args.config]
     line = fn(args, torch, b)
     if args.config == "c3":
-        line["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_c3()
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -4,11 +4,14 @@
     python -m kv_cache_vector_diag_amd.rocprof_summary counters <counter_collection.csv> [...]
     python -m kv_cache_vector_diag_amd.rocprof_summary traffic --fetch F.csv --write W.csv \\
         --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --out traffic.json
+    python -m kv_cache_vector_diag_amd.rocprof_summary busy --csv B.csv --map kernel=key ... --out traffic.json
 
 ``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE readings (KiB) of
 each kernel by the factor that makes the same counter read the known byte
 count of a plain device copy, and records the hash of the kernel sources the
 counters were taken with (a later source change makes the entry stale).
+``busy`` records the mean VALUBusy and MfmaUtil (percent) of each mapped
+kernel's dispatches in the same file, with their own source hash.
 """
 from __future__ import annotations
 
@@ -129,6 +132,20 @@ def cmd_traffic(a) -> None:
     json.dump(out, open(a.out, "w"), indent=1, sort_keys=True)
 
 
+def cmd_busy(a) -> None:
+    agg = per_kernel_counters([a.csv])
+    out = json.load(open(a.out)) if os.path.exists(a.out) else {}
+    for kern, key in (k.split("=") for k in a.map):
+        ent = out.setdefault(key, {"kernel": kern})
+        for counter, field in (("VALUBusy", "valu_busy_pct"), ("MfmaUtil", "mfma_util_pct")):
+            v = agg[kern][counter]
+            ent[field] = sum(v) / len(v)
+        ent["busy_kernel"] = kern
+        ent["busy_source_sha"] = kernel_sources_sha(a.root, kern)
+        print(f"{key}: VALUBusy {ent['valu_busy_pct']:.1f}%  MfmaUtil {ent['mfma_util_pct']:.1f}%")
+    json.dump(out, open(a.out, "w"), indent=1, sort_keys=True)
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -142,11 +159,18 @@ def main(argv=None) -> None:
                    help="kernel=key pairs")
     t.add_argument("--root", default=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     t.add_argument("--out", required=True)
+    u = sub.add_parser("busy")
+    u.add_argument("--csv", required=True)
+    u.add_argument("--map", nargs="+", required=True, help="kernel=key pairs")
+    u.add_argument("--root", default=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    u.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         cmd_stats(a.csv)
     elif a.cmd == "counters":
         cmd_counters(a.csv)
+    elif a.cmd == "busy":
+        cmd_busy(a)
     else:
         cmd_traffic(a)
 
