@@ -28,9 +28,9 @@ bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t
 int launch_encode_fast128(const Layout& L, const void* cbs, int64_t n_cb, const void* x, int dtype, int64_t G,
                           int64_t N, int64_t sx_g, int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s,
                           const PagedOut* po = nullptr);
-// The keys and values of a paged append in one launch, when both kernels take
-// the same workgroup shape (bf16 inputs with 1 or 2 key planes, f16 with 1);
-// returns 1, with nothing enqueued, for other shapes.
+// The keys and values of a paged append in one launch (the value encode runs
+// with the keys' workgroup shape) for bf16 inputs with 1 or 2 key planes and
+// f16 with 1; returns 1, with nothing enqueued, for other shapes.
 int launch_append_fast128(const Layout& K, const Layout& V, const void* kcbs, int64_t n_kcb, const void* vcbs,
                           int64_t n_vcb, const void* k, const void* v, int dtype, int64_t G, int64_t N, int64_t sx_g,
                           int64_t sx_n, uint32_t* kpool, uint32_t* vpool, int32_t* status, hipStream_t s,

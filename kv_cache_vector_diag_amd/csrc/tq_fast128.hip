@@ -38,10 +38,11 @@ using namespace mf;
 constexpr int kD = 128;
 constexpr int kM = 128;
 // Waves per workgroup (one workgroup per CU): 12 (three per SIMD) where the
-// kernel fits in 168 VGPRs, else 8 (two per SIMD, up to 256 VGPRs).
+// kernel fits in 168 VGPRs, else 8 (two per SIMD, up to 256 VGPRs).  Keys take
+// 8: the four projection accumulators stay live across the slices.
 template <int K, bool KEY, int DT, bool HAAR>
 constexpr int waves_for() {
-  return (DT == 0 || (HAAR && DT == 2) || (KEY && (K == 3 || (K == 2 && DT == 2)))) ? 8 : 12;
+  return (KEY || DT == 0 || (HAAR && DT == 2)) ? 8 : 12;
 }
 constexpr int kTile = 32;
 
@@ -61,24 +62,38 @@ struct Enc128Args {
   PagedOut po;               // paged output (the PAGED kernels): rec is the pool
 };
 
-// H_128 = H_4 (x) H_32 (Sylvester order): with row r = 32M + r', column
-// c = 32p + c', H[r][c] = (-1)^popc(M & p) H_32[r'][c'].  So
-//   u = H (D x):  u[32M + r'] = sum_p (-1)^popc(M & p) t_p[r'],
-//   t_p = H_32 (D_p x_p)  (the 32-point transform of block p of D x),
-// i.e. four 32-row MFMA products (two K-chunks each) and a 4-point butterfly.
-// Fragment (p, c2) of the A operand (K-chunk c = 2p + c2 of x), lane l:
-// A[rho = l%32][k = 8(l/32) + e] = H_32[tile_row_index(rho)][16 c2 + k] * D[32p + 16 c2 + k].
+// Rotation u = H (D x) with H = H_128 in Sylvester order, split as
+// H_128 = H_{128/NS} (x) H_NS: with row r = NS a + r', column c = NS b + c',
+// H[r][c] = (-1)^popc(a & b) H_NS[r'][c'].  The NS-point transforms of the
+// blocks of D x run on MFMA (NS/32 row tiles x NS/16 K-chunks per block), the
+// remaining 128/NS-point butterfly across blocks on the VALU:
+//   NS = 32 : 8 MFMAs and a 4-point butterfly (2 add/sub per coordinate);
+//   NS = 64 : 16 MFMAs and a 2-point butterfly (1 per coordinate);
+//   NS = 128: 32 MFMAs, no butterfly.
+// NS = 32 is used: at the 32K-context key encode NS = 64 measured the same and
+// NS = 128 6% slower (the matrix work lowers the clock more than the VALU
+// work it saves).
+// The fragments hold -H D (exact in 16 bits), so the products give v = -u:
+// then u > 0 is exactly the sign bit of v (v is never -0: every MFMA sum
+// starts from a +0 accumulator, and the butterfly adds and subtracts nonzero
+// or +0 operands), one instruction per coordinate.
+// Fragment (Mi, c) for output row tile Mi < NS/32 of the block and K-chunk c of
+// x, lane l: A[rho = l%32][k = 8(l/32) + e] =
+//   -H_NS[32 Mi + tile_row_index(rho)][(16 c + k) mod NS] * D[16 c + k].
+constexpr int kNS = 32;
+constexpr int kRotFrags = (kNS / 32) * 8;
+static_assert(kNS == 32 || kNS == 64 || kNS == 128, "sub-transform size");
 template <bool F16>
 __device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
-  for (int f = threadIdx.x; f < 8 * 64; f += blockDim.x) {
-    const int lane = f & 63, c = f >> 6;      // c = 2p + c2
-    const int row = tile_row_index(lane & 31);
+  for (int f = threadIdx.x; f < kRotFrags * 64; f += blockDim.x) {
+    const int lane = f & 63, c = (f >> 6) & 7, Mi = f >> 9;
+    const int row = 32 * Mi + tile_row_index(lane & 31);
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
       uint32_t word = 0;
       for (int hh = 0; hh < 2; ++hh) {
         const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;     // coordinate of x
-        const uint32_t neg = h_sign(row, col & 31) ^ ((dbits[col >> 5] >> (col & 31)) & 1u);
+        const uint32_t neg = 1u ^ h_sign(row, col & (kNS - 1)) ^ ((dbits[col >> 5] >> (col & 31)) & 1u);
         const uint32_t one = F16 ? 0x3C00u : 0x3F80u;
         word |= (one | (neg << 15)) << (16 * hh);
       }
@@ -131,7 +146,7 @@ __device__ void build_rfrag(u32x4* rfrag, const float* R) {
       uint32_t word = 0;
       for (int hh = 0; hh < 2; ++hh) {
         const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;
-        word |= r_term<F16>(R[row * kD + col], t) << (16 * hh);
+        word |= r_term<F16>(-R[row * kD + col], t) << (16 * hh);   // -R: the products give v = -u
       }
       v[q] = word;
     }
@@ -139,8 +154,10 @@ __device__ void build_rfrag(u32x4* rfrag, const float* R) {
   }
 }
 
-// S fragments (A operand of MFMA#2): fragment (Mp, c), lane l: row rho = l%32 is
-// projection 32Mp + tile_row_index(rho); element e: S[proj][qjl_coord(c, l/32, e)].
+// S fragments (A operand of MFMA#2), negated: the residual is formed as
+// w' = -w (from v = -u), so that (-S) w' = S w.  Fragment (Mp, c), lane l: row
+// rho = l%32 is projection 32Mp + tile_row_index(rho); element e:
+// -S[proj][qjl_coord(c, l/32, e)].
 __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
   for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
     const int lane = f & 63, c = (f >> 6) & 7, Mp = f >> 9;
@@ -149,7 +166,7 @@ __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
     for (int q = 0; q < 4; ++q) {
       const uint32_t lo = S[row * kD + qjl_coord(c, lane >> 5, 2 * q)];
       const uint32_t hi = S[row * kD + qjl_coord(c, lane >> 5, 2 * q + 1)];
-      v[q] = lo | (hi << 16);
+      v[q] = (lo | (hi << 16)) ^ 0x80008000u;
     }
     sfrag[f] = v;
   }
@@ -174,9 +191,8 @@ __device__ inline uint32_t* paged_slot(const Enc128Args& a, int64_t g, int64_t t
 
 // The encode of workgroup `bid` of a launch over a's groups (the kernels below
 // run it for their own workgroup index).
-template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
+template <int K, bool KEY, int DT, bool HAAR, bool PAGED, int kWaves>
 __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid) {
-  constexpr int kWaves = waves_for<K, KEY, DT, HAAR>();
   constexpr int kRotBytes = HAAR ? 98304 : 32768;
   static_assert(!HAAR || DT != 0, "the Haar rotation takes 16-bit inputs");
   extern __shared__ __align__(16) uint8_t smem[];
@@ -280,10 +296,15 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
     } else {
 #pragma unroll
       for (int c = 0; c < 8; ++c) xb[c] = xr[c];
+      // |x|^2: the 8 squares of a chunk summed in float32 by dot2 (exact
+      // products), the chunk sums in float64
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 8; ++c) {
+        float part = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ss += DT == 1 ? pair_sumsq_bf16(xb[c][q]) : pair_sumsq_f16(xb[c][q]);
+        for (int q = 0; q < 4; ++q) part = DT == 1 ? sumsq2_bf16(xb[c][q], part) : sumsq2_f16(xb[c][q], part);
+        ss += (double)part;
+      }
     }
 
     // ---- rotation: t_p = H_32 (D_p x_p) on MFMA (four independent accumulation
@@ -319,31 +340,49 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
         }
       }
     }
+    // Walsh-Hadamard: accumulator slot (block b, row tile Mi) = b * NS/32 + Mi
+    // collects the NS-point transform of block b (K-chunks of that block)
 #pragma unroll
-    for (int c2 = 0; c2 < (HAAR ? 0 : 2); ++c2) {
+    for (int cc = 0; cc < (HAAR ? 0 : kNS / 16); ++cc) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int c = 2 * p + c2;
-        const u32x4 hf = hfrag[c * 64 + lane];
-        if (DT == 2) {
-          u[p] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(hf), as<f16x8>(xb[c]), u[p], 0, 0, 0);
-        } else {
-          u[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb[c]), u[p], 0, 0, 0);
-          if (DT == 0) {
-            u[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb2[c]), u[p], 0, 0, 0);
-            u[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb3[c]), u[p], 0, 0, 0);
+      for (int b = 0; b < 128 / kNS; ++b) {
+#pragma unroll
+        for (int Mi = 0; Mi < kNS / 32; ++Mi) {
+          const int c = b * (kNS / 16) + cc, slot = b * (kNS / 32) + Mi;
+          const u32x4 hf = hfrag[(Mi * 8 + c) * 64 + lane];
+          if (DT == 2) {
+            u[slot] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(hf), as<f16x8>(xb[c]), u[slot], 0, 0, 0);
+          } else {
+            u[slot] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb[c]), u[slot], 0, 0, 0);
+            if (DT == 0) {
+              u[slot] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb2[c]), u[slot], 0, 0, 0);
+              u[slot] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(hf), as<bf16x8>(xb3[c]), u[slot], 0, 0, 0);
+            }
           }
         }
       }
     }
+    if constexpr (!HAAR && kNS == 32) {
+      // 4-point butterfly across the blocks: tile M = sum_b (-1)^popc(M & b) block b
 #pragma unroll
-    for (int r = 0; r < (HAAR ? 0 : 16); ++r) {
-      const float a0 = u[0][r] + u[1][r], b0 = u[0][r] - u[1][r];
-      const float a1 = u[2][r] + u[3][r], b1 = u[2][r] - u[3][r];
-      u[0][r] = a0 + a1;    // M = 0: + + + +
-      u[1][r] = b0 + b1;    // M = 1: + - + -
-      u[2][r] = a0 - a1;    // M = 2: + + - -
-      u[3][r] = b0 - b1;    // M = 3: + - - +
+      for (int r = 0; r < 16; ++r) {
+        const float a0 = u[0][r] + u[1][r], b0 = u[0][r] - u[1][r];
+        const float a1 = u[2][r] + u[3][r], b1 = u[2][r] - u[3][r];
+        u[0][r] = a0 + a1;    // M = 0: + + + +
+        u[1][r] = b0 + b1;    // M = 1: + - + -
+        u[2][r] = a0 - a1;    // M = 2: + + - -
+        u[3][r] = b0 - b1;    // M = 3: + - - +
+      }
+    } else if constexpr (!HAAR && kNS == 64) {
+      // 2-point butterfly across the halves: tiles Mi and 2 + Mi
+#pragma unroll
+      for (int Mi = 0; Mi < 2; ++Mi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float a = u[Mi][r], b = u[2 + Mi][r];
+          u[Mi][r] = a + b;
+          u[2 + Mi][r] = a - b;
+        }
     }
     if (DT != 0) {
       // the last tile re-reads itself (a cache hit) so that the prefetch
@@ -378,7 +417,31 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
     uint32_t pw[4], tw[NT > 0 ? NT : 1][4];                // sign-half words, thermometer words
     constexpr int KB = K - 1;                              // magnitude bits
     uint32_t mw[KB > 0 ? KB : 1][4];                       // values: magnitude index bits
-    u32x4 whi[KEY ? 8 : 1], wlo[KEY ? 8 : 1];
+    // keys: the four projection row tiles of S w accumulate slice by slice.  The
+    // 16 products of slice M-1 are issued inside slice M's quantization, one
+    // between every 4 VALU instructions, so that they run on the matrix core
+    // while the same wave quantizes instead of in one block of 64 (2-3% faster
+    // at the 32K-context encode, with far fewer waves waiting to issue).
+    f32x16 acc[KEY ? 4 : 1];
+#pragma unroll
+    for (int j = 0; j < (KEY ? 4 : 1); ++j) acc[j] = f32x16{};
+    u32x4 whi[KEY ? 2 : 1], wlo[KEY ? 2 : 1];     // split residual of the previous slice
+    const auto qjl_slice = [&](int Ms) {
+      // (-S) (w'_hi + w'_lo) over chunks 2Ms, 2Ms+1, four row tiles; the two
+      // products on one accumulator are four MFMAs apart
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        u32x4 sf[4];
+#pragma unroll
+        for (int Mp = 0; Mp < 4; ++Mp) sf[Mp] = sfrag[(Mp * 8 + 2 * Ms + p) * 64 + lane];
+#pragma unroll
+        for (int Mp = 0; Mp < 4; ++Mp)
+          acc[Mp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[Mp]), as<f16x8>(whi[p]), acc[Mp], 0, 0, 0);
+#pragma unroll
+        for (int Mp = 0; Mp < 4; ++Mp)
+          acc[Mp] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[Mp]), as<f16x8>(wlo[p]), acc[Mp], 0, 0, 0);
+      }
+    };
     float wsq = 0.0f;
 #pragma unroll
     for (int M = 0; M < 4; ++M) {
@@ -396,7 +459,7 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
 #pragma unroll
         for (int r = 15; r >= 0; --r) {
           const float uu = u[M][r];
-          pos_bit(pacc, uu);
+          pacc = neg_bit(pacc, uu);
           if constexpr (KB == 1) {
             thr_bit(macc[0], uu, tn[0]);
           } else if constexpr (KB == 2) {
@@ -417,15 +480,16 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
       float wv[16];
 #pragma unroll
       for (int r = 15; r >= 0; --r) {
-        const float uu = u[M][r];
-        float nsg;
-        pos_step(pacc, nsg, uu, nbits, 0x80000000u);
+        const float uu = u[M][r];                 // -u
+        pacc = neg_bit(pacc, uu);                 // bit: u > 0
+        // +n where u > 0, -n elsewhere: w' = -w = -u + (+-n) c_mag
+        const float nsg = __uint_as_float((~__float_as_uint(uu) & 0x80000000u) | nbits);
         float mag = cpos[0];
         if (NT > 0) mag = thr_first(tacc[0], uu, tn[0], cpos[0], cpos[NT > 0 ? 1 : 0]);
 #pragma unroll
         for (int t = 1; t < NT; ++t) thr_step(tacc[t], mag, uu, tn[t], cpos[t + 1]);
         if (KEY) {
-          // w = u - n c[idx] with c[idx] = +-mag: fma(+-n, mag, u), -n on the positive half
+          // w' = -(u - n c[idx]) with c[idx] = +-mag: fma(+-n, mag, -u), +n on the positive half
           const float w = fmaf(nsg, mag, uu);
           wsq = fmaf(w, w, wsq);
           wv[r] = w;
@@ -434,7 +498,8 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
       pw[M] = pacc;
 #pragma unroll
       for (int t = 0; t < NT; ++t) tw[t][M] = tacc[t];
-      if (KEY) {
+      if constexpr (KEY) {
+        if (M > 0) qjl_slice(M - 1);
         // B operand of projection chunk c = 2M + p: element e = register 8p + e
 #pragma unroll
         for (int p = 0; p < 2; ++p)
@@ -442,43 +507,34 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
           for (int q = 0; q < 4; ++q) {
             uint32_t h, l;
             split_f16x2(wv[8 * p + 2 * q], wv[8 * p + 2 * q + 1], sc, h, l);
-            whi[2 * M + p][q] = h;
-            wlo[2 * M + p][q] = l;
+            whi[p][q] = h;
+            wlo[p][q] = l;
           }
+        if (M > 0) {
+          // the region's order: the 8 fragment reads, then the 16 products of
+          // slice M-1 each followed by 4 VALU instructions of slice M
+          __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if constexpr (KEY) qjl_slice(3);
 
-    // ---- QJL projection on MFMA (keys); sign bits packed with one alignbit each
+    // ---- QJL signs of S w (keys), one alignbit each
     uint32_t sw[4] = {0, 0, 0, 0};   // inverted sign bits (1 = negative)
     float gam = 0.0f;
     if (KEY) {
-      // two passes of two projection row tiles each (two accumulators live, not
-      // four: the register budget of three waves per SIMD)
 #pragma unroll
-      for (int hp = 0; hp < 2; ++hp) {
-        f32x16 acc[2];
+      for (int j = 0; j < 4; ++j) {
+        uint32_t a2 = 0;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          u32x4 sf[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) sf[j] = sfrag[((2 * hp + j) * 8 + c) * 64 + lane];
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[j]), as<f16x8>(whi[c]), acc[j], 0, 0, 0);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf[j]), as<f16x8>(wlo[c]), acc[j], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint32_t a2 = 0;
-#pragma unroll
-          for (int r = 15; r >= 0; --r) a2 = __builtin_amdgcn_alignbit(a2, __float_as_uint(acc[j][r]), 31);
-          sw[2 * hp + j] = a2;
-        }
+        for (int r = 15; r >= 0; --r) a2 = __builtin_amdgcn_alignbit(a2, __float_as_uint(acc[j][r]), 31);
+        sw[j] = a2;
       }
       auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq), __float_as_uint(wsq), false, false);
       const float tot = __uint_as_float(pg[0]) + __uint_as_float(pg[1]);
@@ -555,21 +611,21 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
 
 template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
 __global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode128_kernel(Enc128Args a) {
-  encode128_body<K, KEY, DT, HAAR, PAGED>(a, blockIdx.x);
+  encode128_body<K, KEY, DT, HAAR, PAGED, waves_for<K, KEY, DT, HAAR>()>(a, blockIdx.x);
 }
 
 // Keys and values of an append in one launch (paged output): the first
 // ka.G * ka.blocks_per_group workgroups encode the keys, the rest the values.
-// Both roles run the same wave count, and the LDS is the keys' (the larger).
+// Both roles run the keys' wave count, and the LDS is the keys' (the larger).
 template <int KK, int KV, int DT>
 __global__ __launch_bounds__((64 * waves_for<KK, true, DT, false>())) void encode128_pair_kernel(Enc128Args ka,
                                                                                                  Enc128Args va) {
-  static_assert(waves_for<KK, true, DT, false>() == waves_for<KV, false, DT, false>(), "one workgroup shape");
+  constexpr int W = waves_for<KK, true, DT, false>();
   const int64_t nk = ka.G * ka.blocks_per_group;
   if ((int64_t)blockIdx.x < nk)
-    encode128_body<KK, true, DT, false, true>(ka, blockIdx.x);
+    encode128_body<KK, true, DT, false, true, W>(ka, blockIdx.x);
   else
-    encode128_body<KV, false, DT, false, true>(va, (int64_t)blockIdx.x - nk);
+    encode128_body<KV, false, DT, false, true, W>(va, (int64_t)blockIdx.x - nk);
 }
 
 // ~256 workgroups (one per CU) in total, at least 8 tiles per wave, never more

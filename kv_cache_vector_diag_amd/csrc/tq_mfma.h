@@ -40,9 +40,20 @@ __device__ inline double pair_sumsq_bf16(uint32_t w) {
   return (double)__builtin_amdgcn_fdot2_f32_bf16(v, v, 0.0f, false);
 }
 
-__device__ inline double pair_sumsq_f16(uint32_t w) {
+// acc + x0^2 + x1^2 of a packed pair (float32, the products exact).
+__device__ inline float sumsq2_bf16(uint32_t w, float acc) {
+  s16x2 v = __builtin_bit_cast(s16x2, w);
+  return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
+}
+
+__device__ inline float sumsq2_f16(uint32_t w, float acc) {
   f16x2 v = __builtin_bit_cast(f16x2, w);
-  return (double)__builtin_amdgcn_fdot2(v, v, 0.0f, false);
+  return __builtin_amdgcn_fdot2(v, v, acc, false);
+}
+
+// 2 acc + (sign bit of v): shifts the sign bit of v in at bit 0.
+__device__ inline uint32_t neg_bit(uint32_t acc, float v) {
+  return __builtin_amdgcn_alignbit(acc, __float_as_uint(v), 31);
 }
 
 
