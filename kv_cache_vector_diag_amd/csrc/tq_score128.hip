@@ -59,6 +59,7 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
   __shared__ sc128::QueryLds<K> qs;
   constexpr int kStage = 64 * ((16 * RW + 63) / 64);   // 8-byte chunks per wave: one tile, rounded up
   __shared__ uint2 stage[kWaves * kStage];
+  __shared__ uint32_t next_tile;                         // the workgroup's tile counter
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: branches on it stay scalar
@@ -135,34 +136,57 @@ __global__ __launch_bounds__(block_threads<K>()) void score128_kernel(Score128Ar
       a.scores + (b * a.Hq + hkv * a.gq) * a.T, 0, (int)(a.gq * a.T * 4), kRsrcWord3);
   uint2* st2 = stage + wave * kStage;
   const uint32_t* st = reinterpret_cast<const uint32_t*>(st2) + col * RW;
-  // The first tiles' records are in flight while the query side is prepared.
-  // Issued in slot order, each followed by two stores past the end of the
-  // scores (dropped by the hardware): on entry the memory operations then stand
-  // in the same order as in the loop (a slot's loads, its two score stores), so
-  // the wait before each slot leaves the later slots' loads in flight.
+  // Tiles are handed out one at a time from the workgroup's counter: the waves
+  // of a SIMD get unequal shares of its issue slots, and with a fixed split
+  // the favoured ones finished ~20 us before the last (at the 32K-context
+  // shape), leaving the tail of the kernel to a few waves and HBM underused.
+  // A wave's first kPrefetch tiles are fixed (wave + sl * kWaves).
+  int64_t slot_tile[kPrefetch];
 #pragma unroll
-  for (int sl = 0; sl < kPrefetch; ++sl) {
-    load_raw(tile0 + wave + sl * kWaves, raw[sl]);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0xC0000000u, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0xC0000040u, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  sc128::query_build<K, kBlock>(qs, qr, a.gq, tid, wave, lane);
+  for (int sl = 0; sl < kPrefetch; ++sl) slot_tile[sl] = tile0 + wave + sl * kWaves;
+  if (tid == 0) next_tile = kPrefetch * kWaves;          // visible after the query side's barriers
+  const auto grab = [&]() -> int64_t {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&next_tile, 1u);
+    return tile0 + (int64_t)__builtin_amdgcn_readfirstlane(v);
+  };
+  // The first tiles' records are in flight while the query side is prepared,
+  // issued once the query loads have landed (at kernel start every workgroup
+  // loads at once, and the small query loads would otherwise wait behind the
+  // records).  Issued in slot order, each followed by two stores past the end
+  // of the scores (dropped by the hardware): on entry the memory operations
+  // then stand in the same order as in the loop (a slot's loads, its two score
+  // stores), so the wait before each slot leaves the later slots' loads in
+  // flight.
+  const auto prefetch = [&]() {
+#pragma unroll
+    for (int sl = 0; sl < kPrefetch; ++sl) {
+      load_raw(slot_tile[sl], raw[sl]);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0xC0000000u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(0u, srs, 0xC0000040u, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  sc128::query_build<K, kBlock>(qs, qr, a.gq, tid, wave, lane, prefetch);
   i32x4 A[NMF];
 #pragma unroll
   for (int f = 0; f < NMF; ++f) A[f] = qs.afrag[f * 64 + lane];
 
-  for (int64_t tile_base = tile0 + wave; tile_base < tile_end; tile_base += kPrefetch * kWaves) {
+  // A wave's tiles come in increasing order, slot after slot, so the loop ends
+  // when slot 0 holds a tile past the range.  The slots after it in the same
+  // pass may hold one too: such a tile reads zeros and stores nothing (one
+  // exit per pass keeps the compiler's waits at one slot's loads).
+  while (slot_tile[0] < tile_end) {
 #pragma unroll
     for (int sl = 0; sl < kPrefetch; ++sl) {
-      const int64_t tile = tile_base + sl * kWaves;
+      const int64_t tile = slot_tile[sl];
       const int64_t tok = tile * 32 + col;
-      const bool valid = tok < rec_end;   // a tile past the range reads zeros and stores nothing
+      const bool valid = tok < rec_end;   // tokens past the range store nothing
 #pragma unroll
       for (int i = 0; i < NCH; ++i) st2[lane + 64 * i] = raw[sl][i];
-      load_raw(tile + kPrefetch * kWaves, raw[sl]);
+      slot_tile[sl] = grab();
+      load_raw(slot_tile[sl], raw[sl]);
       float sa, sb2;
       sc128::score_tile<K>(A, st, qs.consts, a.scale, h, sa, sb2);
       // heads ha, hb >= gq land past the end of the resource, as does an invalid token

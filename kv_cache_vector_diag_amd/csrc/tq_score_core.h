@@ -60,11 +60,17 @@ __device__ __host__ constexpr int subset_bits(int s) {
 template <int K>
 constexpr int key_words() { return 4 * K + 6; }
 
+// qt rows in LDS carry 8 floats of padding after every 32 coordinates: the
+// projection step's four quarter-row threads of a row then read different banks.
+__device__ __host__ constexpr int qt_pad(int j) { return j + 8 * (j >> 5); }
+constexpr int kQtRow = kD + 8 * (kD / 32);
+
 // Query side of one (sequence, kv head): up to 4 query heads.
 template <int K>
 struct QueryLds {
-  float qt[4][kD];
+  float qt[4][kQtRow];                 // qt[hh][qt_pad(j)]
   float pp[4][kM];
+  int vt[4][Masks<K>::kMasks][kD];     // fixed-point values V per head, mask and coordinate
   float qstat[4][2];                   // per head: max |qt_j|, sum qt_j
   float pstat[kPWaves][4][2];          // per projection wave and head: max |p_i|, sum p_i
   float consts[4][4];                  // per head: delta_mse, delta_qjl, C_mse, C_qjl
@@ -120,11 +126,19 @@ __device__ inline void query_load(const QuerySrc& src, QueryRegs<K>& r, int tid,
   }
 }
 
-// The query side from the loaded registers, in three barriers; on return
-// s.afrag and s.consts are complete and visible to the workgroup.
+struct NoStep {
+  __device__ void operator()() const {}
+};
+
+// The query side from the loaded registers, in four barriers; on return
+// s.afrag and s.consts are complete and visible to the workgroup.  `after1`
+// runs on every thread right after the first barrier, once the query loads
+// have landed (a caller issues its own memory traffic there, so that it does
+// not queue in front of them).
 // kBlock (threads) is a multiple of 128 and at least 64 * kPWaves.
-template <int K, int kBlock>
-__device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq, int tid, int wave, int lane) {
+template <int K, int kBlock, typename After1 = NoStep>
+__device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq, int tid, int wave, int lane,
+                                   After1 after1 = After1()) {
   using Mk = Masks<K>;
   constexpr int L = 1 << K;
   constexpr int NMF = Mk::kMfma;
@@ -174,11 +188,11 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
         acc[hh] += __shfl_xor(acc[hh], 1, 64);
         acc[hh] += __shfl_xor(acc[hh], 2, 64);
       }
-      s.qt[qtr][row] = acc[qtr];
+      s.qt[qtr][qt_pad(row)] = acc[qtr];
     }
     __syncthreads();
     if (wave < 4) {
-      const float y0 = s.qt[wave][lane], y1 = s.qt[wave][lane + 64];
+      const float y0 = s.qt[wave][qt_pad(lane)], y1 = s.qt[wave][qt_pad(lane + 64)];
       const float m1 = wave_max_f32(fmaxf(fabsf(y0), fabsf(y1)));
       const float s1 = wave_sum_f32(y0 + y1);
       if (lane == 0) {
@@ -196,8 +210,8 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
       x1 = (lane & hs) ? o1 - x1 : x1 + o1;
     }
     const float y0 = x0 + x1, y1 = x0 - x1;
-    s.qt[wave][lane] = y0;
-    s.qt[wave][lane + 64] = y1;
+    s.qt[wave][qt_pad(lane)] = y0;
+    s.qt[wave][qt_pad(lane + 64)] = y1;
     const float m1 = wave_max_f32(fmaxf(fabsf(y0), fabsf(y1)));
     const float s1 = wave_sum_f32(y0 + y1);
     if (lane == 0) {
@@ -206,8 +220,10 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
     }
   }
   __syncthreads();
+  after1();
   // (2) p = S qt / sqrt(d): threads 4i .. 4i+3 own row i, a quarter of it each,
-  //     all four heads, then a 4-lane reduction; per wave, max |p_i| and sum p_i
+  //     all four heads (qt read as float4, the quarters in different banks),
+  //     then a 4-lane reduction; per wave, max |p_i| and sum p_i
   if (wave < kPWaves) {
     const int prow = tid >> 2, qtr = tid & 3;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -215,13 +231,15 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
     for (int v = 0; v < 4; ++v) {
       const uint32_t ww[4] = {r.srow[v].x, r.srow[v].y, r.srow[v].z, r.srow[v].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const h16x2 pr = __builtin_bit_cast(h16x2, ww[e]);
-        const int j = 32 * qtr + 8 * v + 2 * e;
+      for (int hh = 0; hh < 4; ++hh) {
+        const float4 qa = *reinterpret_cast<const float4*>(&s.qt[hh][qt_pad(32 * qtr + 8 * v)]);
+        const float4 qb = *reinterpret_cast<const float4*>(&s.qt[hh][qt_pad(32 * qtr + 8 * v + 4)]);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
 #pragma unroll
-        for (int hh = 0; hh < 4; ++hh) {
-          acc[hh] = fmaf((float)pr[0], s.qt[hh][j], acc[hh]);
-          acc[hh] = fmaf((float)pr[1], s.qt[hh][j + 1], acc[hh]);
+        for (int e = 0; e < 4; ++e) {
+          const h16x2 pr = __builtin_bit_cast(h16x2, ww[e]);
+          acc[hh] = fmaf((float)pr[0], qv[2 * e], acc[hh]);
+          acc[hh] = fmaf((float)pr[1], qv[2 * e + 1], acc[hh]);
         }
       }
     }
@@ -244,7 +262,8 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
   }
   __syncthreads();
   // (3) per head, the value of one fixed-point unit (2^30 units for the largest
-  //     |2 a_P qt_j| or |2 p_i|) and the constant terms; then the A fragments.
+  //     |2 a_P qt_j| or |2 p_i|) and the constant terms; the fixed-point values
+  //     V; then the A fragments.
   // A fragment of MFMA f = 2*w2 + g, lane l: row m = l%32, K = 16(l/32) + 4q + byte.
   // Lane half hl of MFMA (w2, g) carries list word 2*w2 + hl; bit (8*byte + 4g + q)
   // of that word.  Row m = 8 hh + 4 part + limb holds signed int8 limb `limb` of
@@ -252,7 +271,9 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
   // coordinate j is 2 a_P qt_j (plane masks) or 2 p_j (sign mask) in units,
   // pre-divided by 2^(j mod 8) (-128 for j mod 8 == 7: the top bit of a byte),
   // and its signed base-256 digits are the bytes of V + 0x80808080, each minus 128.
-  // A thread's entries all share one row m (kBlock is a multiple of 128).
+  // Each V is computed once (step 3a, a table in LDS) and its four limbs read
+  // from it (step 3b); a thread's fragment entries all share one row m (kBlock
+  // is a multiple of 128).
   const auto unit_of = [&](int hh, int part) {
     float vm;
     if (part == 0) {
@@ -279,10 +300,22 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
     }
     s.consts[hh][c] = v;
   }
+  for (int e = tid; e < 4 * Mk::kMasks * kD; e += kBlock) {
+    const int j = e % kD, mask = (e / kD) % Mk::kMasks, hh = e / (kD * Mk::kMasks);
+    const bool is_sign_mask = mask == Mk::kPlaneMasks;
+    int V = 0;
+    if (hh < gq) {
+      const float val = is_sign_mask ? 2.0f * s.pp[hh][j] : 2.0f * s.coef[mask] * s.qt[hh][qt_pad(j)];
+      const int sh = j & 7;
+      const double inv_div = sh == 7 ? -1.0 / 128.0 : 1.0 / (double)(1 << sh);
+      V = (int)rint((double)val * (1.0 / (double)unit_of(hh, is_sign_mask ? 1 : 0)) * inv_div);
+    }
+    s.vt[hh][mask][j] = V;
+  }
+  __syncthreads();
   {
     const int m = (tid >> 2) & 31;
     const int hh = m >> 3, part = (m >> 2) & 1, limb = m & 3;
-    const double inv_unit = 1.0 / (double)unit_of(hh, part);
     for (int idx = tid; idx < NMF * 64 * 4; idx += kBlock) {
       const int q = idx & 3, ln = (idx >> 2) & 63, f = idx >> 8;
       const int w2 = f >> 1, g = f & 1;
@@ -293,11 +326,7 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
       if (hh < gq && part == (is_sign_mask ? 1 : 0)) {
 #pragma unroll
         for (int byt = 0; byt < 4; ++byt) {
-          const int jj = 32 * ww + 8 * byt + 4 * g + q;
-          const float val = is_sign_mask ? 2.0f * s.pp[hh][jj] : 2.0f * s.coef[mask] * s.qt[hh][jj];
-          const int sh = jj & 7;
-          const double inv_div = sh == 7 ? -1.0 / 128.0 : 1.0 / (double)(1 << sh);
-          const int V = (int)rint((double)val * inv_unit * inv_div);
+          const int V = s.vt[hh][mask][32 * ww + 8 * byt + 4 * g + q];
           const uint32_t digit = (((uint32_t)V + 0x80808080u) >> (8 * limb)) & 0xFFu;
           packed |= (digit ^ 0x80u) << (8 * byt);
         }
