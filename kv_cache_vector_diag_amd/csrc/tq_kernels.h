@@ -18,6 +18,11 @@ int launch_encode_generic(const CodebookArgs& cb, const void* x, int dtype, int6
 bool tiled_encode_supported(const CodebookArgs& cb);
 int launch_encode_tiled(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N, int64_t sx_g,
                         int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
+// Hadamard encode at head_dim 256 with up to 256 levels (keys: up to 256
+// projections); 16-byte aligned rows of at least head_dim elements.
+bool wide_encode_supported(const CodebookArgs& cb, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N);
+int launch_encode_wide(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N, int64_t sx_g,
+                       int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
                           int32_t* status, hipStream_t s, int64_t out_stride = 0,
                           const ChannelMap& cm = ChannelMap{});
