@@ -91,6 +91,45 @@ __device__ inline float wave_max_f32(float v) {
   return v;
 }
 
+// Lane exchanges without LDS: DPP within a 16-lane row (xor 1 and xor 2 by
+// quad permutation, xor 8 by a rotation of the row by 8), and across the two
+// halves of the wave (xor 32) by a permlane swap.
+template <int C>
+__device__ inline float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), C, 0xF, 0xF, true));
+}
+__device__ inline float xor1_f32(float v) { return dpp_f32<0xB1>(v); }
+__device__ inline float xor2_f32(float v) { return dpp_f32<0x4E>(v); }
+__device__ inline float xor8_f32(float v) { return dpp_f32<0x128>(v); }
+__device__ inline float xor32_f32(float v, int lane) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(lane < 32 ? p[1] : p[0]);
+}
+
+// Sum and maximum over the 64 lanes, the result uniform: within each 16-lane
+// row by DPP (quad permutations, then the half-row and row mirrors), then row 0
+// into row 1 and row 2 into row 3 (row broadcast of lane 15), then row 1 into
+// rows 2-3 (broadcast of lane 31); lane 63 holds the total.
+__device__ inline float wave_sum_uniform(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ inline float wave_max_uniform(float v) {
+  constexpr int kNegInf = (int)0xFF800000u;
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x142, 0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(kNegInf, __float_as_int(v), 0x143, 0xC, 0xF, false)));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // z = u/|x| (float64) rounded toward +infinity.  For every float32 threshold t,
 // t < z_up exactly when t < z, the comparison the quantizer's definition asks
 // for: if z > t then z_up >= z > t; if z <= t then z_up <= t, because t is a

@@ -185,16 +185,16 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
       }
 #pragma unroll
       for (int hh = 0; hh < 4; ++hh) {
-        acc[hh] += __shfl_xor(acc[hh], 1, 64);
-        acc[hh] += __shfl_xor(acc[hh], 2, 64);
+        acc[hh] += xor1_f32(acc[hh]);
+        acc[hh] += xor2_f32(acc[hh]);
       }
       s.qt[qtr][qt_pad(row)] = acc[qtr];
     }
     __syncthreads();
     if (wave < 4) {
       const float y0 = s.qt[wave][qt_pad(lane)], y1 = s.qt[wave][qt_pad(lane + 64)];
-      const float m1 = wave_max_f32(fmaxf(fabsf(y0), fabsf(y1)));
-      const float s1 = wave_sum_f32(y0 + y1);
+      const float m1 = wave_max_uniform(fmaxf(fabsf(y0), fabsf(y1)));
+      const float s1 = wave_sum_uniform(y0 + y1);
       if (lane == 0) {
         s.qstat[wave][0] = m1;
         s.qstat[wave][1] = s1;
@@ -205,15 +205,28 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
     float x1 = ((r.d1 >> (lane & 31)) & 1u) ? -r.q1 : r.q1;
 #pragma unroll
     for (int hs = 1; hs < 64; hs <<= 1) {
-      const float o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
+      // partners xor 1, 2, 8 by DPP and xor 32 by a permlane swap; xor 4 and 16
+      // through the LDS crossbar
+      float o0, o1;
+      if (hs == 1) {
+        o0 = xor1_f32(x0), o1 = xor1_f32(x1);
+      } else if (hs == 2) {
+        o0 = xor2_f32(x0), o1 = xor2_f32(x1);
+      } else if (hs == 8) {
+        o0 = xor8_f32(x0), o1 = xor8_f32(x1);
+      } else if (hs == 32) {
+        o0 = xor32_f32(x0, lane), o1 = xor32_f32(x1, lane);
+      } else {
+        o0 = __shfl_xor(x0, hs, 64), o1 = __shfl_xor(x1, hs, 64);
+      }
       x0 = (lane & hs) ? o0 - x0 : x0 + o0;
       x1 = (lane & hs) ? o1 - x1 : x1 + o1;
     }
     const float y0 = x0 + x1, y1 = x0 - x1;
     s.qt[wave][qt_pad(lane)] = y0;
     s.qt[wave][qt_pad(lane + 64)] = y1;
-    const float m1 = wave_max_f32(fmaxf(fabsf(y0), fabsf(y1)));
-    const float s1 = wave_sum_f32(y0 + y1);
+    const float m1 = wave_max_uniform(fmaxf(fabsf(y0), fabsf(y1)));
+    const float s1 = wave_sum_uniform(y0 + y1);
     if (lane == 0) {
       s.qstat[wave][0] = m1;
       s.qstat[wave][1] = s1;
@@ -245,15 +258,15 @@ __device__ inline void query_build(QueryLds<K>& s, const QueryRegs<K>& r, int gq
     }
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
-      acc[hh] += __shfl_xor(acc[hh], 1, 64);
-      acc[hh] += __shfl_xor(acc[hh], 2, 64);
+      acc[hh] += xor1_f32(acc[hh]);
+      acc[hh] += xor2_f32(acc[hh]);
       acc[hh] *= 0.08838834764831845f;          // 1/sqrt(128)
     }
     s.pp[qtr][prow] = acc[qtr];
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
-      const float pm = wave_max_f32(fabsf(acc[hh]));
-      const float ps = wave_sum_f32(qtr == 0 ? acc[hh] : 0.0f);
+      const float pm = wave_max_uniform(fabsf(acc[hh]));
+      const float ps = wave_sum_uniform(qtr == 0 ? acc[hh] : 0.0f);
       if (lane == 0) {
         s.pstat[wave][hh][0] = pm;
         s.pstat[wave][hh][1] = ps;
