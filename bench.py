@@ -15,10 +15,10 @@ then 100 timed steps by default, reported as mean and median.  A plain
 device copy is timed in the same run, and each kernel's bandwidth is also
 given as a fraction of it.
 
-Prints ONE JSON line.  `--config c1|c2|c4|c5|haar|paged|gram` measures the
-single-head latency, the prefill-encode, the long-context attend, the
-mixed-precision layer, the Haar-rotation, the paged-cache decode and the
-Gram-table scoring rows instead (also one line each).
+Prints ONE JSON line.  `--config c1|c2|c4|c5|haar|paged|gram|decode` measures
+the single-head latency, the prefill-encode, the long-context attend, the
+mixed-precision layer, the Haar-rotation, the paged-cache decode, the
+Gram-table scoring and the value-decode rows instead (also one line each).
 """
 from __future__ import annotations
 
@@ -710,6 +710,49 @@ def bench_gram(args, torch, b):
                                   scs["median"])}
 
 
+def bench_decode(args, torch, b):
+    """Value decode of the prefill cache: the 4-bit value records of 32 layers x
+    8 kv heads x 4096 tokens (d = 128, from encoding the prefill workload's bf16
+    values once, before timing) back to float32, one launch per step."""
+    from kv_cache_vector_diag_amd import inputs
+    dev = "cuda:0"
+    L, Hkv, T, d, seed, bits = 32, 8, 4096, 128, 1, 4
+    G = L * Hkv
+    vw = b.tq_record_bytes(d, bits, 0, b.ROLE_VALUE) // 4
+    vcb = b.make_codebooks(G, d, bits, 0, seed, b.ROLE_VALUE, device=dev)
+    _, Vf, _ = inputs.kv_outliers(seed, G, T, d)
+    V = inputs.to_torch(Vf, "bf16", dev)
+    del Vf
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    vrec = b.tq_encode_values(vcb, G, V, d, bits, status=status)
+    del V
+    outs = [torch.empty((G, T, d), dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def step(i, ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_decode_values(vcb, G, vrec, d, bits, out=outs[i % 2], status=status)
+        if ev:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    ms_step, (d_l,), _ = _run_timed(torch, step, args.steps, 1)
+    assert int(status.item()) == 0
+    ds = _stat(d_l)
+    nbytes = G * T * (vw * 4 + d * 4) + vcb.numel()
+    gbps = nbytes / (ds["mean"] * 1e-3) / 1e9
+    return {"metric": "value decode GB/s (4-bit records -> fp32)", "value": gbps, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "ms_per_step_median": ds["median"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "value decode: 32 layers x 8 kv heads x 4096 tokens, d=128, 4-bit value records "
+                                   "(of the prefill workload's bf16 values) to fp32"},
+            "copy_GBps": args.copy_gbps, "decode_ms": ds["mean"], "decode_ms_median": ds["median"],
+            "vectors_per_s": G * T / (ds["mean"] * 1e-3),
+            "roofline": _roofline(gbps, nbytes, "decode_values", "decode_values_c2", args.copy_gbps, ds["mean"],
+                                  ds["median"])}
+
+
 def bench_c1(args, torch, b):
     """Single head: 1024 fp32 N(0,1) keys and values (seed 42), head_dim 128,
     keys b=3 (128 projections), values 3 bits, one fp32 query.  One step =
@@ -790,7 +833,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "haar", "paged", "gram"])
+    ap.add_argument("--config", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "haar", "paged", "gram", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -830,7 +873,7 @@ def main():
         return
     args.copy_gbps = copy_gbps(torch)
     fn = {"c1": bench_c1, "c2": bench_c2, "c3": bench_c3, "c4": bench_c4, "c5": bench_c5, "haar": bench_haar,
-          "paged": bench_paged, "gram": bench_gram}[args.config]
+          "paged": bench_paged, "gram": bench_gram, "decode": bench_decode}[args.config]
     line = fn(args, torch, b)
     if args.config == "c3":
         line["cpu_baseline"] = cpu

@@ -109,6 +109,9 @@ int tq_decode_values_ex(int head_dim, int bits, int rotation, const void* cbs, i
   if (G * N == 0) return TQ_OK;
   if (!cbs || !rec || !out) return TQ_ERR_NULL;
   CodebookArgs cb = make_cb_args(cbs, n_cb, L);
+  if (decode_wh_supported(cb, G, N, out))
+    return launch_decode_wh(cb, static_cast<const uint32_t*>(rec), G, N, out, status,
+                            static_cast<hipStream_t>(stream));
   return launch_decode_generic(cb, static_cast<const uint32_t*>(rec), G, N, out, status,
                                static_cast<hipStream_t>(stream));
 }

@@ -23,6 +23,11 @@ int launch_encode_tiled(const CodebookArgs& cb, const void* x, int dtype, int64_
 bool wide_encode_supported(const CodebookArgs& cb, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N);
 int launch_encode_wide(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N, int64_t sx_g,
                        int64_t sx_n, uint32_t* rec, int32_t* status, hipStream_t s);
+// Value decode of the Walsh-Hadamard codec at d in {32, 64, 128, 256}, k <= 8,
+// into a 16-byte aligned [G][N][d] output; needs N >= 2048 / d.
+bool decode_wh_supported(const CodebookArgs& cb, int64_t G, int64_t N, const void* out);
+int launch_decode_wh(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
+                     int32_t* status, hipStream_t s);
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
                           int32_t* status, hipStream_t s, int64_t out_stride = 0,
                           const ChannelMap& cm = ChannelMap{});

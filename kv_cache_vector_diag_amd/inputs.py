@@ -15,6 +15,8 @@ SeedSequence([seed, stream, group]).
   * sign_bits:      ceil(d/32) uint32 words of fair random bits.
   * block_codes:    uniform indices in [0, N) [M][nb] and norms [M] drawn as
                     |N(0, I_d)| (chi with d degrees of freedom), float32.
+  * plane_words:    fair random uint32 words [G][N][n_words] (random bit
+                    planes of value codes) and chi(d) norms [G][N], float32.
 bf16 inputs are the float32 draws rounded to nearest-even by torch.
 """
 from __future__ import annotations
@@ -97,6 +99,13 @@ def block_codes(seed: int, M: int, nb: int, N: int, d: int, stream: int = STREAM
     idx = r.integers(0, N, (M, nb), dtype=np.int64)
     norms = np.sqrt(r.chisquare(d, M)).astype(np.float32)
     return idx, norms
+
+
+def plane_words(seed: int, G: int, N: int, n_words: int, d: int, stream: int = STREAM_CODES):
+    r = _rng(seed, stream)
+    words = r.integers(0, 1 << 32, (G, N, n_words), dtype=np.uint64).astype(np.uint32)
+    norms = np.sqrt(r.chisquare(d, (G, N))).astype(np.float32)
+    return words, norms
 
 
 def to_torch(a: np.ndarray, dtype: str = "bf16", device=None):

@@ -34,6 +34,7 @@ KERNELS = {
     "encode_generic": "encode_generic",
     "scores_generic": "score_generic",
     "decode_generic": "decode_generic",
+    "decode_wh_kernel": "decode_values",
     "attend_part": "attend_part",
     "attend_merge": "attend_merge",
     "attend_mfma": "attend_mfma",
@@ -49,12 +50,16 @@ KERNELS = {
 
 # kernels instantiated for keys and values: (short name, index of the KEY template argument)
 ROLE_KERNELS = {"encode128_kernel": ("encode", 1), "encode_tiled_kernel": ("tiled", -1),
-                "split256_kernel": ("split256", -1)}
+                "encode_wide_kernel": ("wide", 1), "split256_kernel": ("split256", -1)}
 
 # sources each measured kernel is built from (a change to any makes its counters stale)
 _COMMON = ["tq_device.h", "tq_layout.h", "tq_mfma.h", "tq_fast.h", "../../include/tq.h"]
 KERNEL_SOURCES = {
     "encode_keys": ["tq_fast128.hip"] + _COMMON,
+    "encode_values": ["tq_fast128.hip"] + _COMMON,
+    "wide_keys": ["tq_wide.hip", "tq_kernels.h"] + _COMMON,
+    "wide_values": ["tq_wide.hip", "tq_kernels.h"] + _COMMON,
+    "decode_values": ["tq_decode.hip", "tq_kernels.h"] + _COMMON,
     "score": ["tq_score128.hip", "tq_score_core.h"] + _COMMON,
     "attend_fused": ["tq_attend.hip", "tq_score_core.h", "tq_kernels.h"] + _COMMON,
     "gram_scores": ["tq_gram.hip", "tq_kernels.h"] + _COMMON,
