@@ -580,7 +580,8 @@ def bench_haar(args, torch, b):
     S rho as in the Walsh-Hadamard kernel; the roofline is its algorithmic
     arithmetic (2 d^2 + 2 m d flops per key) against the dense bf16 MFMA peak.
     The score kernel rotates each query by R and is otherwise the Walsh-Hadamard
-    one."""
+    one.  The same keys at head_dim 64 (64 projections; R and S padded to 128
+    on the matrix cores) are encoded and timed beside the step."""
     from kv_cache_vector_diag_amd import inputs
     dev = "cuda:0"
     B, Hkv, Hq, T, d, bits, m, seed = 16, 8, 32, 4096, 128, 3, 128, 3
@@ -611,6 +612,25 @@ def bench_haar(args, torch, b):
     assert int(status.item()) == 0
     es, ss = _stat(enc_l), _stat(sc_l)
     enc_ms, sc_ms = es["mean"], ss["mean"]
+    # the same keys at head_dim 64 (padded to 128 on the matrix cores)
+    d64 = 64
+    w64 = b.tq_record_bytes_ex(d64, bits, d64, b.ROLE_KEY, rot) // 4
+    kcb64 = b.make_codebooks(Hkv, d64, bits, d64, seed, b.ROLE_KEY, device=dev, rotation=rot)
+    K64 = inputs.to_torch(inputs.kv_normal(seed, G, T, d64), "bf16", dev)
+    rec64 = torch.empty((G, T, w64), dtype=torch.int32, device=dev)
+
+    def step64(i, ev=None):
+        if ev:
+            ev[0].record()
+        b.tq_encode_keys(kcb64, Hkv, K64, d64, bits, d64, rec=rec64, status=status, rotation=rot)
+        if ev:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step64(i)
+    _, (e64_l,), _ = _run_timed(torch, step64, args.steps, 1)
+    assert int(status.item()) == 0
+    e64 = _stat(e64_l)
     flops = G * T * (2 * d * d + 2 * m * d)
     tflops = flops / (enc_ms * 1e-3) / 1e12
     enc_bytes = G * T * (d * 2 + words * 4) + kcb.numel()
@@ -625,6 +645,8 @@ def bench_haar(args, torch, b):
             "encode_ms": enc_ms, "encode_ms_median": es["median"], "encode_GBps": enc_bytes / (enc_ms * 1e-3) / 1e9,
             "encode_keys_per_s": G * T / (enc_ms * 1e-3), "score_ms": sc_ms, "score_ms_median": ss["median"],
             "score_GBps": sc_bytes / (sc_ms * 1e-3) / 1e9,
+            "encode_d64_ms": e64["mean"], "encode_d64_ms_median": e64["median"],
+            "encode_d64_keys_per_s": G * T / (e64["mean"] * 1e-3),
             # the binding bound of the encode is HBM (its MFMA share is reported beside it)
             "roofline": _roofline(enc_bytes / (enc_ms * 1e-3) / 1e9, enc_bytes, "encode (Haar)", None,
                                   args.copy_gbps, enc_ms, es["median"]),

@@ -39,10 +39,11 @@ constexpr int kD = 128;
 constexpr int kM = 128;
 // Waves per workgroup (one workgroup per CU): 12 (three per SIMD) where the
 // kernel fits in 168 VGPRs, else 8 (two per SIMD, up to 256 VGPRs).  Keys take
-// 8: the four projection accumulators stay live across the slices.
-template <int K, bool KEY, int DT, bool HAAR>
+// 8: the four projection accumulators stay live across the slices; so do the
+// padded Haar kernels (their masks and record staging).
+template <int K, bool KEY, int DT, bool HAAR, bool PAD = false>
 constexpr int waves_for() {
-  return (KEY || DT == 0 || (HAAR && DT == 2)) ? 8 : 12;
+  return (KEY || DT == 0 || (HAAR && DT == 2) || PAD) ? 8 : 12;
 }
 constexpr int kTile = 32;
 
@@ -60,6 +61,11 @@ struct Enc128Args {
   int64_t tiles_per_block;
   int64_t blocks_per_group;
   PagedOut po;               // paged output (the PAGED kernels): rec is the pool
+  // head_dim and projections of the codebook: 128 and 128, except for the
+  // padded Haar kernels (PAD), which run a smaller head_dim as 128 with zero
+  // rows and columns of R and S and zero input coordinates
+  int dv, mv;
+  float inv_sqrt_dv;         // 1 / sqrt(dv)
 };
 
 // Rotation u = H (D x) with H = H_128 in Sylvester order, split as
@@ -136,8 +142,9 @@ __device__ uint32_t r_term(float r, int t) {
   return t == 0 ? b0 : (t == 1 ? b1 : b2);
 }
 
+// R is dv x dv (row-major); rows and columns past dv are zero.
 template <bool F16>
-__device__ void build_rfrag(u32x4* rfrag, const float* R) {
+__device__ void build_rfrag(u32x4* rfrag, const float* R, int dv) {
   for (int f = threadIdx.x; f < 96 * 64; f += blockDim.x) {
     const int lane = f & 63, c = (f >> 6) & 7, M = (f >> 9) & 3, t = f >> 11;
     const int row = 32 * M + tile_row_index(lane & 31);
@@ -146,7 +153,9 @@ __device__ void build_rfrag(u32x4* rfrag, const float* R) {
       uint32_t word = 0;
       for (int hh = 0; hh < 2; ++hh) {
         const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;
-        word |= r_term<F16>(-R[row * kD + col], t) << (16 * hh);   // -R: the products give v = -u
+        // -R: the products give v = -u
+        const float r = (row < dv && col < dv) ? -R[row * dv + col] : 0.0f;
+        word |= r_term<F16>(r, t) << (16 * hh);
       }
       v[q] = word;
     }
@@ -158,14 +167,16 @@ __device__ void build_rfrag(u32x4* rfrag, const float* R) {
 // w' = -w (from v = -u), so that (-S) w' = S w.  Fragment (Mp, c), lane l: row
 // rho = l%32 is projection 32Mp + tile_row_index(rho); element e:
 // -S[proj][qjl_coord(c, l/32, e)].
-__device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
+// S is mv x dv (row-major); rows past mv and columns past dv are zero.
+__device__ void build_sfrag(u32x4* sfrag, const uint16_t* S, int dv, int mv) {
   for (int f = threadIdx.x; f < 4 * 8 * 64; f += blockDim.x) {
     const int lane = f & 63, c = (f >> 6) & 7, Mp = f >> 9;
     const int row = 32 * Mp + tile_row_index(lane & 31);
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
-      const uint32_t lo = S[row * kD + qjl_coord(c, lane >> 5, 2 * q)];
-      const uint32_t hi = S[row * kD + qjl_coord(c, lane >> 5, 2 * q + 1)];
+      const int c0 = qjl_coord(c, lane >> 5, 2 * q), c1 = qjl_coord(c, lane >> 5, 2 * q + 1);
+      const uint32_t lo = (row < mv && c0 < dv) ? S[row * dv + c0] : 0u;
+      const uint32_t hi = (row < mv && c1 < dv) ? S[row * dv + c1] : 0u;
       v[q] = (lo | (hi << 16)) ^ 0x80008000u;
     }
     sfrag[f] = v;
@@ -173,9 +184,15 @@ __device__ void build_sfrag(u32x4* sfrag, const uint16_t* S) {
 }
 
 
-// LDS of encode128_kernel: rotation fragments, S fragments (keys), constants.
-template <bool KEY, bool HAAR>
-constexpr size_t enc_lds_bytes() { return (HAAR ? 98304 : 32768) + (KEY ? 32768 : 0) + 128; }
+// LDS of encode128_kernel: rotation fragments, S fragments (keys), constants,
+// and for the padded kernels a record staging row per wave (32 records of up
+// to 18 words, 8 waves).
+constexpr int kPadRecMax = 18;
+constexpr size_t kPadStageBytes = 8 * 32 * kPadRecMax * 4;
+template <bool KEY, bool HAAR, bool PAD = false>
+constexpr size_t enc_lds_bytes() {
+  return (HAAR ? 98304 : 32768) + (KEY ? 32768 : 0) + 128 + (PAD ? kPadStageBytes : 0);
+}
 
 // The page slot of token tok of group g for paged output, or null (the status
 // word flagged) when the position or its page lies outside the table or pool.
@@ -191,10 +208,11 @@ __device__ inline uint32_t* paged_slot(const Enc128Args& a, int64_t g, int64_t t
 
 // The encode of workgroup `bid` of a launch over a's groups (the kernels below
 // run it for their own workgroup index).
-template <int K, bool KEY, int DT, bool HAAR, bool PAGED, int kWaves>
+template <int K, bool KEY, int DT, bool HAAR, bool PAGED, int kWaves, bool PAD = false>
 __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid) {
   constexpr int kRotBytes = HAAR ? 98304 : 32768;
   static_assert(!HAAR || DT != 0, "the Haar rotation takes 16-bit inputs");
+  static_assert(!PAD || (HAAR && !PAGED), "padding is for the Haar rotation, contiguous records");
   extern __shared__ __align__(16) uint8_t smem[];
   u32x4* hfrag = reinterpret_cast<u32x4*>(smem);                // rotation: 8 (Hadamard) or 96 (Haar) fragments
   u32x4* sfrag = reinterpret_cast<u32x4*>(smem + kRotBytes);    // 32 KB (keys)
@@ -207,16 +225,16 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
   const uint8_t* blob = a.cbs + (g % a.n_cb) * a.stride;
   if (threadIdx.x == 0 && a.status) {
     const BlobHeader* hd = reinterpret_cast<const BlobHeader*>(blob);
-    if (hd->magic != kBlobMagic || hd->version != kBlobVersion || hd->head_dim != kD || hd->bits != a.bits ||
-        hd->role != a.role || hd->projections != (KEY ? kM : 0) ||
+    if (hd->magic != kBlobMagic || hd->version != kBlobVersion || hd->head_dim != a.dv || hd->bits != a.bits ||
+        hd->role != a.role || hd->projections != (KEY ? a.mv : 0) ||
         (int)hd->rotation != (HAAR ? kRotHaar : kRotHadamard))
       atomicOr(a.status, TQ_STATUS_BAD_BLOB);
   }
   if constexpr (HAAR)
-    build_rfrag<DT == 2>(hfrag, reinterpret_cast<const float*>(blob + a.off_d));
+    build_rfrag<DT == 2>(hfrag, reinterpret_cast<const float*>(blob + a.off_d), PAD ? a.dv : kD);
   else
     build_hfrag<DT == 2>(hfrag, reinterpret_cast<const uint32_t*>(blob + a.off_d));
-  if (KEY) build_sfrag(sfrag, reinterpret_cast<const uint16_t*>(blob + a.off_s));
+  if (KEY) build_sfrag(sfrag, reinterpret_cast<const uint16_t*>(blob + a.off_s), PAD ? a.dv : kD, PAD ? a.mv : kM);
   if (threadIdx.x < L / 2) consts[threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_c)[L / 2 + threadIdx.x];
   if (threadIdx.x < NT) consts[16 + threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_t)[L / 2 + threadIdx.x];
   __syncthreads();
@@ -235,9 +253,17 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
   const uint32_t* xb16 = reinterpret_cast<const uint32_t*>(a.x);
   constexpr int RW = KEY ? (K * 4 + 4 + 2) : (K * 4 + 1);
   // (paged output stores through per-lane page slots; its resource is empty)
+  const int RWo = PAD ? a.rec_words : RW;   // record words in memory
   const __amdgpu_buffer_rsrc_t rrs =
-      __builtin_amdgcn_make_buffer_rsrc(PAGED ? a.rec : a.rec + g * a.N * RW, 0, PAGED ? 0 : (int)(a.N * RW * 4),
+      __builtin_amdgcn_make_buffer_rsrc(PAGED ? a.rec : a.rec + g * a.N * RWo, 0, PAGED ? 0 : (int)(a.N * RWo * 4),
                                         kRsrcWord3);
+  // padded kernels: plane words and sign words of the smaller record, this
+  // wave's record staging row
+  const int Wv = (a.dv + 31) / 32, SWv = (a.mv + 31) / 32;
+  uint32_t* stage = reinterpret_cast<uint32_t*>(smem + kRotBytes + (KEY ? 32768 : 0) + 128) + wave * 32 * kPadRecMax;
+  // coordinates (and projections) 32 M + 16 h + r exist for r < lim - 32 M
+  const int dlim = a.dv - 16 * h, mlim = a.mv - 16 * h;
+  const auto live16 = [](int n) -> uint32_t { return n <= 0 ? 0u : (n >= 16 ? 0xFFFFu : (1u << n) - 1u); };
 
   // bf16/f16 inputs: the next tile's rows are loaded while this tile is encoded
   const auto row_ptr = [&](int64_t t) {
@@ -248,7 +274,12 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
   if (DT != 0) {
     const u32x4* xp = row_ptr(tile0 + wave);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) xr[c] = xp[2 * c + h];   // tail lanes read row 0, never stored
+    for (int c = 0; c < 8; ++c) {
+      // tail lanes read row 0, never stored; padded chunks read the row start and are zeroed
+      const bool in = !PAD || 16 * c + 8 * h < a.dv;
+      xr[c] = xp[in ? 2 * c + h : 0];
+      if (!in) xr[c] = u32x4{0u, 0u, 0u, 0u};
+    }
     // as many dropped stores as a tile stores, so that on entry the memory
     // operations stand in the loop's order and its first wait is the same
     __builtin_amdgcn_sched_barrier(0);
@@ -389,7 +420,11 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
       // registers are written on every iteration
       const u32x4* xp = row_ptr(tile + kWaves < tile_end ? tile + kWaves : tile);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) xr[c] = xp[2 * c + h];
+      for (int c = 0; c < 8; ++c) {
+        const bool in = !PAD || 16 * c + 8 * h < a.dv;
+        xr[c] = xp[in ? 2 * c + h : 0];
+        if (!in) xr[c] = u32x4{0u, 0u, 0u, 0u};
+      }
     }
 
     // ---- norm (float64, both halves of the vector)
@@ -490,7 +525,8 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
         for (int t = 1; t < NT; ++t) thr_step(tacc[t], mag, uu, tn[t], cpos[t + 1]);
         if (KEY) {
           // w' = -(u - n c[idx]) with c[idx] = +-mag: fma(+-n, mag, -u), +n on the positive half
-          const float w = fmaf(nsg, mag, uu);
+          float w = fmaf(nsg, mag, uu);
+          if (PAD && r >= dlim - 32 * M) w = 0.0f;   // no residual at padded coordinates
           wsq = fmaf(w, w, wsq);
           wv[r] = w;
         }
@@ -538,7 +574,7 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
       }
       auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq), __float_as_uint(wsq), false, false);
       const float tot = __uint_as_float(pg[0]) + __uint_as_float(pg[1]);
-      gam = sqrtf(tot) * 0.08838834764831845f;   // |w| / sqrt(128)
+      gam = sqrtf(tot) * (PAD ? a.inv_sqrt_dv : 0.08838834764831845f);   // |w| / sqrt(d)
     }
 
     // ---- plane words: MSB plane = [z > 0]; the lower planes hold cnt on the
@@ -550,7 +586,7 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
 #pragma unroll
     for (int M = 0; M < 4; ++M) {
       uint32_t pl[K];
-      pl[K - 1] = pw[M];
+      pl[K - 1] = pw[M] & (PAD ? live16(dlim - 32 * M) : 0xFFFFu);
 #pragma unroll
       for (int p = 0; p < K - 1; ++p) {
         uint32_t cb = 0;
@@ -562,13 +598,16 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
           for (int t = 0; t < NT; ++t)
             if (((t + 1) & ((1 << p) - 1)) == 0) cb ^= tw[t][M];
         }
-        pl[p] = ~(cb ^ pw[M]) & 0xFFFFu;   // pos ? cnt_p : ~cnt_p
+        pl[p] = ~(cb ^ pw[M]) & (PAD ? live16(dlim - 32 * M) : 0xFFFFu);   // pos ? cnt_p : ~cnt_p
       }
       for (int p = 0; p < K; ++p) part[p * 4 + M] = h ? (pl[p] << 16) : (pl[p] & 0xFFFFu);
     }
     if (KEY) {
 #pragma unroll
-      for (int Mp = 0; Mp < 4; ++Mp) part[K * 4 + Mp] = h ? ((~sw[Mp]) << 16) : ((~sw[Mp]) & 0xFFFFu);
+      for (int Mp = 0; Mp < 4; ++Mp) {
+        const uint32_t sv = ~sw[Mp] & (PAD ? live16(mlim - 32 * Mp) : 0xFFFFu);
+        part[K * 4 + Mp] = h ? (sv << 16) : sv;
+      }
     }
     // complete two words per swap: half 0 finishes word 2i (and stores it), half 1 word 2i+1
     constexpr int NP = KEY ? K * 4 + 4 : K * 4;
@@ -597,6 +636,34 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
           if (wi < R) dst[wi] = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
         }
       }
+    } else if constexpr (PAD) {
+      // the record of a smaller head_dim: plane p word M < Wv at p Wv + M, sign
+      // word Mp < SWv after the planes, then n32 (and gamma); through this
+      // wave's staging row, then stored as the tile's contiguous records
+#pragma unroll
+      for (int q = 0; q < (R + 1) / 2; ++q) {
+        const int wi = 2 * q + h;
+        if (wi >= R) continue;
+        const uint32_t v = h ? words[(2 * q + 1) < R ? 2 * q + 1 : 0] : words[2 * q];
+        int t;
+        if (wi < K * 4) {
+          t = (wi & 3) < Wv ? (wi >> 2) * Wv + (wi & 3) : -1;
+        } else if (KEY && wi < K * 4 + 4) {
+          t = wi - K * 4 < SWv ? K * Wv + (wi - K * 4) : -1;
+        } else {
+          t = K * Wv + (KEY ? SWv : 0) + (wi - (KEY ? K * 4 + 4 : K * 4));
+        }
+        if (t >= 0) stage[col * RWo + t] = v;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int ntok = (int)(a.N - tile * kTile < kTile ? a.N - tile * kTile : kTile);
+      const uint32_t base = (uint32_t)(tile * kTile * RWo * 4);
+      for (int e = lane; e < ntok * RWo; e += 64) __builtin_amdgcn_raw_buffer_store_b32(stage[e], rrs, base + 4u * e, 0, 0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     } else {
       const uint32_t ro = valid ? (uint32_t)(tok * R * 4) : 0xC0000000u;
 #pragma unroll
@@ -609,9 +676,9 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
   }
 }
 
-template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
-__global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR>())) void encode128_kernel(Enc128Args a) {
-  encode128_body<K, KEY, DT, HAAR, PAGED, waves_for<K, KEY, DT, HAAR>()>(a, blockIdx.x);
+template <int K, bool KEY, int DT, bool HAAR, bool PAGED, bool PAD = false>
+__global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR, PAD>())) void encode128_kernel(Enc128Args a) {
+  encode128_body<K, KEY, DT, HAAR, PAGED, waves_for<K, KEY, DT, HAAR, PAD>(), PAD>(a, blockIdx.x);
 }
 
 // Keys and values of an append in one launch (paged output): the first
@@ -639,20 +706,20 @@ inline void split_tiles(Enc128Args& a, int waves) {
   a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
 }
 
-template <int K, bool KEY, int DT, bool HAAR, bool PAGED>
+template <int K, bool KEY, int DT, bool HAAR, bool PAGED, bool PAD = false>
 int launch_one(Enc128Args a, hipStream_t s) {
-  split_tiles(a, waves_for<K, KEY, DT, HAAR>());
-  const size_t lds = enc_lds_bytes<KEY, HAAR>();
+  split_tiles(a, waves_for<K, KEY, DT, HAAR, PAD>());
+  const size_t lds = enc_lds_bytes<KEY, HAAR, PAD>();
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_kernel<K, KEY, DT, HAAR, PAGED>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_kernel<K, KEY, DT, HAAR, PAGED, PAD>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return -10;
     attr_set = true;
   }
   const int64_t blocks = a.G * a.blocks_per_group;
-  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT, HAAR, PAGED>), dim3((unsigned)blocks),
-                     dim3(64 * waves_for<K, KEY, DT, HAAR>()), lds, s, a);
+  hipLaunchKernelGGL((encode128_kernel<K, KEY, DT, HAAR, PAGED, PAD>), dim3((unsigned)blocks),
+                     dim3(64 * waves_for<K, KEY, DT, HAAR, PAD>()), lds, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
@@ -664,6 +731,8 @@ int launch_dt(const Enc128Args& a, int dt, bool haar, bool paged, hipStream_t s)
     if (dt == TQ_F16) return launch_one<K, KEY, 2, false, true>(a, s);
     return launch_one<K, KEY, 0, false, true>(a, s);
   }
+  if (haar && a.dv < kD)
+    return dt == TQ_F16 ? launch_one<K, KEY, 2, true, false, true>(a, s) : launch_one<K, KEY, 1, true, false, true>(a, s);
   if (haar) return dt == TQ_F16 ? launch_one<K, KEY, 2, true, false>(a, s) : launch_one<K, KEY, 1, true, false>(a, s);
   if (dt == TQ_BF16) return launch_one<K, KEY, 1, false, false>(a, s);
   if (dt == TQ_F16) return launch_one<K, KEY, 2, false, false>(a, s);
@@ -673,11 +742,16 @@ int launch_dt(const Enc128Args& a, int dt, bool haar, bool paged, hipStream_t s)
 }  // namespace
 
 bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N) {
-  if (L.d != kD) return false;
-  // Haar: 16-bit inputs (their products with 16-bit terms of R are exact)
-  if (L.rotation != kRotHadamard && !(L.rotation == kRotHaar && dtype != TQ_F32)) return false;
+  // Haar: 16-bit inputs (their products with 16-bit terms of R are exact); a
+  // head_dim below 128 that is a multiple of 8 runs padded to 128, with up to
+  // 128 projections
+  const bool haar = L.rotation == kRotHaar && dtype != TQ_F32;
+  if (L.rotation != kRotHadamard && !haar) return false;
+  const bool pad = haar && L.d < kD && L.d >= 8 && L.d % 8 == 0;
+  if (L.d != kD && !pad) return false;
   if (N > (int64_t(1) << 30) / (4 * L.rec_words)) return false;   // 32-bit buffer offsets per group
-  if (L.role == TQ_ROLE_KEY && (L.m != kM || L.k < 1 || L.k > 3)) return false;
+  if (L.role == TQ_ROLE_KEY && (L.k < 1 || L.k > 3)) return false;
+  if (L.role == TQ_ROLE_KEY && (pad ? (L.m < 1 || L.m > kM) : L.m != kM)) return false;
   if (L.role == TQ_ROLE_VALUE && (L.k < 1 || L.k > 4)) return false;
   const int esz = dtype == TQ_F32 ? 4 : 2;
   if ((reinterpret_cast<uintptr_t>(x) & 15) || ((sx_g * esz) & 15) || ((sx_n * esz) & 15)) return false;
@@ -700,6 +774,9 @@ Enc128Args make_args(const Layout& L, const void* cbs, int64_t n_cb, const void*
   a.bits = L.bits; a.role = L.role; a.rec_words = L.rec_words;
   a.off_c = L.off_c; a.off_t = L.off_t; a.off_d = L.off_d; a.off_s = L.off_s;
   a.tiles_per_group = (N + kTile - 1) / kTile;
+  a.dv = L.d;
+  a.mv = L.role == TQ_ROLE_KEY ? L.m : 0;
+  a.inv_sqrt_dv = (float)(1.0 / sqrt((double)L.d));
   return a;
 }
 
