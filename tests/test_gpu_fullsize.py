@@ -153,6 +153,26 @@ def test_mixed_precision_layers_full(gpu_lib):
             en, eo = split.encode_split(sq, Xg[toks], ch)
             reps.append(compare_records(sq.normal, rec_np(rn[gs])[toks], en, fraction=False))
             reps.append(compare_records(sq.outlier, rec_np(ro[gs])[toks], eo, fraction=False))
+        # the first split layer's records through the split score / decode calls
+        # (all 16384 tokens of its 8 heads), sampled tokens against the oracle
+        toks = _sample_tokens(rng, T, 200)
+        sqs = [split.split_quantizer(d, n_out, 3, seed + s0 + h, role) for h in range(Hkv)]
+        ch8 = chan[:Hkv].cpu().numpy()
+        rn8, ro8 = rec_np(rn[:Hkv]), rec_np(ro[:Hkv])
+        if key:
+            q = inputs.to_torch(inputs.queries(seed, 1, 4 * Hkv, d), "bf16", DEV)
+            sc = b.tq_scores_split(cbn, cbo, GS, chan[:Hkv], rn[:Hkv].reshape(1, Hkv, T, -1),
+                                   ro[:Hkv].reshape(1, Hkv, T, -1), q, d, n_out, 3, status=st)
+            torch.cuda.synchronize()
+            ref = split.scores_split(sqs, ch8, rn8[:, toks][None], ro8[:, toks][None], inputs.exact_values(q))
+            assert_close(sc.cpu().numpy()[:, :, toks], ref, "split scores (full layer)")
+        else:
+            dec = b.tq_decode_values_split(cbn, cbo, GS, chan[:Hkv], rn[:Hkv], ro[:Hkv], d, n_out, 3, status=st)
+            torch.cuda.synchronize()
+            for h in (0, Hkv - 1):
+                ref = split.decode_values_split(sqs[h], ch8[h], rn8[h][toks], ro8[h][toks])
+                assert_close(dec[h].cpu().numpy()[toks], ref, f"split decode (full layer) h={h}")
+        assert int(st.item()) == 0
         toks = _sample_tokens(rng, T, 300)
         q8 = tq.Quantizer(d, 8, d if key else 0, seed + 3, role)
         reps.append(compare_records(q8, rec_np(r8[3])[toks], tq.encode(q8, inputs.exact_values(X[3])[toks]),
