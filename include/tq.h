@@ -231,9 +231,12 @@ int tq_attend_static(int head_dim, int k_bits, int v_bits, int projections, int 
  * of bf16/f16 inputs run R x on the matrix cores (R in three exact 16-bit
  * terms) at head_dim 128 and, padded to 128, at head_dims below 128 that are
  * multiples of 8 (keys of up to 4 bits with up to 128 projections, values of
- * up to 4 bits, 16-byte aligned rows).  At head_dim 128 the scores and the
- * fused attention (128 projections) rotate the query by R; other Haar encodes
- * and scores run on the float64 per-vector kernels.  The attention's value partials run on the same
+ * up to 4 bits, 16-byte aligned rows); bf16 encodes at head_dims in (128, 256]
+ * that are multiples of 8 stream R through the matrix cores in 16-column
+ * chunks (keys of up to 4 bits with up to 256 projections, values of up to 4
+ * bits).  At head_dim 128 the scores and the fused attention (128
+ * projections) rotate the query by R; other Haar encodes and scores run on the
+ * float64 per-vector kernels.  The attention's value partials run on the same
  * MFMA kernels as for Walsh-Hadamard codebooks when head_dim is a multiple of
  * 32. */
 int tq_encode_keys_ex(int head_dim, int bits, int projections, int rotation,

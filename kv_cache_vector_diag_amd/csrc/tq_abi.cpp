@@ -53,6 +53,9 @@ int encode_common(int role, int head_dim, int bits, int projections, int rotatio
     return launch_encode_fast128(L, cbs, n_cb, x, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
                                  static_cast<hipStream_t>(stream));
   CodebookArgs cb = make_cb_args(cbs, n_cb, L);
+  if (haar256_supported(cb, x_dtype, x, sx_g, sx_n, N))
+    return launch_haar256(cb, x, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
+                          static_cast<hipStream_t>(stream));
   if (wide_encode_supported(cb, x_dtype, x, sx_g, sx_n, N))
     return launch_encode_wide(cb, x, x_dtype, G, N, sx_g, sx_n, static_cast<uint32_t*>(rec), status,
                               static_cast<hipStream_t>(stream));

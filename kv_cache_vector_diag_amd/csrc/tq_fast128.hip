@@ -334,7 +334,10 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
         float part = 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) part = DT == 1 ? sumsq2_bf16(xb[c][q], part) : sumsq2_f16(xb[c][q], part);
-        ss += (double)part;
+        if (DT == 1 && part < 0x1p-100f)
+          ss += sumsq8_bf16_f64(xb[c]);   // squares below the float32 range: the chunk again in float64
+        else
+          ss += (double)part;
       }
     }
 
@@ -438,17 +441,30 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
     const bool finite = ss <= 3.4028234663852886e38;
     if (a.status && __ballot(valid && !finite && h == 0) != 0 && lane == 0) atomicOr(a.status, TQ_STATUS_NON_FINITE);
     const float n32 = (float)sqrt(ss);
+    // A norm below 2^-40 would leave the residual's float32 squares to
+    // underflow: such a token is quantized with u and n scaled by 2^64 (exact;
+    // z = u / n and the signs are unchanged), gamma scaled back at the end.
+    const bool tiny = n32 < 0x1p-40f;
+    const float uscale_inv = tiny ? 0x1p-64f : 1.0f;
+    if (__ballot(tiny) != 0) {
+      const float f = tiny ? 0x1p64f : 1.0f;
+#pragma unroll
+      for (int M = 0; M < 4; ++M)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) u[M][r] *= f;
+    }
+    const float nq = tiny ? n32 * 0x1p64f : n32;   // the norm in the units of u
     // power-of-two scale that brings the residual to O(1) for the f16 split
-    const uint32_t nexp = (__float_as_uint(n32) >> 23) & 0xFFu;
-    const float sc = (n32 > 0.0f && nexp < 253u) ? __uint_as_float((254u - nexp) << 23) : 1.0f;
+    const uint32_t nexp = (__float_as_uint(nq) >> 23) & 0xFFu;
+    const float sc = (nq > 0.0f && nexp < 253u) ? __uint_as_float((254u - nexp) << 23) : 1.0f;
 
     // ---- quantize, pack planes, residual.  Lane half h holds coordinates
     // 32M + 16h + r in register r of tile M; bits are shifted in from r = 15 down
     // to 0 so that bit r of the 16-bit partial word is coordinate 32M + 16h + r.
     float tn[NT > 0 ? NT : 1];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) tn[t] = tpos[t] * n32;   // thresholds in units of u
-    const uint32_t nbits = __float_as_uint(n32);
+    for (int t = 0; t < NT; ++t) tn[t] = tpos[t] * nq;   // thresholds in units of u
+    const uint32_t nbits = __float_as_uint(nq);
     uint32_t pw[4], tw[NT > 0 ? NT : 1][4];                // sign-half words, thermometer words
     constexpr int KB = K - 1;                              // magnitude bits
     uint32_t mw[KB > 0 ? KB : 1][4];                       // values: magnitude index bits
@@ -574,7 +590,7 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
       }
       auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq), __float_as_uint(wsq), false, false);
       const float tot = __uint_as_float(pg[0]) + __uint_as_float(pg[1]);
-      gam = sqrtf(tot) * (PAD ? a.inv_sqrt_dv : 0.08838834764831845f);   // |w| / sqrt(d)
+      gam = sqrtf(tot) * uscale_inv * (PAD ? a.inv_sqrt_dv : 0.08838834764831845f);   // |w| / sqrt(d)
     }
 
     // ---- plane words: MSB plane = [z > 0]; the lower planes hold cnt on the

@@ -28,6 +28,11 @@ int launch_encode_wide(const CodebookArgs& cb, const void* x, int dtype, int64_t
 bool decode_wh_supported(const CodebookArgs& cb, int64_t G, int64_t N, const void* out);
 int launch_decode_wh(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
                      int32_t* status, hipStream_t s);
+// Haar encode on MFMA for head_dim in (128, 256], a multiple of 8, bf16 input
+// (keys up to 4 bits with up to 256 projections, values up to 4 bits).
+bool haar256_supported(const CodebookArgs& cb, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N);
+int launch_haar256(const CodebookArgs& cb, const void* x, int64_t G, int64_t N, int64_t sx_g, int64_t sx_n,
+                   uint32_t* rec, int32_t* status, hipStream_t s);
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
                           int32_t* status, hipStream_t s, int64_t out_stride = 0,
                           const ChannelMap& cm = ChannelMap{});

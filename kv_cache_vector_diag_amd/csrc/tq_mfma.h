@@ -46,6 +46,19 @@ __device__ inline float sumsq2_bf16(uint32_t w, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
 }
 
+// Sum of squares of four packed bf16 pairs in float64, exactly: for chunks
+// whose float32 pair sums may have lost squares to underflow (|x| < 2^-63).
+__device__ inline double sumsq8_bf16_f64(u32x4 w) {
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double lo = (double)__uint_as_float(w[q] << 16), hi = (double)__uint_as_float(w[q] & 0xFFFF0000u);
+    s = fma(lo, lo, s);
+    s = fma(hi, hi, s);
+  }
+  return s;
+}
+
 __device__ inline float sumsq2_f16(uint32_t w, float acc) {
   f16x2 v = __builtin_bit_cast(f16x2, w);
   return __builtin_amdgcn_fdot2(v, v, acc, false);
@@ -71,6 +84,16 @@ __device__ inline void split_f16x2(float w0, float w1, float sc, uint32_t& hi, u
       "v_fma_mixhi_f16 %[l], %[w1], %[sc], -%[h] op_sel:[0,0,1] op_sel_hi:[0,0,1]"
       : [h] "=&v"(hi), [l] "=&v"(lo)
       : [w0] "v"(w0), [w1] "v"(w1), [sc] "v"(sc));
+}
+
+// Squares of a split residual pair, in the scaled domain: hh += hi.hi and
+// hl += hi.lo over both halves (binary16 products are exact in float32), so
+// that (w sc)^2 = hi^2 + 2 hi lo + lo^2 is summed as hh + 2 hl (lo^2 is below
+// 2^-22 of it).  Unlike w^2 it cannot underflow for tiny inputs.
+__device__ inline void split_sumsq(uint32_t hi, uint32_t lo, float& hh, float& hl) {
+  const f16x2 h = __builtin_bit_cast(f16x2, hi), l = __builtin_bit_cast(f16x2, lo);
+  hh = __builtin_amdgcn_fdot2(h, h, hh, false);
+  hl = __builtin_amdgcn_fdot2(h, l, hl, false);
 }
 
 // First threshold step of the quantizer: above = |u| > tn; acc = 2*acc + above;

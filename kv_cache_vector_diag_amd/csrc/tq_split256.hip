@@ -159,6 +159,25 @@ struct SplitArgs {
   bool xcd_major;
 };
 
+// |w| of a token from the square sums of its two lane halves.  The float32
+// squares of a tiny residual can underflow (norms below ~2^-40), so such
+// tokens take it from the scaled split terms instead: (w sc)^2 = hi.hi +
+// 2 hi.lo (+ lo^2, below 2^-22 of it), square-rooted before unscaling.
+__device__ inline float split_gamma(float wsq, float n32, float sc, const u32x4* whi, const u32x4* wlo, int nchunks) {
+  float sq = wsq;
+  const bool tiny = n32 < 0x1p-40f;
+  if (tiny) {
+    float hh = 0.0f, hl = 0.0f;
+    for (int c = 0; c < nchunks; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split_sumsq(whi[c][q], wlo[c][q], hh, hl);
+    sq = fmaf(2.0f, hl, hh);
+  }
+  const auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(sq), __float_as_uint(sq), false, false);
+  const float tot = __uint_as_float(pg[0]) + __uint_as_float(pg[1]);
+  return tiny ? sqrtf(tot) / sc : sqrtf(tot);
+}
+
 // Quantize one 32-row result tile (lane half h holds coordinates 16h + r in
 // register r): sign word, thermometer words, and (keys) the residual, scaled
 // by the power of two sc and split into f16 hi/lo pairs (two K-chunks of 4
@@ -364,8 +383,13 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         if (more) dma(nxt, nbase, nent);
         __builtin_amdgcn_sched_barrier(0);                 // the DMA before the x chunk load
         if (c + kXPre < kKC) xb[c + kXPre] = *reinterpret_cast<const u32x4*>(xr + 8 * (c + kXPre) + 4 * h);
+        {
+          double part = 0.0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ss += pair_sumsq_bf16(xb[c][q]);
+          for (int q = 0; q < 4; ++q) part += pair_sumsq_bf16(xb[c][q]);
+          // squares below the float32 range: the chunk again, exactly in float64
+          ss += part < 0x1p-100 ? sumsq8_bf16_f64(xb[c]) : part;
+        }
         const bf16x8 xv = as<bf16x8>(xb[c]);
         // pieces outer, row tiles inner: consecutive MFMAs use different accumulators
 #pragma unroll
@@ -428,8 +452,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         }
         sw_o = sign_word(acc);
         asm volatile("" : "+v"(sw_o));
-        auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq_o), __float_as_uint(wsq_o), false, false);
-        gam_o = sqrtf(__uint_as_float(pg[0]) + __uint_as_float(pg[1])) * 0.17677669529663688f;   // / sqrt(32)
+        gam_o = split_gamma(wsq_o, no32, sco, who, wlo_o, 2) * 0.17677669529663688f;   // / sqrt(32)
       }
 
       // ---- normal part: quantize the 7 row tiles
@@ -480,8 +503,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
           sw_n[mp] = sign_word(acc);
           asm volatile("" : "+v"(sw_n[mp]));   // materialise here (not next to the stores)
         }
-        auto pg = __builtin_amdgcn_permlane32_swap(__float_as_uint(wsq_n), __float_as_uint(wsq_n), false, false);
-        gam_n = sqrtf(__uint_as_float(pg[0]) + __uint_as_float(pg[1])) * 0.06681531047810609f;   // / sqrt(224)
+        gam_n = split_gamma(wsq_n, nn32, scn, whn, wln, kQC) * 0.06681531047810609f;   // / sqrt(224)
       }
 
       // ---- records (built in every lane, stored for valid tokens only: keeping

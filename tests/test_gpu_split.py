@@ -160,3 +160,32 @@ def test_split_mfma_path_bad_channel_flagged(gpu_lib):
     b.tq_encode_split(tq.ROLE_KEY, cbn, cbo, 1, X, d, n_out, bits, chan, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & b.STATUS_BAD_CHANNEL
+
+
+@pytest.mark.parametrize("role", [tq.ROLE_KEY, tq.ROLE_VALUE])
+def test_split_encode_tiny_rows(gpu_lib, role):
+    """Rows scaled by 1e-30 and 1e-20 (squares below the float32 range) and a zero
+    row among ordinary ones, on the MFMA split kernel."""
+    import torch
+    b = gpu_lib
+    G, N, d, n_out, bits, seed = 2, 90, 256, 32, 3, 8
+    Xf, _ = inputs.kv_channel_std(seed, G, N, d)
+    Xf[:, 3] *= np.float32(1e-30)
+    Xf[:, 4] *= np.float32(1e-20)
+    Xf[:, 5] = 0.0
+    X = inputs.to_torch(Xf, "bf16", DEV)
+    chan = b.tq_outlier_channels(X, d, n_out)
+    cbn, cbo = b.split_codebooks(G, d, n_out, bits, seed, role, device=DEV)
+    sqs = split.split_quantizers(G, d, n_out, bits, seed, role)
+    st = _status()
+    rn, ro = b.tq_encode_split(role, cbn, cbo, G, X, d, n_out, bits, chan, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    xv = inputs.exact_values(X)
+    c = chan.cpu().numpy()
+    reps = []
+    for g in range(G):
+        en, eo = split.encode_split(sqs[g], xv[g], c[g])
+        reps.append(compare_records(sqs[g].normal, rec_np(rn)[g], en, fraction=False))
+        reps.append(compare_records(sqs[g].outlier, rec_np(ro)[g], eo, fraction=False))
+    check_mismatch_fraction(reps)
