@@ -711,12 +711,14 @@ __global__ __launch_bounds__((64 * waves_for<KK, true, DT, false>())) void encod
     encode128_body<KV, false, DT, false, true, W>(va, (int64_t)blockIdx.x - nk);
 }
 
-// ~256 workgroups (one per CU) in total, at least 8 tiles per wave, never more
-// than the group holds; a multiple of the wave count.
+// ~256 workgroups (one per CU) in total, never more tiles than the group
+// holds; a multiple of the wave count.
 inline void split_tiles(Enc128Args& a, int waves) {
-  int64_t per_block = (a.tiles_per_group * a.G + 255) / 256;
-  per_block = per_block < waves * 8 ? waves * 8 : per_block;
-  per_block = (per_block + waves - 1) / waves * waves;
+  // tiles per wave: the launch spread over ~256 workgroups, at least one (a
+  // small launch takes more workgroups rather than more tiles per wave)
+  const int64_t total = a.tiles_per_group * a.G;
+  const int64_t tpw = (total + 256 * waves - 1) / (256 * waves);
+  int64_t per_block = (tpw < 1 ? 1 : tpw) * waves;
   if (per_block > a.tiles_per_group) per_block = (a.tiles_per_group + waves - 1) / waves * waves;
   a.tiles_per_block = per_block;
   a.blocks_per_group = (a.tiles_per_group + per_block - 1) / per_block;
