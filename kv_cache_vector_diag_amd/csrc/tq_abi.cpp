@@ -269,8 +269,8 @@ int tq_append_kv(int head_dim, int k_bits, int v_bits, int projections, const vo
   const int64_t G = head_major ? H_kv : B * H_kv, N = head_major ? B : 1;
   const int64_t sx_g = head_dim, sx_n = head_major ? H_kv * head_dim : head_dim;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // The MFMA encode writes each record straight into its page slot.
-  if (fast128_encode_supported(K, x_dtype, k_new, sx_g, sx_n, N) &&
+  // The MFMA encode writes each record straight into its page slot (head_dim 128).
+  if (head_dim == 128 && fast128_encode_supported(K, x_dtype, k_new, sx_g, sx_n, N) &&
       fast128_encode_supported(V, x_dtype, v_new, sx_g, sx_n, N)) {
     const PagedOut po{page_table, pos, max_pages, num_pages, H_kv, tokens_per_page, head_major};
     rc = launch_append_fast128(K, V, kcbs, n_kcb, vcbs, n_vcb, k_new, v_new, x_dtype, G, N, sx_g, sx_n,

@@ -90,7 +90,9 @@ constexpr int kNS = 32;
 constexpr int kRotFrags = (kNS / 32) * 8;
 static_assert(kNS == 32 || kNS == 64 || kNS == 128, "sub-transform size");
 template <bool F16>
-__device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
+// dv: the codebook's head_dim (its D holds dv bits; columns past it multiply
+// zero inputs and take no sign).
+__device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits, int dv) {
   for (int f = threadIdx.x; f < kRotFrags * 64; f += blockDim.x) {
     const int lane = f & 63, c = (f >> 6) & 7, Mi = f >> 9;
     const int row = 32 * Mi + tile_row_index(lane & 31);
@@ -99,7 +101,8 @@ __device__ void build_hfrag(u32x4* hfrag, const uint32_t* dbits) {
       uint32_t word = 0;
       for (int hh = 0; hh < 2; ++hh) {
         const int col = 16 * c + 8 * (lane >> 5) + 2 * q + hh;     // coordinate of x
-        const uint32_t neg = 1u ^ h_sign(row, col & (kNS - 1)) ^ ((dbits[col >> 5] >> (col & 31)) & 1u);
+        const uint32_t dsg = col < dv ? (dbits[col >> 5] >> (col & 31)) & 1u : 0u;
+        const uint32_t neg = 1u ^ h_sign(row, col & (kNS - 1)) ^ dsg;
         const uint32_t one = F16 ? 0x3C00u : 0x3F80u;
         word |= (one | (neg << 15)) << (16 * hh);
       }
@@ -212,7 +215,7 @@ template <int K, bool KEY, int DT, bool HAAR, bool PAGED, int kWaves, bool PAD =
 __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid) {
   constexpr int kRotBytes = HAAR ? 98304 : 32768;
   static_assert(!HAAR || DT != 0, "the Haar rotation takes 16-bit inputs");
-  static_assert(!PAD || (HAAR && !PAGED), "padding is for the Haar rotation, contiguous records");
+  static_assert(!PAD || (DT != 0 && !PAGED), "padding takes 16-bit inputs and contiguous records");
   extern __shared__ __align__(16) uint8_t smem[];
   u32x4* hfrag = reinterpret_cast<u32x4*>(smem);                // rotation: 8 (Hadamard) or 96 (Haar) fragments
   u32x4* sfrag = reinterpret_cast<u32x4*>(smem + kRotBytes);    // 32 KB (keys)
@@ -233,7 +236,7 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
   if constexpr (HAAR)
     build_rfrag<DT == 2>(hfrag, reinterpret_cast<const float*>(blob + a.off_d), PAD ? a.dv : kD);
   else
-    build_hfrag<DT == 2>(hfrag, reinterpret_cast<const uint32_t*>(blob + a.off_d));
+    build_hfrag<DT == 2>(hfrag, reinterpret_cast<const uint32_t*>(blob + a.off_d), PAD ? a.dv : kD);
   if (KEY) build_sfrag(sfrag, reinterpret_cast<const uint16_t*>(blob + a.off_s), PAD ? a.dv : kD, PAD ? a.mv : kM);
   if (threadIdx.x < L / 2) consts[threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_c)[L / 2 + threadIdx.x];
   if (threadIdx.x < NT) consts[16 + threadIdx.x] = reinterpret_cast<const float*>(blob + a.off_t)[L / 2 + threadIdx.x];
@@ -744,13 +747,15 @@ int launch_one(Enc128Args a, hipStream_t s) {
 template <int K, bool KEY>
 int launch_dt(const Enc128Args& a, int dt, bool haar, bool paged, hipStream_t s) {
   if (paged) {
-    if (haar) return -13;
+    if (haar || a.dv != kD) return -13;
     if (dt == TQ_BF16) return launch_one<K, KEY, 1, false, true>(a, s);
     if (dt == TQ_F16) return launch_one<K, KEY, 2, false, true>(a, s);
     return launch_one<K, KEY, 0, false, true>(a, s);
   }
   if (haar && a.dv < kD)
     return dt == TQ_F16 ? launch_one<K, KEY, 2, true, false, true>(a, s) : launch_one<K, KEY, 1, true, false, true>(a, s);
+  if (a.dv < kD)
+    return dt == TQ_F16 ? launch_one<K, KEY, 2, false, false, true>(a, s) : launch_one<K, KEY, 1, false, false, true>(a, s);
   if (haar) return dt == TQ_F16 ? launch_one<K, KEY, 2, true, false>(a, s) : launch_one<K, KEY, 1, true, false>(a, s);
   if (dt == TQ_BF16) return launch_one<K, KEY, 1, false, false>(a, s);
   if (dt == TQ_F16) return launch_one<K, KEY, 2, false, false>(a, s);
@@ -760,12 +765,14 @@ int launch_dt(const Enc128Args& a, int dt, bool haar, bool paged, hipStream_t s)
 }  // namespace
 
 bool fast128_encode_supported(const Layout& L, int dtype, const void* x, int64_t sx_g, int64_t sx_n, int64_t N) {
-  // Haar: 16-bit inputs (their products with 16-bit terms of R are exact); a
-  // head_dim below 128 that is a multiple of 8 runs padded to 128, with up to
-  // 128 projections
+  // Haar: 16-bit inputs (their products with 16-bit terms of R are exact).  A
+  // smaller head_dim runs padded to 128 with 16-bit inputs and up to 128
+  // projections: for Haar any multiple of 8; for Walsh-Hadamard a power of two
+  // (zero inputs past d: the first d rows of H_128 D x are then H_d D x)
   const bool haar = L.rotation == kRotHaar && dtype != TQ_F32;
   if (L.rotation != kRotHadamard && !haar) return false;
-  const bool pad = haar && L.d < kD && L.d >= 8 && L.d % 8 == 0;
+  const bool pad = dtype != TQ_F32 && L.d < kD && L.d >= 8 && L.d % 8 == 0 &&
+                   (haar || (L.d & (L.d - 1)) == 0);
   if (L.d != kD && !pad) return false;
   if (N > (int64_t(1) << 30) / (4 * L.rec_words)) return false;   // 32-bit buffer offsets per group
   if (L.role == TQ_ROLE_KEY && (L.k < 1 || L.k > 3)) return false;

@@ -3,7 +3,8 @@
 and columns of R and S, zero input coordinates, padded coordinates and
 projections masked out of the record); in (128, 256] with bf16 inputs, R
 streamed through LDS in 16-column chunks; and edge rows (zero, tiny, huge,
-one-hot) on every MFMA encode.  Records against the oracle for key
+one-hot) on every MFMA encode; Walsh-Hadamard head dims below 128 (powers
+of two, 16-bit inputs) padded the same way.  Records against the oracle for key
 widths 2-4 with up to 128 projections, value widths 1-4, bf16 and f16, ragged
 and strided token ranges, shared and per-head codebooks; then scores and
 decoded values of those records against the oracle."""
@@ -113,7 +114,7 @@ def test_haar_wide_head_encode(gpu_lib, d, kb, m, vb, G, N, n_cb, stride):
     check_mismatch_fraction(reps)
 
 
-@pytest.mark.parametrize("d,rot", [(128, "wh"), (128, "haar"), (64, "haar"), (256, "haar")])
+@pytest.mark.parametrize("d,rot", [(128, "wh"), (64, "wh"), (128, "haar"), (64, "haar"), (256, "haar")])
 def test_encode_edge_rows_bf16(gpu_lib, d, rot):
     """Zero, tiny (1e-30 and 1e-20: squares below the float32 range), huge (1e10)
     and one-hot bf16 rows on the MFMA encodes (keys b=4, values 4 bits)."""
@@ -139,3 +140,36 @@ def test_encode_edge_rows_bf16(gpu_lib, d, rot):
         assert int(st.item()) == 0
         xv = inputs.exact_values(X)
         check_mismatch_fraction([compare_records(qz[0], rec_np(rec)[0], tq.encode(qz[0], xv[0]), fraction=False)])
+
+
+@pytest.mark.parametrize("d,kb,m,vb,dtype,G,N,n_cb", [
+    (64, 3, 64, 3, "bf16", 3, 700, 3),
+    (64, 4, 128, 4, "f16", 2, 333, 1),
+    (32, 2, 32, 2, "bf16", 2, 257, 2),
+    (16, 4, 16, 1, "bf16", 2, 129, 1),
+    (8, 3, 5, 4, "f16", 1, 65, 1),
+])
+def test_hadamard_padded_encode(gpu_lib, d, kb, m, vb, dtype, G, N, n_cb):
+    """Walsh-Hadamard head dims below 128 (powers of two, 16-bit inputs) on the
+    MFMA encode: with zero inputs past d, the first d rows of H_128 D x are H_d D x."""
+    import torch
+    b = gpu_lib
+    seed = 700 + d + kb
+    K = inputs.to_torch(inputs.kv_normal(seed, G, N, d, inputs.STREAM_K), dtype, DEV)
+    V = inputs.to_torch(inputs.kv_normal(seed, G, N, d, inputs.STREAM_V), dtype, DEV)
+    kcb = b.make_codebooks(n_cb, d, kb, m, seed, b.ROLE_KEY, device=DEV)
+    vcb = b.make_codebooks(n_cb, d, vb, 0, seed + 50, b.ROLE_VALUE, device=DEV)
+    kq = tq.quantizers(n_cb, d, kb, m, seed, tq.ROLE_KEY)
+    vq = tq.quantizers(n_cb, d, vb, 0, seed + 50, tq.ROLE_VALUE)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    krec = b.tq_encode_keys(kcb, n_cb, K, d, kb, m, status=st)
+    vrec = b.tq_encode_values(vcb, n_cb, V, d, vb, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    kx, vx = inputs.exact_values(K), inputs.exact_values(V)
+    kr, vr = rec_np(krec), rec_np(vrec)
+    reps = []
+    for g in range(G):
+        reps.append(compare_records(kq[g % n_cb], kr[g], tq.encode(kq[g % n_cb], kx[g]), fraction=False))
+        reps.append(compare_records(vq[g % n_cb], vr[g], tq.encode(vq[g % n_cb], vx[g]), fraction=False))
+    check_mismatch_fraction(reps)
