@@ -179,8 +179,8 @@ int tq_scores(int head_dim, int bits, int projections,
 /* Attention output over compressed K and V for one decode step:
  * o[b][hq] = sum_t softmax_t(scores[b][hq][t]) * x^_t, the values decoded on
  * the fly (never materialised) and summed in the rotated domain, one inverse
- * transform per (b, hq); the softmax is split over chunks of 1024 tokens and
- * merged by log-sum-exp.  `work` is caller scratch of
+ * transform per (b, hq); the softmax is split over chunks of 1024 tokens (512
+ * on the fused path below) and merged by log-sum-exp.  `work` is caller scratch of
  * tq_attend_workspace_bytes(...) bytes: the scores (or, where the scores are
  * computed inside the chunk pass, the prepared query side of each (b, kv head)),
  * then the per-chunk partials.  At head_dim 128 with 128 projections, key and

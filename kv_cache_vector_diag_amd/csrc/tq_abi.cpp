@@ -148,7 +148,7 @@ int tq_scores_ex(int head_dim, int bits, int projections, int rotation, const vo
 
 // Scratch of tq_attend: the scores [B][H_q][T] or, on the fused path, the
 // prepared query side of each (b, kv head) (at most B*H_q of them), then
-// (256-byte aligned) the per-chunk partials [B*H_q][ceil(T/1024)][head_dim + 2]
+// (256-byte aligned) the per-chunk partials [B*H_q][ceil(T/512)][head_dim + 2]
 // of the split softmax.
 static size_t attend_scores_bytes(int64_t B, int64_t H_q, int64_t T) {
   const size_t sc = (size_t)(B * H_q * T) * sizeof(float), qp = attend_qprep_bytes(B * H_q);
@@ -157,7 +157,9 @@ static size_t attend_scores_bytes(int64_t B, int64_t H_q, int64_t T) {
 
 size_t tq_attend_workspace_bytes(int head_dim, int64_t B, int64_t H_q, int64_t T) {
   if (head_dim < 2 || head_dim > kMaxHeadDim || B < 0 || H_q < 0 || T < 0) return 0;
-  return attend_scores_bytes(B, H_q, T) + (size_t)(B * H_q * attend_chunks(T) * (head_dim + 2)) * sizeof(float) +
+  // partials of the finer of the two chunkings (the fused pass's)
+  const int64_t chunks = attend_fused_chunks(T) > attend_chunks(T) ? attend_fused_chunks(T) : attend_chunks(T);
+  return attend_scores_bytes(B, H_q, T) + (size_t)(B * H_q * chunks * (head_dim + 2)) * sizeof(float) +
          256;
 }
 

@@ -408,15 +408,20 @@ __global__ __launch_bounds__(kBlock) void attend_mfma_kernel(MfmaPartArgs a) {
 // ---- fused decode attention at head_dim 128 (keys and values, k <= 3 planes
 // each).  A small kernel prepares the query side of every (sequence, kv head)
 // once (the score kernel's fixed-point MFMA fragments, tq_score_core.h) into
-// the workspace; then one workgroup per (sequence, kv head, chunk of kChunk
+// the workspace; then one workgroup per (sequence, kv head, chunk of kFChunk
 // tokens) issues all of its loads at once (fragments, key tiles, value norms
 // and records), scores the chunk's keys straight into LDS, and runs the chunk
 // softmax and the value MFMA above on them, writing the same per-chunk partials
 // for attend_merge_kernel.  No score reaches memory.
-constexpr int kFBlock = 512;               // 8 waves
+// Small workgroups (4 waves, 512 tokens) so that four share a CU: the phases of
+// a chunk (loads, scores, softmax, values) then overlap across workgroups
+// (with one workgroup per CU the step took 1.45x as long as with two).
+constexpr int64_t kFChunk = 512;           // tokens per fused workgroup
+constexpr int kFBlock = 256;               // 4 waves
 constexpr int kFWaves = kFBlock / 64;
+constexpr int kQBlock = 512;               // query-side workgroup (8 waves)
 constexpr size_t kQprepBytes = 20 * 1024 + 256;   // per group: fragments (<= 20 MFMAs x 1 KB), constants
-constexpr int kFSub = 512;                 // tokens per value sub-chunk (two per chunk)
+constexpr int kFSub = 256;                 // tokens per value sub-chunk (two per chunk)
 constexpr int kFRecStride = kFSub + 4;     // as kRecStride and kTbStride, for kFSub tokens
 constexpr int kFTbStride = kFSub + 32;
 
@@ -431,7 +436,7 @@ struct QprepArgs {
 };
 
 template <int KK>
-__global__ __launch_bounds__(kFBlock) void attend_qprep_kernel(QprepArgs a) {
+__global__ __launch_bounds__(kQBlock) void attend_qprep_kernel(QprepArgs a) {
   constexpr int NMF = sc128::Masks<KK>::kMfma;
   __shared__ sc128::QueryLds<KK> qs;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -447,9 +452,9 @@ __global__ __launch_bounds__(kFBlock) void attend_qprep_kernel(QprepArgs a) {
                                                        : nullptr};
   sc128::QueryRegs<KK> qr;
   sc128::query_load<KK>(src, qr, tid, wave, lane);
-  sc128::query_build<KK, kFBlock>(qs, qr, a.gq, tid, wave, lane);
+  sc128::query_build<KK, kQBlock>(qs, qr, a.gq, tid, wave, lane);
   uint8_t* out = a.qws + g * kQprepBytes;
-  for (int e = tid; e < NMF * 64; e += kFBlock) reinterpret_cast<sc128::i32x4*>(out)[e] = qs.afrag[e];
+  for (int e = tid; e < NMF * 64; e += kQBlock) reinterpret_cast<sc128::i32x4*>(out)[e] = qs.afrag[e];
   if (tid < 16) reinterpret_cast<float*>(out + NMF * 1024)[tid] = qs.consts[tid >> 2][tid & 3];
 }
 
@@ -474,8 +479,8 @@ __host__ __device__ inline FusedLds fused_lds(int gq, int kv_planes, int kk_plan
   const int rwv = 4 * kv_planes + 1, nm = 1 << (kv_planes - 1);
   const int nch = (16 * (4 * kk_planes + 6) + 63) / 64;
   FusedLds o;
-  o.wq = 0;                                                   // scores, weights, digit bytes [gq][kChunk]
-  o.rec = a16((size_t)gq * kChunk * 4);                       // value words [rwv][kFRecStride]
+  o.wq = 0;                                                   // scores, weights, digit bytes [gq][kFChunk]
+  o.rec = a16((size_t)gq * kFChunk * 4);                      // value words [rwv][kFRecStride]
   o.tb = o.rec + a16((size_t)rwv * kFRecStride * 4);          // bytes [nm][4][4][kFTbStride]
   o.af = o.tb + (size_t)nm * 4 * 4 * kFTbStride;              // i32x4 [kFSub/32][2][33]
   o.kst = o.af + (size_t)(kFSub / 32) * kAfGroup * 16;        // key tiles: uint2 [kFWaves][64 nch]
@@ -492,11 +497,11 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
   constexpr int NM = 1 << (KV - 1);               // odd value-plane subsets
   constexpr int W = 4;                            // value plane words (d = 128)
   constexpr int RWV = KV * W + 1;                 // value record words
-  constexpr int kTiles = kChunk / 32 / kFWaves;   // key tiles per wave
-  constexpr int kPer = kChunk / kFBlock;          // tokens per thread in the softmax
+  constexpr int kTiles = kFChunk / 32 / kFWaves;   // key tiles per wave
+  constexpr int kPer = kFChunk / kFBlock;          // tokens per thread in the softmax
   constexpr int kVH = kFBlock / kFSub;            // staging threads per value token
   constexpr int kVW = (RWV + kVH - 1) / kVH;      // value words per staging thread and sub-chunk
-  constexpr int kNS = kChunk / kFSub;             // value sub-chunks
+  constexpr int kNS = kFChunk / kFSub;             // value sub-chunks
   constexpr int d = sc128::kD;
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ float consts[4][4];
@@ -517,8 +522,8 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
 
   const int64_t g = blockIdx.x / a.chunks, c = blockIdx.x % a.chunks;
   const int64_t b = g / a.Hkv, hkv = g % a.Hkv;
-  const int64_t t0 = c * kChunk;
-  const int nt = (int)(a.T - t0 < kChunk ? a.T - t0 : kChunk);
+  const int64_t t0 = c * kFChunk;
+  const int nt = (int)(a.T - t0 < kFChunk ? a.T - t0 : kFChunk);
   const uint8_t* vblob = blob_of(a.vcb, g);
   if (tid == 0 && a.status && blob_mismatch(a.vcb, vblob)) atomicOr(a.status, TQ_STATUS_BAD_BLOB);
   const int h = lane >> 5, col = lane & 31, kh = lane >> 5;
@@ -582,8 +587,8 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
     float sa, sb;
     sc128::score_tile<KK>(A, st, consts, a.scale, h, sa, sb);
     const int tt = (wave + kFWaves * k) * 32 + col;
-    if (2 * h < gq) wf[(2 * h) * kChunk + tt] = sa;
-    if (2 * h + 1 < gq) wf[(2 * h + 1) * kChunk + tt] = sb;
+    if (2 * h < gq) wf[(2 * h) * kFChunk + tt] = sa;
+    if (2 * h + 1 < gq) wf[(2 * h + 1) * kFChunk + tt] = sb;
   }
   __syncthreads();
 
@@ -599,7 +604,7 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
           const int t = tid + i * kFBlock;
-          sv[hh][i] = t < nt ? wf[hh * kChunk + t] : -INFINITY;
+          sv[hh][i] = t < nt ? wf[hh * kFChunk + t] : -INFINITY;
           mloc[hh] = fmaxf(mloc[hh], sv[hh][i]);
         }
         mloc[hh] = wave_max_f32(mloc[hh]);
@@ -647,7 +652,7 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
         const int t = tid + i * kFBlock;
         const uint32_t v = (uint32_t)rint((double)sv[hh][i] * fs);   // <= 2^27
         tot += (double)v;                           // integers: exact in any order
-        wd[hh * kChunk + t] = (v & 0x7Fu) | ((v << 1) & 0x7F00u) | ((v << 2) & 0x7F0000u) | ((v << 3) & 0x7F000000u);
+        wd[hh * kFChunk + t] = (v & 0x7Fu) | ((v << 1) & 0x7F00u) | ((v << 2) & 0x7F0000u) | ((v << 3) & 0x7F000000u);
       }
       tot = wave_sum_f64(tot);
       if (lane == 0) womega[wave][hh] = tot;
@@ -664,6 +669,7 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
   i32x16v acc[NM];
 #pragma unroll
   for (int m = 0; m < NM; ++m) acc[m] = i32x16v{};
+  constexpr int kVPar = kFWaves / 4;              // waves per value word
   const int vw = wave & 3, vpar = wave >> 2;
 #pragma unroll
   for (int sc = 0; sc < kNS; ++sc) {
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
     for (int e = tid; e < gq * (kFSub / 4); e += kFBlock) {
       const int hh = e / (kFSub / 4), qd = e % (kFSub / 4);
       const int gi = qd >> 3, half = (qd >> 2) & 1, q = qd & 3;
-      const uint4 x4 = *reinterpret_cast<const uint4*>(wd + hh * kChunk + s0 + 4 * qd);
+      const uint4 x4 = *reinterpret_cast<const uint4*>(wd + hh * kFChunk + s0 + 4 * qd);
       const uint32_t x[4] = {x4.x, x4.y, x4.z, x4.w};
       uint32_t y[4];
       transpose4x4(x, y);
@@ -707,7 +713,7 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
     }
     __syncthreads();
     const uint32_t bit = 0x01010101u << (col & 7);
-    for (int gi = vpar; gi < (ns + 31) / 32; gi += 2) {
+    for (int gi = vpar; gi < (ns + 31) / 32; gi += kVPar) {
       const i32x4v av = af[gi * kAfGroup + 33 * kh + col];
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -723,7 +729,7 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
   // value records' area on, free now); a[j] = unit * sum_P a_P (2 M_P[j] - W)
   __syncthreads();
   int* xch = reinterpret_cast<int*>(smem + lay.rec);   // [4 waves][NM][8 regs][64 lanes]
-  if (wave >= 4) {
+  if (kVPar > 1 && wave >= 4) {
 #pragma unroll
     for (int m = 0; m < NM; ++m)
 #pragma unroll
@@ -746,7 +752,8 @@ __global__ __launch_bounds__(kFBlock) void attend_fused_kernel(FusedArgs a) {
         int64_t mv = 0;
 #pragma unroll
         for (int l = 3; l >= 0; --l)
-          mv = mv * 128 + (int64_t)acc[m][4 * q + l] + (int64_t)xch[((vw * NM + m) * 8 + 4 * q + l) * 64 + lane];
+          mv = mv * 128 + (int64_t)acc[m][4 * q + l] +
+               (kVPar > 1 ? (int64_t)xch[((vw * NM + m) * 8 + 4 * q + l) * 64 + lane] : 0);
         mv = e7 == 7 ? -(mv >> 7) : (mv >> e7);
         tot += vcoef[m] * (double)(2 * mv - (int64_t)omega);
       }
@@ -884,6 +891,7 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
 }  // namespace
 
 int64_t attend_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
+int64_t attend_fused_chunks(int64_t T) { return (T + kFChunk - 1) / kFChunk; }
 
 namespace {
 
@@ -977,15 +985,15 @@ int launch_attend_fused(const CodebookArgs& kcb, const CodebookArgs& vcb, const 
                         int64_t Hq, float scale, uint8_t* qws, float* part, float* out, int32_t* status,
                         hipStream_t s) {
   if (B * Hq == 0) return 0;
-  const int64_t chunks = attend_chunks(T);
+  const int64_t chunks = attend_fused_chunks(T);
   const int64_t groups = B * Hkv;
   const int gq = (int)(Hq / Hkv);
   if (chunks > 0) {
     QprepArgs qa{kcb, q, q_dtype, Hkv, Hq, gq, qws, status};
     switch (kcb.k) {
-      case 1: hipLaunchKernelGGL(attend_qprep_kernel<1>, dim3((unsigned)groups), dim3(kFBlock), 0, s, qa); break;
-      case 2: hipLaunchKernelGGL(attend_qprep_kernel<2>, dim3((unsigned)groups), dim3(kFBlock), 0, s, qa); break;
-      case 3: hipLaunchKernelGGL(attend_qprep_kernel<3>, dim3((unsigned)groups), dim3(kFBlock), 0, s, qa); break;
+      case 1: hipLaunchKernelGGL(attend_qprep_kernel<1>, dim3((unsigned)groups), dim3(kQBlock), 0, s, qa); break;
+      case 2: hipLaunchKernelGGL(attend_qprep_kernel<2>, dim3((unsigned)groups), dim3(kQBlock), 0, s, qa); break;
+      case 3: hipLaunchKernelGGL(attend_qprep_kernel<3>, dim3((unsigned)groups), dim3(kQBlock), 0, s, qa); break;
       default: return -13;
     }
     if (hipGetLastError() != hipSuccess) return -10;

@@ -45,6 +45,8 @@ int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t 
 // Split-token attention output (any power-of-two d in [8, 512], value k <= 8):
 // per-chunk partials in `part` ([B*Hq][attend_chunks(T)][d + 2] floats), then a merge.
 int64_t attend_chunks(int64_t T);
+// Chunks of the fused pass (512 tokens): it writes partials [B*Hq][attend_fused_chunks(T)][d + 2].
+int64_t attend_fused_chunks(int64_t T);
 // Fused attention (d = m = 128, k <= 3 for keys and values): the query side of
 // each (b, kv head) into `qws` (attend_qprep_bytes(B * Hkv) bytes), then scores
 // straight from the key records into the chunk partials, then the merge; `part`
