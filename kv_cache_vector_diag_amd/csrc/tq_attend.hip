@@ -775,14 +775,22 @@ struct MergeArgs {
   float* out;            // [B][Hq][d]
 };
 
-__global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
+// One workgroup per (b, query head) merges that row's chunk partials.  Its
+// 16 waves hold kU chunk rows per thread in flight; the first batch is issued
+// before the pass over the chunk maxima (the rows do not depend on the
+// weights), so at 256 chunks per row and d = 128 every load of the row is in
+// flight at once and the kernel waits about one memory round trip.
+constexpr int kMBlock = 1024;
+
+__global__ __launch_bounds__(kMBlock) void attend_merge_kernel(MergeArgs a) {
   constexpr int kWTile = 2048;             // chunk weights held in LDS at a time
   constexpr int kU = 16;                   // chunk rows in flight per thread
+  constexpr int kMWaves = kMBlock / 64;
   __shared__ float v[kMaxHeadDim];
   __shared__ float wsh[kWTile];
   __shared__ float lsh[kWTile];
-  __shared__ float part[2 * kBlock];       // [row class][d]: rp * d = 2 * kBlock floats
-  __shared__ float red[kBlock / 64];
+  __shared__ float part[2 * kMBlock];      // [row class][d]: rp * d = 2 * kMBlock floats
+  __shared__ float red[kMWaves];
   const int tid = threadIdx.x;
   const int d = a.vcb.d;
   const int64_t bh = blockIdx.x;
@@ -790,9 +798,23 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   const int64_t g = b * a.Hkv + hq * a.Hkv / a.Hq;
   const uint8_t* blob = blob_of(a.vcb, g);
   const float* p = a.part + bh * a.chunks * (d + 2);
+  // thread = (coordinate pair jp, row class cg): rows c = cg, cg + rp, ... of each
+  // tile are summed in order, then the rp classes in order through LDS (threads
+  // past rp classes, where d does not divide 2 kMBlock, take no rows)
+  const int tpr = d / 2, rp = kMBlock / tpr;
+  const int jp = tid % tpr, cg = tid / tpr < rp ? tid / tpr : kWTile;
+  const auto load_rows = [&](float2* pv, int64_t c0, int c, int nc) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int cc = c + rp * u;
+      pv[u] = cc < nc ? *reinterpret_cast<const float2*>(p + (c0 + cc) * (d + 2) + 2 * jp) : float2{0.0f, 0.0f};
+    }
+  };
+  float2 pv[kU];
+  load_rows(pv, 0, cg, (int)(a.chunks < kWTile ? a.chunks : kWTile));
   // chunk maxima (and, for the first tile, the maxima and sums kept in LDS)
   float mx = -INFINITY;
-  for (int64_t c = tid; c < a.chunks; c += kBlock) {
+  for (int64_t c = tid; c < a.chunks; c += kMBlock) {
     const float2 ml = *reinterpret_cast<const float2*>(p + c * (d + 2) + d);
     mx = fmaxf(mx, ml.x);
     if (c < kWTile) {
@@ -803,19 +825,16 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   mx = wave_max_f32(mx);
   if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kMWaves; ++w) mx = fmaxf(mx, red[w]);
   __syncthreads();
-  // thread = (coordinate pair jp, row class cg): rows c = cg, cg + rp, ... of each
-  // tile are summed in order, then the rp classes in order through LDS (threads
-  // past rp classes, where d does not divide 2 kBlock, take no rows)
-  const int tpr = d / 2, rp = kBlock / tpr;
-  const int jp = tid % tpr, cg = tid / tpr < rp ? tid / tpr : kWTile;
   float l = 0.0f;
   float2 aj = {0.0f, 0.0f};
   for (int64_t c0 = 0; c0 < a.chunks; c0 += kWTile) {
     const int nc = (int)(a.chunks - c0 < kWTile ? a.chunks - c0 : kWTile);
     // rescale factor of each chunk, once
-    for (int c = tid; c < nc; c += kBlock) {
+    for (int c = tid; c < nc; c += kMBlock) {
       float m_c, l_c;
       if (c0 == 0) {
         m_c = wsh[c];
@@ -831,12 +850,7 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
     }
     __syncthreads();
     for (int c = cg; c < nc; c += rp * kU) {
-      float2 pv[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int cc = c + rp * u;
-        pv[u] = cc < nc ? *reinterpret_cast<const float2*>(p + (c0 + cc) * (d + 2) + 2 * jp) : float2{0.0f, 0.0f};
-      }
+      if (c0 != 0 || c != cg) load_rows(pv, c0, c, nc);   // the first batch is already in flight
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int cc = c + rp * u;
@@ -854,18 +868,20 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   l = wave_sum_f32(l);
   if ((tid & 63) == 0) red[tid >> 6] = l;
   __syncthreads();
-  for (int j = tid; j < d; j += kBlock) {
+  for (int j = tid; j < d; j += kMBlock) {
     float t = 0.0f;
     for (int q = 0; q < rp; ++q) t += part[q * d + j];
     v[j] = t;
   }
   __syncthreads();
-  l = red[0] + red[1] + red[2] + red[3];
+  l = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kMWaves; ++w) l += red[w];
   const float norm = l > 0.0f ? 1.0f / ((float)d * l) : 0.0f;
   if (a.vcb.rotation == kRotHaar) {
     // x^ = (n/d) R^T c: o_j = sum_i R[i][j] a_i / (d l), R row-major at off_d
     const float* R = reinterpret_cast<const float*>(blob + a.vcb.off_d);
-    for (int j = tid; j < d; j += kBlock) {
+    for (int j = tid; j < d; j += kMBlock) {
       float o = 0.0f;
       for (int i = 0; i < d; ++i) o = fmaf(R[i * d + j], v[i], o);
       a.out[bh * d + j] = o * norm;
@@ -874,7 +890,7 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
   }
   const uint32_t* dbits = reinterpret_cast<const uint32_t*>(blob + a.vcb.off_d);
   for (int h = 1; h < d; h <<= 1) {
-    for (int q = tid; q < d / 2; q += kBlock) {
+    for (int q = tid; q < d / 2; q += kMBlock) {
       int i = (q / h) * 2 * h + (q % h);
       float x0 = v[i], x1 = v[i + h];
       v[i] = x0 + x1;
@@ -882,7 +898,7 @@ __global__ __launch_bounds__(kBlock) void attend_merge_kernel(MergeArgs a) {
     }
     __syncthreads();
   }
-  for (int j = tid; j < d; j += kBlock) {
+  for (int j = tid; j < d; j += kMBlock) {
     const float o = v[j] * norm;
     a.out[bh * d + j] = ((dbits[j >> 5] >> (j & 31)) & 1u) ? -o : o;
   }
@@ -1026,7 +1042,7 @@ int launch_attend_fused(const CodebookArgs& kcb, const CodebookArgs& vcb, const 
     if (rc) return rc;
   }
   MergeArgs ma{vcb, part, Hkv, Hq, chunks, out};
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kBlock), 0, s, ma);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kMBlock), 0, s, ma);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
@@ -1061,7 +1077,7 @@ int launch_attend_split(const CodebookArgs& vcb, const uint32_t* vrec, const flo
     if (hipGetLastError() != hipSuccess) return -10;
   }
   MergeArgs ma{vcb, part, Hkv, Hq, chunks, out};
-  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kBlock), 0, s, ma);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3((unsigned)(B * Hq)), dim3(kMBlock), 0, s, ma);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
