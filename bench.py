@@ -368,21 +368,23 @@ def bench_c4(args, torch, b):
 
     wall, (graph_l,), _ = _run_timed(torch, replay, args.steps, 1)
     gs, es = _stat(graph_l), _stat(eager_l)
-    ms = gs["mean"]
+    # The line is the eager loop: for these three long launches graph replay
+    # measured slower, on the device too (0.122 against 0.116 ms per step)
+    ms = es["mean"]
     fused_bytes = G * T * (kw + vw) * 4 + q.numel() * 2 + out.numel() * 4
     cp = args.copy_gbps
     return {"metric": "long-context decode step tokens/s (scores -> softmax -> V from compressed K, V)",
-            "value": B * T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": wall, "ms_per_step_median": gs["median"],
+            "value": B * T / (ms_eager * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_eager, "ms_per_step_median": es["median"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "long-context step: B=4, 8 kv heads, 8 q heads, 131072 tokens, d=128, "
                                    "turbo2 K + 2-bit V",
-                       "launch": "HIP graph per step (eager launches: ms_per_step_eager)"},
+                       "launch": "eager, one tq_attend call per step (HIP graph replay: ms_per_step_graph)"},
             "copy_GBps": cp, "ms_per_step_device": ms,
-            "ms_per_step_eager": ms_eager, "ms_per_step_eager_device": es["mean"],
-            "ms_per_step_eager_device_median": es["median"],
+            "ms_per_step_graph": wall, "ms_per_step_graph_device": gs["mean"],
+            "ms_per_step_graph_device_median": gs["median"],
             "roofline": _roofline(fused_bytes / (ms * 1e-3) / 1e9, fused_bytes, "attend (step)", "attend_c4", cp,
-                                  ms, gs["median"])}
+                                  ms, es["median"])}
 
 
 def bench_c5(args, torch, b):
@@ -480,9 +482,9 @@ def bench_c5(args, torch, b):
 def bench_paged(args, torch, b):
     """Paged decode step at the 32K-context shape: append one token (key and
     value, every kv head of every sequence) into pages of 256 tokens, then score
-    32 query heads against the 32768 paged keys of each sequence.  The kernel
-    breakdown comes from an eager loop with HIP events; the step time from the
-    same step captured in a HIP graph and replayed."""
+    32 query heads against the 32768 paged keys of each sequence.  The step
+    time and the kernel breakdown come from an eager loop with HIP events; the
+    same step captured in a HIP graph and replayed is reported beside it."""
     from kv_cache_vector_diag_amd import inputs
     dev = "cuda:0"
     B, Hkv, Hq, T, d, kb, vb, m, P, seed = 16, 8, 32, 32768, 128, 3, 3, 128, 256, 3
@@ -526,12 +528,12 @@ def bench_paged(args, torch, b):
 
     for i in range(args.warmup):
         step(i)
-    ms_eager, (ap_l, sc_l), _ = _run_timed(torch, step, args.steps, 2, first=args.warmup)
+    ms_eager, (ap_l, sc_l), eager_whole = _run_timed(torch, step, args.steps, 2, first=args.warmup)
     assert int(status.item()) == 0
     aps, scs = _stat(ap_l), _stat(sc_l)
     ap_ms, sc_ms = aps["mean"], scs["mean"]
-    # the step as a decode loop runs it: captured once per pool in a HIP graph
-    # and replayed, so the launches cost no host time between kernels
+    # the same step captured once per pool in a HIP graph and replayed (for
+    # these launches measured slower than the eager loop, which is the line)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -556,13 +558,14 @@ def bench_paged(args, torch, b):
     sc_bytes = G * T * kw * 4 + B * Hq * T * 4 + q.numel() * 2 + kcb.numel()
     ap_bytes = G * (2 * d * 2 + (kw + vw) * 4)            # vectors in, records written into their page slots
     return {"metric": "paged decode step tokens/s (append one token per sequence + score the paged 32K context)",
-            "value": B * T / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "value": B * T / (ms_eager * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_eager, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "paged cache: 16 seq x 8 kv heads x 32768 tokens in pages of 256, d=128, turbo3 "
                                    "keys + 3-bit values appended, 32 bf16 query heads scored",
-                       "launch": "HIP graph per step (eager launches: ms_per_step_eager)"},
-            "ms_per_step_median": statistics.median(g_l), "ms_per_step_eager": ms_eager, "copy_GBps": args.copy_gbps,
+                       "launch": "eager, an append and a score call per step (HIP graph replay: ms_per_step_graph)"},
+            "ms_per_step_median": statistics.median(eager_whole), "ms_per_step_graph": ms_step,
+            "ms_per_step_graph_median": statistics.median(g_l), "copy_GBps": args.copy_gbps,
             "append_us": ap_ms * 1e3, "append_us_median": aps["median"] * 1e3,
             "append_tokens_per_s": G / (ap_ms * 1e-3), "append_bytes": ap_bytes,
             "score_ms": sc_ms, "score_ms_median": scs["median"],
@@ -695,7 +698,8 @@ def bench_gram(args, torch, b):
     assert int(status.item()) == 0
     scs = _stat(sc_l)
     sc_ms = scs["mean"]
-    # the step captured in a HIP graph per record cache and replayed
+    # the same step captured in a HIP graph per record cache and replayed (for
+    # these launches measured slower than the eager loop, which is the line)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -719,13 +723,15 @@ def bench_gram(args, torch, b):
     assert int(status.item()) == 0
     sc_bytes = G * T * words * 4 + B * Hq * T * 4 + qrec.numel() * 4 + table.numel() * 4
     sc_gbps = sc_bytes / (sc_ms * 1e-3) / 1e9
-    return {"metric": "Gram-table score tokens/s (block-codebook codes, no decode)", "value": B * T / (ms_step * 1e-3),
-            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+    return {"metric": "Gram-table score tokens/s (block-codebook codes, no decode)", "value": B * T / (ms_eager * 1e-3),
+            "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_eager,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": "Gram-table scoring: 16 seq x 8 kv heads x 32768 tokens, d=128, blocks of 4, "
                                    "32 codewords (24-byte records), 32 bf16 query heads encoded per step",
-                       "launch": "HIP graph per step (eager launches: ms_per_step_eager)"},
-            "ms_per_step_median": statistics.median(g_l), "ms_per_step_eager": ms_eager, "copy_GBps": args.copy_gbps,
+                       "launch": "eager, a query encode and a score call per step (HIP graph replay: "
+                                 "ms_per_step_graph)"},
+            "ms_per_step_graph": ms_step, "ms_per_step_graph_median": statistics.median(g_l),
+            "copy_GBps": args.copy_gbps,
             "score_ms": sc_ms, "score_ms_median": scs["median"], "score_GBps": sc_gbps,
             "score_tokens_per_s": B * T / (sc_ms * 1e-3),
             "roofline": _roofline(sc_gbps, sc_bytes, "gram_scores", "score_gram", args.copy_gbps, sc_ms,
