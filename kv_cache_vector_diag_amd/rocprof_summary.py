@@ -9,7 +9,8 @@
 ``traffic`` scales the per-dispatch FETCH_SIZE / WRITE_SIZE readings (KiB) of
 each kernel by the factor that makes the same counter read the known byte
 count of a plain device copy, and records the hash of the kernel sources the
-counters were taken with (a later source change makes the entry stale).
+counters were taken with (a later source change makes the entry stale).  A
+map entry "a+b+c=key" records a step of kernels that each run once per step.
 ``busy`` records the mean VALUBusy and MfmaUtil (percent) of each mapped
 kernel's dispatches in the same file, with their own source hash.
 """
@@ -62,6 +63,8 @@ KERNEL_SOURCES = {
     "decode_values": ["tq_decode.hip", "tq_kernels.h"] + _COMMON,
     "score": ["tq_score128.hip", "tq_score_core.h"] + _COMMON,
     "attend_fused": ["tq_attend.hip", "tq_score_core.h", "tq_kernels.h"] + _COMMON,
+    "attend_qprep": ["tq_attend.hip", "tq_score_core.h", "tq_kernels.h"] + _COMMON,
+    "attend_merge": ["tq_attend.hip", "tq_kernels.h"] + _COMMON,
     "gram_scores": ["tq_gram.hip", "tq_kernels.h"] + _COMMON,
 }
 
@@ -85,10 +88,15 @@ def short_name(kernel_name: str) -> str:
 
 
 def kernel_sources_sha(root: str, kernel: str) -> str:
-    """Hash of the sources of one measured kernel (short name, e.g. encode_keys)."""
+    """Hash of the sources of one measured kernel (short name, e.g. encode_keys),
+    or of a step of several ("attend_qprep+attend_fused+attend_merge": the union
+    of their sources, each file once)."""
     h = hashlib.sha256()
     csrc = os.path.join(root, "kv_cache_vector_diag_amd", "csrc")
-    for name in KERNEL_SOURCES[kernel]:
+    names = []
+    for part in kernel.split("+"):
+        names += [n for n in KERNEL_SOURCES[part] if n not in names]
+    for name in names:
         h.update(open(os.path.normpath(os.path.join(csrc, name)), "rb").read())
     return h.hexdigest()[:16]
 
@@ -127,10 +135,14 @@ def cmd_traffic(a) -> None:
     out = json.load(open(a.out)) if os.path.exists(a.out) else {}
     for kern, key in (k.split("=") for k in a.map):
         sha = kernel_sources_sha(a.root, kern)
-        fv = fetch[kern]["FETCH_SIZE"]
-        wv = write[kern]["WRITE_SIZE"]
-        rd = sum(fv) / len(fv) * 1024.0 * f_factor
-        wr = sum(wv) / len(wv) * 1024.0 * w_factor
+        # a step of several kernels ("a+b"): each runs once per step, so the
+        # step's bytes are the sum of the kernels' per-dispatch means
+        rd = wr = 0.0
+        for part in kern.split("+"):
+            fv = fetch[part]["FETCH_SIZE"]
+            wv = write[part]["WRITE_SIZE"]
+            rd += sum(fv) / len(fv) * 1024.0 * f_factor
+            wr += sum(wv) / len(wv) * 1024.0 * w_factor
         out[key] = {"kernel": kern, "hbm_bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
                     "fetch_factor": f_factor, "write_factor": w_factor, "source_sha": sha}
         print(f"{key}: read {rd / 1e6:.1f} MB  write {wr / 1e6:.1f} MB  (factors {f_factor:.3f}, {w_factor:.3f})")

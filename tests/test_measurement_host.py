@@ -90,3 +90,30 @@ def test_kernel_source_sets_exist():
         for f in files:
             assert os.path.exists(os.path.normpath(os.path.join(ROOT, "kv_cache_vector_diag_amd", "csrc", f))), f
         assert len(rs.kernel_sources_sha(ROOT, kern)) == 16
+
+
+def test_traffic_of_a_step_of_kernels(tmp_path, monkeypatch):
+    """A map entry a+b+c=key sums the kernels' per-dispatch means (one launch
+    of each per step) and hashes the union of their sources."""
+    qp = "void tq::(anonymous namespace)::attend_qprep_kernel<1>(x)"
+    fu = "void tq::(anonymous namespace)::attend_fused_kernel<1, 2>(x)"
+    mg = "tq::(anonymous namespace)::attend_merge_kernel(x)"
+    cp = "__amd_rocclr_copyBuffer"
+    _counter_csv(tmp_path / "f.csv", [(qp, "FETCH_SIZE", 10.0), (fu, "FETCH_SIZE", 1000.0), (fu, "FETCH_SIZE", 1004.0),
+                                      (mg, "FETCH_SIZE", 40.0)])
+    _counter_csv(tmp_path / "w.csv", [(qp, "WRITE_SIZE", 5.0), (fu, "WRITE_SIZE", 60.0), (mg, "WRITE_SIZE", 1.0)])
+    _counter_csv(tmp_path / "cf.csv", [(cp, "FETCH_SIZE", 524288.0)])
+    _counter_csv(tmp_path / "cw.csv", [(cp, "WRITE_SIZE", 1048576.0)])
+    out = tmp_path / "traffic.json"
+    step = "attend_qprep+attend_fused+attend_merge"
+    rs.main(["traffic", "--fetch", str(tmp_path / "f.csv"), "--write", str(tmp_path / "w.csv"),
+             "--copy-fetch", str(tmp_path / "cf.csv"), "--copy-write", str(tmp_path / "cw.csv"),
+             "--map", f"{step}=attend_c4", "--out", str(out)])
+    ent = json.load(open(out))["attend_c4"]
+    assert ent["read_bytes"] == pytest.approx((10.0 + 1002.0 + 40.0) * 1024 * 2)
+    assert ent["write_bytes"] == pytest.approx((5.0 + 60.0 + 1.0) * 1024)
+    assert ent["source_sha"] == rs.kernel_sources_sha(ROOT, step)
+    assert rs.kernel_sources_sha(ROOT, step) != rs.kernel_sources_sha(ROOT, "attend_merge")
+    import bench
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    assert bench._traffic("attend_c4", 0.0) == pytest.approx(ent["hbm_bytes_per_launch"])
