@@ -496,6 +496,8 @@ int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t 
                           const void* q, int q_dtype, int64_t Hq, float scale, float* scores,
                           int32_t* status, hipStream_t s, int64_t q_row, const ChannelMap& cm, bool accumulate) {
   if (B * Hq * T == 0) return 0;
+  if (lut_scores_supported(cb, T))
+    return launch_scores_lut(cb, krec, B, Hkv, T, q, q_dtype, Hq, scale, scores, status, s, q_row, cm, accumulate);
   ScoreArgs a{cb, krec, B, Hkv, T, q, q_dtype, Hq, scale, scores, status, q_row > 0 ? q_row : cb.d, cm,
               accumulate ? 1 : 0};
   const int64_t chunks = (T + kScoreBlock - 1) / kScoreBlock;

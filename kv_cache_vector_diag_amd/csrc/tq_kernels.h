@@ -42,6 +42,13 @@ int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t 
                           const void* q, int q_dtype, int64_t Hq, float scale, float* scores,
                           int32_t* status, hipStream_t s, int64_t q_row = 0,
                           const ChannelMap& cm = ChannelMap{}, bool accumulate = false);
+// Scores through byte tables in LDS (tq_score_lut.hip): keys with k <= 3 index
+// planes, any head_dim (Walsh-Hadamard: a power of two); launch_scores_generic
+// takes this route whenever it is supported.
+bool lut_scores_supported(const CodebookArgs& cb, int64_t T);
+int launch_scores_lut(const CodebookArgs& cb, const uint32_t* krec, int64_t B, int64_t Hkv, int64_t T,
+                      const void* q, int q_dtype, int64_t Hq, float scale, float* scores, int32_t* status,
+                      hipStream_t s, int64_t q_row, const ChannelMap& cm, bool accumulate);
 // Split-token attention output (any power-of-two d in [8, 512], value k <= 8):
 // per-chunk partials in `part` ([B*Hq][attend_chunks(T)][d + 2] floats), then a merge.
 int64_t attend_chunks(int64_t T);
