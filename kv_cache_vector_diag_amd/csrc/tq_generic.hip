@@ -479,6 +479,8 @@ int launch_encode_generic(const CodebookArgs& cb, const void* x, int dtype, int6
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
                           int32_t* status, hipStream_t s, int64_t out_stride, const ChannelMap& cm) {
   if (G * N == 0) return 0;
+  if (haar_decode_mfma_supported(cb, cm.map != nullptr))
+    return launch_decode_haar_mfma(cb, rec, G, N, out, status, s, out_stride, cm);
   DecodeArgs a{cb, rec, G, N, out, status, out_stride > 0 ? out_stride : cb.d, cm};
   hipLaunchKernelGGL(decode_generic_kernel, dim3(grid_for(G * N, 1 << 16)), dim3(64), 0, s, a);
   return hipGetLastError() == hipSuccess ? 0 : -10;

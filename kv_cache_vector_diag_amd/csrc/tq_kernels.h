@@ -36,6 +36,12 @@ int launch_haar256(const CodebookArgs& cb, const void* x, int64_t G, int64_t N, 
 int launch_decode_generic(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
                           int32_t* status, hipStream_t s, int64_t out_stride = 0,
                           const ChannelMap& cm = ChannelMap{});
+// Value decode on the matrix cores (tq_decode_haar.hip): Haar codebooks, and
+// Walsh-Hadamard ones under a channel map; d <= 256, any value bits.
+// launch_decode_generic takes this route whenever it is supported.
+bool haar_decode_mfma_supported(const CodebookArgs& cb, bool mapped);
+int launch_decode_haar_mfma(const CodebookArgs& cb, const uint32_t* rec, int64_t G, int64_t N, float* out,
+                            int32_t* status, hipStream_t s, int64_t out_stride, const ChannelMap& cm);
 int launch_rotate_generic(const CodebookArgs& cb, const void* x, int dtype, int64_t G, int64_t N,
                           int64_t sx_g, int64_t sx_n, float* u, float* norms, hipStream_t s);
 int launch_scores_generic(const CodebookArgs& cb, const uint32_t* krec, int64_t B, int64_t Hkv, int64_t T,

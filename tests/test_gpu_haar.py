@@ -149,3 +149,23 @@ def test_haar_fused_attend_d128(gpu_lib, kb, vb, B, Hkv, Hq, T):
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert_close(o.cpu().numpy(), tq.attend(kq, rec_np(krec), vq, rec_np(vrec), inputs.exact_values(q)), "attend")
+
+
+@pytest.mark.parametrize("d,vb,N", [(256, 8, 300), (224, 6, 130), (128, 8, 129), (33, 7, 64), (9, 5, 200)])
+def test_haar_decode_wide_codebooks(gpu_lib, d, vb, N):
+    """Decode of Haar values with 5-8-bit codebooks (up to 256 centroids) on the
+    matrix-core route, head dims across its K-chunk counts (2, 4, 8, 16), groups
+    that end mid-tile, two codebooks: decoded vectors against the oracle's."""
+    import torch
+    b = gpu_lib
+    seed, G = 41, 2
+    V = inputs.to_torch(inputs.kv_normal(seed, G, N, d, inputs.STREAM_V), "bf16", DEV)
+    vcb, vq = _haar(b, G, d, vb, 0, seed, tq.ROLE_VALUE)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    vrec = b.tq_encode_values(vcb, G, V, d, vb, status=st, rotation=b.ROT_HAAR)
+    dec = b.tq_decode_values(vcb, G, vrec, d, vb, status=st, rotation=b.ROT_HAAR)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    vr = rec_np(vrec)
+    for g in range(G):
+        assert_close(dec[g].cpu().numpy(), tq.decode_values(vq[g], vr[g]), f"decode d={d} bits={vb} g={g}")
