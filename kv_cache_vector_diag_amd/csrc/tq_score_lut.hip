@@ -22,8 +22,8 @@
 //   * the chunk's records go to LDS once (consecutive threads, consecutive
 //     words), rows padded to an odd word count;
 //   * the query side of up to 4 query heads of the kv head at once, so that R
-//     and S are read once per batch: qt (Walsh-Hadamard in LDS, or a row of R
-//     per thread), p (a row of S per thread), their sums;
+//     and S are read once per batch: qt (Walsh-Hadamard in LDS, or R q on the
+//     matrix cores), p (S qt on the matrix cores), their sums;
 //   * per head: the two byte tables, then one token per thread.
 #include <hip/hip_runtime.h>
 
@@ -31,9 +31,12 @@
 
 #include "tq_device.h"
 #include "tq_kernels.h"
+#include "tq_mfma.h"
 
 namespace tq {
 namespace {
+
+using namespace mf;
 
 constexpr int kLBlock = 512;             // 8 waves
 constexpr int kHB = 4;                   // query heads whose query side is built together
@@ -74,6 +77,25 @@ __host__ __device__ inline LutLds lut_lds(int tch, int rwp, int W, int Ws, int d
   o.qraw = o.pp + (size_t)kHB * 32 * Ws * 4;
   o.total = o.qraw + (size_t)kHB * d * 4;
   return o;
+}
+
+// Three bfloat16 terms of 8 float32 values (t0 + t1 + t2 = x exactly: each
+// term takes the top 8 significant bits of what remains), packed two per word.
+__device__ inline void split3_bf16(const float (&x)[8], u32x4 (&t)[3]) {
+  uint32_t w[3][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float r0 = x[2 * q], r1 = x[2 * q + 1];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const uint32_t h0 = __float_as_uint(r0) & 0xFFFF0000u, h1 = __float_as_uint(r1) & 0xFFFF0000u;
+      w[p][q] = (h0 >> 16) | h1;
+      r0 -= __uint_as_float(h0);
+      r1 -= __uint_as_float(h1);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) t[p] = u32x4{w[p][0], w[p][1], w[p][2], w[p][3]};
 }
 
 // sum of the four byte-table entries of a 32-bit mask word at byte positions 4w..4w+3
@@ -141,104 +163,80 @@ __global__ __launch_bounds__(kLBlock) void scores_lut_kernel(LutArgs a) {
   const float* R = reinterpret_cast<const float*>(blob + a.cb.off_d);
   const _Float16* S = reinterpret_cast<const _Float16*>(blob + a.cb.off_s);
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
-  // vout[hh][r] = sum_i M[r][i] vin[hh][i] for rows r < nrows of a row-major
-  // [nrows][d] matrix, zero for nrows <= r < ostride.  Row tiles (an even
-  // number of rows) go through the byte-table area (free until the tables are
-  // built): 16-byte buffer loads by consecutive threads, all in flight at once,
-  // widened into rows of odd stride; two adjacent lanes share a (row, head),
-  // each summing half of the row.  F16: the matrix is binary16, else float32; `scale`
-  // multiplies every entry.  Starts and ends with a barrier.
-  const int tstride = (d + 1) | 1;
-  const int trows_max = ((int)((4 * (W + Ws) * 1024) / (4 * tstride))) & ~1;
-  float* tile = lq;
+  // vout[hh][r] = scale sum_i M[r][i] vin[hh][i] for the rows r < nrows of a
+  // row-major [nrows][d] matrix M (binary16 or float32), zero for nrows <= r <
+  // ostride (a multiple of 32), on v_mfma_f32_32x32x16_bf16: rows are the M
+  // side (32 per tile, a tile per wave), the heads of the batch the N side.
+  // Both operands are split into three bfloat16 terms (24 significant bits
+  // and the float32 exponent range; binary16 entries need two), and the
+  // products of terms down to about 2^-20 of the sum are kept.  Row pieces of
+  // 8 entries are 16-byte buffer loads when d is a multiple of 8 (then no
+  // piece crosses a row or the end), else single entries.  Ends with a barrier.
   int nh = 0;
-  const auto tile_matvec = [&](auto f16_tag, const void* mat, int nrows, float scale, const float* vin, int istride,
+  const auto mfma_matvec = [&](auto f16_tag, const void* mat, int nrows, float scale, const float* vin, int istride,
                                float* vout, int ostride) {
     constexpr bool F16 = decltype(f16_tag)::value;
-    constexpr int EPL = F16 ? 8 : 4;                  // entries per 16-byte load
+    constexpr int NT = F16 ? 2 : 3;                   // bfloat16 terms of a matrix entry
     const __amdgpu_buffer_rsrc_t ms = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(mat), 0, (int)((int64_t)nrows * d * (F16 ? 2 : 4)), kRsrcWord3);
-    constexpr int kPL = 8;                            // 16-byte pieces per thread and tile
-    // the matrix is read in whole 16-byte pieces only when its size is a
-    // multiple of 16 bytes (so that no piece straddles its end), else entry by entry
-    const bool wide = ((int64_t)nrows * d * (F16 ? 2 : 4)) % 16 == 0;
-    const int lim = kLBlock / (2 * nh) & ~1, cap = (kPL * kLBlock * EPL / d) & ~1;
-    int trows = trows_max < lim ? trows_max : lim;
-    if (trows > cap) trows = cap;
-    for (int r0 = 0; r0 < ostride; r0 += trows) {
-      const int nr = nrows - r0 < trows ? (nrows - r0 > 0 ? nrows - r0 : 0) : trows;
-      const int nq = (nr * d + EPL - 1) / EPL;        // 16-byte pieces of the tile
-      __syncthreads();                                // the previous tile is read
-      if (!wide) {
-        for (int e0 = tid; e0 < nr * d; e0 += kU * kLBlock) {
-          float x[kU];
+    const bool pieces = (d & 7) == 0;
+    const int nkc = (d + 15) / 16, hcol = lane & 31, hk = lane >> 5;
+    for (int M = wave; M < ostride / 32; M += kLBlock / 64) {
+      const int row = 32 * M + hcol;
+      f32x16 acc = {};
+#pragma unroll 8
+      for (int c = 0; c < nkc; ++c) {
+        const int k0 = 16 * c + 8 * hk;
+        float av[8], bv[8];
+        const bool rok = row < nrows && k0 < d;
+        if (pieces) {
+          const uint32_t off = rok ? (uint32_t)(((int64_t)row * d + k0) * (F16 ? 2 : 4)) : 0xC0000000u;
+          if constexpr (F16) {
+            const uint4 w = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ms, off, 0, 0));
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int e = e0 + u * kLBlock;
-            const uint32_t off = e < nr * d ? (uint32_t)(((int64_t)r0 * d + e) * (F16 ? 2 : 4)) : 0xC0000000u;
+            for (int e = 0; e < 8; ++e)
+              av[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)((ww[e >> 1] >> (16 * (e & 1))) & 0xFFFFu));
+          } else {
+            const uint4 w0 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ms, off, 0, 0));
+            const uint4 w1 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ms, off + 16u, 0, 0));
+            const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = __uint_as_float(ww[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const bool ok = row < nrows && k0 + e < d;
+            const uint32_t off = ok ? (uint32_t)(((int64_t)row * d + k0 + e) * (F16 ? 2 : 4)) : 0xC0000000u;
             if constexpr (F16)
-              x[u] = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(ms, off, 0, 0));
+              av[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(ms, off, 0, 0));
             else
-              x[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ms, off, 0, 0));
-          }
-#pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int e = e0 + u * kLBlock;
-            if (e < nr * d) {
-              const int r = e / d, i = e - r * d;
-              tile[r * tstride + i] = x[u] * scale;
-            }
+              av[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ms, off, 0, 0));
           }
         }
-      }
-      uint4 v[kPL];
 #pragma unroll
-      for (int u = 0; u < kPL; ++u) {
-        const int qq = tid + u * kLBlock;
-        v[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-            ms, wide && qq < nq ? (uint32_t)(((int64_t)r0 * d + (int64_t)qq * EPL) * (F16 ? 2 : 4)) : 0xC0000000u, 0, 0));
-      }
-#pragma unroll
-      for (int u = 0; u < kPL; ++u) {
-        const int qq = tid + u * kLBlock;
-        if (wide && qq < nq) {
-          const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-          int r = (qq * EPL) / d, i = qq * EPL - r * d;   // stepped along the piece
-#pragma unroll
-          for (int c = 0; c < EPL; ++c, ++i) {
-            if (i == d) {
-              i = 0;
-              ++r;
-            }
-            if (r < nr) {
-              float x;
-              if constexpr (F16) {
-                const uint32_t hw = (w4[c >> 1] >> (16 * (c & 1))) & 0xFFFFu;
-                x = (float)__builtin_bit_cast(_Float16, (uint16_t)hw);
-              } else {
-                x = __uint_as_float(w4[c]);
-              }
-              tile[r * tstride + i] = x * scale;
-            }
-          }
+        for (int e = 0; e < 8; ++e) {
+          if (k0 + e >= d) av[e] = 0.0f;
+          bv[e] = hcol < nh && k0 + e < d ? vin[hcol * istride + k0 + e] : 0.0f;
         }
+        u32x4 at[3], bt[3];
+        split3_bf16(av, at);
+        split3_bf16(bv, bt);
+        // term pairs (i, j) with i + j <= 2
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(at[0]), as<bf16x8>(bt[0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(at[0]), as<bf16x8>(bt[1]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(at[1]), as<bf16x8>(bt[0]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(at[0]), as<bf16x8>(bt[2]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(at[1]), as<bf16x8>(bt[1]), acc, 0, 0, 0);
+        if constexpr (NT == 3)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(at[2]), as<bf16x8>(bt[0]), acc, 0, 0, 0);
       }
-      __syncthreads();
-      // two adjacent lanes per (row, head), each summing half of the row
-      const int span = ostride - r0 < trows ? ostride - r0 : trows;
-      const int pair = tid >> 1, half = tid & 1;
-      float acc = 0.0f;
-      const bool act = pair < span * nh;
-      const int r = act ? pair % span : 0, hh = act ? pair / span : 0;
-      if (act && r < nr) {
-        const float* tr = tile + r * tstride;
-        const float* vv = vin + hh * istride;
-        const int i0 = half ? d / 2 : 0, i1 = half ? d : d / 2;
-#pragma unroll 4
-        for (int i = i0; i < i1; ++i) acc = fmaf(tr[i], vv[i], acc);
+      // register k of lane half hk holds row 32M + 8(k >> 2) + 4hk + (k & 3), column (head) hcol
+      if (hcol < nh) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) vout[hcol * ostride + 32 * M + 8 * (k >> 2) + 4 * hk + (k & 3)] = acc[k] * scale;
       }
-      acc += __shfl_xor(acc, 1, 64);
-      if (act && half == 0) vout[hh * ostride + r0 + r] = acc;
     }
     __syncthreads();
   };
@@ -256,7 +254,7 @@ __global__ __launch_bounds__(kLBlock) void scores_lut_kernel(LutArgs a) {
     __syncthreads();
     if (haar) {
       // qt = R q, R streamed through LDS in row tiles (zero past d)
-      tile_matvec(std::false_type{}, R, d, 1.0f, qraw, d, qt, dq);
+      mfma_matvec(std::false_type{}, R, d, 1.0f, qraw, d, qt, dq);
     } else {
       // qt = H (D q): butterflies in LDS (d a power of two), zero past d
       for (int e = tid; e < nh * dq; e += kLBlock) {
@@ -278,7 +276,7 @@ __global__ __launch_bounds__(kLBlock) void scores_lut_kernel(LutArgs a) {
     }
     __syncthreads();
     // p = S qt / sqrt(d), S streamed through LDS in row tiles (zero past m)
-    tile_matvec(std::true_type{}, S, m, inv_sqrt_d, qt, dq, pp, mq);
+    mfma_matvec(std::true_type{}, S, m, inv_sqrt_d, qt, dq, pp, mq);
     __syncthreads();
     if (wave < nh) {
       float s1 = 0.0f, s2 = 0.0f;
