@@ -169,3 +169,26 @@ def test_haar_decode_wide_codebooks(gpu_lib, d, vb, N):
     vr = rec_np(vrec)
     for g in range(G):
         assert_close(dec[g].cpu().numpy(), tq.decode_values(vq[g], vr[g]), f"decode d={d} bits={vb} g={g}")
+
+
+@pytest.mark.parametrize("d,m,kb,Hkv,Hq,T", [(96, 96, 2, 2, 6, 700), (96, 40, 3, 1, 8, 513), (160, 160, 4, 1, 12, 300),
+                                             (48, 64, 3, 2, 10, 1100)])
+def test_haar_scores_head_batches(gpu_lib, d, m, kb, Hkv, Hq, T):
+    """Scores at head dims off the MFMA score kernel with 3 to 12 query heads per
+    kv head: the table-driven kernel prepares the query side four heads at a
+    time, so these cover partial and several batches, chunks of 512 tokens
+    and a ragged last chunk; scores of the GPU's records against the oracle."""
+    import torch
+    b = gpu_lib
+    seed, B = 77, 1
+    G = B * Hkv
+    K = inputs.to_torch(inputs.kv_normal(seed, G, T, d, inputs.STREAM_K), "bf16", DEV)
+    q = inputs.to_torch(inputs.queries(seed, B, Hq, d), "bf16", DEV)
+    kcb, kq = _haar(b, Hkv, d, kb, m, seed, tq.ROLE_KEY)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    krec = b.tq_encode_keys(kcb, Hkv, K, d, kb, m, status=st, rotation=b.ROT_HAAR)
+    krec4 = krec.view(B, Hkv, T, -1)
+    s = b.tq_scores(kcb, Hkv, krec4, q, d, kb, m, status=st, rotation=b.ROT_HAAR)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert_close(s.cpu().numpy(), tq.scores(kq, rec_np(krec4), inputs.exact_values(q)), f"scores d={d} Hq={Hq}")
