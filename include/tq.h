@@ -235,10 +235,13 @@ int tq_attend_static(int head_dim, int k_bits, int v_bits, int projections, int 
  * that are multiples of 8 stream R through the matrix cores in 16-column
  * chunks (keys of up to 4 bits with up to 256 projections, values of up to 4
  * bits).  At head_dim 128 the scores and the fused attention (128
- * projections) rotate the query by R; other Haar encodes and scores run on the
- * float64 per-vector kernels.  The attention's value partials run on the same
- * MFMA kernels as for Walsh-Hadamard codebooks when head_dim is a multiple of
- * 32. */
+ * projections) rotate the query by R; scores at other head dims of keys with
+ * up to 4 bits run a table-driven kernel (byte tables of the rotated query and
+ * its projection in LDS, R q and S q on the matrix cores); value decodes at
+ * head dims up to 256 run x^ = U R on the matrix cores (both in two-term
+ * binary16); other Haar encodes, scores and decodes run on the float64
+ * per-vector kernels.  The attention's value partials run on the same MFMA
+ * kernels as for Walsh-Hadamard codebooks when head_dim is a multiple of 32. */
 int tq_encode_keys_ex(int head_dim, int bits, int projections, int rotation,
                       const void* cbs, int64_t n_cb,
                       const void* x, int x_dtype, int64_t G, int64_t N,
@@ -392,7 +395,9 @@ int tq_encode_split(int role, int head_dim, int n_outlier, int bits,
 /* Scores from split key records: scores[b][hq][t] = scale * (estimate of the
  * normal part + estimate of the outlier part), each part scored from its records
  * against the query channels the map selects; scale <= 0 means 1/sqrt(head_dim).
- * chan has one row per (b, kv head) group, b*H_kv + h. */
+ * chan has one row per (b, kv head) group, b*H_kv + h.  Parts of keys with up to
+ * 4 bits run the table-driven score kernel (the outlier part adding into the
+ * normal part's scores), larger codebooks the per-token kernel. */
 int tq_scores_split(int head_dim, int n_outlier, int bits,
                     const void* cbs_normal, const void* cbs_outlier, int64_t n_cb, const int32_t* chan,
                     const void* krec_normal, const void* krec_outlier, int64_t B, int64_t H_kv, int64_t T,
@@ -400,7 +405,9 @@ int tq_scores_split(int head_dim, int n_outlier, int bits,
                     void* stream);
 
 /* Decode split value records to out [G][N][head_dim] float32 (both parts
- * decoded and scattered back to their channels). */
+ * decoded and scattered back to their channels; parts of up to 256 channels run
+ * x^ = U M on the matrix cores, M = R or the +-1 (D H)^T, written through the
+ * channel map). */
 int tq_decode_values_split(int head_dim, int n_outlier, int bits,
                            const void* cbs_normal, const void* cbs_outlier, int64_t n_cb, const int32_t* chan,
                            const void* rec_normal, const void* rec_outlier, int64_t G, int64_t N,
