@@ -10,8 +10,8 @@
 //      normal rotation R' = R P_n (224 x 256, R = sqrt(224) Q of the Haar
 //        codebook, P_n selects the normal channels), split exactly into three
 //        bf16 pieces (24 significant bits);
-//      outlier rotation H_32 D_o P_o (32 x 256, exact +-1/0) and the outlier
-//        gather P_o (0/1);
+//      the outlier gather P_o (0/1) and the outlier rotation H_32 D_o (32 x 32,
+//        exact +-1) applied to the gathered channels after the contraction;
 //      keys: the QJL matrices S_n (224 x 224) and S_o (32 x 32), binary16, their
 //        columns permuted to the rotation-result layout.
 //  * One workgroup (8 waves) encodes 256 tokens per step, one 32-token tile per
@@ -49,16 +49,16 @@ constexpr int kFragLanes = 64;       // one fragment: 64 lanes x 16 bytes
 constexpr int kRPieces = 3;
 constexpr int kSliceR = kMT * kRPieces;           // rotation fragments of one K-chunk (21)
 constexpr int kOffR = 0;                          // [c][m][piece]
-constexpr int kOffOR = kOffR + kKC * kSliceR;     // outlier rotation [c]
-constexpr int kOffOP = kOffOR + kKC;              // outlier gather [c]
-constexpr int kOffSO = kOffOP + kKC;              // outlier QJL [c < 2]
+constexpr int kOffOP = kOffR + kKC * kSliceR;     // outlier gather [c]
+constexpr int kOffHO = kOffOP + kKC;              // outlier rotation H_32 D_o of the gathered channels [c < 2]
+constexpr int kOffSO = kOffHO + 2;                // outlier QJL [c < 2]
 constexpr int kOffS = kOffSO + 2;                 // normal QJL [m'][c < 14]
-constexpr int kFragsValue = kOffSO;               // 368
-constexpr int kFragsKey = kOffS + kMT * kQC;      // 468
+constexpr int kFragsValue = kOffSO;               // 354
+constexpr int kFragsKey = kOffS + kMT * kQC;      // 454
 constexpr int kSliceS = kQC;                      // fragments per projection slice (14)
-constexpr int kOutFrags = 2 * kKC + 2;            // outlier fragments kept in LDS (34)
+constexpr int kOutFrags = kKC + 4;                // outlier fragments kept in LDS (20)
 
-constexpr size_t kLdsOut = (size_t)kOutFrags * kFragLanes * 16;     // 34 KB
+constexpr size_t kLdsOut = (size_t)kOutFrags * kFragLanes * 16;     // 20 KB
 constexpr size_t kLdsBytes = kLdsOut + 256;   // the two slice buffers are static arrays
 
 struct PrepArgs {
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void split256_prep_kernel(PrepArgs a) {
     for (int hh = 0; hh < 2; ++hh) {
       const int e = 2 * q + hh;
       uint32_t b16 = 0;
-      if (f < kOffOR) {                       // R' piece (c, m, piece): r = p1 + p2 + p3 in bf16
+      if (f < kOffOP) {                       // R' piece (c, m, piece): r = p1 + p2 + p3 in bf16
         const int c = f / kSliceR, m = (f % kSliceR) / kRPieces, piece = f % kRPieces;
         const int p = inv[16 * c + 8 * hl + e];
         if (p >= kNo) {
@@ -124,11 +124,11 @@ __global__ __launch_bounds__(256) void split256_prep_kernel(PrepArgs a) {
           }
           b16 = pb;
         }
-      } else if (f < kOffOP) {                // H_32 D_o P_o
-        const int p = inv[16 * (f - kOffOR) + 8 * hl + e];
-        if (p >= 0 && p < kNo) b16 = 0x3F80u | ((h_sign(row, p) ^ ((dbits_o >> p) & 1u)) << 15);
-      } else if (f < kOffSO) {                // P_o: result row r = channel chan[r]
+      } else if (f < kOffHO) {                // P_o: result row r = channel chan[r]
         if (inv[16 * (f - kOffOP) + 8 * hl + e] == row) b16 = 0x3F80u;
+      } else if (f < kOffSO) {                // H_32 D_o, columns in the gather's result order
+        const int p = qjl_coord(f - kOffHO, hl, e);
+        b16 = 0x3F80u | ((h_sign(row, p) ^ ((dbits_o >> p) & 1u)) << 15);
       } else if (f < kOffS) {                 // S_o, columns in result order
         b16 = So[row * kNo + qjl_coord(f - kOffSO, hl, e)];
       } else {                                // S_n, columns in result order
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       if (bad) atomicOr(a.status, TQ_STATUS_BAD_BLOB);
     }
     const u32x4* fr = a.frag + (int64_t)g * a.frags * kFragLanes;
-    for (int i = tid; i < (KEY ? kOutFrags : 2 * kKC) * kFragLanes; i += kThreads) ofr[i] = fr[kOffOR * kFragLanes + i];
+    for (int i = tid; i < (KEY ? kOutFrags : kKC + 2) * kFragLanes; i += kThreads) ofr[i] = fr[kOffOP * kFragLanes + i];
     if (tid < LN / 2) consts[tid] = reinterpret_cast<const float*>(bn + a.off_cn)[LN / 2 + tid];
     if (tid < NTN) consts[8 + tid] = reinterpret_cast<const float*>(bn + a.off_tn)[LN / 2 + tid];
     if (tid < LO / 2) consts[16 + tid] = reinterpret_cast<const float*>(bo + a.off_co)[LO / 2 + tid];
@@ -361,11 +361,11 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
       __syncthreads();                                     // slice buffers free
       dma(slice_a, kOffR * kFragLanes, kSliceEntries);
 
-      // ---- rotation, chunk-outer: u[m] (normal tiles), uo (outlier), xo (outlier gather)
+      // ---- rotation, chunk-outer: u[m] (normal tiles), xo (outlier gather)
       f32x16 u[kMT];
 #pragma unroll
       for (int m = 0; m < kMT; ++m) u[m] = f32x16{};
-      f32x16 uo = {}, xo = {};
+      f32x16 xo = {};
 #pragma unroll
       for (int c = 0; c < kKC; ++c) {
         // this wave's slice DMA has landed: it was issued before the one x chunk
@@ -400,8 +400,20 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
                                                            u[m], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);               // a few fragments live at a time
         }
-        uo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[c * kFragLanes + lane]), xv, uo, 0, 0, 0);
-        xo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[(kKC + c) * kFragLanes + lane]), xv, xo, 0, 0, 0);
+        xo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[c * kFragLanes + lane]), xv, xo, 0, 0, 0);
+      }
+      // ---- outlier rotation uo = H_32 D_o x_o from the gathered channels (exact
+      // bf16 values): lane half h holds channel 16h + r of the map in register r,
+      // K-chunk c' takes registers 8c' .. 8c' + 7 (the fragments' column order)
+      f32x16 uo = {};
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        u32x4 bx;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          bx[q] = (__float_as_uint(xo[8 * cc + 2 * q]) >> 16) | (__float_as_uint(xo[8 * cc + 2 * q + 1]) & 0xFFFF0000u);
+        uo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as<bf16x8>(ofr[(kKC + cc) * kFragLanes + lane]), as<bf16x8>(bx),
+                                                     uo, 0, 0, 0);
       }
 
       // ---- norms (float64): |x|^2 from pair sums, |x_o|^2 from the exact gather
@@ -446,7 +458,7 @@ __global__ __launch_bounds__(kThreads) void split256_kernel(SplitArgs a) {
         f32x16 acc = {};
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const u32x4 sf = ofr[(2 * kKC + c) * kFragLanes + lane];
+          const u32x4 sf = ofr[(kKC + 2 + c) * kFragLanes + lane];
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(who[c]), acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as<f16x8>(sf), as<f16x8>(wlo_o[c]), acc, 0, 0, 0);
         }
