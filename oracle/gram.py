@@ -17,7 +17,7 @@ What it follows (page: "fib-quant 0.1.0-beta.4 README"):
     (4 KB at N = 32) estimates the inner product of a query with a stored
     code without decoding it (no inverse rotation, no norm scaling).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   G1  the codebook (N codewords of dimension k) is an input.  The pages build
       it by spherical-Beta seeding and Lloyd refinement, which they leave
       underspecified; the scorer works for any codebook.

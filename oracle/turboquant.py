@@ -20,7 +20,7 @@ projections, seed); ``attention_scores`` returns, per stored key, the inner
 product estimate times 1/sqrt(head_dim), before softmax; ``decode_values``;
 ``MultiHeadKvCache::new`` gives head h the seed ``seed + h`` (wrapping).
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   R1  rotation Pi = H D / sqrt(d), D applied first, Sylvester order; z =
       H(D x)/|x| so that z ~ N(0, 1) per coordinate.
   R2  quantizer index idx_j = #{i : t_i < z_j} (ties go to the lower cell),

@@ -1,6 +1,6 @@
 """Comparison helpers for GPU-vs-oracle parity (used by the gpu tests).
 
-Tolerances (the benchmark spec): codes and signs bit-exact except coordinates within
+Tolerances: codes and signs bit-exact except coordinates within
 1e-6 of a decision boundary (z within 1e-6 of a threshold; |(S rho)_i| within
 1e-6 gamma of 0); the number of such mismatches must stay below 1e-5 of all
 coordinates -- a rate, so it is checked over all the coordinates a test encodes

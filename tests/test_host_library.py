@@ -112,9 +112,9 @@ def test_split_host_validation():
     assert lib.tq_outlier_channels(256, 256, None, 1, 1, 1, 256, 256, None, None, 0, None) == -5
     assert lib.tq_outlier_channels(600, 8, None, 1, 1, 1, 600, 600, None, None, 0, None) == -2
     assert lib.tq_outlier_workspace_bytes(256, 256, 16384) == 256 * 32 * 256 * 16 + 256
-    # MFMA split path scratch: per-group fragments (keys 468, values 368 of 1 KiB)
-    assert b.tq_encode_split_workspace_bytes(0, 256, 32, 3, 224) == 224 * 468 * 1024
-    assert b.tq_encode_split_workspace_bytes(1, 256, 32, 3, 224) == 224 * 368 * 1024
+    # MFMA split path scratch: per-group fragments (keys 454, values 354 of 1 KiB)
+    assert b.tq_encode_split_workspace_bytes(0, 256, 32, 3, 224) == 224 * 454 * 1024
+    assert b.tq_encode_split_workspace_bytes(1, 256, 32, 3, 224) == 224 * 354 * 1024
     assert b.tq_encode_split_workspace_bytes(0, 256, 32, 5, 224) == 0      # shape without the MFMA path
     assert b.tq_encode_split_workspace_bytes(0, 128, 32, 3, 224) == 0
     assert b.tq_codebook_bytes_ex(224, 3, 224, 0, 2) == 0
