@@ -39,6 +39,21 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _check_symbols(lib: str) -> None:
+    """Refuse a library that leaves one of its own symbols undefined.
+
+    The host pass can skip a kernel template's launch stub without a
+    diagnostic; the shared link then succeeds and the load fails later.
+    """
+    r = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        return                      # no nm: nothing to check with
+    own = [line.split()[-1] for line in r.stdout.splitlines() if line.split()[-1].startswith("_ZN2tq")]
+    if own:
+        os.remove(lib)
+        raise RuntimeError("libtq.so leaves its own symbols undefined:\n  " + "\n  ".join(own))
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
@@ -48,6 +63,7 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    _check_symbols(tmp)
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
