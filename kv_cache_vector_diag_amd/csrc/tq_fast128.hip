@@ -532,6 +532,7 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
         continue;
       }
       float wv[16];
+      uint32_t macc2[2] = {0u, 0u};               // keys with three thresholds: magnitude index bits
 #pragma unroll
       for (int r = 15; r >= 0; --r) {
         const float uu = u[M][r];                 // -u
@@ -539,9 +540,18 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
         // +n where u > 0, -n elsewhere: w' = -w = -u + (+-n) c_mag
         const float nsg = __uint_as_float((~__float_as_uint(uu) & 0x80000000u) | nbits);
         float mag = cpos[0];
-        if (NT > 0) mag = thr_first(tacc[0], uu, tn[0], cpos[0], cpos[NT > 0 ? 1 : 0]);
+        if constexpr (KEY && NT == 3) {
+          // three thresholds: the magnitude index by binary search (the same
+          // |u| > tn compares), its bits shifted into words, and the centroid
+          // chosen pairwise: 8 instructions instead of 3 x 3
+          const uint64_t m1 = thr_bit(macc2[1], uu, tn[1]);
+          const uint64_t m0 = thr_bit(macc2[0], uu, sel_mask(m1, tn[2], tn[0]));
+          mag = sel_mask(m0, sel_mask(m1, cpos[3], cpos[1]), sel_mask(m1, cpos[2], cpos[0]));
+        } else {
+          if (NT > 0) mag = thr_first(tacc[0], uu, tn[0], cpos[0], cpos[NT > 0 ? 1 : 0]);
 #pragma unroll
-        for (int t = 1; t < NT; ++t) thr_step(tacc[t], mag, uu, tn[t], cpos[t + 1]);
+          for (int t = 1; t < NT; ++t) thr_step(tacc[t], mag, uu, tn[t], cpos[t + 1]);
+        }
         if (KEY) {
           // w' = -(u - n c[idx]) with c[idx] = +-mag: fma(+-n, mag, -u), +n on the positive half
           float w = fmaf(nsg, mag, uu);
@@ -553,6 +563,10 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
       pw[M] = pacc;
 #pragma unroll
       for (int t = 0; t < NT; ++t) tw[t][M] = tacc[t];
+      if constexpr (KEY && NT == 3) {
+        mw[0][M] = macc2[0];
+        mw[1][M] = macc2[1];
+      }
       if constexpr (KEY) {
         if (M > 0) qjl_slice(M - 1);
         // B operand of projection chunk c = 2M + p: element e = register 8p + e
@@ -609,7 +623,7 @@ __device__ __forceinline__ void encode128_body(const Enc128Args& a, int64_t bid)
 #pragma unroll
       for (int p = 0; p < K - 1; ++p) {
         uint32_t cb = 0;
-        if constexpr (!KEY && KB <= 3) {
+        if constexpr ((!KEY && KB <= 3) || (KEY && NT == 3)) {
           cb = mw[p][M];                   // bit p of cnt from the binary search
         } else {
           // bit p of cnt = XOR of the thermometer bits [cnt >= j] for j a multiple of 2^p
