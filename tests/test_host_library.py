@@ -195,3 +195,26 @@ def test_gram_calls_validate_before_touching_the_gpu():
     assert lib.tq_gram_scores(128, 4, 32, None, None, None, 0, 2, 10, 4, 0.0, None, None) == 0
     assert lib.tq_gram_scores(128, 4, 32, None, None, None, 1, 2, 10, 4, 0.0, None, None) == -8
     assert "InvalidCodebook" in lib.tq_status_string(-15).decode()
+
+
+def test_build_refuses_undefined_own_symbols(tmp_path):
+    """The build's last check: a shared library that leaves one of the
+    library's own (tq::) symbols undefined is refused and removed, as when the
+    host pass drops a kernel's launch stub; one without such a symbol passes."""
+    import shutil
+    import subprocess
+    from kv_cache_vector_diag_amd import build_lib
+    if shutil.which("g++") is None or shutil.which("nm") is None:
+        pytest.skip("needs g++ and nm")
+    bad_src = tmp_path / "bad.cpp"
+    bad_src.write_text("namespace tq { void missing_stub(); }\nextern \"C\" void entry() { tq::missing_stub(); }\n")
+    good_src = tmp_path / "good.cpp"
+    good_src.write_text("namespace tq { void stub() {} }\nextern \"C\" void entry() { tq::stub(); }\n")
+    bad, good = tmp_path / "libbad.so", tmp_path / "libgood.so"
+    for src, lib in ((bad_src, bad), (good_src, good)):
+        subprocess.run(["g++", "-shared", "-fPIC", "-o", str(lib), str(src)], check=True)
+    build_lib._check_symbols(str(good))
+    assert good.exists()
+    with pytest.raises(RuntimeError, match="_ZN2tq12missing_stubEv"):
+        build_lib._check_symbols(str(bad))
+    assert not bad.exists()
