@@ -784,8 +784,9 @@ def bench_decode(args, torch, b):
 def bench_c1(args, torch, b):
     """Single head: 1024 fp32 N(0,1) keys and values (seed 42), head_dim 128,
     keys b=3 (128 projections), values 3 bits, one fp32 query.  One step =
-    encode K, encode V, score the query, decode V: a latency-bound shape (four
-    launches of a few workgroups), timed as a HIP graph replay and eagerly."""
+    encode K and V (one launch, tq_encode_kv), score the query, decode V: a
+    latency-bound shape (three launches of a few workgroups), timed as a HIP
+    graph replay and eagerly."""
     from kv_cache_vector_diag_amd import inputs
     dev = "cuda:0"
     d, N, seed = 128, 1024, 42
@@ -805,22 +806,19 @@ def bench_c1(args, torch, b):
     def step(i, ev=None):
         if ev:
             ev[0].record()
-        b.tq_encode_keys(kcb, 1, K, d, 3, 128, rec=krec, status=status)
+        b.tq_encode_kv(kcb, 1, vcb, 1, K, V, d, 3, 3, 128, krec=krec, vrec=vrec, status=status)
         if ev:
             ev[1].record()
-        b.tq_encode_values(vcb, 1, V, d, 3, rec=vrec, status=status)
-        if ev:
-            ev[2].record()
         b.tq_scores(kcb, 1, krec.view(1, 1, N, kw), q, d, 3, 128, out=scores, status=status)
         if ev:
-            ev[3].record()
+            ev[2].record()
         b.tq_decode_values(vcb, 1, vrec, d, 3, out=dec, status=status)
         if ev:
-            ev[4].record()
+            ev[3].record()
 
     for i in range(args.warmup):
         step(i)
-    ms_eager, segs, whole = _run_timed(torch, step, args.steps, 4)
+    ms_eager, segs, whole = _run_timed(torch, step, args.steps, 3)
     assert int(status.item()) == 0
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -842,14 +840,14 @@ def bench_c1(args, torch, b):
     ms_step, (g_l,), _ = _run_timed(torch, replay, args.steps, 1)
     assert int(status.item()) == 0
     gs = _stat(g_l)
-    names = ["encode_keys", "encode_values", "score", "decode_values"]
+    names = ["encode_kv", "score", "decode_values"]
     return {"metric": "single-head step latency (encode K + V, score, decode V)", "value": gs["median"] * 1e3,
             "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
             "ms_per_step_median": gs["median"], "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": "single head: 1024 tokens, d=128, fp32 N(0,1) K and V (seed 42), K b=3 "
                                    "(128 projections), V 3-bit, one fp32 query",
-                       "launch": "HIP graph per step (value: median replay, device events)"},
+                       "launch": "HIP graph per step: tq_encode_kv (K and V in one launch), score, decode (value: median replay, device events)"},
             "step_us_mean": gs["mean"] * 1e3, "step_us_eager_median": statistics.median(whole) * 1e3,
             "ms_per_step_eager": ms_eager,
             "kernels_us_median_eager": {n: statistics.median(v) * 1e3 for n, v in zip(names, segs)},

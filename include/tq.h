@@ -156,6 +156,21 @@ int tq_encode_values(int head_dim, int bits,
                      int64_t sx_g, int64_t sx_n,
                      void* rec, int32_t* status, void* stream);
 
+/* Keys and values of the same tokens in one call: tq_encode_keys on k into
+ * krec and tq_encode_values on v into vrec (README "Architecture": keys take
+ * the MSE stage and the QJL residual, values the MSE stage only), with the
+ * same group count, token count, strides and input dtype for k and v; each
+ * side has its own codebooks.  Records are bit for bit those of the two
+ * calls.  With turbo3 keys, 2- or 3-bit values, head_dim 128 and f32 or bf16
+ * inputs the two encodes share one launch (workgroups take key or value
+ * ranges); other shapes run the two encodes one after the other.  Errors as
+ * for the two calls, checked for both before anything is enqueued. */
+int tq_encode_kv(int head_dim, int k_bits, int v_bits, int projections,
+                 const void* kcbs, int64_t n_kcb, const void* vcbs, int64_t n_vcb,
+                 const void* k, const void* v, int x_dtype, int64_t G, int64_t N,
+                 int64_t sx_g, int64_t sx_n,
+                 void* krec, void* vrec, int32_t* status, void* stream);
+
 /* Decode value records [G][N] -> out [G][N][head_dim] float32:
  * x^ = (n/head_dim) * D (H c[idx])  (bitpolar decode_values). */
 int tq_decode_values(int head_dim, int bits,

@@ -25,7 +25,7 @@ STATUS_BAD_BLOB = 2
 STATUS_BAD_CHANNEL = 4
 
 EXPORTS = ["tq_codebook_bytes", "tq_record_bytes", "tq_make_codebook", "tq_encode_keys",
-           "tq_encode_values", "tq_decode_values", "tq_scores", "tq_attend_workspace_bytes",
+           "tq_encode_values", "tq_encode_kv", "tq_decode_values", "tq_scores", "tq_attend_workspace_bytes",
            "tq_attend", "tq_rotate", "tq_memory_stats", "tq_status_string", "tq_codebook_bytes_ex",
            "tq_record_bytes_ex", "tq_make_codebook_ex", "tq_outlier_workspace_bytes", "tq_outlier_channels",
            "tq_encode_split", "tq_scores_split", "tq_decode_values_split", "tq_encode_split_workspace_bytes",
@@ -60,6 +60,9 @@ def load() -> ctypes.CDLL:
                                    c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
         "tq_encode_values": (c_int, [c_int, c_int, c_void_p, c_int64, c_void_p, c_int, c_int64, c_int64,
                                      c_int64, c_int64, c_void_p, c_void_p, c_void_p]),
+        "tq_encode_kv": (c_int, [c_int, c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_void_p,
+                                 c_void_p, c_int, c_int64, c_int64, c_int64, c_int64, c_void_p, c_void_p, c_void_p,
+                                 c_void_p]),
         "tq_decode_values": (c_int, [c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_void_p,
                                      c_void_p, c_void_p]),
         "tq_scores": (c_int, [c_int, c_int, c_int, c_void_p, c_int64, c_void_p, c_int64, c_int64, c_int64,
@@ -338,6 +341,38 @@ def tq_encode_keys(cbs, n_cb, x, head_dim, bits, projections, rec=None, status=N
                                       _dtype_code(x), G, N, sg, sn, _ptr(rec), _ptr(status), _stream(x))
     _check(rc, "tq_encode_keys")
     return rec
+
+
+def tq_encode_kv(kcbs, n_kcb, vcbs, n_vcb, k, v, head_dim, k_bits, v_bits, projections, krec=None, vrec=None,
+                 status=None):
+    """Keys k and values v of the same tokens ([G][N][head_dim] each, same dtype
+    and strides) -> (key records, value records), as tq_encode_keys and
+    tq_encode_values give them; one launch where the library can share it."""
+    import torch
+    G, N, sg, sn = _groups(k, head_dim)
+    dev = k.device
+    _tensor(v, "v", dev)
+    if tuple(v.shape) != tuple(k.shape) or v.dtype != k.dtype or v.stride() != k.stride():
+        raise ValueError(f"v must match k in shape, dtype and strides (k {tuple(k.shape)} {k.dtype} {k.stride()}, "
+                         f"v {tuple(v.shape)} {v.dtype} {v.stride()})")
+    kw = _words(tq_record_bytes(head_dim, k_bits, projections, ROLE_KEY), "key records")
+    vw = _words(tq_record_bytes(head_dim, v_bits, 0, ROLE_VALUE), "value records")
+    _codebooks(kcbs, "kcbs", dev, n_kcb, tq_codebook_bytes(head_dim, k_bits, projections, ROLE_KEY))
+    _codebooks(vcbs, "vcbs", dev, n_vcb, tq_codebook_bytes(head_dim, v_bits, 0, ROLE_VALUE))
+    if krec is not None:
+        _shaped(krec, "krec", dev, (G, N, kw), _i32())
+    if vrec is not None:
+        _shaped(vrec, "vrec", dev, (G, N, vw), _i32())
+    _status(status, dev)
+    _on_gpu(dev)
+    if krec is None:
+        krec = torch.empty((G, N, kw), dtype=torch.int32, device=dev)
+    if vrec is None:
+        vrec = torch.empty((G, N, vw), dtype=torch.int32, device=dev)
+    rc = load().tq_encode_kv(head_dim, k_bits, v_bits, projections, _ptr(kcbs), n_kcb, _ptr(vcbs), n_vcb, _ptr(k),
+                             _ptr(v), _dtype_code(k), G, N, sg, sn, _ptr(krec), _ptr(vrec), _ptr(status), _stream(k))
+    _check(rc, "tq_encode_kv")
+    return krec, vrec
 
 
 def tq_encode_values(cbs, n_cb, x, head_dim, bits, rec=None, status=None, rotation=ROT_HADAMARD):

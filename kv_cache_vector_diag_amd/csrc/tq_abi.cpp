@@ -119,6 +119,31 @@ int tq_decode_values_ex(int head_dim, int bits, int rotation, const void* cbs, i
                                static_cast<hipStream_t>(stream));
 }
 
+int tq_encode_kv(int head_dim, int k_bits, int v_bits, int projections, const void* kcbs, int64_t n_kcb,
+                 const void* vcbs, int64_t n_vcb, const void* k, const void* v, int x_dtype, int64_t G, int64_t N,
+                 int64_t sx_g, int64_t sx_n, void* krec, void* vrec, int32_t* status, void* stream) {
+  Layout K, V;
+  int rc = make_layout(head_dim, k_bits, projections, TQ_ROLE_KEY, &K, kRotHadamard);
+  if (rc) return rc;
+  rc = make_layout(head_dim, v_bits, 0, TQ_ROLE_VALUE, &V, kRotHadamard);
+  if (rc) return rc;
+  rc = check_input(K, kcbs, n_kcb, k, x_dtype, G, N, sx_g, sx_n);
+  if (rc || G * N == 0) return rc;
+  rc = check_input(V, vcbs, n_vcb, v, x_dtype, G, N, sx_g, sx_n);
+  if (rc) return rc;
+  if (!krec || !vrec) return TQ_ERR_NULL;
+  if (fast128_encode_supported(K, x_dtype, k, sx_g, sx_n, N) && fast128_encode_supported(V, x_dtype, v, sx_g, sx_n, N)) {
+    rc = launch_encode_pair_fast128(K, V, kcbs, n_kcb, vcbs, n_vcb, k, v, x_dtype, G, N, sx_g, sx_n,
+                                    static_cast<uint32_t*>(krec), static_cast<uint32_t*>(vrec), status,
+                                    static_cast<hipStream_t>(stream));
+    if (rc != 1) return rc;
+  }
+  // other shapes: the two encodes one after the other
+  rc = tq_encode_keys(head_dim, k_bits, projections, kcbs, n_kcb, k, x_dtype, G, N, sx_g, sx_n, krec, status, stream);
+  if (rc) return rc;
+  return tq_encode_values(head_dim, v_bits, vcbs, n_vcb, v, x_dtype, G, N, sx_g, sx_n, vrec, status, stream);
+}
+
 int tq_scores(int head_dim, int bits, int projections, const void* cbs, int64_t n_cb, const void* krec,
               int64_t B, int64_t H_kv, int64_t T, const void* q, int q_dtype, int64_t H_q, float scale,
               float* scores, int32_t* status, void* stream) {

@@ -36,6 +36,15 @@ int launch_append_fast128(const Layout& K, const Layout& V, const void* kcbs, in
                           int64_t sx_n, uint32_t* kpool, uint32_t* vpool, int32_t* status, hipStream_t s,
                           const PagedOut& po);
 
+// Keys and values of the same tokens in one launch (contiguous records): turbo3
+// keys (2 planes) with 2- or 3-bit values, Walsh-Hadamard, f32 or bf16 inputs,
+// both sides passing fast128_encode_supported.  Returns 1 (nothing launched)
+// for other shapes.
+int launch_encode_pair_fast128(const Layout& K, const Layout& V, const void* kcbs, int64_t n_kcb, const void* vcbs,
+                               int64_t n_vcb, const void* k, const void* v, int dtype, int64_t G, int64_t N,
+                               int64_t sx_g, int64_t sx_n, uint32_t* krec, uint32_t* vrec, int32_t* status,
+                               hipStream_t s);
+
 // Scores with the int8-MFMA kernel: head_dim 128, 128 projections, key bits
 // 2..4, 1, 2 or 4 query heads per kv head, 8-byte aligned records, and a
 // group's records and scores each under 2^30 bytes (32-bit buffer offsets).

@@ -717,15 +717,15 @@ __global__ __launch_bounds__((64 * waves_for<K, KEY, DT, HAAR, PAD>())) void enc
 // Keys and values of an append in one launch (paged output): the first
 // ka.G * ka.blocks_per_group workgroups encode the keys, the rest the values.
 // Both roles run the keys' wave count, and the LDS is the keys' (the larger).
-template <int KK, int KV, int DT>
+template <int KK, int KV, int DT, bool PAGED = true>
 __global__ __launch_bounds__((64 * waves_for<KK, true, DT, false>())) void encode128_pair_kernel(Enc128Args ka,
                                                                                                  Enc128Args va) {
   constexpr int W = waves_for<KK, true, DT, false>();
   const int64_t nk = ka.G * ka.blocks_per_group;
   if ((int64_t)blockIdx.x < nk)
-    encode128_body<KK, true, DT, false, true, W>(ka, blockIdx.x);
+    encode128_body<KK, true, DT, false, PAGED, W>(ka, blockIdx.x);
   else
-    encode128_body<KV, false, DT, false, true, W>(va, (int64_t)blockIdx.x - nk);
+    encode128_body<KV, false, DT, false, PAGED, W>(va, (int64_t)blockIdx.x - nk);
 }
 
 // ~256 workgroups (one per CU) in total, never more tiles than the group
@@ -819,7 +819,7 @@ Enc128Args make_args(const Layout& L, const void* cbs, int64_t n_cb, const void*
   return a;
 }
 
-template <int KK, int KV, int DT>
+template <int KK, int KV, int DT, bool PAGED = true>
 int launch_pair(Enc128Args ka, Enc128Args va, hipStream_t s) {
   constexpr int W = waves_for<KK, true, DT, false>();
   split_tiles(ka, W);
@@ -827,13 +827,14 @@ int launch_pair(Enc128Args ka, Enc128Args va, hipStream_t s) {
   const size_t lds = enc_lds_bytes<true, false>();
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_pair_kernel<KK, KV, DT>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&encode128_pair_kernel<KK, KV, DT, PAGED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
       return -10;
     attr_set = true;
   }
   const int64_t blocks = ka.G * ka.blocks_per_group + va.G * va.blocks_per_group;
-  hipLaunchKernelGGL((encode128_pair_kernel<KK, KV, DT>), dim3((unsigned)blocks), dim3(64 * W), lds, s, ka, va);
+  hipLaunchKernelGGL((encode128_pair_kernel<KK, KV, DT, PAGED>), dim3((unsigned)blocks), dim3(64 * W), lds, s, ka,
+                     va);
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
@@ -861,6 +862,23 @@ int launch_append_fast128(const Layout& K, const Layout& V, const void* kcbs, in
   if (dtype == TQ_BF16 && K.k == 1) return launch_pair_v<1, 1>(ka, va, V.k, s);
   if (dtype == TQ_BF16 && K.k == 2) return launch_pair_v<2, 1>(ka, va, V.k, s);
   if (dtype == TQ_F16 && K.k == 1) return launch_pair_v<1, 2>(ka, va, V.k, s);
+  return 1;
+}
+
+int launch_encode_pair_fast128(const Layout& K, const Layout& V, const void* kcbs, int64_t n_kcb, const void* vcbs,
+                               int64_t n_vcb, const void* k, const void* v, int dtype, int64_t G, int64_t N,
+                               int64_t sx_g, int64_t sx_n, uint32_t* krec, uint32_t* vrec, int32_t* status,
+                               hipStream_t s) {
+  // head_dim 128 only: the padded bodies of smaller head dims are not paired
+  if (K.d != kD || V.d != kD || K.rotation != kRotHadamard || V.rotation != kRotHadamard || K.k != 2 || V.k < 2 ||
+      V.k > 3)
+    return 1;
+  const Enc128Args ka = make_args(K, kcbs, n_kcb, k, G, N, sx_g, sx_n, krec, status, nullptr);
+  const Enc128Args va = make_args(V, vcbs, n_vcb, v, G, N, sx_g, sx_n, vrec, status, nullptr);
+  // turbo3 keys with 2- or 3-bit values, 32-bit or bfloat16 inputs: both
+  // encodes in one launch, each workgroup taking a key or a value range
+  if (dtype == TQ_F32) return V.k == 2 ? launch_pair<2, 2, 0, false>(ka, va, s) : launch_pair<2, 3, 0, false>(ka, va, s);
+  if (dtype == TQ_BF16) return V.k == 2 ? launch_pair<2, 2, 1, false>(ka, va, s) : launch_pair<2, 3, 1, false>(ka, va, s);
   return 1;
 }
 

@@ -13,7 +13,7 @@ import torch
 
 from kv_cache_vector_diag_amd import binding as b
 
-DEVICE_CALLS = {"tq_encode_keys", "tq_encode_values", "tq_decode_values", "tq_scores", "tq_attend", "tq_rotate",
+DEVICE_CALLS = {"tq_encode_keys", "tq_encode_values", "tq_encode_kv", "tq_decode_values", "tq_scores", "tq_attend", "tq_rotate",
                 "tq_outlier_channels", "tq_encode_split", "tq_scores_split", "tq_decode_values_split",
                 "tq_encode_keys_ex", "tq_encode_values_ex", "tq_decode_values_ex", "tq_scores_ex", "tq_attend_ex",
                 "tq_append_kv", "tq_scores_paged", "tq_gram_table", "tq_gram_encode", "tq_gram_scores"}
@@ -65,6 +65,23 @@ def test_encode_checks(lib):
     with pytest.raises(ValueError, match="on the GPU"):
         lib.tq_encode_keys(_cbs(2), 2, x, D, BITS, M, rec=torch.zeros((2, 5, KW), dtype=torch.int32),
                            status=torch.zeros(1, dtype=torch.int32))
+
+
+def test_encode_kv_checks(lib):
+    k = torch.zeros((2, 5, D), dtype=torch.bfloat16)
+    vcb = _cbs(2, b.ROLE_VALUE, 3, 0)
+    with pytest.raises(ValueError, match="v must match k"):
+        lib.tq_encode_kv(_cbs(2), 2, vcb, 2, k, torch.zeros((2, 4, D), dtype=torch.bfloat16), D, BITS, 3, M)
+    with pytest.raises(ValueError, match="v must match k"):
+        lib.tq_encode_kv(_cbs(2), 2, vcb, 2, k, torch.zeros((2, 5, D), dtype=torch.float32), D, BITS, 3, M)
+    with pytest.raises(ValueError, match="krec has shape"):
+        lib.tq_encode_kv(_cbs(2), 2, vcb, 2, k, k.clone(), D, BITS, 3, M, krec=torch.zeros((2, 5, KW + 1), dtype=torch.int32))
+    with pytest.raises(ValueError, match="vrec has shape"):
+        lib.tq_encode_kv(_cbs(2), 2, vcb, 2, k, k.clone(), D, BITS, 3, M, vrec=torch.zeros((2, 5, VW - 1), dtype=torch.int32))
+    with pytest.raises(ValueError, match="vcbs holds"):
+        lib.tq_encode_kv(_cbs(2), 2, _cbs(1, b.ROLE_VALUE, 3, 0), 2, k, k.clone(), D, BITS, 3, M)
+    with pytest.raises(ValueError, match="on the GPU"):
+        lib.tq_encode_kv(_cbs(2), 2, vcb, 2, k, k.clone(), D, BITS, 3, M)
 
 
 def test_decode_and_score_checks(lib):

@@ -1,5 +1,6 @@
 """Host-side checks of libtq (no GPU): exports, sizes, errors, and the codebook
 blob against the oracle's independent regeneration of c, t, D and S."""
+import ctypes
 import math
 import os
 import re
@@ -172,6 +173,20 @@ def test_device_calls_validate_before_touching_the_gpu():
     assert lib.tq_encode_values(128, 9, None, 1, None, 0, 1, 1, 128, 128, None, None, None) == -3
     assert lib.tq_scores(128, 3, 128, None, 1, None, 1, 3, 10, None, 0, 4, 0.0, None, None, None) == -5
     assert lib.tq_decode_values(128, 3, None, 1, None, 0, 10, None, None, None) == 0
+    # tq_encode_kv: both sides' parameters and inputs are checked before any launch
+    assert lib.tq_encode_kv(128, 3, 9, 128, None, 1, None, 1, None, None, 0, 1, 1, 128, 128, None, None, None,
+                            None) == -3
+    assert lib.tq_encode_kv(96, 3, 3, 128, None, 1, None, 1, None, None, 0, 1, 1, 96, 96, None, None, None,
+                            None) == -2
+    assert lib.tq_encode_kv(128, 3, 3, 128, None, 1, None, 1, None, None, 0, 0, 5, 128, 128, None, None, None,
+                            None) == 0
+    assert lib.tq_encode_kv(128, 3, 3, 128, None, 1, None, 1, None, None, 0, 2, 5, 128, 128, None, None, None,
+                            None) == -8
+    one = ctypes.c_void_p(16)
+    assert lib.tq_encode_kv(128, 3, 3, 128, one, 1, one, 0, one, one, 0, 2, 5, 128, 128, one, one, None,
+                            None) == -7
+    assert lib.tq_encode_kv(128, 3, 3, 128, one, 1, one, 1, one, one, 0, 2, 5, 128, 128, one, None, None,
+                            None) == -8
 
 
 def test_gram_calls_validate_before_touching_the_gpu():
