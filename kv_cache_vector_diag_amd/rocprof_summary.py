@@ -29,7 +29,7 @@ KERNELS = {
     "gram_scores_generic": "gram_scores_generic",
     "gram_encode": "gram_encode",
     "gram_table": "gram_table",
-    "encode128_pair_kernel": "append_pair",
+    "encode128_pair_kernel": "encode_pair",
     "encode128_kernel": "encode",
     "score128_kernel": "score",
     "encode_generic": "encode_generic",

@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
      "gram_scores_generic"),
     ("tq::(anonymous namespace)::gram_encode_kernel(tq::GramEncArgs)", "gram_encode"),
     ("void tq::(anonymous namespace)::encode128_pair_kernel<2, 3, 1>(tq::(anonymous namespace)::Enc128Args, "
-     "tq::(anonymous namespace)::Enc128Args)", "append_pair"),
+     "tq::(anonymous namespace)::Enc128Args)", "encode_pair"),
     ("void tq::(anonymous namespace)::encode_wide_kernel<0, true>(tq::(anonymous namespace)::WideArgs)",
      "wide_keys"),
     ("void tq::(anonymous namespace)::encode_wide_kernel<2, false>(tq::(anonymous namespace)::WideArgs)",
